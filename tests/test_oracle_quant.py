@@ -1,0 +1,284 @@
+"""Pins of the oracle's quantisers (no GPU).
+
+Definitions: paper.rainbus.top, sections "FP8 量化 (E4M3 格式)" (S = max|X| / 448,
+X_hat = [X / S]), "Per-group / Per-block 量化粒度" (1x128 groups for activations
+and gradients, 128x128 blocks for weights), "方法步骤详情" steps 4-5 (1x128 ->
+128x1 requantisation of the saved FP8 activation; fused RMSNorm).
+
+Pins: hand-derived golden groups placed at known (row, group) / block
+positions (pins the scale layout too), exact Fraction arithmetic on small
+inputs, invariants (bound, sign symmetry, power-of-two equivariance,
+permutation, independence, per-element error bound), cross-function
+identities, math.fsum and torch's rms_norm (library) for the RMSNorm.
+"""
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import exact
+import golden_io
+import oracle
+from quantized_rl_amd.synth import f32_to_bf16_bits
+
+
+def bf16(a):
+    a = np.asarray(a, np.float32)
+    out = f32_to_bf16_bits(a)
+    assert np.array_equal(oracle.bf16_bits_to_f32(out), a), "fixture value not exact in bf16"
+    return out
+
+
+def rand_f32(rng, shape, heavy=True):
+    x = rng.standard_normal(shape).astype(np.float32)
+    if heavy:
+        x *= np.exp2(rng.integers(-12, 12, size=shape)).astype(np.float32)
+    return oracle.bf16_bits_to_f32(f32_to_bf16_bits(x))  # bf16-representable
+
+
+# ---------------------------------------------------------------- golden
+
+@pytest.mark.parametrize("case", golden_io.quant_cases(), ids=lambda c: c["name"])
+def test_golden_act_group(case):
+    rng = np.random.default_rng(1)
+    x = rand_f32(rng, (3, 512))
+    x[1, 256:384] = np.array(case["x"], np.float32)  # row 1, group 2
+    q, s = oracle.quant_act_1x128(bf16(x))
+    assert s.shape == (4, 3)
+    assert s[2, 1] == np.float32(case["S"])
+    assert np.array_equal(q[1, 256:384], np.array(case["q"], np.uint8))
+
+
+@pytest.mark.parametrize("case", golden_io.quant_cases(), ids=lambda c: c["name"])
+def test_golden_weight_block(case):
+    rng = np.random.default_rng(2)
+    w = rand_f32(rng, (256, 384))
+    blk = np.zeros((128, 128), np.float32)
+    cols = (np.arange(128) * 37) % 128  # one value per row, a permutation of columns
+    blk[np.arange(128), cols] = np.array(case["x"], np.float32)
+    w[128:256, 256:384] = blk  # block (nb=1, kb=2)
+    q, s = oracle.quant_weight_128x128(bf16(w))
+    assert s.shape == (2, 3)
+    assert s[1, 2] == np.float32(case["S"])
+    qb = q[128:256, 256:384]
+    want = np.zeros((128, 128), np.uint8)
+    want[np.arange(128), cols] = np.array(case["q"], np.uint8)
+    assert np.array_equal(qb, want)
+
+
+# ---------------------------------------------------------------- exact arithmetic
+
+def test_act_matches_exact_fractions():
+    rng = np.random.default_rng(3)
+    x = rand_f32(rng, (3, 256))
+    x[0, :128] = oracle.bf16_bits_to_f32(f32_to_bf16_bits(x[0, :128] * np.float32(2.0 ** -120)))  # subnormal scale
+    x[2, 128:] = 0.0
+    x[2, 130] = -0.0
+    q, s = oracle.quant_act_1x128(bf16(x))
+    for r in range(3):
+        for g in range(2):
+            S, codes = exact.quant_group([float(v) for v in x[r, 128 * g:128 * g + 128]])
+            assert Fraction(float(s[g, r])) == S
+            assert list(q[r, 128 * g:128 * g + 128]) == codes
+
+
+def test_weight_matches_exact_fractions():
+    rng = np.random.default_rng(4)
+    w = rand_f32(rng, (128, 256))
+    q, s = oracle.quant_weight_128x128(bf16(w))
+    for kb in range(2):
+        blk = w[:, 128 * kb:128 * kb + 128]
+        amax = max(abs(Fraction(float(v))) for v in blk.ravel())
+        S = exact.rn_f32(amax / 448)
+        assert Fraction(float(s[0, kb])) == S
+        for i, j in zip(rng.integers(0, 128, 300), rng.integers(0, 128, 300)):
+            v = float(blk[i, j])
+            want = exact.e4m3_code(exact.rn_f32(Fraction(v) / S), math.copysign(1.0, v) < 0)
+            assert q[i, 128 * kb + j] == want
+
+
+# ---------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("seed", range(4))
+def test_act_invariants(seed):
+    rng = np.random.default_rng(100 + seed)
+    x = rand_f32(rng, (17, 384))
+    q, s = oracle.quant_act_1x128(bf16(x))
+    dec = oracle.e4m3_decode(q)
+    assert np.all(np.abs(dec) <= 448.0)
+    g = x.reshape(17, 3, 128)
+    amax = np.abs(g).max(axis=2)
+    # the group's largest element maps to +-448 (S is normal here)
+    arg = np.abs(g).argmax(axis=2)
+    qg = q.reshape(17, 3, 128)
+    top = np.take_along_axis(qg, arg[:, :, None], axis=2)[:, :, 0]
+    assert np.all((top & 0x7F) == 0x7E)
+    assert np.array_equal(s.T, (amax / np.float32(448)).astype(np.float32))
+    # sign symmetry
+    q2, s2 = oracle.quant_act_1x128(bf16(-x))
+    assert np.array_equal(q2, q ^ 0x80) and np.array_equal(s2, s)
+    # power-of-two equivariance (bit-exact)
+    for j in (-5, 3):
+        q3, s3 = oracle.quant_act_1x128(bf16(x * np.float32(2.0 ** j)))
+        assert np.array_equal(q3, q) and np.array_equal(s3, s * np.float32(2.0 ** j))
+    # permutation inside each group permutes the codes
+    perm = rng.permutation(128)
+    xp = g[:, :, perm].reshape(17, 384)
+    q4, s4 = oracle.quant_act_1x128(bf16(xp))
+    assert np.array_equal(q4, qg[:, :, perm].reshape(17, 384)) and np.array_equal(s4, s)
+    # rows are independent
+    q5, s5 = oracle.quant_act_1x128(bf16(x[5:6]))
+    assert np.array_equal(q5, q[5:6]) and np.array_equal(s5, s[:, 5:6])
+    # per-element error bound: |x - S q| <= S * h(x / S) * (1 + 2^-20), h = half the E4M3 spacing
+    S = np.repeat(s.T, 128, axis=1).astype(np.float64)
+    y = np.abs(x / S)
+    h = np.where(y < 2.0 ** -6, 2.0 ** -10, np.exp2(np.floor(np.log2(np.maximum(y, 2.0 ** -6))) - 4))
+    err = np.abs(x - S * dec)
+    assert np.all(err <= S * h * (1 + 2.0 ** -20))
+    assert np.all(err <= amax.repeat(128, axis=1) / 28 * (1 + 2.0 ** -20))
+
+
+def test_act_zero_groups_and_empty():
+    x = np.zeros((2, 256), np.float32)
+    x[1, :] = -0.0
+    q, s = oracle.quant_act_1x128(bf16(x))
+    assert np.all(s == 1.0)
+    assert np.all(q[0] == 0) and np.all(q[1] == 0x80)
+    q, s = oracle.quant_act_1x128(np.zeros((0, 256), np.uint16))
+    assert q.shape == (0, 256) and s.shape == (2, 0)
+    with pytest.raises(ValueError):
+        oracle.quant_act_1x128(np.zeros((2, 100), np.uint16))
+    with pytest.raises(ValueError):
+        oracle.quant_act_1x128(bf16(np.full((1, 128), np.inf, np.float32)))
+
+
+def test_weight_layout_and_cross_identity():
+    rng = np.random.default_rng(5)
+    w = np.clip(rand_f32(rng, (256, 384), heavy=False), -0.875, 0.875) * np.float32(0.5)
+    # every 1x128 group of every block holds the block's largest magnitude (+-1
+    # times the block's power of two), so the block scale equals every group
+    # scale and the codes must agree with the 1x128 quantiser; the block scales
+    # then differ by exactly the powers of two
+    for nb in range(2):
+        for kb in range(3):
+            blk = w[128 * nb:128 * nb + 128, 128 * kb:128 * kb + 128]
+            blk[np.arange(128), (np.arange(128) * 5) % 128] = np.where(np.arange(128) % 2, 1.0, -1.0)
+            blk *= np.float32(2.0 ** (3 * nb + kb))
+    q, s = oracle.quant_weight_128x128(bf16(w))
+    qa, sa = oracle.quant_act_1x128(bf16(w))
+    assert np.array_equal(q, qa)
+    for nb in range(2):
+        for kb in range(3):
+            assert np.all(sa[kb, 128 * nb:128 * nb + 128] == s[nb, kb])
+    assert s[0, 0] == np.float32(1.0) / np.float32(448.0)
+    ratios = s / s[0, 0]
+    assert np.array_equal(ratios, np.exp2(3 * np.arange(2)[:, None] + np.arange(3)[None, :]))
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def test_pairwise_sum_order():
+    # adjacent pairs first: (1 + 0) + (2^-24 + 2^-24) = 1 + 2^-23, while a
+    # left-to-right sum would lose both small terms
+    v = np.array([[1.0, 0.0, 2.0 ** -24, 2.0 ** -24]], np.float32)
+    assert oracle.pairwise_sum_f32(v)[0] == np.float32(1 + 2.0 ** -23)
+    # odd lengths carry the last element up: [a, b, c] -> (a + b) + c
+    v = np.array([[2.0 ** -24, 2.0 ** -24, 1.0]], np.float32)
+    assert oracle.pairwise_sum_f32(v)[0] == np.float32(1 + 2.0 ** -23)
+
+
+@pytest.mark.parametrize("n", [1, 5, 128, 640, 4096, 5120])
+def test_pairwise_sum_accuracy(n):
+    rng = np.random.default_rng(n)
+    v = (rng.standard_normal((3, n)) ** 2).astype(np.float32)
+    got = oracle.pairwise_sum_f32(v)
+    for r in range(3):
+        ref = math.fsum(float(a) for a in v[r])
+        assert abs(float(got[r]) - ref) <= ref * math.ceil(math.log2(max(n, 2))) * 2.0 ** -24 * 1.01
+    # zero padding to a power of two does not change the result
+    p = 1 << (n - 1).bit_length()
+    vp = np.zeros((3, p), np.float32)
+    vp[:, :n] = v
+    assert np.array_equal(oracle.pairwise_sum_f32(vp), got)
+
+
+@pytest.mark.parametrize("k", [128, 4096, 5120])
+def test_rmsnorm_against_torch_and_exact(k):
+    rng = np.random.default_rng(k)
+    x = rand_f32(rng, (4, k), heavy=False)
+    x[0, :5] *= 50
+    x = oracle.bf16_bits_to_f32(f32_to_bf16_bits(x))
+    gamma = oracle.bf16_bits_to_f32(f32_to_bf16_bits((1 + 0.05 * rng.standard_normal(k)).astype(np.float32)))
+    eps = 1e-6
+    y = oracle.rmsnorm_f32(f32_to_bf16_bits(x), f32_to_bf16_bits(gamma), eps)
+    yt = torch.nn.functional.rms_norm(torch.from_numpy(x), (k,), weight=torch.from_numpy(gamma), eps=eps).numpy()
+    assert np.allclose(y, yt, rtol=1e-6, atol=0)
+    # against exact arithmetic (row 1): relative error of a few fp32 roundings
+    ss = sum(Fraction(float(a)) ** 2 for a in x[1])
+    d = ss / k + Fraction(float(np.float32(eps)))
+    inv = 1.0 / math.sqrt(float(d))
+    ref = x[1].astype(np.float64) * inv * gamma.astype(np.float64)
+    assert np.allclose(y[1], ref, rtol=2.0 ** -20, atol=0)
+
+
+def test_rmsnorm_quant_composition_and_zero_row():
+    rng = np.random.default_rng(9)
+    x = f32_to_bf16_bits(rand_f32(rng, (3, 512), heavy=False))
+    x[2] = 0
+    g = f32_to_bf16_bits((1 + 0.05 * rng.standard_normal(512)).astype(np.float32))
+    q, s = oracle.rmsnorm_quant(x, g, 1e-6)
+    q2, s2 = oracle.quant_act_1x128_f32(oracle.rmsnorm_f32(x, g, 1e-6))
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+    assert np.all(q[2] == 0) and np.all(s[:, 2] == 1.0)
+
+
+# ---------------------------------------------------------------- requant 1x128 -> 128x1
+
+def test_requant_closed_form():
+    # codes +-1.0 (0x38 / 0xb8) with row scales 2^-(m % 4): the column values are
+    # +-1, +-1/2, +-1/4, +-1/8, so S' = fl32(1/448) and the quotients are within
+    # 2^-22 (relative) of 448, 224, 112, 56 -> codes 7e, 76, 6e, 66
+    m, k = 256, 256
+    q = np.full((m, k), 0x38, np.uint8)
+    q[:, 1::2] = 0xB8
+    s = np.tile(np.exp2(-(np.arange(m) % 4)).astype(np.float32), (k // 128, 1))
+    qt, st = oracle.requant_transpose_128x1(q, s)
+    assert qt.shape == (k, m) and st.shape == (m // 128, k)
+    assert np.all(st == np.float32(Fraction(1, 448)))
+    want = np.array([0x7E, 0x76, 0x6E, 0x66], np.uint8)[np.arange(m) % 4]
+    assert np.array_equal(qt[0::2], np.tile(want, (k // 2, 1)))
+    assert np.array_equal(qt[1::2], np.tile(want | 0x80, (k // 2, 1)))
+
+
+def test_requant_matches_exact_fractions():
+    rng = np.random.default_rng(11)
+    x = rand_f32(rng, (256, 256))
+    q, s = oracle.quant_act_1x128(bf16(x))
+    qt, st = oracle.requant_transpose_128x1(q, s)
+    for k in (0, 1, 77, 128, 200, 255):
+        for mb in range(2):
+            rows = range(128 * mb, 128 * mb + 128)
+            v = [exact.rn_f32(exact.decode(int(q[m, k])) * Fraction(float(s[k // 128, m]))) for m in rows]
+            vf = [float(a) for a in v]
+            # the sign of a zero value is that of its code
+            vf = [math.copysign(a, -1.0 if q[m, k] & 0x80 else 1.0) for a, m in zip(vf, rows)]
+            S, codes = exact.quant_group(vf)
+            assert Fraction(float(st[mb, k])) == S
+            assert list(qt[k, 128 * mb:128 * mb + 128]) == codes
+
+
+def test_requant_identity_and_equivariance():
+    rng = np.random.default_rng(12)
+    x = rand_f32(rng, (384, 256))
+    q, s = oracle.quant_act_1x128(bf16(x))
+    qt, st = oracle.requant_transpose_128x1(q, s)
+    v = (oracle.e4m3_decode(q).astype(np.float32) * np.repeat(s.T, 128, axis=1)).astype(np.float32)
+    qa, sa = oracle.quant_act_1x128_f32(np.ascontiguousarray(v.T))
+    assert np.array_equal(qt, qa) and np.array_equal(st, sa)
+    qt2, st2 = oracle.requant_transpose_128x1(q, s * np.float32(4))
+    assert np.array_equal(qt2, qt) and np.array_equal(st2, st * np.float32(4))
+    with pytest.raises(ValueError):
+        oracle.requant_transpose_128x1(q[:200], s[:, :200])

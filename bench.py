@@ -1,0 +1,193 @@
+"""Benchmark of the FP8 linear layer hot path on one MI355X.
+
+One step is one forward + backward pass of the Qwen3-8B MLP up-projection
+linear (M = 8192 tokens, K = 4096, N = 12288) through every kernel of the path:
+
+    rmsnorm_quant(X, gamma)        -> QX, SX      fused RMSNorm + 1x128 quantisation
+    quantize_weight_128x128(W)     -> QW, SW      once per weight update
+    gemm_fprop(QX, SX, QW, SW)     -> Y           FProp  (1x128)x(128x128)
+    quantize_act_1x128(dY)         -> QdY, SdY    BF16 gradient -> FP8
+    gemm_dgrad(QdY, SdY, QW, SW)   -> dX          DGrad, weight blocks transposed
+    requant_transpose_128x1(QX)    -> QXt, SXt    saved FP8 activation -> 128x1
+    requant_transpose_128x1(QdY)   -> QdYt, SdYt
+    gemm_wgrad(QdYt, SdYt, QXt, SXt) -> dW        WGrad  (1x128)x(128x1)
+
+Inputs are seeded synthetic bf16 tensors (X ~ N(0,1) with 4 outlier channels
+x50, W ~ N(0, 0.02), dY ~ N(0, 1e-3), gamma ~ N(1, 0.05)), resident in HBM
+before the timed region.  ``value`` is the step's GEMM work (3 x 2MNK FLOP)
+divided by the step time.  Per-kernel times come from HIP events recorded on
+the launch stream around every kernel of the timed steps; the ``roofline``
+object describes the slowest GEMM against the dense FP8 MFMA peak.  The
+``cpu_baseline`` runs the CPU oracle on a 256-token slice of the same step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "block-scaled FP8 GEMM TFLOP/s (FProp/DGrad/WGrad) + % of FP8 MFMA peak"
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 (E4M3) MFMA
+HBM_PEAK_GBS = 8000.0
+
+M, K, N = 8192, 4096, 12288
+EPS = 1e-6
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_work():
+    """Algorithmic FLOPs (GEMMs) or bytes (memory-bound kernels) per launch."""
+    g = 2.0 * M * N * K
+    act = lambda r, c: r * c * (2 + 1) + 4 * r * c // 128            # bf16 in, u8 + f32 scales out
+    req = lambda r, c: 2 * (r * c + 4 * r * c // 128)                # u8 + scales in, same out
+    return {
+        "rmsnorm_quant": ("GB/s", act(M, K) + 2 * K),
+        "quantize_weight_128x128": ("GB/s", N * K * 3 + 4 * N * K // (128 * 128)),
+        "gemm_fprop": ("TFLOP/s", g),
+        "quantize_act_1x128": ("GB/s", act(M, N)),
+        "gemm_dgrad": ("TFLOP/s", g),
+        "requant_x": ("GB/s", req(M, K)),
+        "requant_dy": ("GB/s", req(M, N)),
+        "gemm_wgrad": ("TFLOP/s", g),
+    }
+
+
+def cpu_baseline(d, gamma):
+    """The oracle on a 256-token slice of the step (all rows of the path)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    ms = 256
+    x, dy = d["x"][:ms], d["dy"][:ms]
+    t0 = time.perf_counter()
+    qx, sx = oracle.rmsnorm_quant(x, gamma, EPS)
+    qw, sw = oracle.quant_weight_128x128(d["w"])
+    oracle.gemm_fprop_ref(qx, sx, qw, sw)
+    qdy, sdy = oracle.quant_act_1x128(dy)
+    oracle.gemm_dgrad_ref(qdy, sdy, qw, sw)
+    qxt, sxt = oracle.requant_transpose_128x1(qx, sx)
+    qdyt, sdyt = oracle.requant_transpose_128x1(qdy, sdy)
+    oracle.gemm_wgrad_ref(qdyt, sdyt, qxt, sxt)
+    dt = time.perf_counter() - t0
+    flops = 3 * 2.0 * ms * N * K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"one step on a {ms}-token slice (M={ms}, K={K}, N={N}): rmsnorm_quant, "
+                      f"full weight quantisation, quant dY, requant x2, fp64 FProp/DGrad/WGrad; "
+                      f"{dt:.2f} s; quantisers single-threaded numpy, GEMMs numpy BLAS"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (this path is the one-GPU share; see DESIGN.md); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import quantized_rl_amd as jet
+    from quantized_rl_amd import synth
+
+    dev = torch.device("cuda:0")
+    d = synth.linear_8b_up(m=M, n=N, k=K)
+    g_host = synth.decode_8b(16)["gamma"]  # gamma ~ N(1, 0.05), [4096]
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, w, dy, gamma = bf16(d["x"]), bf16(d["w"]), bf16(d["dy"]), bf16(g_host)
+    u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+    qx, sx = torch.empty((M, K), dtype=u8, device=dev), torch.empty((K // 128, M), dtype=f32, device=dev)
+    qw, sw = torch.empty((N, K), dtype=u8, device=dev), torch.empty((N // 128, K // 128), dtype=f32, device=dev)
+    qdy, sdy = torch.empty((M, N), dtype=u8, device=dev), torch.empty((N // 128, M), dtype=f32, device=dev)
+    qxt, sxt = torch.empty((K, M), dtype=u8, device=dev), torch.empty((M // 128, K), dtype=f32, device=dev)
+    qdyt, sdyt = torch.empty((N, M), dtype=u8, device=dev), torch.empty((M // 128, N), dtype=f32, device=dev)
+    y = torch.empty((M, N), dtype=bf, device=dev)
+    dx = torch.empty((M, K), dtype=bf, device=dev)
+    dw = torch.empty((N, K), dtype=bf, device=dev)
+
+    steps = [
+        ("rmsnorm_quant", lambda: jet.rmsnorm_quant(x, gamma, EPS, qx, sx)),
+        ("quantize_weight_128x128", lambda: jet.quantize_weight_128x128(w, qw, sw)),
+        ("gemm_fprop", lambda: jet.gemm_fprop(qx, sx, qw, sw, y)),
+        ("quantize_act_1x128", lambda: jet.quantize_act_1x128(dy, qdy, sdy)),
+        ("gemm_dgrad", lambda: jet.gemm_dgrad(qdy, sdy, qw, sw, dx)),
+        ("requant_x", lambda: jet.requant_transpose_128x1(qx, sx, qxt, sxt)),
+        ("requant_dy", lambda: jet.requant_transpose_128x1(qdy, sdy, qdyt, sdyt)),
+        ("gemm_wgrad", lambda: jet.gemm_wgrad(qdyt, sdyt, qxt, sxt, dw)),
+    ]
+
+    for _ in range(args.warmup):
+        for _, fn in steps:
+            fn()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, (_, fn) in enumerate(steps):
+            fn()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {name: [] for name, _ in steps}
+    step_ms = []
+    for s in range(args.steps):
+        for i, (name, _) in enumerate(steps):
+            per[name].append(ev[s][i].elapsed_time(ev[s][i + 1]))
+        step_ms.append(ev[s][0].elapsed_time(ev[s][-1]))
+    ms_per_step = float(np.mean(step_ms))
+    work = kernel_work()
+    gemm_flops = 3 * 2.0 * M * N * K
+    value = gemm_flops / (ms_per_step * 1e-3) / 1e12
+
+    kernels = {}
+    for name, (unit, amount) in work.items():
+        avg_ms = float(np.mean(per[name]))
+        rate = amount / (avg_ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+        peak = MFMA_FP8_PEAK_TFLOPS if unit == "TFLOP/s" else HBM_PEAK_GBS
+        kernels[name] = {"avg_us": round(avg_ms * 1e3, 2), "rate": round(rate, 1), "unit": unit,
+                         "frac": round(rate / peak, 4)}
+    dom = max(("gemm_fprop", "gemm_dgrad", "gemm_wgrad"), key=lambda k: kernels[k]["avg_us"])
+    roof = {"bound": "mfma", "kernel": dom, "achieved": kernels[dom]["rate"],
+            "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(kernels[dom]["rate"] / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": "qwen3_8b_mlp_up_proj_fwd_bwd", "M": M, "K": K, "N": N,
+                   "x_quant": "rmsnorm_quant", "seed": 1},
+        "roofline": roof,
+        "kernels": kernels,
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(d, g_host)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * jetfp8.h -- C ABI of the MI355X (gfx950) FP8 linear-layer library.
+ *
+ * The operations are those of the mixed-granularity FP8 linear layer of
+ * Jet-RL ("Jet-RL: Enabling On-Policy FP8 Reinforcement Learning with Unified
+ * Training and Rollout Precision Flow", arXiv 2601.14243).  Citations name the
+ * page and its section:
+ *   [P3-FP8]   paper.rainbus.top summary, section "FP8 量化 (E4M3 格式)"
+ *              (E4M3, largest value 448, S = max|X| / 448, X_hat = [X / S]);
+ *   [P3-GRAN]  same page, section "Per-group / Per-block 量化粒度"
+ *              (1x128 groups for activations and gradients, 128x128 blocks
+ *              for weights);
+ *   [P3-LAYOUT] same page, section "GEMM 量化布局（Row-wise 与 Column-wise）"
+ *              (FProp Y = X W^T, WGrad dW = dY^T X, DGrad dX = dY W);
+ *   [P3-CORE]  same page, section "核心方法" (all three GEMMs in FP8;
+ *              FProp (1x128)x(128x128), DGrad the same, WGrad
+ *              (1x128)x(128x1));
+ *   [P3-STEPS] same page, section "方法步骤详情" (steps 1-5: quantisation
+ *              granularity, forward GEMM, FP8 activation saving, backward with
+ *              BF16 dY and the 1x128 -> 128x1 requantisation, fused RMSNorm);
+ *   [P3-NOVEL] same page, section "技术新颖性" (forward saves 1x128, backward
+ *              needs 128x1).
+ *
+ * Conventions common to every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers to contiguous row-major arrays.
+ *   bf16 values are passed as uint16_t bit patterns; FP8 values as uint8_t
+ *   OCP E4M3FN bit patterns (0x7E = 448; 0x7F/0xFF are NaN and never
+ *   produced); scales are IEEE fp32.
+ * - A 1x128-grouped tensor Q[R][C] carries scales S[C/128][R]: S[g][r] scales
+ *   elements r*C + 128*g ... r*C + 128*g + 127 ("group-major").  A 128x128
+ *   blocked weight Q[N][K] carries S[N/128][K/128].
+ * - The cast is round-to-nearest-even to the nearest E4M3 value, saturating
+ *   at +-448, sign of zero kept.  S = amax / 448 is an IEEE fp32 division;
+ *   S = 1 when amax == 0.  q = cast(fl32(x / S)).  Quantiser outputs are
+ *   bit-exact functions of their inputs.
+ * - GEMMs accumulate each 128-deep block product in fp32, multiply it by the
+ *   product of the two operands' fp32 scales for that block, add it to an fp32
+ *   accumulator, and round the result to bf16 (nearest even).
+ * - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *   enqueues work on it and returns; the caller keeps the buffers alive until
+ *   the stream has reached them.
+ * - Ownership: the caller allocates and frees every buffer.  The library never
+ *   allocates, frees or retains device memory and keeps no pointer after a call
+ *   returns.
+ * - Errors: shapes and pointers are checked on the host before anything is
+ *   enqueued; an invalid call returns a nonzero status and writes nothing.
+ *   Requirements: every pointer 16-byte aligned (except when its tensor is
+ *   empty); outputs must not overlap inputs or each other; sizes >= 0 and at
+ *   most 2^31 - 1 per dimension; the divisibility rules stated per function.
+ *   A status of JETFP8_ELAUNCH reports a HIP error from the enqueue itself.
+ * - Inputs must be finite (NaN/Inf are outside the contract; the kernels do
+ *   not hang on them, but the result is unspecified).
+ * - Identical inputs give bitwise identical outputs (no atomics, no split-K
+ *   races).  Entry points are reentrant and thread-safe.
+ */
+#ifndef JETFP8_H
+#define JETFP8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  JETFP8_OK = 0,
+  JETFP8_EINVAL = 1,       /* bad shape (negative, not a multiple of 128, too large) */
+  JETFP8_EALIGN = 2,       /* a pointer is not 16-byte aligned */
+  JETFP8_ENULL = 3,        /* a required pointer is NULL */
+  JETFP8_EALIAS = 4,       /* an output overlaps an input or another output */
+  JETFP8_EUNSUPPORTED = 5, /* valid request this build does not implement */
+  JETFP8_ELAUNCH = 6       /* HIP reported an error when enqueuing */
+};
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* jetfp8_status_string(int status);
+
+/*
+ * quantize_act_1x128 -- 1x128 per-group E4M3 quantisation of an activation or
+ * a gradient [P3-FP8], [P3-GRAN], [P3-STEPS] steps 1, 2 and 4.
+ *   x : bf16 [M][K] input.
+ *   q : u8   [M][K] output codes.
+ *   s : f32  [K/128][M] output scales (group-major).
+ * K % 128 == 0; M >= 0 (any M).  M == 0 or K == 0 is a no-op.
+ */
+int quantize_act_1x128(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s,
+                       void* stream);
+
+/*
+ * quantize_weight_128x128 -- 128x128 per-block E4M3 quantisation of a weight
+ * [P3-FP8], [P3-GRAN], [P3-STEPS] step 1.  One output object serves FProp,
+ * DGrad (read transposed, [P3-STEPS] step 4) and rollout.
+ *   w : bf16 [N][K] input (BF16 master weight, [P3-CORE]).
+ *   q : u8   [N][K] output codes.
+ *   s : f32  [N/128][K/128] output block scales.
+ * N % 128 == 0 and K % 128 == 0.
+ */
+int quantize_weight_128x128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s,
+                            void* stream);
+
+/*
+ * rmsnorm_quant -- fused RMSNorm + 1x128 quantisation ([P3-STEPS] step 5
+ * names a fused RMSNorm kernel; the formula is the standard RMSNorm in fp32):
+ *   ss  = fp32 pairwise-tree sum over the row of x*x (adjacent pairs, level by
+ *         level; equivalently the row zero-padded to a power of two);
+ *   inv = fl32(1 / fl32(sqrt(fl32(fl32(ss / K) + eps))));
+ *   y   = fl32(fl32(x * inv) * gamma);  y is then quantised as in
+ *         quantize_act_1x128, with no intermediate bf16 rounding.
+ *   x : bf16 [M][K]; gamma : bf16 [K]; eps : fp32.
+ *   q : u8 [M][K]; s : f32 [K/128][M].
+ * K % 128 == 0 and 0 < K <= 65536; M >= 0.
+ */
+int rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps,
+                  uint8_t* q, float* s, void* stream);
+
+/*
+ * requant_transpose_128x1 -- requantise a saved 1x128 FP8 tensor into 128x1
+ * groups along its rows (the token dimension) and store it transposed
+ * ([P3-STEPS] steps 3-4, [P3-NOVEL]).  Used on the saved (QX, SX) and on
+ * (QdY, SdY) to feed gemm_wgrad.
+ *   v[m][k] = fl32(decode(q[m][k]) * s[k/128][m]);
+ *   for each column k and 128-row block mb: S' = amax / 448 (1 if 0),
+ *   qt[k][m] = cast(fl32(v[m][k] / S')), st[mb][k] = S'.
+ *   q : u8 [M][K]; s : f32 [K/128][M].
+ *   qt : u8 [K][M]; st : f32 [M/128][K].
+ * M % 128 == 0 and K % 128 == 0.
+ */
+int requant_transpose_128x1(const uint8_t* q, const float* s, int64_t M, int64_t K, uint8_t* qt,
+                            float* st, void* stream);
+
+/*
+ * gemm_fprop -- forward GEMM Y = X W^T with (1x128) x (128x128) scaling
+ * ([P3-LAYOUT], [P3-CORE], [P3-STEPS] step 2):
+ *   Y[m][n] = sum_kb sx[kb][m] * sw[n/128][kb] * sum_{k in kb} qx[m][k] * qw[n][k].
+ *   qx : u8 [M][K], sx : f32 [K/128][M]   (quantize_act_1x128 / rmsnorm_quant output)
+ *   qw : u8 [N][K], sw : f32 [N/128][K/128] (quantize_weight_128x128 output)
+ *   y  : bf16 [M][N].
+ * K % 128 == 0, N % 128 == 0, M >= 0 (any M).  K == 0 writes zeros.
+ */
+int gemm_fprop(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw, int64_t M,
+               int64_t N, int64_t K, uint16_t* y, void* stream);
+
+/*
+ * gemm_dgrad -- input-gradient GEMM dX = dY W, same (1x128) x (128x128)
+ * configuration as FProp with the weight blocks used transposed ([P3-LAYOUT],
+ * [P3-CORE], [P3-STEPS] step 4):
+ *   dX[m][k] = sum_nb sdy[nb][m] * sw[nb][k/128] * sum_{n in nb} qdy[m][n] * qw[n][k].
+ *   qdy : u8 [M][N], sdy : f32 [N/128][M]  (quantize_act_1x128 of the bf16 dY)
+ *   qw  : u8 [N][K], sw : f32 [N/128][K/128] (the same object FProp reads)
+ *   dx  : bf16 [M][K].
+ * N % 128 == 0, K % 128 == 0, M >= 0 (any M).  N == 0 writes zeros.
+ */
+int gemm_dgrad(const uint8_t* qdy, const float* sdy, const uint8_t* qw, const float* sw, int64_t M,
+               int64_t N, int64_t K, uint16_t* dx, void* stream);
+
+/*
+ * gemm_wgrad -- weight-gradient GEMM dW = dY^T X with (1x128) x (128x1)
+ * scaling, contracting over the M tokens ([P3-LAYOUT], [P3-CORE],
+ * [P3-STEPS] step 4).  Both operands come from requant_transpose_128x1:
+ *   dW[n][k] = sum_mb sdyt[mb][n] * sxt[mb][k] * sum_{m in mb} qdyt[n][m] * qxt[k][m].
+ *   qdyt : u8 [N][M], sdyt : f32 [M/128][N]
+ *   qxt  : u8 [K][M], sxt  : f32 [M/128][K]
+ *   dw   : bf16 [N][K].
+ * M % 128 == 0, N % 128 == 0, K % 128 == 0.  M == 0 writes zeros.
+ */
+int gemm_wgrad(const uint8_t* qdyt, const float* sdyt, const uint8_t* qxt, const float* sxt,
+               int64_t M, int64_t N, int64_t K, uint16_t* dw, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JETFP8_H */

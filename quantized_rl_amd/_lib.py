@@ -1,0 +1,194 @@
+"""ctypes binding of libjetfp8.so (argument marshalling only).
+
+Each wrapper takes torch tensors that live on a HIP device, allocates any
+missing outputs with torch (the library itself never allocates), and calls
+the C entry point of the same name on the current torch stream.  There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libjetfp8.so")
+
+_c_p = ctypes.c_void_p
+_c_i64 = ctypes.c_int64
+
+SIGNATURES = {
+    "quantize_act_1x128": [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p],
+    "quantize_weight_128x128": [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p],
+    "rmsnorm_quant": [_c_p, _c_p, _c_i64, _c_i64, ctypes.c_float, _c_p, _c_p, _c_p],
+    "requant_transpose_128x1": [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p],
+    "gemm_fprop": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
+    "gemm_dgrad": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
+    "gemm_wgrad": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
+}
+
+STATUS = {0: "JETFP8_OK", 1: "JETFP8_EINVAL", 2: "JETFP8_EALIGN", 3: "JETFP8_ENULL",
+          4: "JETFP8_EALIAS", 5: "JETFP8_EUNSUPPORTED", 6: "JETFP8_ELAUNCH"}
+
+_lib = None
+
+
+class JetFP8Error(RuntimeError):
+    def __init__(self, name, status, msg):
+        super().__init__(f"{name}: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+def lib():
+    """Load libjetfp8.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m quantized_rl_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, argt in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = argt
+            fn.restype = ctypes.c_int
+        L.jetfp8_status_string.argtypes = [ctypes.c_int]
+        L.jetfp8_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def call_raw(name, *args):
+    """Call an entry point with raw integer pointers; returns the status code."""
+    return getattr(lib(), name)(*args)
+
+
+def _check(name, status):
+    if status != 0:
+        raise JetFP8Error(name, status, lib().jetfp8_status_string(status).decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(dev):
+    torch = _torch()
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need(t, dtype, shape, what):
+    torch = _torch()
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{what}: expected contiguous {dtype} {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: expected a device tensor")
+    return t
+
+
+def _empty(shape, dtype, dev):
+    return _torch().empty(shape, dtype=dtype, device=dev)
+
+
+def quantize_act_1x128(x, q=None, s=None):
+    """x bf16 [M, K] -> (q uint8 [M, K], s float32 [K/128, M])."""
+    torch = _torch()
+    M, K = x.shape
+    _need(x, torch.bfloat16, (M, K), "x")
+    q = _empty((M, K), torch.uint8, x.device) if q is None else _need(q, torch.uint8, (M, K), "q")
+    s = _empty((K // 128, M), torch.float32, x.device) if s is None else \
+        _need(s, torch.float32, (K // 128, M), "s")
+    _check("quantize_act_1x128", lib().quantize_act_1x128(
+        x.data_ptr(), M, K, q.data_ptr(), s.data_ptr(), _stream(x.device)))
+    return q, s
+
+
+def quantize_weight_128x128(w, q=None, s=None):
+    """w bf16 [N, K] -> (q uint8 [N, K], s float32 [N/128, K/128])."""
+    torch = _torch()
+    N, K = w.shape
+    _need(w, torch.bfloat16, (N, K), "w")
+    q = _empty((N, K), torch.uint8, w.device) if q is None else _need(q, torch.uint8, (N, K), "q")
+    s = _empty((N // 128, K // 128), torch.float32, w.device) if s is None else \
+        _need(s, torch.float32, (N // 128, K // 128), "s")
+    _check("quantize_weight_128x128", lib().quantize_weight_128x128(
+        w.data_ptr(), N, K, q.data_ptr(), s.data_ptr(), _stream(w.device)))
+    return q, s
+
+
+def rmsnorm_quant(x, gamma, eps, q=None, s=None):
+    """x bf16 [M, K], gamma bf16 [K] -> (q uint8 [M, K], s float32 [K/128, M])."""
+    torch = _torch()
+    M, K = x.shape
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(gamma, torch.bfloat16, (K,), "gamma")
+    q = _empty((M, K), torch.uint8, x.device) if q is None else _need(q, torch.uint8, (M, K), "q")
+    s = _empty((K // 128, M), torch.float32, x.device) if s is None else \
+        _need(s, torch.float32, (K // 128, M), "s")
+    _check("rmsnorm_quant", lib().rmsnorm_quant(
+        x.data_ptr(), gamma.data_ptr(), M, K, float(eps), q.data_ptr(), s.data_ptr(),
+        _stream(x.device)))
+    return q, s
+
+
+def requant_transpose_128x1(q, s, qt=None, st=None):
+    """(q uint8 [M, K], s f32 [K/128, M]) -> (qt uint8 [K, M], st f32 [M/128, K])."""
+    torch = _torch()
+    M, K = q.shape
+    _need(q, torch.uint8, (M, K), "q")
+    _need(s, torch.float32, (K // 128, M), "s")
+    qt = _empty((K, M), torch.uint8, q.device) if qt is None else _need(qt, torch.uint8, (K, M), "qt")
+    st = _empty((M // 128, K), torch.float32, q.device) if st is None else \
+        _need(st, torch.float32, (M // 128, K), "st")
+    _check("requant_transpose_128x1", lib().requant_transpose_128x1(
+        q.data_ptr(), s.data_ptr(), M, K, qt.data_ptr(), st.data_ptr(), _stream(q.device)))
+    return qt, st
+
+
+def gemm_fprop(qx, sx, qw, sw, y=None):
+    """Y bf16 [M, N] = X W^T from (qx [M,K], sx [K/128,M]) and (qw [N,K], sw [N/128,K/128])."""
+    torch = _torch()
+    M, K = qx.shape
+    N = qw.shape[0]
+    _need(qx, torch.uint8, (M, K), "qx")
+    _need(sx, torch.float32, (K // 128, M), "sx")
+    _need(qw, torch.uint8, (N, K), "qw")
+    _need(sw, torch.float32, (N // 128, K // 128), "sw")
+    y = _empty((M, N), torch.bfloat16, qx.device) if y is None else _need(y, torch.bfloat16, (M, N), "y")
+    _check("gemm_fprop", lib().gemm_fprop(
+        qx.data_ptr(), sx.data_ptr(), qw.data_ptr(), sw.data_ptr(), M, N, K, y.data_ptr(),
+        _stream(qx.device)))
+    return y
+
+
+def gemm_dgrad(qdy, sdy, qw, sw, dx=None):
+    """dX bf16 [M, K] = dY W from (qdy [M,N], sdy [N/128,M]) and (qw [N,K], sw [N/128,K/128])."""
+    torch = _torch()
+    M, N = qdy.shape
+    K = qw.shape[1]
+    _need(qdy, torch.uint8, (M, N), "qdy")
+    _need(sdy, torch.float32, (N // 128, M), "sdy")
+    _need(qw, torch.uint8, (N, K), "qw")
+    _need(sw, torch.float32, (N // 128, K // 128), "sw")
+    dx = _empty((M, K), torch.bfloat16, qdy.device) if dx is None else \
+        _need(dx, torch.bfloat16, (M, K), "dx")
+    _check("gemm_dgrad", lib().gemm_dgrad(
+        qdy.data_ptr(), sdy.data_ptr(), qw.data_ptr(), sw.data_ptr(), M, N, K, dx.data_ptr(),
+        _stream(qdy.device)))
+    return dx
+
+
+def gemm_wgrad(qdyt, sdyt, qxt, sxt, dw=None):
+    """dW bf16 [N, K] = dY^T X from (qdyt [N,M], sdyt [M/128,N]) and (qxt [K,M], sxt [M/128,K])."""
+    torch = _torch()
+    N, M = qdyt.shape
+    K = qxt.shape[0]
+    _need(qdyt, torch.uint8, (N, M), "qdyt")
+    _need(sdyt, torch.float32, (M // 128, N), "sdyt")
+    _need(qxt, torch.uint8, (K, M), "qxt")
+    _need(sxt, torch.float32, (M // 128, K), "sxt")
+    dw = _empty((N, K), torch.bfloat16, qdyt.device) if dw is None else \
+        _need(dw, torch.bfloat16, (N, K), "dw")
+    _check("gemm_wgrad", lib().gemm_wgrad(
+        qdyt.data_ptr(), sdyt.data_ptr(), qxt.data_ptr(), sxt.data_ptr(), M, N, K, dw.data_ptr(),
+        _stream(qdyt.device)))
+    return dw

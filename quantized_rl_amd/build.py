@@ -1,0 +1,61 @@
+"""Build the gfx950 FP8 linear-layer library (libjetfp8.so) in-tree with hipcc.
+
+Usage: ``python -m quantized_rl_amd.build`` (or ``build()`` from Python).
+The library lands next to this file; it is always rebuilt when called.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libjetfp8.so")
+SOURCES = ["api.cpp", "quant_kernels.hip", "gemm_kernels.hip"]
+
+# -ffp-contract=off: every fp32 multiply and add of the quantisers is its own
+#   rounding step (no fused multiply-add), as their definitions state.
+# -fhip-fp32-correctly-rounded-divide-sqrt: IEEE division and square root.
+# -packed-fp32-ops disabled: no v_pk_{add,mul,fma}_f32 in generated code.
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-ffp-contract=off",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-fno-gpu-flush-denormals-to-zero",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+]
+
+
+def hipcc():
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found; the library needs ROCm's hipcc to build")
+    return exe
+
+
+def build(verbose=False):
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *FLAGS, "-x", "hip", *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = "\n".join(
+        ln for ln in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in ln
+    )
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + msgs)
+    if verbose and msgs.strip():
+        print(msgs, flush=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-q" not in sys.argv)
+    print(LIB)

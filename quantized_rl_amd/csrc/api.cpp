@@ -1,0 +1,132 @@
+// C ABI of the FP8 linear-layer library: host-side validation, then launch.
+//
+// Every argument is checked before anything is enqueued, so an invalid call
+// writes nothing.  The checks need no GPU, so they are exercised on the CPU.
+#include <stdint.h>
+
+#include <initializer_list>
+
+#include "../../include/jetfp8.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = 2147483647;  // 2^31 - 1
+
+struct Buf {
+  const void* p;
+  int64_t bytes;  // 0 for an empty tensor
+};
+
+bool dim_ok(int64_t d) { return d >= 0 && d <= kMaxDim; }
+
+int check_ptrs(std::initializer_list<Buf> ins, std::initializer_list<Buf> outs) {
+  auto check_one = [](const Buf& b) -> int {
+    if (b.bytes == 0) return JETFP8_OK;
+    if (b.p == nullptr) return JETFP8_ENULL;
+    if (reinterpret_cast<uintptr_t>(b.p) & 15u) return JETFP8_EALIGN;
+    return JETFP8_OK;
+  };
+  for (const Buf& b : ins)
+    if (int st = check_one(b)) return st;
+  for (const Buf& b : outs)
+    if (int st = check_one(b)) return st;
+  auto overlap = [](const Buf& a, const Buf& b) {
+    if (a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + static_cast<uintptr_t>(b.bytes) && b0 < a0 + static_cast<uintptr_t>(a.bytes);
+  };
+  for (const Buf* o = outs.begin(); o != outs.end(); ++o) {
+    for (const Buf& i : ins)
+      if (overlap(*o, i)) return JETFP8_EALIAS;
+    for (const Buf* o2 = o + 1; o2 != outs.end(); ++o2)
+      if (overlap(*o, *o2)) return JETFP8_EALIAS;
+  }
+  return JETFP8_OK;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? JETFP8_OK : JETFP8_ELAUNCH; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* jetfp8_status_string(int status) {
+  switch (status) {
+    case JETFP8_OK: return "ok";
+    case JETFP8_EINVAL: return "invalid shape";
+    case JETFP8_EALIGN: return "pointer not 16-byte aligned";
+    case JETFP8_ENULL: return "null pointer";
+    case JETFP8_EALIAS: return "output overlaps an input or another output";
+    case JETFP8_EUNSUPPORTED: return "unsupported";
+    case JETFP8_ELAUNCH: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int quantize_act_1x128(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s,
+                       void* stream) {
+  if (!dim_ok(M) || !dim_ok(K) || K % 128) return JETFP8_EINVAL;
+  const int64_t n = M * K;
+  if (int st = check_ptrs({{x, 2 * n}}, {{q, n}, {s, 4 * (n / 128)}})) return st;
+  return launched(jetfp8::launch_quant_act(x, M, K, q, s, as_stream(stream)));
+}
+
+int quantize_weight_128x128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s,
+                            void* stream) {
+  if (!dim_ok(N) || !dim_ok(K) || N % 128 || K % 128) return JETFP8_EINVAL;
+  const int64_t n = N * K;
+  if (int st = check_ptrs({{w, 2 * n}}, {{q, n}, {s, 4 * (n / (128 * 128))}})) return st;
+  return launched(jetfp8::launch_quant_weight(w, N, K, q, s, as_stream(stream)));
+}
+
+int rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps,
+                  uint8_t* q, float* s, void* stream) {
+  if (!dim_ok(M) || K <= 0 || K > 65536 || K % 128) return JETFP8_EINVAL;
+  const int64_t n = M * K;
+  if (int st = check_ptrs({{x, 2 * n}, {gamma, 2 * K}}, {{q, n}, {s, 4 * (n / 128)}})) return st;
+  return launched(jetfp8::launch_rmsnorm_quant(x, gamma, M, K, eps, q, s, as_stream(stream)));
+}
+
+int requant_transpose_128x1(const uint8_t* q, const float* s, int64_t M, int64_t K, uint8_t* qt,
+                            float* st, void* stream) {
+  if (!dim_ok(M) || !dim_ok(K) || M % 128 || K % 128) return JETFP8_EINVAL;
+  const int64_t n = M * K;
+  if (int e = check_ptrs({{q, n}, {s, 4 * (n / 128)}}, {{qt, n}, {st, 4 * (n / 128)}})) return e;
+  return launched(jetfp8::launch_requant(q, s, M, K, qt, st, as_stream(stream)));
+}
+
+int gemm_fprop(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw, int64_t M,
+               int64_t N, int64_t K, uint16_t* y, void* stream) {
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || N % 128 || K % 128) return JETFP8_EINVAL;
+  if (int st = check_ptrs({{qx, M * K}, {sx, 4 * (M * K / 128)}, {qw, N * K},
+                           {sw, 4 * (N * K / (128 * 128))}},
+                          {{y, 2 * M * N}}))
+    return st;
+  return launched(jetfp8::launch_gemm_fprop(qx, sx, qw, sw, M, N, K, y, as_stream(stream)));
+}
+
+int gemm_dgrad(const uint8_t* qdy, const float* sdy, const uint8_t* qw, const float* sw, int64_t M,
+               int64_t N, int64_t K, uint16_t* dx, void* stream) {
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || N % 128 || K % 128) return JETFP8_EINVAL;
+  if (int st = check_ptrs({{qdy, M * N}, {sdy, 4 * (M * N / 128)}, {qw, N * K},
+                           {sw, 4 * (N * K / (128 * 128))}},
+                          {{dx, 2 * M * K}}))
+    return st;
+  return launched(jetfp8::launch_gemm_dgrad(qdy, sdy, qw, sw, M, N, K, dx, as_stream(stream)));
+}
+
+int gemm_wgrad(const uint8_t* qdyt, const float* sdyt, const uint8_t* qxt, const float* sxt,
+               int64_t M, int64_t N, int64_t K, uint16_t* dw, void* stream) {
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || M % 128 || N % 128 || K % 128)
+    return JETFP8_EINVAL;
+  if (int st = check_ptrs({{qdyt, N * M}, {sdyt, 4 * (N * M / 128)}, {qxt, K * M},
+                           {sxt, 4 * (K * M / 128)}},
+                          {{dw, 2 * N * K}}))
+    return st;
+  return launched(jetfp8::launch_gemm_wgrad(qdyt, sdyt, qxt, sxt, M, N, K, dw, as_stream(stream)));
+}
+
+}  // extern "C"

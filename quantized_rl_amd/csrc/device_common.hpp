@@ -1,0 +1,81 @@
+// Device helpers shared by the gfx950 kernels of the FP8 linear layer.
+//
+// E4M3 here is the OCP E4M3FN format (largest finite value 448), the format
+// fixed by the Jet-RL pages (paper.rainbus.top, section "FP8 量化 (E4M3 格式)").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "exact_math.hpp"
+
+namespace jetfp8 {
+
+constexpr int kGroup = 128;        // quantisation group / block edge
+constexpr float kE4M3Max = 448.0f;
+
+// bf16 bits -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 values -> two E4M3 codes, packed into the low (hi_half = false) or
+// high 16 bits of `old`.  Rounding is nearest-even; the explicit clamp to
+// +-448 gives saturation (the hardware conversion alone turns values of 480 and
+// above into NaN).  On gfx950 v_cvt_pk_fp8_f32 of a value in [-448, 448] equals
+// the nearest-even E4M3 code, sign of zero and fp32 subnormals included; this
+// was checked exhaustively over every non-NaN fp32 bit pattern.
+__device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old, bool hi_half) {
+  a = __builtin_amdgcn_fmed3f(a, -kE4M3Max, kE4M3Max);
+  b = __builtin_amdgcn_fmed3f(b, -kE4M3Max, kE4M3Max);
+  return hi_half ? __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, true)
+                 : __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
+}
+
+// S = amax / 448 as an IEEE fp32 division (this file is compiled with
+// correctly rounded fp32 division); S = 1 for an all-zero group.
+__device__ __forceinline__ float scale_from_amax(float amax) {
+  return amax == 0.0f ? 1.0f : amax / kE4M3Max;
+}
+
+// Max over the 16 lanes of a quarter-wave (lanes 16q .. 16q+15).
+__device__ __forceinline__ float quarter_wave_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1, 16));
+  v = fmaxf(v, __shfl_xor(v, 2, 16));
+  v = fmaxf(v, __shfl_xor(v, 4, 16));
+  v = fmaxf(v, __shfl_xor(v, 8, 16));
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = quarter_wave_max(v);
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+
+// Quantise eight fp32 values of one group with inverse scale `inv_s`;
+// returns their eight codes as two dwords (element order preserved).
+__device__ __forceinline__ uint2 quant8(const float (&f)[8], double inv_s) {
+  int lo = cvt_pk_e4m3(div_by_scale(f[0], inv_s), div_by_scale(f[1], inv_s), 0, false);
+  lo = cvt_pk_e4m3(div_by_scale(f[2], inv_s), div_by_scale(f[3], inv_s), lo, true);
+  int hi = cvt_pk_e4m3(div_by_scale(f[4], inv_s), div_by_scale(f[5], inv_s), 0, false);
+  hi = cvt_pk_e4m3(div_by_scale(f[6], inv_s), div_by_scale(f[7], inv_s), hi, true);
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+// Eight bf16 values (one 16-byte load) -> fp32.
+__device__ __forceinline__ void unpack_bf16x8(uint4 v, float (&f)[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+__device__ __forceinline__ float absmax8(const float (&f)[8]) {
+  float a = fabsf(f[0]);
+#pragma unroll
+  for (int i = 1; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
+  return a;
+}
+
+}  // namespace jetfp8

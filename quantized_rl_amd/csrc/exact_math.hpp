@@ -1,0 +1,64 @@
+// Exactly rounded fp32 helpers used by the quantisation kernels.
+//
+// Host and device code: the host build exists so that the CPU test-suite can
+// check these functions exhaustively against x86's IEEE fp32 division and
+// square root (tests/test_exact_math.py).
+#pragma once
+
+#include <stdint.h>
+#include <string.h>
+
+#if defined(__HIPCC__)
+#include <hip/hip_runtime.h>
+#define JETFP8_HD __host__ __device__ __forceinline__
+#else
+#define JETFP8_HD inline
+#endif
+
+namespace jetfp8 {
+
+JETFP8_HD uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+JETFP8_HD float f32_from_bits(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+JETFP8_HD uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = f32_bits(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// fl32(x / S) computed as fl32(fl64(x * fl64(1 / S))), with inv_s = fl64(1 / S).
+//
+// Why this equals the correctly rounded fp32 quotient: inv_s and the fp64
+// product each add a relative error of at most 2^-53, so z = fl64(x * inv_s) is
+// within 2^-51.9 (relative) of x / S.  For fp32 x and S, x / S is never an fp32
+// rounding midpoint (a midpoint has an odd 25-bit significand, so S times it
+// needs more than 24 significant bits), and its relative distance to the
+// nearest midpoint is at least 2^-49 (x - S * midpoint is a nonzero multiple of
+// the last place of that product).  So z rounds to the same fp32 value as
+// x / S.  Quotients below 2^-126 may round differently in the fp32 subnormal
+// range, where the E4M3 cast gives a zero code either way.
+JETFP8_HD float div_by_scale(float x, double inv_s) { return (float)((double)x * inv_s); }
+
+// Correctly rounded fp32 square root of a non-negative finite d.
+//
+// The hardware square root is only accurate to about one ulp, so the result is
+// settled exactly: c is within one ulp of sqrt(d); sqrt(d) lies above the
+// midpoint m between c and its upper neighbour iff d > m * m, and below the
+// lower midpoint iff d < m' * m'.  Each midpoint has at most 25 significant
+// bits, so its square is exact in fp64, and d is exact in fp64: both tests are
+// exact.  (sqrt(d) is never exactly a midpoint: its square would need more
+// than 24 significant bits.)
+JETFP8_HD float sqrt_rn(float d) {
+  const float c = (float)__builtin_sqrt((double)d);
+  if (!(d > 0.0f) || !(c < 3.0e38f)) return c;
+  const float up = f32_from_bits(f32_bits(c) + 1u);
+  const float dn = f32_from_bits(f32_bits(c) - 1u);
+  const double mu = 0.5 * ((double)c + (double)up);
+  const double md = 0.5 * ((double)c + (double)dn);
+  const double dd = (double)d;
+  if (dd > mu * mu) return up;
+  if (dd < md * md) return dn;
+  return c;
+}
+
+}  // namespace jetfp8

@@ -1,0 +1,26 @@
+// Kernel launchers of the FP8 linear layer (internal; shapes already validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jetfp8 {
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s,
+                            hipStream_t stream);
+hipError_t launch_quant_weight(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s,
+                               hipStream_t stream);
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K,
+                                float eps, uint8_t* q, float* s, hipStream_t stream);
+hipError_t launch_requant(const uint8_t* q, const float* s, int64_t M, int64_t K, uint8_t* qt,
+                          float* st, hipStream_t stream);
+hipError_t launch_gemm_fprop(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
+                             int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
+hipError_t launch_gemm_dgrad(const uint8_t* qdy, const float* sdy, const uint8_t* qw,
+                             const float* sw, int64_t M, int64_t N, int64_t K, uint16_t* dx,
+                             hipStream_t stream);
+hipError_t launch_gemm_wgrad(const uint8_t* qdyt, const float* sdyt, const uint8_t* qxt,
+                             const float* sxt, int64_t M, int64_t N, int64_t K, uint16_t* dw,
+                             hipStream_t stream);
+
+}  // namespace jetfp8

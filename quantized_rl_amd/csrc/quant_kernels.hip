@@ -1,0 +1,315 @@
+// Quantisation kernels of the FP8 linear layer for gfx950 (HBM-bound).
+//
+//   quantize_act_1x128       1x128 per-group E4M3 quantisation (activations, gradients)
+//   quantize_weight_128x128  128x128 per-block E4M3 quantisation (weights)
+//   rmsnorm_quant            fused RMSNorm + 1x128 quantisation
+//   requant_transpose_128x1  saved 1x128 FP8 -> 128x1 groups along tokens, stored transposed
+//
+// Definitions: Jet-RL pages, paper.rainbus.top summary, sections
+// "FP8 量化 (E4M3 格式)", "Per-group / Per-block 量化粒度" and "方法步骤详情"
+// (steps 1-5).  Every quantiser output is a bit-exact function of its input.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace jetfp8 {
+
+// ---------------------------------------------------------------------------
+// 1x128 activation / gradient quantisation.
+//
+// A workgroup of 256 threads owns a tile of kActRows rows x one 128-column
+// group.  Each quarter-wave (16 lanes x 16 bytes = one 256-byte bf16 group)
+// handles one row at a time; every lane issues all of its loads before any
+// arithmetic so that kActRows / 16 groups are in flight per quarter-wave.
+// Scales of consecutive rows of one group are contiguous in S[g][*], so the
+// scale stores of a tile fill whole cache lines.
+constexpr int kActRows = 64;
+constexpr int kActIters = kActRows / 16;
+
+__global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t* __restrict__ x,
+                                                              int64_t M, int64_t K,
+                                                              uint8_t* __restrict__ q,
+                                                              float* __restrict__ s) {
+  const int lane16 = threadIdx.x & 15;
+  const int quarter = threadIdx.x >> 4;  // 0..15
+  const int64_t g = blockIdx.y;
+  const int64_t row0 = (int64_t)blockIdx.x * kActRows + quarter;
+
+  uint4 v[kActIters];
+#pragma unroll
+  for (int it = 0; it < kActIters; ++it) {
+    const int64_t r = row0 + 16 * it;
+    if (r < M)
+      v[it] = *reinterpret_cast<const uint4*>(x + r * K + g * kGroup + lane16 * 8);
+    else
+      v[it] = make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int it = 0; it < kActIters; ++it) {
+    const int64_t r = row0 + 16 * it;
+    float f[8];
+    unpack_bf16x8(v[it], f);
+    const float amax = quarter_wave_max(absmax8(f));
+    const float sc = scale_from_amax(amax);
+    const double inv = 1.0 / (double)sc;
+    const uint2 codes = quant8(f, inv);
+    if (r < M) {
+      *reinterpret_cast<uint2*>(q + r * K + g * kGroup + lane16 * 8) = codes;
+      if (lane16 == 0) s[g * M + r] = sc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 weight quantisation: one workgroup per block.  Each thread keeps its
+// 64 elements (eight 16-byte loads) in registers across the block-wide amax.
+__global__ __launch_bounds__(256) void quant_weight_128x128_kernel(const uint16_t* __restrict__ w,
+                                                                   int64_t N, int64_t K,
+                                                                   uint8_t* __restrict__ q,
+                                                                   float* __restrict__ s) {
+  __shared__ float wave_amax[4];
+  const int lane16 = threadIdx.x & 15;
+  const int rsub = threadIdx.x >> 4;  // 0..15
+  const int64_t kb = blockIdx.x, nb = blockIdx.y;
+  const uint16_t* base = w + (nb * kGroup) * K + kb * kGroup + lane16 * 8;
+
+  uint4 v[8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it)
+    v[it] = *reinterpret_cast<const uint4*>(base + (int64_t)(rsub + 16 * it) * K);
+  float amax = 0.0f;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    float f[8];
+    unpack_bf16x8(v[it], f);
+    amax = fmaxf(amax, absmax8(f));
+  }
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) wave_amax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wave_amax[0], wave_amax[1]), fmaxf(wave_amax[2], wave_amax[3]));
+  const float sc = scale_from_amax(amax);
+  const double inv = 1.0 / (double)sc;
+  uint8_t* qbase = q + (nb * kGroup) * K + kb * kGroup + lane16 * 8;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    float f[8];
+    unpack_bf16x8(v[it], f);
+    *reinterpret_cast<uint2*>(qbase + (int64_t)(rsub + 16 * it) * K) = quant8(f, inv);
+  }
+  if (threadIdx.x == 0) s[nb * (K / kGroup) + kb] = sc;
+}
+
+// ---------------------------------------------------------------------------
+// Fused RMSNorm + 1x128 quantisation: one workgroup (256 threads) per row.
+//
+// The sum of squares follows the pairwise tree over the row zero-padded to a
+// power of two.  Pass j covers elements [2048 j, 2048 j + 2048): thread t owns
+// the 8 contiguous elements starting at 2048 j + 8 t and sums them as a
+// balanced tree; a xor-butterfly over the wave (offsets 1..32) builds the
+// 512-element subtrees, and the four wave sums are combined as (w0+w1)+(w2+w3).
+// The per-pass sums are then combined by the same pairwise rule.  Every
+// partial is a node of the canonical tree, so the fp32 result is exactly the
+// oracle's.  Then each quarter-wave quantises 128-element groups.
+constexpr int kNormPass = 2048;
+constexpr int kNormMaxPasses = 32;  // K <= 65536
+
+__device__ __forceinline__ float tree8_sq(const float (&f)[8]) {
+  const float a = f[0] * f[0] + f[1] * f[1];  // contraction is disabled for this file
+  const float b = f[2] * f[2] + f[3] * f[3];
+  const float c = f[4] * f[4] + f[5] * f[5];
+  const float d = f[6] * f[6] + f[7] * f[7];
+  return (a + b) + (c + d);
+}
+
+__global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ gamma,
+                                                            int64_t M, int64_t K, float eps,
+                                                            uint8_t* __restrict__ q,
+                                                            float* __restrict__ s) {
+  __shared__ float part[kNormMaxPasses][4];
+  __shared__ float inv_sh;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * K;
+  const int passes = (int)((K + kNormPass - 1) / kNormPass);
+
+  for (int j = 0; j < passes; ++j) {
+    const int64_t e = (int64_t)j * kNormPass + 8 * t;
+    float v = 0.0f;
+    if (e < K) {
+      float f[8];
+      unpack_bf16x8(*reinterpret_cast<const uint4*>(xr + e), f);
+      v = tree8_sq(f);
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off, 64);
+    if (lane == 0) part[j][wave] = v;
+  }
+  __syncthreads();
+  if (t == 0) {
+    float ps[kNormMaxPasses];
+    int n = passes;
+    for (int j = 0; j < n; ++j) ps[j] = (part[j][0] + part[j][1]) + (part[j][2] + part[j][3]);
+    while (n > 1) {  // pairwise tree over the per-pass sums, odd tail carried
+      const int h = n / 2;
+      for (int j = 0; j < h; ++j) ps[j] = ps[2 * j] + ps[2 * j + 1];
+      if (n & 1) ps[h] = ps[n - 1];
+      n = h + (n & 1);
+    }
+    const float ms = ps[0] / (float)K;
+    const float d = ms + eps;
+    inv_sh = 1.0f / sqrt_rn(d);
+  }
+  __syncthreads();
+  const float inv = inv_sh;
+
+  // quantisation: quarter-wave qw handles groups qw, qw + 16, ...
+  const int lane16 = t & 15, quarter = t >> 4;
+  const int64_t ngroups = K / kGroup;
+  for (int64_t g = quarter; g < ngroups; g += 16) {
+    const int64_t e = g * kGroup + lane16 * 8;
+    float f[8], gm[8];
+    unpack_bf16x8(*reinterpret_cast<const uint4*>(xr + e), f);
+    unpack_bf16x8(*reinterpret_cast<const uint4*>(gamma + e), gm);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (f[i] * inv) * gm[i];
+    const float amax = quarter_wave_max(absmax8(f));
+    const float sc = scale_from_amax(amax);
+    const double dinv = 1.0 / (double)sc;
+    *reinterpret_cast<uint2*>(q + row * K + e) = quant8(f, dinv);
+    if (lane16 == 0) s[g * M + row] = sc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Requantisation 1x128 -> 128x1 with transposed store.
+//
+// A workgroup of 128 threads owns a 128-token x 128-feature tile: it stages the
+// 16 KB of codes and the tile's 128 input scales in LDS, then lane k reads
+// column k with the gfx950 LDS transpose read (ds_read_b64_tr_b8: within each
+// 16-lane group, lane i receives byte (i & 7) of the 8-byte rows addressed by
+// lanes 2j + (i >> 3), j = 0..7 -- i.e. one column of an 8 x 16 byte block).
+// The lane dequantises its 128 values (fp32), takes their amax, and writes its
+// 128 requantised codes as one contiguous row of Qt.
+constexpr int kRqPitch = 128 + 16;  // LDS row pitch in bytes (16-byte pad)
+
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+
+// Four E4M3 codes packed in a dword -> fp32 (exact; v_cvt_f32_fp8 with byte select).
+__device__ __forceinline__ void decode4(uint32_t w, float (&v)[4]) {
+  v[0] = __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+  v[1] = __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+  v[2] = __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+  v[3] = __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+}
+
+__device__ __forceinline__ v2i_t lds_read_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) v2i_t*)((__attribute__((address_space(3))) uint8_t*)(p)));
+}
+
+__global__ __launch_bounds__(128) void requant_transpose_kernel(const uint8_t* __restrict__ q,
+                                                                const float* __restrict__ s,
+                                                                int64_t M, int64_t K,
+                                                                uint8_t* __restrict__ qt,
+                                                                float* __restrict__ st) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kGroup * kRqPitch];
+  __shared__ float sc_in[kGroup];
+  const int t = threadIdx.x;
+  const int64_t kg = blockIdx.x;  // feature group (128 columns)
+  const int64_t mb = blockIdx.y;  // token block (128 rows)
+  const uint8_t* src = q + (mb * kGroup) * K + kg * kGroup;
+
+  // 128 rows x 8 chunks of 16 bytes = 1024 chunks, 8 per thread
+  uint4 c[8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int id = t + 128 * it, r = id >> 3, ch = id & 7;
+    c[it] = *reinterpret_cast<const uint4*>(src + (int64_t)r * K + ch * 16);
+  }
+  sc_in[t] = s[kg * M + mb * kGroup + t];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int id = t + 128 * it, r = id >> 3, ch = id & 7;
+    *reinterpret_cast<uint4*>(tile + r * kRqPitch + ch * 16) = c[it];
+  }
+  __syncthreads();
+
+  // lane -> column: 16-lane group gi covers columns 16 gi .. 16 gi + 15
+  const int li = t & 15, gi = t >> 4;
+  const int col = 16 * gi + li;
+  // address this lane supplies for row block j: row 8 j + (li >> 1), bytes 8 (li & 1) of the 16 columns
+  const uint8_t* abase = tile + (li >> 1) * kRqPitch + 16 * gi + 8 * (li & 1);
+  uint32_t w[32];  // 128 codes of column `col`, rows 0..127 in order
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const v2i_t r = lds_read_tr8(abase + 8 * j * kRqPitch);
+    w[2 * j] = (uint32_t)r.x;
+    w[2 * j + 1] = (uint32_t)r.y;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    float d[4];
+    decode4(w[i], d);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) amax = fmaxf(amax, fabsf(d[b] * sc_in[4 * i + b]));
+  }
+  const float sc = scale_from_amax(amax);
+  const double inv = 1.0 / (double)sc;
+  uint8_t* dst = qt + (kg * kGroup + col) * M + mb * kGroup;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {  // 16 codes per 16-byte store
+    uint32_t o[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int wi = 4 * i + h;
+      float v[4];
+      decode4(w[wi], v);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) v[b] = v[b] * sc_in[4 * wi + b];
+      int p = cvt_pk_e4m3(div_by_scale(v[0], inv), div_by_scale(v[1], inv), 0, false);
+      p = cvt_pk_e4m3(div_by_scale(v[2], inv), div_by_scale(v[3], inv), p, true);
+      o[h] = (uint32_t)p;
+    }
+    *reinterpret_cast<uint4*>(dst + 16 * i) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  st[mb * K + kg * kGroup + col] = sc;
+}
+
+// ---------------------------------------------------------------------------
+// launchers (shapes validated by the caller)
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s,
+                            hipStream_t stream) {
+  if (M == 0 || K == 0) return hipSuccess;
+  dim3 grid((unsigned)((M + kActRows - 1) / kActRows), (unsigned)(K / kGroup));
+  hipLaunchKernelGGL(quant_act_1x128_kernel, grid, dim3(256), 0, stream, x, M, K, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weight(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s,
+                               hipStream_t stream) {
+  if (N == 0 || K == 0) return hipSuccess;
+  dim3 grid((unsigned)(K / kGroup), (unsigned)(N / kGroup));
+  hipLaunchKernelGGL(quant_weight_128x128_kernel, grid, dim3(256), 0, stream, w, N, K, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K,
+                                float eps, uint8_t* q, float* s, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3((unsigned)M), dim3(256), 0, stream, x, gamma, M, K,
+                     eps, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_requant(const uint8_t* q, const float* s, int64_t M, int64_t K, uint8_t* qt,
+                          float* st, hipStream_t stream) {
+  if (M == 0 || K == 0) return hipSuccess;
+  dim3 grid((unsigned)(K / kGroup), (unsigned)(M / kGroup));
+  hipLaunchKernelGGL(requant_transpose_kernel, grid, dim3(128), 0, stream, q, s, M, K, qt, st);
+  return hipGetLastError();
+}
+
+}  // namespace jetfp8

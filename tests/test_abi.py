@@ -1,0 +1,99 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point,
+and its host-side validation rejects bad arguments before enqueuing anything.
+
+Pointers here are fake integers; every call either fails validation or has an
+empty output, so no kernel is ever launched.
+"""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+from quantized_rl_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "jetfp8.h")
+OK, EINVAL, EALIGN, ENULL, EALIAS = 0, 1, 2, 3, 4
+A = 1 << 20  # fake, 16-byte aligned addresses, far apart
+P = [A * (i + 1) for i in range(10)]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_seven_entry_points():
+    names = declared_functions()
+    for n in ["quantize_act_1x128", "quantize_weight_128x128", "rmsnorm_quant",
+              "requant_transpose_128x1", "gemm_fprop", "gemm_dgrad", "gemm_wgrad",
+              "jetfp8_status_string"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(jetlib):
+    for name in declared_functions():
+        assert hasattr(jetlib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings(jetlib):
+    for code in range(7):
+        assert jetlib.jetfp8_status_string(code)
+    assert jetlib.jetfp8_status_string(99) == b"unknown status"
+
+
+def c(name, *args):
+    return _lib.call_raw(name, *args)
+
+
+def test_quantize_act_validation(jetlib):
+    assert c("quantize_act_1x128", P[0], 4, 100, P[1], P[2], 0) == EINVAL
+    assert c("quantize_act_1x128", P[0], -1, 128, P[1], P[2], 0) == EINVAL
+    assert c("quantize_act_1x128", P[0], 1 << 31, 128, P[1], P[2], 0) == EINVAL
+    assert c("quantize_act_1x128", 0, 4, 128, P[1], P[2], 0) == ENULL
+    assert c("quantize_act_1x128", P[0], 4, 128, 0, P[2], 0) == ENULL
+    assert c("quantize_act_1x128", P[0] + 8, 4, 128, P[1], P[2], 0) == EALIGN
+    assert c("quantize_act_1x128", P[0], 4, 128, P[0] + 512, P[2], 0) == EALIAS  # q inside x
+    assert c("quantize_act_1x128", P[0], 4, 128, P[1], P[1] + 256, 0) == EALIAS  # s inside q
+    assert c("quantize_act_1x128", P[0], 4, 128, P[0] + 1024, P[2], 0) != EALIAS  # adjacent is fine
+    assert c("quantize_act_1x128", 0, 0, 128, 0, 0, 0) == OK  # empty: nothing to do
+
+
+def test_quantize_weight_and_rmsnorm_validation(jetlib):
+    assert c("quantize_weight_128x128", P[0], 100, 128, P[1], P[2], 0) == EINVAL
+    assert c("quantize_weight_128x128", P[0], 128, 100, P[1], P[2], 0) == EINVAL
+    assert c("quantize_weight_128x128", P[0], 128, 128, P[1], P[1] + 16384 - 16, 0) == EALIAS
+    assert c("rmsnorm_quant", P[0], P[1], 4, 0, 1e-6, P[2], P[3], 0) == EINVAL
+    assert c("rmsnorm_quant", P[0], P[1], 4, 65536 + 128, 1e-6, P[2], P[3], 0) == EINVAL
+    assert c("rmsnorm_quant", P[0], 0, 4, 128, 1e-6, P[2], P[3], 0) == ENULL
+    assert c("rmsnorm_quant", P[0], P[1], 4, 128, 1e-6, P[1], P[3], 0) == EALIAS  # q over gamma
+    assert c("rmsnorm_quant", 0, P[1], 0, 128, 1e-6, 0, 0, 0) == OK
+
+
+def test_requant_validation(jetlib):
+    assert c("requant_transpose_128x1", P[0], P[1], 200, 128, P[2], P[3], 0) == EINVAL
+    assert c("requant_transpose_128x1", P[0], P[1], 128, 200, P[2], P[3], 0) == EINVAL
+    assert c("requant_transpose_128x1", P[0], P[1], 128, 128, P[2], P[2] + 64, 0) == EALIAS
+    assert c("requant_transpose_128x1", P[0], P[1] + 4, 128, 128, P[2], P[3], 0) == EALIGN
+    assert c("requant_transpose_128x1", 0, 0, 0, 128, 0, 0, 0) == OK
+
+
+def test_gemm_validation(jetlib):
+    # fprop(qx, sx, qw, sw, M, N, K, y)
+    assert c("gemm_fprop", P[0], P[1], P[2], P[3], 16, 100, 128, P[4], 0) == EINVAL
+    assert c("gemm_fprop", P[0], P[1], P[2], P[3], 16, 128, 64, P[4], 0) == EINVAL
+    assert c("gemm_fprop", P[0], P[1], P[2], P[3], 16, 128, 128, P[0], 0) == EALIAS
+    assert c("gemm_fprop", P[0], P[1], 0, P[3], 16, 128, 128, P[4], 0) == ENULL
+    assert c("gemm_fprop", P[0], P[1], P[2], P[3] + 4, 16, 128, 128, P[4], 0) == EALIGN
+    assert c("gemm_fprop", 0, 0, P[2], P[3], 0, 128, 128, 0, 0) == OK  # M = 0
+    assert c("gemm_dgrad", P[0], P[1], P[2], P[3], 16, 128, 96, P[4], 0) == EINVAL
+    assert c("gemm_dgrad", P[0], P[1], P[2], P[3], 16, 128, 128, P[2] + 32, 0) == EALIAS
+    assert c("gemm_dgrad", 0, 0, P[2], P[3], 0, 128, 128, 0, 0) == OK
+    # wgrad(qdyt, sdyt, qxt, sxt, M, N, K, dw): M must be a multiple of 128
+    assert c("gemm_wgrad", P[0], P[1], P[2], P[3], 100, 128, 128, P[4], 0) == EINVAL
+    assert c("gemm_wgrad", P[0], P[1], P[2], P[3], 128, 128, 128, P[3], 0) == EALIAS
+    assert c("gemm_wgrad", P[0], P[1], P[2], P[3], 128, 0, 128, 0, 0) == OK  # N = 0: empty output

@@ -1,0 +1,22 @@
+"""Host checks of the device helpers that must round exactly (no GPU).
+
+The quantisation kernels compute fl32(x / S) as fl32(fl64(x * fl64(1/S))) and
+the RMSNorm square root with an exact midpoint test; both are compiled here for
+the host from the same header and compared bit for bit with x86's IEEE fp32
+division and square root.
+"""
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def test_exact_math_helpers(tmp_path):
+    exe = tmp_path / "exact_math_check"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-o", str(exe),
+                    os.path.join(HERE, "exact_math_check.cpp")], check=True)
+    res = subprocess.run([str(exe), "5"], capture_output=True, text=True, timeout=600)
+    print(res.stdout)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "0 mismatches" in res.stdout.splitlines()[-1]

@@ -1,0 +1,260 @@
+"""GPU parity of the block-scaled FP8 GEMMs against the fp64 oracle.
+
+gemm_fprop, gemm_dgrad and gemm_wgrad are called through the C ABI on seeded
+codes and scales (the same arrays go to the oracle), on end-to-end pipelines
+from bf16 inputs (each side quantises with its own quantiser), and at the
+full 8B up-projection shape on sampled outputs.  Acceptance: normwise
+||Y - bf16(Yref)|| / ||Yref|| <= 1e-3 and elementwise
+|Y - bf16(Yref)| <= ulp_bf16 + 1e-3 rms(Yref); exact-integer cases must match
+bit for bit; metamorphic relations (scale doubling, sign flip, DGrad = FProp on
+the transposed weight) hold bit for bit on the GPU alone.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_common import Guarded, bf16_dev, f32_dev, host, u8_dev
+import quantized_rl_amd as jet
+from quantized_rl_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+SMALL_CODES = np.array([0x00, 0x38, 0xB8, 0x40, 0xC0, 0x30], np.uint8)  # 0, +-1, +-2, 0.5
+
+
+def codes(rng, shape, small=False, full_range=False):
+    """FP8 operand codes.  Default: the oracle's cast of N(0, 1) * 100 draws with a
+    few x8 outlier columns (the value structure of quantised activations and
+    weights).  full_range: every finite code equally likely -- an adversarial
+    mix of magnitudes inside one 128-deep block."""
+    if small:
+        return SMALL_CODES[rng.integers(0, len(SMALL_CODES), size=shape)]
+    if full_range:
+        q = rng.integers(0, 256, size=shape).astype(np.uint8)
+        q[(q & 0x7F) == 0x7F] = 0x7E
+        return q
+    v = rng.standard_normal(shape).astype(np.float32) * np.float32(100)
+    v[..., rng.integers(0, shape[-1], size=max(1, shape[-1] // 256))] *= np.float32(8)
+    return oracle.e4m3_encode(v)
+
+
+def scales(rng, shape, pow2=False):
+    if pow2:
+        return np.exp2(rng.integers(-3, 4, size=shape)).astype(np.float32)
+    return (rng.uniform(0.5, 2.0, size=shape) * np.exp2(rng.integers(-12, -4, size=shape))).astype(np.float32)
+
+
+def check(y, ref, what, rms=None):
+    r = oracle.check_gemm(y, ref, rms=rms)
+    assert r["ok"], f"{what}: {r}"
+    return r
+
+
+# ---------------------------------------------------------------- FProp
+
+FPROP_SHAPES = [(256, 384, 512), (1, 128, 128), (16, 384, 256), (64, 256, 128), (200, 384, 512),
+                (130, 128, 1024), (257, 640, 384)]
+
+
+@pytest.mark.parametrize("m,n,k", FPROP_SHAPES)
+def test_fprop_random(m, n, k):
+    rng = np.random.default_rng(m * 7 + n + k)
+    qx, qw = codes(rng, (m, k)), codes(rng, (n, k))
+    sx, sw = scales(rng, (k // 128, m)), scales(rng, (n // 128, k // 128))
+    yg = Guarded((m, n), torch.bfloat16)
+    jet.gemm_fprop(u8_dev(qx), f32_dev(sx), u8_dev(qw), f32_dev(sw), yg.t)
+    torch.cuda.synchronize()
+    assert yg.intact()
+    check(host(yg.t), oracle.gemm_fprop_ref(qx, sx, qw, sw), f"fprop {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(256, 384, 512), (200, 256, 1024)])
+def test_fprop_full_range_codes(m, n, k):
+    """Every finite E4M3 code equally likely: the widest spread of product
+    magnitudes inside each 128-deep block."""
+    rng = np.random.default_rng(m + n + 2 * k)
+    qx, qw = codes(rng, (m, k), full_range=True), codes(rng, (n, k), full_range=True)
+    sx, sw = scales(rng, (k // 128, m)), scales(rng, (n // 128, k // 128))
+    y = host(jet.gemm_fprop(u8_dev(qx), f32_dev(sx), u8_dev(qw), f32_dev(sw)))
+    check(y, oracle.gemm_fprop_ref(qx, sx, qw, sw), f"fprop full-range {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(64, 256, 256), (33, 384, 128)])
+def test_fprop_exact_integer(m, n, k):
+    rng = np.random.default_rng(m + n + k)
+    qx, qw = codes(rng, (m, k), small=True), codes(rng, (n, k), small=True)
+    sx, sw = scales(rng, (k // 128, m), pow2=True), scales(rng, (n // 128, k // 128), pow2=True)
+    y = host(jet.gemm_fprop(u8_dev(qx), f32_dev(sx), u8_dev(qw), f32_dev(sw)))
+    want = oracle.f64_to_bf16_bits(oracle.gemm_fprop_ref(qx, sx, qw, sw))
+    assert np.array_equal(y, want)
+
+
+def test_fprop_metamorphic_and_deterministic():
+    rng = np.random.default_rng(3)
+    m, n, k = 200, 384, 512
+    qx, qw = u8_dev(codes(rng, (m, k))), u8_dev(codes(rng, (n, k)))
+    sx, sw = f32_dev(scales(rng, (k // 128, m))), f32_dev(scales(rng, (n // 128, k // 128)))
+    y = host(jet.gemm_fprop(qx, sx, qw, sw))
+    y2 = host(jet.gemm_fprop(qx, sx, qw, sw))
+    assert np.array_equal(y, y2)
+    yd = host(jet.gemm_fprop(qx, sx, qw, sw * 2)).view(np.int16)
+    assert np.array_equal(torch.from_numpy(yd).view(torch.bfloat16).float().numpy(),
+                          2 * torch.from_numpy(y.view(np.int16)).view(torch.bfloat16).float().numpy())
+    yn = host(jet.gemm_fprop(qx ^ 0x80, sx, qw, sw))
+    assert np.array_equal(yn, y ^ 0x8000)
+
+
+def test_fprop_k_zero_writes_zeros():
+    y = torch.full((5, 128), 1.0, dtype=torch.bfloat16, device="cuda:0")
+    e8 = torch.empty((5, 0), dtype=torch.uint8, device="cuda:0")
+    jet.gemm_fprop(e8, torch.empty((0, 5), device="cuda:0"), torch.empty((128, 0), dtype=torch.uint8, device="cuda:0"),
+                   torch.empty((1, 0), device="cuda:0"), y)
+    assert torch.count_nonzero(y).item() == 0
+
+
+# ---------------------------------------------------------------- DGrad
+
+DGRAD_SHAPES = [(256, 384, 512), (1, 128, 128), (16, 256, 384), (200, 512, 256), (129, 128, 640)]
+
+
+@pytest.mark.parametrize("m,n,k", DGRAD_SHAPES)
+def test_dgrad_random(m, n, k):
+    rng = np.random.default_rng(m * 5 + n + k)
+    qdy, qw = codes(rng, (m, n)), codes(rng, (n, k))
+    sdy, sw = scales(rng, (n // 128, m)), scales(rng, (n // 128, k // 128))
+    dg = Guarded((m, k), torch.bfloat16)
+    jet.gemm_dgrad(u8_dev(qdy), f32_dev(sdy), u8_dev(qw), f32_dev(sw), dg.t)
+    torch.cuda.synchronize()
+    assert dg.intact()
+    check(host(dg.t), oracle.gemm_dgrad_ref(qdy, sdy, qw, sw), f"dgrad {m}x{n}x{k}")
+
+
+def test_dgrad_exact_integer_and_equals_fprop_on_transposed_weight():
+    rng = np.random.default_rng(11)
+    m, n, k = 96, 384, 256
+    qdy, qw = codes(rng, (m, n), small=True), codes(rng, (n, k), small=True)
+    sdy, sw = scales(rng, (n // 128, m), pow2=True), scales(rng, (n // 128, k // 128), pow2=True)
+    dx = host(jet.gemm_dgrad(u8_dev(qdy), f32_dev(sdy), u8_dev(qw), f32_dev(sw)))
+    assert np.array_equal(dx, oracle.f64_to_bf16_bits(oracle.gemm_dgrad_ref(qdy, sdy, qw, sw)))
+    qdy, qw = codes(rng, (m, n)), codes(rng, (n, k))
+    sdy, sw = scales(rng, (n // 128, m)), scales(rng, (n // 128, k // 128))
+    dx = host(jet.gemm_dgrad(u8_dev(qdy), f32_dev(sdy), u8_dev(qw), f32_dev(sw)))
+    yf = host(jet.gemm_fprop(u8_dev(qdy), f32_dev(sdy), u8_dev(np.ascontiguousarray(qw.T)),
+                             f32_dev(np.ascontiguousarray(sw.T))))
+    assert np.array_equal(dx, yf)
+
+
+# ---------------------------------------------------------------- WGrad
+
+WGRAD_SHAPES = [(128, 128, 128), (256, 384, 512), (384, 256, 256), (1024, 128, 384)]
+
+
+@pytest.mark.parametrize("m,n,k", WGRAD_SHAPES)
+def test_wgrad_random(m, n, k):
+    rng = np.random.default_rng(m * 3 + n + k)
+    qdyt, qxt = codes(rng, (n, m)), codes(rng, (k, m))
+    sdyt, sxt = scales(rng, (m // 128, n)), scales(rng, (m // 128, k))
+    dg = Guarded((n, k), torch.bfloat16)
+    jet.gemm_wgrad(u8_dev(qdyt), f32_dev(sdyt), u8_dev(qxt), f32_dev(sxt), dg.t)
+    torch.cuda.synchronize()
+    assert dg.intact()
+    check(host(dg.t), oracle.gemm_wgrad_ref(qdyt, sdyt, qxt, sxt), f"wgrad {m}x{n}x{k}")
+
+
+def test_wgrad_exact_integer():
+    rng = np.random.default_rng(12)
+    m, n, k = 256, 256, 384
+    qdyt, qxt = codes(rng, (n, m), small=True), codes(rng, (k, m), small=True)
+    sdyt, sxt = scales(rng, (m // 128, n), pow2=True), scales(rng, (m // 128, k), pow2=True)
+    dw = host(jet.gemm_wgrad(u8_dev(qdyt), f32_dev(sdyt), u8_dev(qxt), f32_dev(sxt)))
+    assert np.array_equal(dw, oracle.f64_to_bf16_bits(oracle.gemm_wgrad_ref(qdyt, sdyt, qxt, sxt)))
+
+
+# ---------------------------------------------------------------- end to end
+
+def test_linear_small_end_to_end():
+    d = synth.linear_small()
+    qx, sx = jet.quantize_act_1x128(bf16_dev(d["x"]))
+    qw, sw = jet.quantize_weight_128x128(bf16_dev(d["w"]))
+    y = host(jet.gemm_fprop(qx, sx, qw, sw))
+    qxo, sxo = oracle.quant_act_1x128(d["x"])
+    qwo, swo = oracle.quant_weight_128x128(d["w"])
+    check(y, oracle.gemm_fprop_ref(qxo, sxo, qwo, swo), "linear_small fprop")
+
+
+def _sampled(y, ref_fn, rows, cols, what):
+    ref = ref_fn(rows, cols)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    return check(y[np.ix_(rows, cols)], ref, what, rms=rms)
+
+
+def test_linear_8b_up_forward_backward_sampled():
+    """Full 8B up-projection step at M=8192, K=4096, N=12288 on the GPU; the
+    oracle checks 48x48 sampled outputs of each GEMM (its operands quantised by
+    the oracle from the same bf16 inputs)."""
+    d = synth.linear_8b_up()
+    M, K = d["x"].shape
+    N = d["w"].shape[0]
+    x, w, dy = bf16_dev(d["x"]), bf16_dev(d["w"]), bf16_dev(d["dy"])
+    qx, sx = jet.quantize_act_1x128(x)
+    qw, sw = jet.quantize_weight_128x128(w)
+    y = host(jet.gemm_fprop(qx, sx, qw, sw))
+    qdy, sdy = jet.quantize_act_1x128(dy)
+    dx = host(jet.gemm_dgrad(qdy, sdy, qw, sw))
+    qxt, sxt = jet.requant_transpose_128x1(qx, sx)
+    qdyt, sdyt = jet.requant_transpose_128x1(qdy, sdy)
+    dw = host(jet.gemm_wgrad(qdyt, sdyt, qxt, sxt))
+
+    rng = np.random.default_rng(0)
+    rows_m = np.sort(rng.choice(M, 48, replace=False))
+    cols_n = np.sort(rng.choice(N, 48, replace=False))
+    cols_k = np.sort(rng.choice(K, 48, replace=False))
+
+    # FProp: rows of X (1x128 groups are per row) and the 128-row weight bands of the sampled n
+    qxo, sxo = oracle.quant_act_1x128(d["x"][rows_m])
+    bands = sorted({int(c) // 128 for c in cols_n})
+
+    def w_band_rows(cols):
+        out_q = np.zeros((len(cols), K), np.uint8)
+        out_s = np.zeros((len(cols), K // 128), np.float32)
+        for nb in bands:
+            qb, sb = oracle.quant_weight_128x128(d["w"][128 * nb:128 * nb + 128])
+            for i, c in enumerate(cols):
+                if c // 128 == nb:
+                    out_q[i] = qb[c - 128 * nb]
+                    out_s[i] = sb[0]
+        return out_q, out_s
+
+    qwr, swr = w_band_rows(cols_n)
+    ref = oracle.dequant_groups(qxo, sxo) @ (oracle.e4m3_decode(qwr) * np.repeat(swr.astype(np.float64), 128, axis=1)).T
+    check(y[np.ix_(rows_m, cols_n)], ref, "fprop 8192x12288x4096", rms=float(np.sqrt(np.mean(ref ** 2))))
+
+    # DGrad: rows of dY and the 128-column weight bands of the sampled k
+    qdyo, sdyo = oracle.quant_act_1x128(d["dy"][rows_m])
+    kbands = sorted({int(c) // 128 for c in cols_k})
+    wcols = np.zeros((N, len(cols_k)))
+    for kb in kbands:
+        qb, sb = oracle.quant_weight_128x128(np.ascontiguousarray(d["w"][:, 128 * kb:128 * kb + 128]))
+        deq = oracle.dequant_blocks(qb, sb)
+        for i, c in enumerate(cols_k):
+            if c // 128 == kb:
+                wcols[:, i] = deq[:, c - 128 * kb]
+    ref = oracle.dequant_groups(qdyo, sdyo) @ wcols
+    check(dx[np.ix_(rows_m, cols_k)], ref, "dgrad 8192x4096 (N=12288)", rms=float(np.sqrt(np.mean(ref ** 2))))
+
+    # WGrad: requantised columns n of dY and k of X over all M tokens
+    def requant_cols(src, cols):
+        out = np.zeros((len(cols), M))
+        for g in sorted({int(c) // 128 for c in cols}):
+            qg, sg = oracle.quant_act_1x128(np.ascontiguousarray(src[:, 128 * g:128 * g + 128]))
+            qt, st = oracle.requant_transpose_128x1(qg, sg)
+            deq = oracle.dequant_groups(qt, st)  # [128, M]
+            for i, c in enumerate(cols):
+                if c // 128 == g:
+                    out[i] = deq[c - 128 * g]
+        return out
+
+    ref = requant_cols(d["dy"], cols_n) @ requant_cols(d["x"], cols_k).T
+    check(dw[np.ix_(cols_n, cols_k)], ref, "wgrad 12288x4096 (M=8192)", rms=float(np.sqrt(np.mean(ref ** 2))))

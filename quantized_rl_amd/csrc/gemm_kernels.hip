@@ -27,6 +27,7 @@ namespace jetfp8 {
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));
 typedef int v2i_t __attribute__((ext_vector_type(2)));
+typedef int v4i_t __attribute__((ext_vector_type(4)));
 
 enum GemmMode { kFprop = 0, kDgrad = 1, kWgrad = 2 };
 
@@ -210,6 +211,289 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(const uint8_t* __
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile kernel: 256 x 256 output tile, 8 waves (2 x 4) of 128 x 64, two
+// waves per SIMD.  Operand tiles move global -> LDS with buffer loads that
+// write LDS directly (buffer_load_dwordx4 ... lds: each lane's 16 bytes land
+// at the wave's LDS base + 16 * lane), double-buffered: the next K-block's
+// loads are in flight while the current one is multiplied.  A workgroup reads
+// 64 KB of operands per 128-deep K-block for 16.8 MFLOP (256 FLOP per byte
+// from L2, against 128 for a 128 x 128 tile), and each wave reads 24 KB of
+// fragments from LDS for 4.2 MFLOP.  Buffer resources give 32-bit offsets and
+// the hardware range check: rows past the end of A read as zero and stores
+// past the end of C are dropped.
+//
+// LDS rows are 128 bytes (one K-block of one operand row); 16-byte chunk c of
+// row r lives at chunk position c ^ f(r), f(r) = (r & 7) ^ bit3(r) ^ bit5(r).
+// With that, the 16 rows read by one quarter-wave's ds_read_b128 hit 16
+// distinct 4-bank groups, and the 8-row blocks read by ds_read_b64_tr_b8 in two
+// quarter-waves hit distinct 2-bank pairs.
+constexpr int kLBM = 256, kLBN = 256;
+constexpr int kLThreads = 512;
+constexpr int kLStage = kLBM * kBK + kLBN * kBK;  // 64 KB per stage (A then B)
+constexpr int kGroupM = 8;                        // tile-row group of the launch order
+constexpr uint32_t kRsrcWord3 = 0x00020000u;      // raw buffer, 32-bit dwords
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ int lf(int r) { return (r & 7) ^ ((r >> 3) & 1) ^ ((r >> 5) & 1); }
+__device__ __forceinline__ int loff(int r, int c) { return r * 128 + ((c ^ lf(r)) << 4); }
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kRsrcWord3);
+}
+
+__device__ __forceinline__ void buf_to_lds16(rsrc_t r, uint8_t* lds_wave_base, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_wave_base), 16,
+                                           voff, soff, 0, 0);
+}
+
+// vmcnt(0): wait for every outstanding vector-memory load of this wave
+// (including the LDS-direct loads); expcnt and lgkmcnt left at their maxima.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// One stage of operand tiles (A then B) and its scales, as separate LDS
+// objects: the loop below is unrolled over the two stages so that every LDS
+// access names its stage statically, which lets the compiler see that the
+// fragment reads of one stage do not alias the in-flight direct loads into
+// the other (otherwise it waits for those loads before every read).
+struct LStage {
+  uint8_t ab[kLStage];
+  float sa[kLBM];
+  float sb[kLBN];
+};
+
+template <int kMode>
+struct LargeTile {
+  int t, l, w, wm, wn, lr, lk;
+  uint32_t M, N, K, row0, col0, nkb, t8, arow;
+  bool b_half;
+  rsrc_t ra, rb;
+  uint32_t va[4], vb[4];
+  const float* sa;
+  const float* sb;
+
+  // Direct loads of K-block kb into stage st: wave w fills 32 rows of each
+  // operand tile, 8 rows (1 KB) per instruction; lane l covers row l / 8 of
+  // the 8, chunk position l % 8, i.e. logical chunk (l % 8) ^ f(row).
+  __device__ __forceinline__ void issue(uint32_t kb, LStage& st) {
+    uint8_t* As = st.ab;
+    uint8_t* Bs = st.ab + kLBM * kBK;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      buf_to_lds16(ra, As + (32 * w + 8 * p) * 128, va[p], kb * kBK);
+      if (kMode == kDgrad)
+        buf_to_lds16(rb, Bs + (w >> 2) * (128 * 128) + (32 * (w & 3) + 8 * p) * 128, vb[p], kb * kBK * N);
+      else
+        buf_to_lds16(rb, Bs + (32 * w + 8 * p) * 128, vb[p], kb * kBK);
+    }
+  }
+  // scales of one K-block: threads 0..255 fetch the A-row scales, threads
+  // 256..511 the B-column scales (WGrad) -- or, for the per-block B scale of
+  // FProp / DGrad, the A-row scales again (unused); no divergent branches
+  __device__ __forceinline__ float load_scale(uint32_t kb) const {
+    return b_half ? sb[kb * N + col0 + t8] : sa[kb * M + arow];
+  }
+  __device__ __forceinline__ void store_scale(LStage& st, float x) const {
+    (t >= kLBM ? st.sb : st.sa)[t8] = x;
+  }
+
+  // Multiply the K-block held in stage st into the accumulators.
+  __device__ __forceinline__ void compute(const LStage& st, uint32_t kb, v4f_t (&acc)[8][4]) const {
+    const uint8_t* As = st.ab;
+    const uint8_t* Bs = st.ab + kLBM * kBK;
+    v8i_t bf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (kMode == kDgrad) {
+        const int col = wn * 64 + 16 * j;  // within the 256-column tile
+        const uint8_t* half = Bs + (col >> 7) * (128 * 128);
+        const int chunk = (col & 127) >> 4;
+        v2i_t part[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int n = 32 * lk + 8 * q4 + (lr >> 1);
+          part[q4] = lds_tr8(half + loff(n, chunk) + 8 * (lr & 1));
+        }
+        bf[j] = v8i_t{part[0].x, part[0].y, part[1].x, part[1].y,
+                      part[2].x, part[2].y, part[3].x, part[3].y};
+      } else {
+        const int r = wn * 64 + 16 * j + lr;
+        const uint4 x0 = *reinterpret_cast<const uint4*>(Bs + loff(r, 2 * lk));
+        const uint4 x1 = *reinterpret_cast<const uint4*>(Bs + loff(r, 2 * lk + 1));
+        bf[j] = v8i_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                      (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      }
+    }
+    float sbcol[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float sblk = 0.0f;
+    if (kMode == kWgrad) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sbcol[j] = st.sb[wn * 64 + 16 * j + lr];
+    } else {
+      const uint32_t cb = (col0 + wn * 64) / kBN;  // the wave's 64 columns lie in one 128-block
+      sblk = (kMode == kFprop) ? sb[cb * nkb + kb] : sb[kb * (N / kBN) + cb];
+    }
+
+    // Software pipeline over the 32 (row, column) sub-tiles, row-major: step q
+    // issues the MFMA of sub-tile q, then rescales the partial of sub-tile
+    // q - 2 into its accumulators, so two MFMAs separate every partial from
+    // its use; the A fragment and row scales of the next row sub-tile are read
+    // from LDS a row ahead.  Scheduling barriers pin the order.
+    auto read_a = [&](int i, v8i_t& af, float (&srow)[4]) {
+      const int r = wm * 128 + 16 * i + lr;
+      const uint4 x0 = *reinterpret_cast<const uint4*>(As + loff(r, 2 * lk));
+      const uint4 x1 = *reinterpret_cast<const uint4*>(As + loff(r, 2 * lk + 1));
+      af = v8i_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      const float4 s4 = *reinterpret_cast<const float4*>(&st.sa[wm * 128 + 16 * i + 4 * lk]);
+      srow[0] = s4.x; srow[1] = s4.y; srow[2] = s4.z; srow[3] = s4.w;
+    };
+    // row scales use three buffers: those of row sub-tile i are still read by
+    // its last two rescales after the reads for row i + 2 ... are issued
+    v8i_t af[2];
+    float srow[3][4];
+    v4f_t part[3];
+    read_a(0, af[0], srow[0]);
+#pragma unroll
+    for (int q = 0; q < 34; ++q) {
+      const int i = q >> 2, j = q & 3;
+      if (q < 32 && j == 0 && i + 1 < 8) read_a(i + 1, af[(i + 1) & 1], srow[(i + 1) % 3]);
+      if (q < 32) part[q % 3] = mfma_fp8(af[i & 1], bf[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q >= 2) {
+        const int qp = q - 2, pi = qp >> 2, pj = qp & 3;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sc = (kMode == kWgrad) ? srow[pi % 3][e] * sbcol[pj] : srow[pi % 3][e] * sblk;
+          acc[pi][pj][e] = fmaf(part[qp % 3][e], sc, acc[pi][pj][e]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
+template <int kMode>
+__global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t* __restrict__ A,
+                                                                    const float* __restrict__ sa,
+                                                                    const uint8_t* __restrict__ B,
+                                                                    const float* __restrict__ sb,
+                                                                    uint32_t M, uint32_t N, uint32_t K,
+                                                                    uint16_t* __restrict__ C) {
+  __shared__ __attribute__((aligned(16))) LStage st0;
+  __shared__ __attribute__((aligned(16))) LStage st1;
+
+  LargeTile<kMode> g;
+  g.t = threadIdx.x;
+  g.l = g.t & 63;
+  g.w = __builtin_amdgcn_readfirstlane(g.t >> 6);  // wave index, held in a scalar register
+  g.wm = g.w >> 2;                                  // wave tile: rows wm*128 .. +128,
+  g.wn = g.w & 3;                                   //            cols wn*64 .. +64
+  g.lr = g.l & 15;
+  g.lk = g.l >> 4;
+  g.M = M; g.N = N; g.K = K;
+  g.sa = sa; g.sb = sb;
+
+  // launch order: spread over the 8 XCDs so that each XCD gets one contiguous
+  // range of tiles, then walk tile-row groups of kGroupM rows column by column
+  const uint32_t ntm = (M + kLBM - 1) / kLBM, ntn = N / kLBN, total = ntm * ntn;
+  uint32_t id = blockIdx.x;
+  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+  const uint32_t per_group = kGroupM * ntn;
+  const uint32_t g0 = (id / per_group) * kGroupM;
+  const uint32_t gm = (ntm - g0) < (uint32_t)kGroupM ? (ntm - g0) : (uint32_t)kGroupM;
+  g.row0 = (g0 + (id % per_group) % gm) * kLBM;
+  g.col0 = ((id % per_group) / gm) * kLBN;
+  g.nkb = K / kBK;
+  g.t8 = (uint32_t)g.t & 255u;
+  g.arow = (g.row0 + g.t8) < M ? (g.row0 + g.t8) : (M - 1);
+  g.b_half = (kMode == kWgrad) && g.t >= kLBM;
+  g.ra = make_rsrc(A, M * K);
+  g.rb = make_rsrc(B, N * K);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = 32 * g.w + 8 * p + (g.l >> 3);
+    g.va[p] = (g.row0 + r) * K + (((g.l & 7) ^ lf(r)) << 4);
+    if (kMode == kDgrad) {
+      // B tile = W[kb*128 + rr][col0 + 128 h + ...]: two 128-column halves of
+      // 128 contraction rows; this wave fills half h = w / 4, rows 32 (w % 4) ..
+      const int rr = 32 * (g.w & 3) + 8 * p + (g.l >> 3);
+      g.vb[p] = rr * N + g.col0 + 128 * (g.w >> 2) + (((g.l & 7) ^ lf(rr)) << 4);
+    } else {
+      g.vb[p] = (g.col0 + r) * K + (((g.l & 7) ^ lf(r)) << 4);
+    }
+  }
+
+  v4f_t acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  g.store_scale(st0, g.load_scale(0));
+  g.issue(0, st0);
+  wait_vmem();
+  __syncthreads();
+
+  // Two K-blocks per trip: compute stage 0 while stage 1 loads, then the
+  // reverse.  The prefetch past the last block reloads the last block (the
+  // loop stays free of branches; nkb >= 1).
+  const uint32_t last = g.nkb - 1;
+#pragma clang loop unroll(disable)
+  for (uint32_t kb = 0; kb < g.nkb; kb += 2) {
+    {
+      const uint32_t kn = kb + 1 <= last ? kb + 1 : last;
+      const float x = g.load_scale(kn);
+      g.issue(kn, st1);
+      g.compute(st0, kb, acc);
+      g.store_scale(st1, x);
+      wait_vmem();
+      __syncthreads();
+    }
+    if (kb + 1 <= last) {
+      const uint32_t kn = kb + 2 <= last ? kb + 2 : last;
+      const float x = g.load_scale(kn);
+      g.issue(kn, st0);
+      g.compute(st1, kb + 1, acc);
+      g.store_scale(st0, x);
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  // epilogue: stage the bf16 tile in LDS with a row pitch of 512 + 16 bytes
+  // (rows 0..127 fill stage 0, rows 128..255 stage 1: 128 * 528 bytes is
+  // exactly one stage object), then write it out with 16-byte buffer stores
+  // (rows past M fall outside the buffer and are dropped)
+  constexpr int kPitch = kLBN * 2 + 16;
+  static_assert(128 * kPitch == sizeof(LStage), "epilogue staging must fill one stage exactly");
+  const rsrc_t rc = make_rsrc(C, M * N * 2u);
+  auto crow = [&](int r) -> uint8_t* {
+    return (r < 128 ? reinterpret_cast<uint8_t*>(&st0) : reinterpret_cast<uint8_t*>(&st1)) + (r & 127) * kPitch;
+  };
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = g.wm * 128 + 16 * i + 4 * g.lk + e, c = g.wn * 64 + 16 * j + g.lr;
+        *reinterpret_cast<uint16_t*>(crow(r) + 2 * c) = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const int id16 = g.t + kLThreads * p;  // 16-byte chunk id: 32 per row
+    const int r = id16 >> 5, c16 = id16 & 31;
+    const uint4 v = *reinterpret_cast<const uint4*>(crow(r) + 16 * c16);
+    const v4i_t d = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(d, rc, ((g.row0 + r) * N + g.col0 + 8 * c16) * 2u, 0, 0);
+  }
+}
+
+
 __global__ void fill_zero_u16(uint16_t* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -230,6 +514,15 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
                               hipStream_t stream) {
   if (Mr == 0 || Nc == 0) return hipSuccess;
   if (Kc == 0) return launch_zero(C, Mr * Nc, stream);
+  // the large-tile kernel works with 32-bit byte offsets
+  const bool fits32 = (Mr + kLBM) * Kc < (int64_t(1) << 31) && Nc * Kc < (int64_t(1) << 31) &&
+                      (Mr + kLBM) * Nc * 2 < (int64_t(1) << 31);
+  if (Nc % kLBN == 0 && Mr >= kLBM && fits32) {
+    const int64_t tiles = ((Mr + kLBM - 1) / kLBM) * (Nc / kLBN);
+    hipLaunchKernelGGL(gemm_fp8_large_kernel<kMode>, dim3((unsigned)tiles), dim3(kLThreads), 0,
+                       stream, A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)(Nc / kBN), (unsigned)((Mr + kBM - 1) / kBM));
   hipLaunchKernelGGL(gemm_fp8_kernel<kMode>, grid, dim3(kThreads), 0, stream, A, sa, B, sb, Mr, Nc,
                      Kc, C);

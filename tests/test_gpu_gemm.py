@@ -54,8 +54,11 @@ def check(y, ref, what, rms=None):
 
 # ---------------------------------------------------------------- FProp
 
+# shapes with N % 256 == 0 and M >= 256 run the 256 x 256 large-tile kernel,
+# the others the 128 x 128 kernel
 FPROP_SHAPES = [(256, 384, 512), (1, 128, 128), (16, 384, 256), (64, 256, 128), (200, 384, 512),
-                (130, 128, 1024), (257, 640, 384)]
+                (130, 128, 1024), (257, 640, 384),
+                (256, 256, 256), (300, 512, 384), (513, 768, 640), (1024, 1280, 2048)]
 
 
 @pytest.mark.parametrize("m,n,k", FPROP_SHAPES)
@@ -81,7 +84,7 @@ def test_fprop_full_range_codes(m, n, k):
     check(y, oracle.gemm_fprop_ref(qx, sx, qw, sw), f"fprop full-range {m}x{n}x{k}")
 
 
-@pytest.mark.parametrize("m,n,k", [(64, 256, 256), (33, 384, 128)])
+@pytest.mark.parametrize("m,n,k", [(64, 256, 256), (33, 384, 128), (256, 256, 256), (300, 512, 256)])
 def test_fprop_exact_integer(m, n, k):
     rng = np.random.default_rng(m + n + k)
     qx, qw = codes(rng, (m, k), small=True), codes(rng, (n, k), small=True)
@@ -116,7 +119,8 @@ def test_fprop_k_zero_writes_zeros():
 
 # ---------------------------------------------------------------- DGrad
 
-DGRAD_SHAPES = [(256, 384, 512), (1, 128, 128), (16, 256, 384), (200, 512, 256), (129, 128, 640)]
+DGRAD_SHAPES = [(256, 384, 512), (1, 128, 128), (16, 256, 384), (200, 512, 256), (129, 128, 640),
+                (300, 640, 256), (777, 256, 768), (1024, 2048, 1280)]
 
 
 @pytest.mark.parametrize("m,n,k", DGRAD_SHAPES)
@@ -131,9 +135,9 @@ def test_dgrad_random(m, n, k):
     check(host(dg.t), oracle.gemm_dgrad_ref(qdy, sdy, qw, sw), f"dgrad {m}x{n}x{k}")
 
 
-def test_dgrad_exact_integer_and_equals_fprop_on_transposed_weight():
-    rng = np.random.default_rng(11)
-    m, n, k = 96, 384, 256
+@pytest.mark.parametrize("m,n,k", [(96, 384, 256), (300, 384, 512)])
+def test_dgrad_exact_integer_and_equals_fprop_on_transposed_weight(m, n, k):
+    rng = np.random.default_rng(11 + m)
     qdy, qw = codes(rng, (m, n), small=True), codes(rng, (n, k), small=True)
     sdy, sw = scales(rng, (n // 128, m), pow2=True), scales(rng, (n // 128, k // 128), pow2=True)
     dx = host(jet.gemm_dgrad(u8_dev(qdy), f32_dev(sdy), u8_dev(qw), f32_dev(sw)))
@@ -148,7 +152,8 @@ def test_dgrad_exact_integer_and_equals_fprop_on_transposed_weight():
 
 # ---------------------------------------------------------------- WGrad
 
-WGRAD_SHAPES = [(128, 128, 128), (256, 384, 512), (384, 256, 256), (1024, 128, 384)]
+WGRAD_SHAPES = [(128, 128, 128), (256, 384, 512), (384, 256, 256), (1024, 128, 384),
+                (256, 256, 256), (384, 512, 768), (1024, 1280, 512), (2048, 256, 1024)]
 
 
 @pytest.mark.parametrize("m,n,k", WGRAD_SHAPES)
@@ -163,9 +168,9 @@ def test_wgrad_random(m, n, k):
     check(host(dg.t), oracle.gemm_wgrad_ref(qdyt, sdyt, qxt, sxt), f"wgrad {m}x{n}x{k}")
 
 
-def test_wgrad_exact_integer():
-    rng = np.random.default_rng(12)
-    m, n, k = 256, 256, 384
+@pytest.mark.parametrize("m,n,k", [(256, 256, 384), (384, 256, 512)])
+def test_wgrad_exact_integer(m, n, k):
+    rng = np.random.default_rng(12 + m + k)
     qdyt, qxt = codes(rng, (n, m), small=True), codes(rng, (k, m), small=True)
     sdyt, sxt = scales(rng, (m // 128, n), pow2=True), scales(rng, (m // 128, k), pow2=True)
     dw = host(jet.gemm_wgrad(u8_dev(qdyt), f32_dev(sdyt), u8_dev(qxt), f32_dev(sxt)))

@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy (torch copy_), whose HBM counters "
+                         "calibrate FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -132,6 +135,13 @@ def main():
         ("requant_dy", lambda: jet.requant_transpose_128x1(qdy, sdy, qdyt, sdyt)),
         ("gemm_wgrad", lambda: jet.gemm_wgrad(qdyt, sdyt, qxt, sxt, dw)),
     ]
+
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         for _, fn in steps:

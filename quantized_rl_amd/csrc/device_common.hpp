@@ -63,6 +63,22 @@ __device__ __forceinline__ uint2 quant8(const float (&f)[8], double inv_s) {
   return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Streaming (non-temporal) 16-byte load / 8- and 16-byte stores: the
+// quantisers touch each byte once, so they bypass cache retention.
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream8(void* p, uint2 v) {
+  __builtin_nontemporal_store(u32x2_t{v.x, v.y}, reinterpret_cast<u32x2_t*>(p));
+}
+__device__ __forceinline__ void st_stream16(void* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+}
+
 // Eight bf16 values (one 16-byte load) -> fp32.
 __device__ __forceinline__ void unpack_bf16x8(uint4 v, float (&f)[8]) {
   f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);

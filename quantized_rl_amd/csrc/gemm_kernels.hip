@@ -259,10 +259,15 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // the other (otherwise it waits for those loads before every read).
 struct LStage {
   uint8_t ab[kLStage];
-  float sa[kLBM];
-  float sb[kLBN];
+  float sa[kLBM];  // A-row scales, transposed: row r at [(r % 16) * 16 + r / 16]
+  float sb[kLBN];  // WGrad: B-column scales; FProp/DGrad: [0], [1] = the two block scales
 };
 
+// The MFMAs take the B-tile fragment as their first operand and the A-tile
+// fragment as their second, so D = (B-sub-tile) x (A-sub-tile)^T: lane l holds
+// output row 16 i + (l % 16) of its A sub-tile and the four consecutive output
+// columns 16 j + 4 (l / 16) .. + 3 of its B sub-tile.  One row scale then
+// covers a whole 4-value partial, and the epilogue writes 8-byte pieces.
 template <int kMode>
 struct LargeTile {
   int t, l, w, wm, wn, lr, lk;
@@ -272,6 +277,26 @@ struct LargeTile {
   uint32_t va[4], vb[4];
   const float* sa;
   const float* sb;
+  // LDS byte offsets inside a stage (see compute())
+  uint32_t a_even, a_odd, b_even, b_odd, s_row;
+  uint32_t dv[4];
+
+  __device__ __forceinline__ void setup_offsets() {
+    const uint32_t f0 = (uint32_t)((lr & 7) ^ ((lr >> 3) & 1));
+    const uint32_t ra0 = (uint32_t)(wm * 128 + lr) * 128u;
+    a_even = ra0 + (((uint32_t)(2 * lk) ^ f0) << 4);
+    a_odd = ra0 + (((uint32_t)(2 * lk + 1) ^ f0) << 4);
+    const uint32_t rb0 = (uint32_t)(kLBM * kBK) + (uint32_t)(wn * 64 + lr) * 128u;
+    b_even = rb0 + (((uint32_t)(2 * lk) ^ f0) << 4);
+    b_odd = rb0 + (((uint32_t)(2 * lk + 1) ^ f0) << 4);
+    s_row = (uint32_t)(lr * 16 + wm * 8) * 4u;
+    // DGrad: transposed reads of B[n][c]; n = 32 lk + 8 q + lr / 2, chunk 4 (wn % 2) + j
+    const uint32_t x = (uint32_t)(((lr >> 1) & 7) ^ (lk & 1) ^ (4 * (wn & 1)));
+    const uint32_t dbase = (uint32_t)(kLBM * kBK) + (uint32_t)(wn >> 1) * (128u * 128u) +
+                           (uint32_t)(32 * lk + (lr >> 1)) * 128u + 8u * (uint32_t)(lr & 1);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) dv[v] = dbase + (((uint32_t)v ^ x) << 4);
+  }
 
   // Direct loads of K-block kb into stage st: wave w fills 32 rows of each
   // operand tile, 8 rows (1 KB) per instruction; lane l covers row l / 8 of
@@ -288,83 +313,101 @@ struct LargeTile {
         buf_to_lds16(rb, Bs + (32 * w + 8 * p) * 128, vb[p], kb * kBK);
     }
   }
-  // scales of one K-block: threads 0..255 fetch the A-row scales, threads
-  // 256..511 the B-column scales (WGrad) -- or, for the per-block B scale of
-  // FProp / DGrad, the A-row scales again (unused); no divergent branches
+  // scales of one K-block, staged in LDS with the tiles: threads 0..255 fetch
+  // the A-row scales, threads 256..511 the B scales -- the 256 column scales
+  // (WGrad), or the block scales of the tile's two 128-column halves (FProp,
+  // DGrad; every thread of the half fetches one of the two).  All compute-side
+  // reads are then in-order LDS reads.  No divergent branches.
   __device__ __forceinline__ float load_scale(uint32_t kb) const {
-    return b_half ? sb[kb * N + col0 + t8] : sa[kb * M + arow];
+    if (kMode == kWgrad) return b_half ? sb[kb * N + col0 + t8] : sa[kb * M + arow];
+    const uint32_t cb = col0 / kBN + (t8 & 1u);
+    const uint32_t bi = (kMode == kFprop) ? cb * nkb + kb : kb * (N / kBN) + cb;
+    return t >= kLBM ? sb[bi] : sa[kb * M + arow];
   }
   __device__ __forceinline__ void store_scale(LStage& st, float x) const {
-    (t >= kLBM ? st.sb : st.sa)[t8] = x;
+    if (t >= kLBM) st.sb[t8] = x;
+    else st.sa[(t8 & 15u) * 16u + (t8 >> 4)] = x;
+  }
+
+  __device__ __forceinline__ static v8i_t frag(const uint8_t* base, uint32_t o0, uint32_t o1) {
+    const uint4 x0 = *reinterpret_cast<const uint4*>(base + o0);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(base + o1);
+    return v8i_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
   }
 
   // Multiply the K-block held in stage st into the accumulators.
-  __device__ __forceinline__ void compute(const LStage& st, uint32_t kb, v4f_t (&acc)[8][4]) const {
-    const uint8_t* As = st.ab;
-    const uint8_t* Bs = st.ab + kLBM * kBK;
+  //
+  // Row sub-tile i of the A tile: lane reads row wm*128 + 16 i + lr, logical
+  // chunks 2 lk and 2 lk + 1.  The swizzle f(row) equals f0(lr) ^ bit1(i), so
+  // the two chunk positions are fixed per lane and merely swap when bit 1 of i
+  // is set: two base offsets plus an immediate 2048 i.  The same holds for
+  // the B sub-tiles j.
+  __device__ __forceinline__ void compute(const LStage& st, v4f_t (&acc)[8][4]) const {
+    const uint8_t* S = st.ab;
+    // B fragments are read in the order the first row of MFMAs uses them,
+    // each well ahead of its use (bf[0], bf[1] before the loop, bf[j + 2] at
+    // step j), after the first A fragment: the first MFMA waits for four
+    // reads instead of the whole set.
     v8i_t bf[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    auto read_b = [&](int j) {
       if (kMode == kDgrad) {
-        const int col = wn * 64 + 16 * j;  // within the 256-column tile
-        const uint8_t* half = Bs + (col >> 7) * (128 * 128);
-        const int chunk = (col & 127) >> 4;
         v2i_t part[4];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int n = 32 * lk + 8 * q4 + (lr >> 1);
-          part[q4] = lds_tr8(half + loff(n, chunk) + 8 * (lr & 1));
-        }
+        for (int q4 = 0; q4 < 4; ++q4) part[q4] = lds_tr8(S + dv[j ^ (q4 & 1)] + 1024 * q4);
         bf[j] = v8i_t{part[0].x, part[0].y, part[1].x, part[1].y,
                       part[2].x, part[2].y, part[3].x, part[3].y};
       } else {
-        const int r = wn * 64 + 16 * j + lr;
-        const uint4 x0 = *reinterpret_cast<const uint4*>(Bs + loff(r, 2 * lk));
-        const uint4 x1 = *reinterpret_cast<const uint4*>(Bs + loff(r, 2 * lk + 1));
-        bf[j] = v8i_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                      (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        const bool sw = (j >> 1) & 1;
+        bf[j] = frag(S + 2048 * j, sw ? b_odd : b_even, sw ? b_even : b_odd);
       }
+    };
+    v8i_t af[2];
+    af[0] = frag(S, a_even, a_odd);
+    read_b(0);
+    read_b(1);
+    // row scales of the 8 row sub-tiles (transposed layout: 8 contiguous floats)
+    float srow[8];
+    {
+      const float4 s0 = *reinterpret_cast<const float4*>(reinterpret_cast<const uint8_t*>(st.sa) + s_row);
+      const float4 s1 = *reinterpret_cast<const float4*>(reinterpret_cast<const uint8_t*>(st.sa) + s_row + 16);
+      srow[0] = s0.x; srow[1] = s0.y; srow[2] = s0.z; srow[3] = s0.w;
+      srow[4] = s1.x; srow[5] = s1.y; srow[6] = s1.z; srow[7] = s1.w;
     }
-    float sbcol[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    float sblk = 0.0f;
+    float scol[4][4];
     if (kMode == kWgrad) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sbcol[j] = st.sb[wn * 64 + 16 * j + lr];
+      for (int j = 0; j < 4; ++j) {
+        const float4 c4 = *reinterpret_cast<const float4*>(&st.sb[wn * 64 + 16 * j + 4 * lk]);
+        scol[j][0] = c4.x; scol[j][1] = c4.y; scol[j][2] = c4.z; scol[j][3] = c4.w;
+      }
     } else {
-      const uint32_t cb = (col0 + wn * 64) / kBN;  // the wave's 64 columns lie in one 128-block
-      sblk = (kMode == kFprop) ? sb[cb * nkb + kb] : sb[kb * (N / kBN) + cb];
+      const float sblk = st.sb[wn >> 1];  // the wave's 64 columns lie in one 128-column block
+#pragma unroll
+      for (int i = 0; i < 8; ++i) srow[i] *= sblk;
     }
 
     // Software pipeline over the 32 (row, column) sub-tiles, row-major: step q
     // issues the MFMA of sub-tile q, then rescales the partial of sub-tile
     // q - 2 into its accumulators, so two MFMAs separate every partial from
-    // its use; the A fragment and row scales of the next row sub-tile are read
-    // from LDS a row ahead.  Scheduling barriers pin the order.
-    auto read_a = [&](int i, v8i_t& af, float (&srow)[4]) {
-      const int r = wm * 128 + 16 * i + lr;
-      const uint4 x0 = *reinterpret_cast<const uint4*>(As + loff(r, 2 * lk));
-      const uint4 x1 = *reinterpret_cast<const uint4*>(As + loff(r, 2 * lk + 1));
-      af = v8i_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      const float4 s4 = *reinterpret_cast<const float4*>(&st.sa[wm * 128 + 16 * i + 4 * lk]);
-      srow[0] = s4.x; srow[1] = s4.y; srow[2] = s4.z; srow[3] = s4.w;
-    };
-    // row scales use three buffers: those of row sub-tile i are still read by
-    // its last two rescales after the reads for row i + 2 ... are issued
-    v8i_t af[2];
-    float srow[3][4];
+    // its use; the A fragment of the next row sub-tile is read a row ahead.
+    // Scheduling barriers pin the order.
     v4f_t part[3];
-    read_a(0, af[0], srow[0]);
 #pragma unroll
     for (int q = 0; q < 34; ++q) {
       const int i = q >> 2, j = q & 3;
-      if (q < 32 && j == 0 && i + 1 < 8) read_a(i + 1, af[(i + 1) & 1], srow[(i + 1) % 3]);
-      if (q < 32) part[q % 3] = mfma_fp8(af[i & 1], bf[j]);
+      if (q < 2) read_b(q + 2);
+      if (q < 32 && j == 0 && i + 1 < 8) {
+        const int n = i + 1;
+        const bool sw = (n >> 1) & 1;
+        af[n & 1] = frag(S + 2048 * n, sw ? a_odd : a_even, sw ? a_even : a_odd);
+      }
+      if (q < 32) part[q % 3] = mfma_fp8(bf[j], af[i & 1]);
       __builtin_amdgcn_sched_barrier(0);
       if (q >= 2) {
         const int qp = q - 2, pi = qp >> 2, pj = qp & 3;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float sc = (kMode == kWgrad) ? srow[pi % 3][e] * sbcol[pj] : srow[pi % 3][e] * sblk;
+          const float sc = (kMode == kWgrad) ? srow[pi] * scol[pj][e] : srow[pi];
           acc[pi][pj][e] = fmaf(part[qp % 3][e], sc, acc[pi][pj][e]);
         }
       }
@@ -393,6 +436,7 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
   g.lk = g.l >> 4;
   g.M = M; g.N = N; g.K = K;
   g.sa = sa; g.sb = sb;
+  g.setup_offsets();
 
   // launch order: spread over the 8 XCDs so that each XCD gets one contiguous
   // range of tiles, then walk tile-row groups of kGroupM rows column by column
@@ -445,7 +489,7 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
       const uint32_t kn = kb + 1 <= last ? kb + 1 : last;
       const float x = g.load_scale(kn);
       g.issue(kn, st1);
-      g.compute(st0, kb, acc);
+      g.compute(st0, acc);
       g.store_scale(st1, x);
       wait_vmem();
       __syncthreads();
@@ -454,7 +498,7 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
       const uint32_t kn = kb + 2 <= last ? kb + 2 : last;
       const float x = g.load_scale(kn);
       g.issue(kn, st0);
-      g.compute(st1, kb + 1, acc);
+      g.compute(st1, acc);
       g.store_scale(st0, x);
       wait_vmem();
       __syncthreads();
@@ -474,12 +518,12 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = g.wm * 128 + 16 * i + 4 * g.lk + e, c = g.wn * 64 + 16 * j + g.lr;
-        *reinterpret_cast<uint16_t*>(crow(r) + 2 * c) = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int r = g.wm * 128 + 16 * i + g.lr, c = g.wn * 64 + 16 * j + 4 * g.lk;
+      const uint32_t lo = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
+      const uint32_t hi = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
+      *reinterpret_cast<uint2*>(crow(r) + 2 * c) = make_uint2(lo, hi);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();

@@ -22,7 +22,7 @@ namespace jetfp8 {
 // arithmetic so that kActRows / 16 groups are in flight per quarter-wave.
 // Scales of consecutive rows of one group are contiguous in S[g][*], so the
 // scale stores of a tile fill whole cache lines.
-constexpr int kActRows = 64;
+constexpr int kActRows = 128;
 constexpr int kActIters = kActRows / 16;
 
 __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t* __restrict__ x,
@@ -38,10 +38,7 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t* __
 #pragma unroll
   for (int it = 0; it < kActIters; ++it) {
     const int64_t r = row0 + 16 * it;
-    if (r < M)
-      v[it] = *reinterpret_cast<const uint4*>(x + r * K + g * kGroup + lane16 * 8);
-    else
-      v[it] = make_uint4(0, 0, 0, 0);
+    v[it] = r < M ? ld_stream16(x + r * K + g * kGroup + lane16 * 8) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int it = 0; it < kActIters; ++it) {
@@ -53,7 +50,7 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t* __
     const double inv = 1.0 / (double)sc;
     const uint2 codes = quant8(f, inv);
     if (r < M) {
-      *reinterpret_cast<uint2*>(q + r * K + g * kGroup + lane16 * 8) = codes;
+      st_stream8(q + r * K + g * kGroup + lane16 * 8, codes);
       if (lane16 == 0) s[g * M + r] = sc;
     }
   }
@@ -75,7 +72,7 @@ __global__ __launch_bounds__(256) void quant_weight_128x128_kernel(const uint16_
   uint4 v[8];
 #pragma unroll
   for (int it = 0; it < 8; ++it)
-    v[it] = *reinterpret_cast<const uint4*>(base + (int64_t)(rsub + 16 * it) * K);
+    v[it] = ld_stream16(base + (int64_t)(rsub + 16 * it) * K);
   float amax = 0.0f;
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
@@ -94,7 +91,7 @@ __global__ __launch_bounds__(256) void quant_weight_128x128_kernel(const uint16_
   for (int it = 0; it < 8; ++it) {
     float f[8];
     unpack_bf16x8(v[it], f);
-    *reinterpret_cast<uint2*>(qbase + (int64_t)(rsub + 16 * it) * K) = quant8(f, inv);
+    st_stream8(qbase + (int64_t)(rsub + 16 * it) * K, quant8(f, inv));
   }
   if (threadIdx.x == 0) s[nb * (K / kGroup) + kb] = sc;
 }
@@ -121,6 +118,85 @@ __device__ __forceinline__ float tree8_sq(const float (&f)[8]) {
   return (a + b) + (c + d);
 }
 
+// Rows of up to 8192 elements: one wave per row, the row held in registers.
+// Pass p covers elements [512 p, 512 p + 512): lane l owns the 8 elements at
+// 512 p + 8 l, summed as a balanced tree, then a xor-butterfly over the wave
+// (offsets 1..32) gives the pass's 512-element subtree; the pass sums are
+// combined by the pairwise rule (odd tail carried).  Each partial is a node of
+// the canonical tree of the row zero-padded to a power of two.
+constexpr int kRowPasses = 16;  // K <= 8192
+
+__global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ gamma,
+                                                                 int64_t M, int64_t K, float eps,
+                                                                 uint8_t* __restrict__ q,
+                                                                 float* __restrict__ s) {
+  const int l = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;  // whole waves only
+  const uint16_t* xr = x + row * K;
+  const int passes = (int)((K + 511) / 512);
+
+  uint4 xv[kRowPasses];
+#pragma unroll
+  for (int p = 0; p < kRowPasses; ++p) {
+    const int64_t e = 512 * p + 8 * l;
+    xv[p] = (p < passes && e < K) ? ld_stream16(xr + e) : make_uint4(0, 0, 0, 0);
+  }
+  float ps[kRowPasses];
+#pragma unroll
+  for (int p = 0; p < kRowPasses; ++p) {
+    float v = 0.0f;
+    if (p < passes) {
+      float f[8];
+      unpack_bf16x8(xv[p], f);
+      v = tree8_sq(f);
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off, 64);
+    }
+    ps[p] = v;
+  }
+  // pairwise tree over the pass sums (all lanes hold the same values)
+  int n = passes;
+#pragma unroll
+  for (int lvl = 0; lvl < 4; ++lvl) {
+    if (n > 1) {
+      const int h = n / 2;
+#pragma unroll
+      for (int j = 0; j < kRowPasses / 2; ++j)
+        if (j < h) ps[j] = ps[2 * j] + ps[2 * j + 1];
+      if (n & 1) {
+#pragma unroll
+        for (int j = 0; j < kRowPasses / 2; ++j)
+          if (j == h) ps[j] = ps[n - 1];
+      }
+      n = h + (n & 1);
+    }
+  }
+  const float ms = ps[0] / (float)K;
+  const float inv = 1.0f / sqrt_rn(ms + eps);
+
+  const int lane16 = l & 15, quarter = l >> 4;
+#pragma unroll
+  for (int p = 0; p < kRowPasses; ++p) {
+    const int64_t g = 4 * p + quarter;
+    if (p < passes && g * kGroup < K) {
+      const int64_t e = g * kGroup + lane16 * 8;
+      float f[8], gm[8];
+      unpack_bf16x8(xv[p], f);
+      unpack_bf16x8(*reinterpret_cast<const uint4*>(gamma + e), gm);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = (f[i] * inv) * gm[i];
+      const float amax = quarter_wave_max(absmax8(f));
+      const float sc = scale_from_amax(amax);
+      const double dinv = 1.0 / (double)sc;
+      st_stream8(q + row * K + e, quant8(f, dinv));
+      if (lane16 == 0) s[g * M + row] = sc;
+    }
+  }
+}
+
+// Wider rows: one workgroup (256 threads) per row, two passes over the row.
 __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ gamma,
                                                             int64_t M, int64_t K, float eps,
@@ -184,97 +260,106 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
 // ---------------------------------------------------------------------------
 // Requantisation 1x128 -> 128x1 with transposed store.
 //
-// A workgroup of 128 threads owns a 128-token x 128-feature tile: it stages the
-// 16 KB of codes and the tile's 128 input scales in LDS, then lane k reads
-// column k with the gfx950 LDS transpose read (ds_read_b64_tr_b8: within each
-// 16-lane group, lane i receives byte (i & 7) of the 8-byte rows addressed by
-// lanes 2j + (i >> 3), j = 0..7 -- i.e. one column of an 8 x 16 byte block).
-// The lane dequantises its 128 values (fp32), takes their amax, and writes its
-// 128 requantised codes as one contiguous row of Qt.
+// A workgroup of 256 threads owns a 128-token x 128-feature tile.  It stages
+// the 16 KB of codes and the tile's 128 input scales in LDS; two threads own
+// each column k (tokens 0..63 and 64..127).  A thread reads its 64 codes with
+// the gfx950 LDS transpose read (ds_read_b64_tr_b8: within each 16-lane
+// group, lane i receives byte (i & 7) of the 8-byte rows addressed by lanes
+// 2j + (i >> 3), j = 0..7 -- one column of an 8 x 16 byte block), decodes them
+// (v_cvt_pk_f32_fp8), multiplies by the token scales and keeps the 64 fp32
+// values in registers.  The two halves' amax meet in LDS; each thread then
+// writes its 64 requantised codes into an LDS copy of the Qt tile, which the
+// workgroup stores with full 128-byte rows.
 constexpr int kRqPitch = 128 + 16;  // LDS row pitch in bytes (16-byte pad)
 
 typedef int v2i_t __attribute__((ext_vector_type(2)));
-
-// Four E4M3 codes packed in a dword -> fp32 (exact; v_cvt_f32_fp8 with byte select).
-__device__ __forceinline__ void decode4(uint32_t w, float (&v)[4]) {
-  v[0] = __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
-  v[1] = __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
-  v[2] = __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
-  v[3] = __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
-}
+typedef float v2f_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ v2i_t lds_read_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
       (__attribute__((address_space(3))) v2i_t*)((__attribute__((address_space(3))) uint8_t*)(p)));
 }
 
-__global__ __launch_bounds__(128) void requant_transpose_kernel(const uint8_t* __restrict__ q,
+// Four E4M3 codes packed in a dword -> fp32 (exact).
+__device__ __forceinline__ void decode4(uint32_t w, float (&v)[4]) {
+  const v2f_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const v2f_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  v[0] = lo.x; v[1] = lo.y; v[2] = hi.x; v[3] = hi.y;
+}
+
+__global__ __launch_bounds__(256) void requant_transpose_kernel(const uint8_t* __restrict__ q,
                                                                 const float* __restrict__ s,
                                                                 int64_t M, int64_t K,
                                                                 uint8_t* __restrict__ qt,
                                                                 float* __restrict__ st) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kGroup * kRqPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kGroup * kRqPitch];   // codes [m][k]
+  __shared__ __attribute__((aligned(16))) uint8_t otile[kGroup * kRqPitch];  // codes [k][m]
   __shared__ float sc_in[kGroup];
+  __shared__ float half_amax[2][kGroup];
   const int t = threadIdx.x;
   const int64_t kg = blockIdx.x;  // feature group (128 columns)
   const int64_t mb = blockIdx.y;  // token block (128 rows)
   const uint8_t* src = q + (mb * kGroup) * K + kg * kGroup;
 
-  // 128 rows x 8 chunks of 16 bytes = 1024 chunks, 8 per thread
-  uint4 c[8];
+  // 128 rows x 8 chunks of 16 bytes = 1024 chunks, 4 per thread
+  uint4 c[4];
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int id = t + 128 * it, r = id >> 3, ch = id & 7;
-    c[it] = *reinterpret_cast<const uint4*>(src + (int64_t)r * K + ch * 16);
+  for (int it = 0; it < 4; ++it) {
+    const int id = t + 256 * it, r = id >> 3, ch = id & 7;
+    c[it] = ld_stream16(src + (int64_t)r * K + ch * 16);
   }
-  sc_in[t] = s[kg * M + mb * kGroup + t];
+  if (t < kGroup) sc_in[t] = s[kg * M + mb * kGroup + t];
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int id = t + 128 * it, r = id >> 3, ch = id & 7;
+  for (int it = 0; it < 4; ++it) {
+    const int id = t + 256 * it, r = id >> 3, ch = id & 7;
     *reinterpret_cast<uint4*>(tile + r * kRqPitch + ch * 16) = c[it];
   }
   __syncthreads();
 
-  // lane -> column: 16-lane group gi covers columns 16 gi .. 16 gi + 15
-  const int li = t & 15, gi = t >> 4;
+  // thread -> (column, half): 16-lane group gi covers columns 16 gi .. + 15
+  const int li = t & 15, gi = (t >> 4) & 7, h = t >> 7;
   const int col = 16 * gi + li;
-  // address this lane supplies for row block j: row 8 j + (li >> 1), bytes 8 (li & 1) of the 16 columns
-  const uint8_t* abase = tile + (li >> 1) * kRqPitch + 16 * gi + 8 * (li & 1);
-  uint32_t w[32];  // 128 codes of column `col`, rows 0..127 in order
+  // address this lane supplies for row block j: row 64 h + 8 j + (li >> 1), bytes 8 (li & 1)
+  const uint8_t* abase = tile + (64 * h + (li >> 1)) * kRqPitch + 16 * gi + 8 * (li & 1);
+  float v[64];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < 8; ++j) {
     const v2i_t r = lds_read_tr8(abase + 8 * j * kRqPitch);
-    w[2 * j] = (uint32_t)r.x;
-    w[2 * j + 1] = (uint32_t)r.y;
+    float d[8];
+    decode4((uint32_t)r.x, *reinterpret_cast<float(*)[4]>(&d[0]));
+    decode4((uint32_t)r.y, *reinterpret_cast<float(*)[4]>(&d[4]));
+#pragma unroll
+    for (int b = 0; b < 8; ++b) v[8 * j + b] = d[b] * sc_in[64 * h + 8 * j + b];
   }
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    float d[4];
-    decode4(w[i], d);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) amax = fmaxf(amax, fabsf(d[b] * sc_in[4 * i + b]));
-  }
+  for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  half_amax[h][col] = amax;
+  __syncthreads();
+  amax = fmaxf(half_amax[0][col], half_amax[1][col]);
   const float sc = scale_from_amax(amax);
   const double inv = 1.0 / (double)sc;
-  uint8_t* dst = qt + (kg * kGroup + col) * M + mb * kGroup;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {  // 16 codes per 16-byte store
+  for (int i = 0; i < 4; ++i) {  // 16 codes per 16-byte LDS store
     uint32_t o[4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const int wi = 4 * i + h;
-      float v[4];
-      decode4(w[wi], v);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) v[b] = v[b] * sc_in[4 * wi + b];
-      int p = cvt_pk_e4m3(div_by_scale(v[0], inv), div_by_scale(v[1], inv), 0, false);
-      p = cvt_pk_e4m3(div_by_scale(v[2], inv), div_by_scale(v[3], inv), p, true);
-      o[h] = (uint32_t)p;
+    for (int w = 0; w < 4; ++w) {
+      const int b = 16 * i + 4 * w;
+      int p = cvt_pk_e4m3(div_by_scale(v[b], inv), div_by_scale(v[b + 1], inv), 0, false);
+      p = cvt_pk_e4m3(div_by_scale(v[b + 2], inv), div_by_scale(v[b + 3], inv), p, true);
+      o[w] = (uint32_t)p;
     }
-    *reinterpret_cast<uint4*>(dst + 16 * i) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(otile + col * kRqPitch + 64 * h + 16 * i) = make_uint4(o[0], o[1], o[2], o[3]);
   }
-  st[mb * K + kg * kGroup + col] = sc;
+  if (h == 0) st[mb * K + kg * kGroup + col] = sc;
+  __syncthreads();
+  // store Qt rows kg*128 + r, tokens mb*128 .. +128: 8 threads per 128-byte row
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int id = t + 256 * it, r = id >> 3, ch = id & 7;
+    st_stream16(qt + (kg * kGroup + r) * M + mb * kGroup + ch * 16,
+                *reinterpret_cast<const uint4*>(otile + r * kRqPitch + ch * 16));
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -299,6 +384,11 @@ hipError_t launch_quant_weight(const uint16_t* w, int64_t N, int64_t K, uint8_t*
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K,
                                 float eps, uint8_t* q, float* s, hipStream_t stream) {
   if (M == 0) return hipSuccess;
+  if (K <= 512 * kRowPasses) {
+    hipLaunchKernelGGL(rmsnorm_quant_rows_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream,
+                       x, gamma, M, K, eps, q, s);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3((unsigned)M), dim3(256), 0, stream, x, gamma, M, K,
                      eps, q, s);
   return hipGetLastError();
@@ -308,7 +398,7 @@ hipError_t launch_requant(const uint8_t* q, const float* s, int64_t M, int64_t K
                           float* st, hipStream_t stream) {
   if (M == 0 || K == 0) return hipSuccess;
   dim3 grid((unsigned)(K / kGroup), (unsigned)(M / kGroup));
-  hipLaunchKernelGGL(requant_transpose_kernel, grid, dim3(128), 0, stream, q, s, M, K, qt, st);
+  hipLaunchKernelGGL(requant_transpose_kernel, grid, dim3(256), 0, stream, q, s, M, K, qt, st);
   return hipGetLastError();
 }
 

@@ -20,7 +20,14 @@ the launch stream around every kernel of the timed steps; the ``roofline``
 object describes the slowest GEMM against the dense FP8 MFMA peak.  The
 ``cpu_baseline`` runs the CPU oracle on a 256-token slice of the same step.
 
+``--workload decode_8b`` instead times the rollout decode path at M tokens
+(``--decode-m``, default 16): RMSNorm+quant, FProp against the FP8 QKV and
+gate+up weights, 1x128 quantisation of the down-projection input and the down
+FProp (weights quantised once, outside the timed region).  Decode is bound by
+streaming the FP8 weights, so its kernels also report weight GB/s.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--workload linear_8b_up|decode_8b] [--decode-m M]
 """
 
 import argparse
@@ -45,6 +52,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="linear_8b_up", choices=["linear_8b_up", "decode_8b"])
+    ap.add_argument("--decode-m", type=int, default=16)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (torch copy_), whose HBM counters "
                          "calibrate FETCH_SIZE / WRITE_SIZE")
@@ -96,12 +105,100 @@ def cpu_baseline(d, gamma):
                       f"{dt:.2f} s; quantisers single-threaded numpy, GEMMs numpy BLAS"}
 
 
+def time_steps(torch, steps, n_steps, n_warmup, dev):
+    """Run warm-up steps, then time n_steps steps with HIP events around every
+    kernel (recorded on the launch stream).  Returns (per-kernel ms lists,
+    per-step ms list, wall seconds)."""
+    for _ in range(n_warmup):
+        for _, fn in steps:
+            fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)] for _ in range(n_steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(n_steps):
+        ev[s][0].record(stream)
+        for i, (_, fn) in enumerate(steps):
+            fn()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {name: [] for name, _ in steps}
+    step_ms = []
+    for s in range(n_steps):
+        for i, (name, _) in enumerate(steps):
+            per[name].append(ev[s][i].elapsed_time(ev[s][i + 1]))
+        step_ms.append(ev[s][0].elapsed_time(ev[s][-1]))
+    return per, step_ms, wall
+
+
+def bench_decode(args):
+    import torch
+    import quantized_rl_amd as jet
+    from quantized_rl_amd import synth
+
+    dev = torch.device("cuda:0")
+    m = args.decode_m
+    d = synth.decode_8b(m)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, gamma, h = bf16(d["x"]), bf16(d["gamma"]), bf16(d["down_in"])
+    wq = {k: jet.quantize_weight_128x128(bf16(d[k])) for k in ("w_qkv", "w_gu", "w_down")}
+    torch.cuda.synchronize()
+    qx, sx = jet.rmsnorm_quant(x, gamma, d["eps"])
+    qh, sh = jet.quantize_act_1x128(h)
+    y = {k: torch.empty((m, wq[k][0].shape[0]), dtype=torch.bfloat16, device=dev) for k in wq}
+    steps = [
+        ("rmsnorm_quant", lambda: jet.rmsnorm_quant(x, gamma, d["eps"], qx, sx)),
+        ("gemm_fprop_qkv", lambda: jet.gemm_fprop(qx, sx, *wq["w_qkv"], y["w_qkv"])),
+        ("gemm_fprop_gate_up", lambda: jet.gemm_fprop(qx, sx, *wq["w_gu"], y["w_gu"])),
+        ("quantize_act_1x128", lambda: jet.quantize_act_1x128(h, qh, sh)),
+        ("gemm_fprop_down", lambda: jet.gemm_fprop(qh, sh, *wq["w_down"], y["w_down"])),
+    ]
+    per, step_ms, wall = time_steps(torch, steps, args.steps, args.warmup, dev)
+    ms_per_step = float(np.mean(step_ms))
+    shapes = {"gemm_fprop_qkv": (6144, 4096), "gemm_fprop_gate_up": (24576, 4096), "gemm_fprop_down": (4096, 12288)}
+    flops = sum(2.0 * m * n * k for n, k in shapes.values())
+    kernels = {}
+    for name in per:
+        avg_ms = float(np.mean(per[name]))
+        if name in shapes:
+            n, k = shapes[name]
+            wbytes = n * k + 4 * (n // 128) * (k // 128) + m * k + 2 * m * n
+            kernels[name] = {"avg_us": round(avg_ms * 1e3, 2), "weight_GBps": round(wbytes / (avg_ms * 1e-3) / 1e9, 1),
+                             "frac_hbm": round(wbytes / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "TFLOPs": round(2.0 * m * n * k / (avg_ms * 1e-3) / 1e12, 2)}
+        else:
+            kernels[name] = {"avg_us": round(avg_ms * 1e3, 2)}
+    dom = max(shapes, key=lambda k: kernels[k]["avg_us"])
+    out = {
+        "metric": METRIC, "value": round(flops / (ms_per_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": "qwen3_8b_decode", "M": m, "K": 4096,
+                   "weights": "qkv 6144x4096, gate_up 24576x4096, down 4096x12288", "seed": 2},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["weight_GBps"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": kernels[dom]["frac_hbm"], "traffic": None},
+        "kernels": kernels,
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (this path is the one-GPU share; see DESIGN.md); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "decode_8b":
+        sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+        bench_decode(args)
+        return
     import torch
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     import quantized_rl_amd as jet
@@ -143,29 +240,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
-        for _, fn in steps:
-            fn()
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        ev[s][0].record(stream)
-        for i, (_, fn) in enumerate(steps):
-            fn()
-            ev[s][i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    per = {name: [] for name, _ in steps}
-    step_ms = []
-    for s in range(args.steps):
-        for i, (name, _) in enumerate(steps):
-            per[name].append(ev[s][i].elapsed_time(ev[s][i + 1]))
-        step_ms.append(ev[s][0].elapsed_time(ev[s][-1]))
+    per, step_ms, wall = time_steps(torch, steps, args.steps, args.warmup, dev)
     ms_per_step = float(np.mean(step_ms))
     work = kernel_work()
     gemm_flops = 3 * 2.0 * M * N * K

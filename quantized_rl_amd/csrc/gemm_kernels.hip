@@ -538,6 +538,153 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
 }
 
 
+// ---------------------------------------------------------------------------
+// Decode FProp (M <= 64 tokens, rollout): parallel weight streaming with the
+// sequential accumulation order kept.
+//
+// One workgroup per 16 output columns.  Its kW waves compute the 128-deep
+// block partials P_kb = MFMA(W slice, X slice) of different K-blocks at once
+// (wave w takes K-block c * kW + w of chunk c, with kD K-blocks of loads in
+// flight per wave, loaded straight into registers), and park them in LDS.
+// After each chunk, wave i (one per 16 tokens) folds the chunk's partials in
+// ascending K order: acc = fma(P_kb, fl32(sx * sw), acc) -- exactly the
+// per-element operation sequence of the other FProp kernels, so a token's
+// output is bit-identical whichever kernel and batch size compute it.
+// kW (waves per strip) is chosen at launch so that the chip holds about 2048
+// streaming waves whatever the number of 16-column strips; with kW = 1 the
+// lone wave folds each partial as soon as it is computed, with no LDS.
+template <int kMT, int kW>  // kMT: row sub-tiles of 16 tokens (M <= 16 * kMT)
+struct DecodeCfg {
+  // chunks of loads in flight per wave (a lone wave streams its whole strip)
+  static constexpr int kD = kW == 1 ? (kMT == 1 ? 8 : (kMT == 2 ? 6 : 4)) : ((kMT >= 2 && kW == 16) ? 2 : 4);
+  static_assert(kW == 1 || kW >= kMT, "one folding wave per 16-token sub-tile");
+};
+
+template <int kMT, int kW>
+__global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
+    const uint8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ W,
+    const float* __restrict__ sw, uint32_t M, uint32_t N, uint32_t K, uint16_t* __restrict__ Y) {
+  constexpr int kD = DecodeCfg<kMT, kW>::kD;
+  const int t = threadIdx.x, l = t & 63, lr = l & 15, lk = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const uint32_t n0 = blockIdx.x * 16u;
+  const uint32_t nkb = K / kBK;
+  const uint32_t nch = (nkb + kW - 1) / kW;
+  const rsrc_t rw = make_rsrc(W, N * K);
+  const rsrc_t rx = make_rsrc(X, M * K);
+  const uint32_t w_off = (n0 + lr) * K + 32u * lk;
+  uint32_t x_off[kMT];
+#pragma unroll
+  for (int i = 0; i < kMT; ++i) {
+    const uint32_t m = (16u * i + lr) < M ? (16u * i + lr) : (M - 1);  // ragged tail: repeat the last token
+    x_off[i] = m * K + 32u * lk;
+  }
+  const float* swrow = sw + (n0 / kBN) * nkb;
+
+  v8i_t wr[kD], xr[kD][kMT];
+  auto load = [&](int slot, uint32_t c) {
+    uint32_t kb = c * kW + (uint32_t)w;
+    kb = kb < nkb ? kb : nkb - 1;  // past the end: a valid block whose product is not used
+    const uint32_t kofs = kb * kBK;
+    const v4i_t w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off, kofs, 0);
+    const v4i_t w1 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off + 16u, kofs, 0);
+    wr[slot] = v8i_t{w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int i = 0; i < kMT; ++i) {
+      const v4i_t x0 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_off[i], kofs, 0);
+      const v4i_t x1 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_off[i] + 16u, kofs, 0);
+      xr[slot][i] = v8i_t{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < kD; ++j) load(j, (uint32_t)j);
+
+  if constexpr (kW == 1) {
+    // a lone wave per strip: fold each partial as soon as it is computed
+    v4f_t acc1[kMT];
+    float sxm[kMT];
+#pragma unroll
+    for (int i = 0; i < kMT; ++i) acc1[i] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma clang loop unroll(disable)
+    for (uint32_t c0 = 0; c0 < nch; c0 += kD) {
+#pragma unroll
+      for (int j = 0; j < kD; ++j) {
+        const uint32_t kb = c0 + j;
+        if (kb < nkb) {
+          const float sb = swrow[kb];
+#pragma unroll
+          for (int i = 0; i < kMT; ++i) {
+            const uint32_t m = (16u * i + lr) < M ? (16u * i + lr) : (M - 1);
+            sxm[i] = sx[kb * M + m];
+          }
+#pragma unroll
+          for (int i = 0; i < kMT; ++i) {
+            const v4f_t p = mfma_fp8(wr[j], xr[j][i]);
+            const float sc = sxm[i] * sb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc1[i][e] = fmaf(p[e], sc, acc1[i][e]);
+          }
+          load(j, kb + kD);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kMT; ++i) {
+      const uint32_t m = 16u * i + lr;
+      if (m < M) {
+        const uint32_t lo = f32_to_bf16_rne(acc1[i][0]) | (f32_to_bf16_rne(acc1[i][1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(acc1[i][2]) | (f32_to_bf16_rne(acc1[i][3]) << 16);
+        *reinterpret_cast<uint2*>(Y + (size_t)m * N + n0 + 4 * lk) = make_uint2(lo, hi);
+      }
+    }
+  } else {
+  __shared__ v4f_t part[2][kW][kMT][64];
+  // the folding wave (w < kMT) owns token 16 w + lr, columns n0 + 4 lk .. + 3
+  const uint32_t my_m = (16u * (uint32_t)w + lr) < M ? (16u * (uint32_t)w + lr) : (M - 1);
+  v4f_t acc = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma clang loop unroll(disable)
+  for (uint32_t c0 = 0; c0 < nch; c0 += kD) {
+#pragma unroll
+    for (int j = 0; j < kD; ++j) {
+      const uint32_t c = c0 + j;
+      if (c < nch) {
+        const int buf = (int)(c & 1);
+        if (c * kW + (uint32_t)w < nkb) {
+#pragma unroll
+          for (int i = 0; i < kMT; ++i) part[buf][w][i][l] = mfma_fp8(wr[j], xr[j][i]);
+        }
+        load(j, c + kD);
+        float sc[kW];
+        if (w < kMT) {
+#pragma unroll
+          for (int k = 0; k < kW; ++k) {
+            const uint32_t kb = c * kW + k < nkb ? c * kW + k : nkb - 1;
+            sc[k] = sx[kb * M + my_m] * swrow[kb];
+          }
+        }
+        __syncthreads();
+        if (w < kMT) {
+#pragma unroll
+          for (int k = 0; k < kW; ++k) {
+            if (c * kW + k < nkb) {
+              const v4f_t p = part[buf][k][w][l];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[e] = fmaf(p[e], sc[k], acc[e]);
+            }
+          }
+        }
+      }
+    }
+  }
+  if (w < kMT && 16u * (uint32_t)w + lr < M) {
+    const uint32_t m = 16u * (uint32_t)w + lr;
+    const uint32_t lo = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+    const uint32_t hi = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+    *reinterpret_cast<uint2*>(Y + (size_t)m * N + n0 + 4 * lk) = make_uint2(lo, hi);
+  }
+  }
+}
+
 __global__ void fill_zero_u16(uint16_t* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -552,16 +699,60 @@ static hipError_t launch_zero(uint16_t* p, int64_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int kMT, int kW>
+static void launch_decode_t(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
+                            uint32_t m, uint32_t n, uint32_t k, uint16_t* C, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_fp8_decode_kernel<kMT, kW>), dim3(n / 16), dim3(64 * kW), 0, stream, A, sa, B,
+                     sb, m, n, k, C);
+}
+
+template <int kMT>
+static void launch_decode_m(int kw, const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
+                            uint32_t m, uint32_t n, uint32_t k, uint16_t* C, hipStream_t stream) {
+  switch (kw) {
+    case 1: launch_decode_t<kMT, 1>(A, sa, B, sb, m, n, k, C, stream); break;
+    case 2: launch_decode_t<kMT, (kMT > 2 ? kMT : 2)>(A, sa, B, sb, m, n, k, C, stream); break;
+    case 4: launch_decode_t<kMT, 4>(A, sa, B, sb, m, n, k, C, stream); break;
+    case 8: launch_decode_t<kMT, 8>(A, sa, B, sb, m, n, k, C, stream); break;
+    default: launch_decode_t<kMT, 16>(A, sa, B, sb, m, n, k, C, stream); break;
+  }
+}
+
+static void launch_decode(int mt, int kw, const uint8_t* A, const float* sa, const uint8_t* B,
+                          const float* sb, uint32_t m, uint32_t n, uint32_t k, uint16_t* C,
+                          hipStream_t stream) {
+  if (mt == 1) launch_decode_m<1>(kw, A, sa, B, sb, m, n, k, C, stream);
+  else if (mt == 2) launch_decode_m<2>(kw, A, sa, B, sb, m, n, k, C, stream);
+  else launch_decode_m<4>(kw, A, sa, B, sb, m, n, k, C, stream);
+}
+
 template <int kMode>
 static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
                               int64_t Mr, int64_t Nc, int64_t Kc, uint16_t* C,
                               hipStream_t stream) {
   if (Mr == 0 || Nc == 0) return hipSuccess;
   if (Kc == 0) return launch_zero(C, Mr * Nc, stream);
+  // rollout decode: weight-streaming kernel for up to 64 tokens (FProp)
+  if (kMode == kFprop && Mr <= 64 && Nc * Kc < (int64_t(1) << 31) && Mr * Kc < (int64_t(1) << 31)) {
+    // Waves per strip: enough for about 2048 / mt streaming waves (a wave
+    // with mt token sub-tiles does mt times the MFMA and X-load work per
+    // K-block), or 4096 for long K, where a strip's sequential chain is long;
+    // at most 16, and at most one per two K-blocks.  Measured on the 8B decode
+    // shapes (K = 4096 and 12288, N = 4096 .. 24576, M = 1 .. 64).
+    const int64_t strips = Nc / 16, nkb = Kc / kBK;
+    const int mt = Mr <= 16 ? 1 : (Mr <= 32 ? 2 : 4);
+    const int64_t target = nkb >= 64 ? 4096 : 2048 / mt;
+    int kw = 16;
+    while (kw > 1 && (strips * kw > target || kw > (nkb + 1) / 2)) kw /= 2;
+    if (kw > 1 && kw < mt) kw = mt;  // wave i folds token sub-tile i
+    launch_decode(mt, kw, A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C, stream);
+    return hipGetLastError();
+  }
   // the large-tile kernel works with 32-bit byte offsets
   const bool fits32 = (Mr + kLBM) * Kc < (int64_t(1) << 31) && Nc * Kc < (int64_t(1) << 31) &&
                       (Mr + kLBM) * Nc * 2 < (int64_t(1) << 31);
-  if (Nc % kLBN == 0 && Mr >= kLBM && fits32) {
+  const int64_t large_tiles = ((Mr + kLBM - 1) / kLBM) * (Nc / kLBN);
+  if (Nc % kLBN == 0 && Mr >= kLBM && fits32 && large_tiles >= 256) {
     const int64_t tiles = ((Mr + kLBM - 1) / kLBM) * (Nc / kLBN);
     hipLaunchKernelGGL(gemm_fp8_large_kernel<kMode>, dim3((unsigned)tiles), dim3(kLThreads), 0,
                        stream, A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C);

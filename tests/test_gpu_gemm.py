@@ -263,3 +263,51 @@ def test_linear_8b_up_forward_backward_sampled():
 
     ref = requant_cols(d["dy"], cols_n) @ requant_cols(d["x"], cols_k).T
     check(dw[np.ix_(cols_n, cols_k)], ref, "wgrad 12288x4096 (M=8192)", rms=float(np.sqrt(np.mean(ref ** 2))))
+
+
+# ---------------------------------------------------------------- unified precision flow
+
+def test_fprop_batch_invariant_across_kernels():
+    """The pages' unified flow makes the rollout graph a subgraph of the training
+    forward; at kernel level a token's FProp output must not depend on the batch
+    it is computed in.  Rows computed alone (decode, weight-streaming kernel),
+    in a mid-size batch (128 x 128 kernel) and inside a large training batch
+    (256 x 256 kernel) must be bitwise identical."""
+    rng = np.random.default_rng(21)
+    M, N, K = 2048, 1024, 1024  # 8 x 4 = 32 large tiles: below the large-kernel threshold
+    qx_all, qw = codes(rng, (M, K)), codes(rng, (N, K))
+    sx_all, sw = scales(rng, (K // 128, M)), scales(rng, (N // 128, K // 128))
+    qw_d, sw_d = u8_dev(qw), f32_dev(sw)
+    big_m = 16384  # 64 x 4 = 256 large tiles: the 256 x 256 kernel
+    qx_big = np.concatenate([qx_all] * (big_m // M))
+    sx_big = np.concatenate([sx_all] * (big_m // M), axis=1)
+    y_big = host(jet.gemm_fprop(u8_dev(qx_big), f32_dev(sx_big), qw_d, sw_d))[:M]
+    y_mid = host(jet.gemm_fprop(u8_dev(qx_all), f32_dev(sx_all), qw_d, sw_d))
+    assert np.array_equal(y_mid, y_big), "128x128 vs 256x256 kernel"
+    for m0, m in [(0, 1), (5, 16), (100, 33), (640, 64), (1000, 200)]:
+        y = host(jet.gemm_fprop(u8_dev(qx_all[m0:m0 + m]), f32_dev(np.ascontiguousarray(sx_all[:, m0:m0 + m])),
+                                qw_d, sw_d))
+        assert np.array_equal(y, y_big[m0:m0 + m]), f"rows {m0}..{m0 + m}"
+
+
+@pytest.mark.parametrize("k", [128, 512, 1024, 2048, 4096, 8192])
+@pytest.mark.parametrize("m", [1, 16, 17, 32, 50, 64])
+def test_fprop_decode_wave_splits(m, k):
+    """Decode FProp (M <= 64) at N = 384 (24 strips of 16 columns): K from one
+    K-block to 64 K-blocks walks the waves-per-strip choice through 1, 2, 4, 8
+    and 16, and M through 1, 2 and 4 token sub-tiles (17 and 50 are ragged).
+    Each result matches the oracle and equals, bit for bit, the same rows
+    computed inside a 65-token batch by the 128 x 128 kernel."""
+    n = 384
+    rng = np.random.default_rng(1000 + 13 * m + k)
+    qx, qw = codes(rng, (65, k)), codes(rng, (n, k))
+    sx, sw = scales(rng, (k // 128, 65)), scales(rng, (n // 128, k // 128))
+    qw_d, sw_d = u8_dev(qw), f32_dev(sw)
+    yg = Guarded((m, n), torch.bfloat16)
+    jet.gemm_fprop(u8_dev(qx[:m]), f32_dev(np.ascontiguousarray(sx[:, :m])), qw_d, sw_d, yg.t)
+    y65 = host(jet.gemm_fprop(u8_dev(qx), f32_dev(sx), qw_d, sw_d))
+    torch.cuda.synchronize()
+    assert yg.intact()
+    y = host(yg.t)
+    check(y, oracle.gemm_fprop_ref(qx[:m], np.ascontiguousarray(sx[:, :m]), qw, sw), f"decode fprop {m}x{n}x{k}")
+    assert np.array_equal(y, y65[:m]), "decode kernel vs 128 x 128 kernel"

@@ -259,8 +259,11 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // the other (otherwise it waits for those loads before every read).
 struct LStage {
   uint8_t ab[kLStage];
-  float sa[kLBM];  // A-row scales, transposed: row r at [(r % 16) * 16 + r / 16]
-  float sb[kLBN];  // WGrad: B-column scales; FProp/DGrad: [0], [1] = the two block scales
+  // FProp, DGrad: sc[h] holds fl32(sa(row) * sb(block h)) for the tile's two
+  // 128-column halves h, so the rescale needs no multiply; WGrad: sc[0] holds
+  // the A-row scales, sc[1] the 256 B-column scales in column order.  Rows are
+  // stored transposed: row r at [(r % 16) * 16 + r / 16].
+  float sc[2][kLBM];
 };
 
 // The MFMAs take the B-tile fragment as their first operand and the A-tile
@@ -301,32 +304,38 @@ struct LargeTile {
   // Direct loads of K-block kb into stage st: wave w fills 32 rows of each
   // operand tile, 8 rows (1 KB) per instruction; lane l covers row l / 8 of
   // the 8, chunk position l % 8, i.e. logical chunk (l % 8) ^ f(row).
-  __device__ __forceinline__ void issue(uint32_t kb, LStage& st) {
+  // Piece p < 4 is A rows 32 w + 8 p .., piece 4 + p the matching B rows.
+  __device__ __forceinline__ void issue_piece(uint32_t kb, LStage& st, int piece) const {
     uint8_t* As = st.ab;
     uint8_t* Bs = st.ab + kLBM * kBK;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    const int p = piece & 3;
+    if (piece < 4)
       buf_to_lds16(ra, As + (32 * w + 8 * p) * 128, va[p], kb * kBK);
-      if (kMode == kDgrad)
-        buf_to_lds16(rb, Bs + (w >> 2) * (128 * 128) + (32 * (w & 3) + 8 * p) * 128, vb[p], kb * kBK * N);
-      else
-        buf_to_lds16(rb, Bs + (32 * w + 8 * p) * 128, vb[p], kb * kBK);
-    }
+    else if (kMode == kDgrad)
+      buf_to_lds16(rb, Bs + (w >> 2) * (128 * 128) + (32 * (w & 3) + 8 * p) * 128, vb[p], kb * kBK * N);
+    else
+      buf_to_lds16(rb, Bs + (32 * w + 8 * p) * 128, vb[p], kb * kBK);
   }
-  // scales of one K-block, staged in LDS with the tiles: threads 0..255 fetch
-  // the A-row scales, threads 256..511 the B scales -- the 256 column scales
-  // (WGrad), or the block scales of the tile's two 128-column halves (FProp,
-  // DGrad; every thread of the half fetches one of the two).  All compute-side
-  // reads are then in-order LDS reads.  No divergent branches.
-  __device__ __forceinline__ float load_scale(uint32_t kb) const {
-    if (kMode == kWgrad) return b_half ? sb[kb * N + col0 + t8] : sa[kb * M + arow];
-    const uint32_t cb = col0 / kBN + (t8 & 1u);
+  __device__ __forceinline__ void issue(uint32_t kb, LStage& st) const {
+#pragma unroll
+    for (int piece = 0; piece < 8; ++piece) issue_piece(kb, st, piece);
+  }
+  // Scales of one K-block, staged in LDS with the tiles.  FProp, DGrad:
+  // thread t forms fl32(sa(row t % 256) * sb(block of column half t / 256)),
+  // the factor the rescale applies.  WGrad: threads 0..255 fetch the A-row
+  // scales, threads 256..511 the 256 B-column scales.  All compute-side reads
+  // are then in-order LDS reads.  No divergent branches.  The product is
+  // formed in store_scale, after the block's MFMAs, so that the loads' latency
+  // is never waited for up front.
+  __device__ __forceinline__ float2 load_scale(uint32_t kb) const {
+    if (kMode == kWgrad) return make_float2(b_half ? sb[kb * N + col0 + t8] : sa[kb * M + arow], 1.0f);
+    const uint32_t cb = col0 / kBN + ((uint32_t)t >> 8);
     const uint32_t bi = (kMode == kFprop) ? cb * nkb + kb : kb * (N / kBN) + cb;
-    return t >= kLBM ? sb[bi] : sa[kb * M + arow];
+    return make_float2(sa[kb * M + arow], sb[bi]);
   }
-  __device__ __forceinline__ void store_scale(LStage& st, float x) const {
-    if (t >= kLBM) st.sb[t8] = x;
-    else st.sa[(t8 & 15u) * 16u + (t8 >> 4)] = x;
+  __device__ __forceinline__ void store_scale(LStage& st, float2 x) const {
+    const uint32_t tr = (t8 & 15u) * 16u + (t8 >> 4);
+    st.sc[t >> 8][(kMode == kWgrad && t >= kLBM) ? t8 : tr] = (kMode == kWgrad) ? x.x : x.x * x.y;
   }
 
   __device__ __forceinline__ static v8i_t frag(const uint8_t* base, uint32_t o0, uint32_t o1) {
@@ -342,7 +351,9 @@ struct LargeTile {
   // the two chunk positions are fixed per lane and merely swap when bit 1 of i
   // is set: two base offsets plus an immediate 2048 i.  The same holds for
   // the B sub-tiles j.
-  __device__ __forceinline__ void compute(const LStage& st, v4f_t (&acc)[8][4]) const {
+  // The next K-block's direct loads (into the other stage) are issued one
+  // piece every four MFMAs, spread over the block instead of in one burst.
+  __device__ __forceinline__ void compute(const LStage& st, v4f_t (&acc)[8][4], uint32_t kn, LStage& nxt) const {
     const uint8_t* S = st.ab;
     // B fragments are read in the order the first row of MFMAs uses them,
     // each well ahead of its use (bf[0], bf[1] before the loop, bf[j + 2] at
@@ -365,11 +376,14 @@ struct LargeTile {
     af[0] = frag(S, a_even, a_odd);
     read_b(0);
     read_b(1);
-    // row scales of the 8 row sub-tiles (transposed layout: 8 contiguous floats)
+    // row factors of the 8 row sub-tiles (transposed layout: 8 contiguous
+    // floats); FProp, DGrad: the products for the column half holding the
+    // wave's 64 columns
     float srow[8];
     {
-      const float4 s0 = *reinterpret_cast<const float4*>(reinterpret_cast<const uint8_t*>(st.sa) + s_row);
-      const float4 s1 = *reinterpret_cast<const float4*>(reinterpret_cast<const uint8_t*>(st.sa) + s_row + 16);
+      const uint8_t* sr = reinterpret_cast<const uint8_t*>(st.sc[kMode == kWgrad ? 0 : (wn >> 1)]) + s_row;
+      const float4 s0 = *reinterpret_cast<const float4*>(sr);
+      const float4 s1 = *reinterpret_cast<const float4*>(sr + 16);
       srow[0] = s0.x; srow[1] = s0.y; srow[2] = s0.z; srow[3] = s0.w;
       srow[4] = s1.x; srow[5] = s1.y; srow[6] = s1.z; srow[7] = s1.w;
     }
@@ -377,13 +391,9 @@ struct LargeTile {
     if (kMode == kWgrad) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float4 c4 = *reinterpret_cast<const float4*>(&st.sb[wn * 64 + 16 * j + 4 * lk]);
+        const float4 c4 = *reinterpret_cast<const float4*>(&st.sc[1][wn * 64 + 16 * j + 4 * lk]);
         scol[j][0] = c4.x; scol[j][1] = c4.y; scol[j][2] = c4.z; scol[j][3] = c4.w;
       }
-    } else {
-      const float sblk = st.sb[wn >> 1];  // the wave's 64 columns lie in one 128-column block
-#pragma unroll
-      for (int i = 0; i < 8; ++i) srow[i] *= sblk;
     }
 
     // Software pipeline over the 32 (row, column) sub-tiles, row-major: step q
@@ -402,6 +412,7 @@ struct LargeTile {
         af[n & 1] = frag(S + 2048 * n, sw ? a_odd : a_even, sw ? a_even : a_odd);
       }
       if (q < 32) part[q % 3] = mfma_fp8(bf[j], af[i & 1]);
+      if (q < 32 && j == 1) issue_piece(kn, nxt, i);
       __builtin_amdgcn_sched_barrier(0);
       if (q >= 2) {
         const int qp = q - 2, pi = qp >> 2, pj = qp & 3;
@@ -487,18 +498,16 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
   for (uint32_t kb = 0; kb < g.nkb; kb += 2) {
     {
       const uint32_t kn = kb + 1 <= last ? kb + 1 : last;
-      const float x = g.load_scale(kn);
-      g.issue(kn, st1);
-      g.compute(st0, acc);
+      const float2 x = g.load_scale(kn);
+      g.compute(st0, acc, kn, st1);
       g.store_scale(st1, x);
       wait_vmem();
       __syncthreads();
     }
     if (kb + 1 <= last) {
       const uint32_t kn = kb + 2 <= last ? kb + 2 : last;
-      const float x = g.load_scale(kn);
-      g.issue(kn, st0);
-      g.compute(st1, acc);
+      const float2 x = g.load_scale(kn);
+      g.compute(st1, acc, kn, st0);
       g.store_scale(st0, x);
       wait_vmem();
       __syncthreads();

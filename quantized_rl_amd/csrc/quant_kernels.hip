@@ -16,41 +16,45 @@ namespace jetfp8 {
 // ---------------------------------------------------------------------------
 // 1x128 activation / gradient quantisation.
 //
-// A workgroup of 256 threads owns a tile of kActRows rows x one 128-column
-// group.  Each quarter-wave (16 lanes x 16 bytes = one 256-byte bf16 group)
-// handles one row at a time; every lane issues all of its loads before any
-// arithmetic so that kActRows / 16 groups are in flight per quarter-wave.
-// Scales of consecutive rows of one group are contiguous in S[g][*], so the
-// scale stores of a tile fill whole cache lines.
-constexpr int kActRows = 128;
-constexpr int kActIters = kActRows / 16;
+// A workgroup of 256 threads owns a tile of kActRows rows x 4 groups (512
+// columns).  Every load instruction of a wave reads 1 KB of one row (lane l:
+// bytes 16 l ..), so quarter-wave q holds group 4 c + q of that row; wave w
+// takes rows w, w + 4, ..  Each lane issues all of its loads before any
+// arithmetic.  The launch walks the column tiles of a row band fastest, so
+// the workgroups in flight stream contiguous memory, and the scales of the
+// tile's 32 rows of one group fill a 128-byte line of S[g][*].
+constexpr int kActRows = 32;
+constexpr int kActIters = kActRows / 4;
 
 __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t* __restrict__ x,
                                                               int64_t M, int64_t K,
                                                               uint8_t* __restrict__ q,
                                                               float* __restrict__ s) {
-  const int lane16 = threadIdx.x & 15;
-  const int quarter = threadIdx.x >> 4;  // 0..15
-  const int64_t g = blockIdx.y;
-  const int64_t row0 = (int64_t)blockIdx.x * kActRows + quarter;
+  const int l = threadIdx.x & 63, lane16 = l & 15;
+  const int wave = threadIdx.x >> 6;
+  const int64_t ctiles = (K / kGroup + 3) / 4;
+  const int64_t g = (int64_t)(blockIdx.x % ctiles) * 4 + (l >> 4);
+  const bool g_ok = g * kGroup < K;  // ragged last column tile (K % 512 != 0)
+  const int64_t col = g * kGroup + lane16 * 8;
+  const int64_t row0 = (int64_t)(blockIdx.x / ctiles) * kActRows + wave;
 
   uint4 v[kActIters];
 #pragma unroll
   for (int it = 0; it < kActIters; ++it) {
-    const int64_t r = row0 + 16 * it;
-    v[it] = r < M ? ld_stream16(x + r * K + g * kGroup + lane16 * 8) : make_uint4(0, 0, 0, 0);
+    const int64_t r = row0 + 4 * it;
+    v[it] = (r < M && g_ok) ? ld_stream16(x + r * K + col) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int it = 0; it < kActIters; ++it) {
-    const int64_t r = row0 + 16 * it;
+    const int64_t r = row0 + 4 * it;
     float f[8];
     unpack_bf16x8(v[it], f);
     const float amax = quarter_wave_max(absmax8(f));
     const float sc = scale_from_amax(amax);
     const double inv = 1.0 / (double)sc;
     const uint2 codes = quant8(f, inv);
-    if (r < M) {
-      st_stream8(q + r * K + g * kGroup + lane16 * 8, codes);
+    if (r < M && g_ok) {
+      st_stream8(q + r * K + col, codes);
       if (lane16 == 0) s[g * M + r] = sc;
     }
   }
@@ -123,9 +127,12 @@ __device__ __forceinline__ float tree8_sq(const float (&f)[8]) {
 // 512 p + 8 l, summed as a balanced tree, then a xor-butterfly over the wave
 // (offsets 1..32) gives the pass's 512-element subtree; the pass sums are
 // combined by the pairwise rule (odd tail carried).  Each partial is a node of
-// the canonical tree of the row zero-padded to a power of two.
+// the canonical tree of the row zero-padded to a power of two.  kP (passes) is
+// a template parameter so that all loads -- the row and gamma -- are issued
+// unconditionally up front; only the last pass can be partial.
 constexpr int kRowPasses = 16;  // K <= 8192
 
+template <int kP>
 __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(const uint16_t* __restrict__ x,
                                                                  const uint16_t* __restrict__ gamma,
                                                                  int64_t M, int64_t K, float eps,
@@ -135,56 +142,45 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(const uint16_t*
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;  // whole waves only
   const uint16_t* xr = x + row * K;
-  const int passes = (int)((K + 511) / 512);
 
-  uint4 xv[kRowPasses];
+  uint4 xv[kP], gv[kP];
 #pragma unroll
-  for (int p = 0; p < kRowPasses; ++p) {
+  for (int p = 0; p < kP; ++p) {
     const int64_t e = 512 * p + 8 * l;
-    xv[p] = (p < passes && e < K) ? ld_stream16(xr + e) : make_uint4(0, 0, 0, 0);
+    const bool in = p < kP - 1 || e < K;
+    xv[p] = in ? ld_stream16(xr + e) : make_uint4(0, 0, 0, 0);
+    gv[p] = in ? *reinterpret_cast<const uint4*>(gamma + e) : make_uint4(0, 0, 0, 0);
   }
-  float ps[kRowPasses];
+  float ps[kP];
 #pragma unroll
-  for (int p = 0; p < kRowPasses; ++p) {
-    float v = 0.0f;
-    if (p < passes) {
-      float f[8];
-      unpack_bf16x8(xv[p], f);
-      v = tree8_sq(f);
+  for (int p = 0; p < kP; ++p) {
+    float f[8];
+    unpack_bf16x8(xv[p], f);
+    float v = tree8_sq(f);
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off, 64);
-    }
+    for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off, 64);
     ps[p] = v;
   }
   // pairwise tree over the pass sums (all lanes hold the same values)
-  int n = passes;
 #pragma unroll
-  for (int lvl = 0; lvl < 4; ++lvl) {
-    if (n > 1) {
-      const int h = n / 2;
+  for (int n = kP; n > 1; n = n / 2 + (n & 1)) {
+    const int h = n / 2;
 #pragma unroll
-      for (int j = 0; j < kRowPasses / 2; ++j)
-        if (j < h) ps[j] = ps[2 * j] + ps[2 * j + 1];
-      if (n & 1) {
-#pragma unroll
-        for (int j = 0; j < kRowPasses / 2; ++j)
-          if (j == h) ps[j] = ps[n - 1];
-      }
-      n = h + (n & 1);
-    }
+    for (int j = 0; j < h; ++j) ps[j] = ps[2 * j] + ps[2 * j + 1];
+    if (n & 1) ps[h] = ps[n - 1];
   }
   const float ms = ps[0] / (float)K;
   const float inv = 1.0f / sqrt_rn(ms + eps);
 
   const int lane16 = l & 15, quarter = l >> 4;
 #pragma unroll
-  for (int p = 0; p < kRowPasses; ++p) {
+  for (int p = 0; p < kP; ++p) {
     const int64_t g = 4 * p + quarter;
-    if (p < passes && g * kGroup < K) {
+    if (p < kP - 1 || g * kGroup < K) {
       const int64_t e = g * kGroup + lane16 * 8;
       float f[8], gm[8];
       unpack_bf16x8(xv[p], f);
-      unpack_bf16x8(*reinterpret_cast<const uint4*>(gamma + e), gm);
+      unpack_bf16x8(gv[p], gm);
 #pragma unroll
       for (int i = 0; i < 8; ++i) f[i] = (f[i] * inv) * gm[i];
       const float amax = quarter_wave_max(absmax8(f));
@@ -194,6 +190,13 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(const uint16_t*
       if (lane16 == 0) s[g * M + row] = sc;
     }
   }
+}
+
+template <int kP>
+static void launch_rows(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps,
+                        uint8_t* q, float* s, hipStream_t stream) {
+  hipLaunchKernelGGL(rmsnorm_quant_rows_kernel<kP>, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream,
+                     x, gamma, M, K, eps, q, s);
 }
 
 // Wider rows: one workgroup (256 threads) per row, two passes over the row.
@@ -368,8 +371,8 @@ __global__ __launch_bounds__(256) void requant_transpose_kernel(const uint8_t* _
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s,
                             hipStream_t stream) {
   if (M == 0 || K == 0) return hipSuccess;
-  dim3 grid((unsigned)((M + kActRows - 1) / kActRows), (unsigned)(K / kGroup));
-  hipLaunchKernelGGL(quant_act_1x128_kernel, grid, dim3(256), 0, stream, x, M, K, q, s);
+  const int64_t tiles = ((K / kGroup + 3) / 4) * ((M + kActRows - 1) / kActRows);  // < 2^32
+  hipLaunchKernelGGL(quant_act_1x128_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, M, K, q, s);
   return hipGetLastError();
 }
 
@@ -385,8 +388,24 @@ hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, int64_
                                 float eps, uint8_t* q, float* s, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   if (K <= 512 * kRowPasses) {
-    hipLaunchKernelGGL(rmsnorm_quant_rows_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream,
-                       x, gamma, M, K, eps, q, s);
+    switch ((K + 511) / 512) {
+      case 1: launch_rows<1>(x, gamma, M, K, eps, q, s, stream); break;
+      case 2: launch_rows<2>(x, gamma, M, K, eps, q, s, stream); break;
+      case 3: launch_rows<3>(x, gamma, M, K, eps, q, s, stream); break;
+      case 4: launch_rows<4>(x, gamma, M, K, eps, q, s, stream); break;
+      case 5: launch_rows<5>(x, gamma, M, K, eps, q, s, stream); break;
+      case 6: launch_rows<6>(x, gamma, M, K, eps, q, s, stream); break;
+      case 7: launch_rows<7>(x, gamma, M, K, eps, q, s, stream); break;
+      case 8: launch_rows<8>(x, gamma, M, K, eps, q, s, stream); break;
+      case 9: launch_rows<9>(x, gamma, M, K, eps, q, s, stream); break;
+      case 10: launch_rows<10>(x, gamma, M, K, eps, q, s, stream); break;
+      case 11: launch_rows<11>(x, gamma, M, K, eps, q, s, stream); break;
+      case 12: launch_rows<12>(x, gamma, M, K, eps, q, s, stream); break;
+      case 13: launch_rows<13>(x, gamma, M, K, eps, q, s, stream); break;
+      case 14: launch_rows<14>(x, gamma, M, K, eps, q, s, stream); break;
+      case 15: launch_rows<15>(x, gamma, M, K, eps, q, s, stream); break;
+      default: launch_rows<16>(x, gamma, M, K, eps, q, s, stream); break;
+    }
     return hipGetLastError();
   }
   hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3((unsigned)M), dim3(256), 0, stream, x, gamma, M, K,

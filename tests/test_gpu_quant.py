@@ -156,7 +156,8 @@ def test_rmsnorm_quant_decode_shapes(m):
     assert_same(host(s), so, "s")
 
 
-@pytest.mark.parametrize("m,k", [(1, 128), (5, 640), (3, 2048), (7, 5120), (2, 12288), (2, 65536)])
+@pytest.mark.parametrize("m,k", [(1, 128), (5, 640), (3, 2048), (9, 4096), (7, 5120), (3, 7808), (4, 8192),
+                                 (2, 12288), (2, 65536)])
 def test_rmsnorm_quant_widths(m, k):
     xb = special_rows(m, k, seed=k)
     if m > 1:

@@ -553,21 +553,41 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
 //
 // One workgroup per 16 output columns.  Its kW waves compute the 128-deep
 // block partials P_kb = MFMA(W slice, X slice) of different K-blocks at once
-// (wave w takes K-block c * kW + w of chunk c, with kD K-blocks of loads in
-// flight per wave, loaded straight into registers), and park them in LDS.
-// After each chunk, wave i (one per 16 tokens) folds the chunk's partials in
-// ascending K order: acc = fma(P_kb, fl32(sx * sw), acc) -- exactly the
-// per-element operation sequence of the other FProp kernels, so a token's
-// output is bit-identical whichever kernel and batch size compute it.
-// kW (waves per strip) is chosen at launch so that the chip holds about 2048
-// streaming waves whatever the number of 16-column strips; with kW = 1 the
-// lone wave folds each partial as soon as it is computed, with no LDS.
+// (wave w takes K-block c * kW + w of chunk c, with kD K-blocks of operands
+// and scales in flight per wave, loaded straight into registers), and park
+// them in LDS with their factors fl32(sx * sw).  After each chunk, wave i (one
+// per 16 tokens) folds the chunk's partials in ascending K order:
+// acc = fma(P_kb, fl32(sx * sw), acc) -- exactly the per-element operation
+// sequence of the 128 x 128 and 256 x 256 FProp kernels, so a token's output
+// is bit-identical whichever of these kernels and batch sizes compute it.
+// kW (waves per strip) is chosen at launch from the strip count; with kW = 1
+// the lone wave folds each partial as soon as it is computed, with no LDS.
+//
+// Every prefetch load is issued on every path (clamped to the last block past
+// the end), so the compiler's wait before a slot's use covers that slot's
+// loads only, and the chunk barrier waits for LDS traffic only: a
+// __syncthreads() fence would drain the prefetched global loads every chunk.
 template <int kMT, int kW>  // kMT: row sub-tiles of 16 tokens (M <= 16 * kMT)
 struct DecodeCfg {
   // chunks of loads in flight per wave (a lone wave streams its whole strip)
   static constexpr int kD = kW == 1 ? (kMT == 1 ? 8 : (kMT == 2 ? 6 : 4)) : ((kMT >= 2 && kW == 16) ? 2 : 4);
   static_assert(kW == 1 || kW >= kMT, "one folding wave per 16-token sub-tile");
 };
+
+// Prefetched scale loads use the buffer-load intrinsic, as the operands do:
+// the compiler keeps these where they are issued, while a plain load would be
+// sunk to its use (and then waited for at once).  The offset is held in a
+// vector register even when it is uniform, so that the load takes the vector
+// memory path: a scalar-cache load can return out of order, and every use of
+// one waits for all of them, including the prefetches issued after it.
+__device__ __forceinline__ float ld_scale(rsrc_t r, uint32_t byte_off) {
+  __asm__("" : "+v"(byte_off));
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
+// Workgroup barrier for LDS traffic: waits for this wave's LDS operations,
+// not for its outstanding global loads.
+__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int kMT, int kW>
 __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
@@ -582,15 +602,17 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
   const rsrc_t rw = make_rsrc(W, N * K);
   const rsrc_t rx = make_rsrc(X, M * K);
   const uint32_t w_off = (n0 + lr) * K + 32u * lk;
-  uint32_t x_off[kMT];
+  uint32_t x_off[kMT], xm[kMT];
 #pragma unroll
   for (int i = 0; i < kMT; ++i) {
-    const uint32_t m = (16u * i + lr) < M ? (16u * i + lr) : (M - 1);  // ragged tail: repeat the last token
-    x_off[i] = m * K + 32u * lk;
+    xm[i] = (16u * i + lr) < M ? (16u * i + lr) : (M - 1);  // ragged tail: repeat the last token
+    x_off[i] = xm[i] * K + 32u * lk;
   }
-  const float* swrow = sw + (n0 / kBN) * nkb;
+  const rsrc_t rsx = make_rsrc(sx, nkb * M * 4u);
+  const rsrc_t rsw = make_rsrc(sw + (n0 / kBN) * nkb, nkb * 4u);
 
   v8i_t wr[kD], xr[kD][kMT];
+  float sxr[kD][kMT], swr[kD];
   auto load = [&](int slot, uint32_t c) {
     uint32_t kb = c * kW + (uint32_t)w;
     kb = kb < nkb ? kb : nkb - 1;  // past the end: a valid block whose product is not used
@@ -603,7 +625,9 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
       const v4i_t x0 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_off[i], kofs, 0);
       const v4i_t x1 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_off[i] + 16u, kofs, 0);
       xr[slot][i] = v8i_t{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      sxr[slot][i] = ld_scale(rsx, (kb * M + xm[i]) * 4u);
     }
+    swr[slot] = ld_scale(rsw, kb * 4u);
   };
 #pragma unroll
   for (int j = 0; j < kD; ++j) load(j, (uint32_t)j);
@@ -611,30 +635,23 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
   if constexpr (kW == 1) {
     // a lone wave per strip: fold each partial as soon as it is computed
     v4f_t acc1[kMT];
-    float sxm[kMT];
 #pragma unroll
     for (int i = 0; i < kMT; ++i) acc1[i] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma clang loop unroll(disable)
     for (uint32_t c0 = 0; c0 < nch; c0 += kD) {
 #pragma unroll
       for (int j = 0; j < kD; ++j) {
+        // Branch-free: a step past the end (a clamped, valid block) gets the
+        // factor 0 and leaves acc unchanged bit for bit (acc is never -0).
         const uint32_t kb = c0 + j;
-        if (kb < nkb) {
-          const float sb = swrow[kb];
 #pragma unroll
-          for (int i = 0; i < kMT; ++i) {
-            const uint32_t m = (16u * i + lr) < M ? (16u * i + lr) : (M - 1);
-            sxm[i] = sx[kb * M + m];
-          }
+        for (int i = 0; i < kMT; ++i) {
+          const v4f_t p = mfma_fp8(wr[j], xr[j][i]);
+          const float sc = kb < nkb ? sxr[j][i] * swr[j] : 0.0f;
 #pragma unroll
-          for (int i = 0; i < kMT; ++i) {
-            const v4f_t p = mfma_fp8(wr[j], xr[j][i]);
-            const float sc = sxm[i] * sb;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc1[i][e] = fmaf(p[e], sc, acc1[i][e]);
-          }
-          load(j, kb + kD);
+          for (int e = 0; e < 4; ++e) acc1[i][e] = fmaf(p[e], sc, acc1[i][e]);
         }
+        load(j, kb + kD);
       }
     }
 #pragma unroll
@@ -647,50 +664,178 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
       }
     }
   } else {
-  __shared__ v4f_t part[2][kW][kMT][64];
-  // the folding wave (w < kMT) owns token 16 w + lr, columns n0 + 4 lk .. + 3
-  const uint32_t my_m = (16u * (uint32_t)w + lr) < M ? (16u * (uint32_t)w + lr) : (M - 1);
-  v4f_t acc = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+    __shared__ v4f_t part[2][kW][kMT][64];
+    __shared__ float fac[2][kW][kMT][16];  // fl32(sx * sw) of each parked partial's tokens
+    // the folding wave (w < kMT) owns token 16 w + lr, columns n0 + 4 lk .. + 3
+    v4f_t acc = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma clang loop unroll(disable)
-  for (uint32_t c0 = 0; c0 < nch; c0 += kD) {
+    for (uint32_t c0 = 0; c0 < nch; c0 += kD) {
 #pragma unroll
-    for (int j = 0; j < kD; ++j) {
-      const uint32_t c = c0 + j;
-      if (c < nch) {
+      for (int j = 0; j < kD; ++j) {
+        // Branch-free partials (past the end they are parked but never folded),
+        // so the prefetched loads stay ahead of their uses.
+        const uint32_t c = c0 + j;
         const int buf = (int)(c & 1);
-        if (c * kW + (uint32_t)w < nkb) {
 #pragma unroll
-          for (int i = 0; i < kMT; ++i) part[buf][w][i][l] = mfma_fp8(wr[j], xr[j][i]);
+        for (int i = 0; i < kMT; ++i) {
+          part[buf][w][i][l] = mfma_fp8(wr[j], xr[j][i]);
+          if (lk == 0) fac[buf][w][i][lr] = sxr[j][i] * swr[j];
         }
-        load(j, c + kD);
-        float sc[kW];
-        if (w < kMT) {
+        lds_barrier();
+        {
+          if (w < kMT) {
 #pragma unroll
-          for (int k = 0; k < kW; ++k) {
-            const uint32_t kb = c * kW + k < nkb ? c * kW + k : nkb - 1;
-            sc[k] = sx[kb * M + my_m] * swrow[kb];
-          }
-        }
-        __syncthreads();
-        if (w < kMT) {
+            for (int k = 0; k < kW; ++k) {
+              if (c * kW + k < nkb) {
+                const v4f_t p = part[buf][k][w][l];
+                const float sc = fac[buf][k][w][lr];
 #pragma unroll
-          for (int k = 0; k < kW; ++k) {
-            if (c * kW + k < nkb) {
-              const v4f_t p = part[buf][k][w][l];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) acc[e] = fmaf(p[e], sc[k], acc[e]);
+                for (int e = 0; e < 4; ++e) acc[e] = fmaf(p[e], sc, acc[e]);
+              }
             }
           }
         }
+        load(j, c + kD);
       }
     }
+    if (w < kMT && 16u * (uint32_t)w + lr < M) {
+      const uint32_t m = 16u * (uint32_t)w + lr;
+      const uint32_t lo = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+      const uint32_t hi = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+      *reinterpret_cast<uint2*>(Y + (size_t)m * N + n0 + 4 * lk) = make_uint2(lo, hi);
+    }
   }
-  if (w < kMT && 16u * (uint32_t)w + lr < M) {
-    const uint32_t m = 16u * (uint32_t)w + lr;
-    const uint32_t lo = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-    const uint32_t hi = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
-    *reinterpret_cast<uint2*>(Y + (size_t)m * N + n0 + 4 * lk) = make_uint2(lo, hi);
+}
+
+// ---------------------------------------------------------------------------
+// Mid-size FProp (64 < M <= 256 tokens: large rollout batches).  Too few
+// output tiles to fill the chip without splitting K, so each workgroup owns a
+// 64 x 64 output tile and its 8 waves split the K-blocks: wave w takes blocks
+// w, w + 8, w + 16, .. and folds them in that order into its own fp32 tile,
+// acc = fma(P_kb, fl32(sx * sw), acc), with both operands streamed from
+// global memory straight into registers kMidD K-blocks ahead.  The eight wave
+// tiles are then summed in the fixed tree order
+// ((a0 + a4) + (a2 + a6)) + ((a1 + a5) + (a3 + a7)) through LDS.  The result is
+// deterministic and the same for a row whatever mid-size batch holds it, but
+// it is not the single sequential K fold of the other FProp kernels.
+constexpr int kMidD = 2;  // K-blocks of loads in flight per wave
+
+__global__ __launch_bounds__(512) void gemm_fp8_mid_kernel(const uint8_t* __restrict__ X,
+                                                           const float* __restrict__ sx,
+                                                           const uint8_t* __restrict__ W,
+                                                           const float* __restrict__ sw, uint32_t M,
+                                                           uint32_t N, uint32_t K,
+                                                           uint16_t* __restrict__ Y) {
+  __shared__ v4f_t red[4][16][64];  // 64 KB: one 64 x 64 fp32 tile per partner wave
+  const int t = threadIdx.x, l = t & 63, lr = l & 15, lk = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  // launch order: the row tiles of one 64-column weight slice are adjacent and
+  // on one XCD (blocks are dealt to the 8 XCDs round-robin), so the slice
+  // streams from HBM once and is re-read from that XCD's L2
+  const uint32_t ntm = (M + 63) / 64, total = ntm * (N / 64);
+  uint32_t id = blockIdx.x;
+  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+  const uint32_t m0 = (id % ntm) * 64u, n0 = (id / ntm) * 64u;
+  const uint32_t nkb = K / kBK;
+  const rsrc_t rw = make_rsrc(W, N * K);
+  const rsrc_t rx = make_rsrc(X, M * K);
+  uint32_t x_off[4], w_off[4], xm[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t m = m0 + 16u * i + lr;
+    xm[i] = m < M ? m : M - 1;  // ragged rows: repeat the last token, results not stored
+    x_off[i] = xm[i] * K + 32u * lk;
+    w_off[i] = (n0 + 16u * i + lr) * K + 32u * lk;
   }
+  const rsrc_t rsx = make_rsrc(sx, nkb * M * 4u);
+  const rsrc_t rsw = make_rsrc(sw + (n0 / kBN) * nkb, nkb * 4u);
+  const uint32_t my_n = (uint32_t)w < nkb ? (nkb - (uint32_t)w + 7u) / 8u : 0u;  // this wave's K-blocks
+
+  v8i_t xr[kMidD][4], wr[kMidD][4];
+  float sxr[kMidD][4], swr[kMidD];
+  auto load = [&](int slot, uint32_t j) {
+    uint32_t kb = (uint32_t)w + 8u * j;
+    kb = kb < nkb ? kb : nkb - 1;  // past the end: a valid block whose product is not used
+    const uint32_t kofs = kb * kBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const v4i_t a0 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_off[i], kofs, 0);
+      const v4i_t a1 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_off[i] + 16u, kofs, 0);
+      xr[slot][i] = v8i_t{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const v4i_t b0 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[i], kofs, 0);
+      const v4i_t b1 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[i] + 16u, kofs, 0);
+      wr[slot][i] = v8i_t{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      sxr[slot][i] = ld_scale(rsx, (kb * M + xm[i]) * 4u);
+    }
+    swr[slot] = ld_scale(rsw, kb * 4u);
+  };
+  v4f_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int d = 0; d < kMidD; ++d) load(d, (uint32_t)d);
+
+#pragma clang loop unroll(disable)
+  for (uint32_t c = 0; c < my_n; c += kMidD) {
+#pragma unroll
+    for (int d = 0; d < kMidD; ++d) {
+      {
+        // lane: token m0 + 16 i + lr, columns n0 + 16 j + 4 lk .. + 3.  Branch-
+        // free: a step past this wave's blocks gets the factor 0.
+        const bool valid = c + d < my_n;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float sc = valid ? sxr[d][i] * swr[d] : 0.0f;
+          v4f_t p[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p[j] = mfma_fp8(wr[d][j], xr[d][i]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(p[j][e], sc, acc[i][j][e]);
+        }
+      }
+      load(d, c + d + kMidD);  // on every path (clamped past the end): exact per-slot waits
+    }
+  }
+
+  // fixed-order combine of the eight wave tiles
+#pragma unroll
+  for (int half = 4; half >= 1; half >>= 1) {
+    if (w >= half && w < 2 * half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) red[w - half][4 * i + j][l] = acc[i][j];
+    }
+    __syncthreads();
+    if (w < half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const v4f_t o = red[w][4 * i + j][l];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] = acc[i][j][e] + o[e];
+        }
+    }
+    __syncthreads();
+  }
+  if (w == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t m = m0 + 16u * i + lr;
+      if (m < M) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
+          const uint32_t hi = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
+          *reinterpret_cast<uint2*>(Y + (size_t)m * N + n0 + 16 * j + 4 * lk) = make_uint2(lo, hi);
+        }
+      }
+    }
   }
 }
 
@@ -761,7 +906,25 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
   const bool fits32 = (Mr + kLBM) * Kc < (int64_t(1) << 31) && Nc * Kc < (int64_t(1) << 31) &&
                       (Mr + kLBM) * Nc * 2 < (int64_t(1) << 31);
   const int64_t large_tiles = ((Mr + kLBM - 1) / kLBM) * (Nc / kLBN);
-  if (Nc % kLBN == 0 && Mr >= kLBM && fits32 && large_tiles >= 256) {
+  // 65..256 rows: the K-split mid kernel unless the 256 x 256 kernel is
+  // expected to be faster.  Estimates (measured rates): the mid kernel moves
+  // (N/64) M K + ceil(M/64) N K operand bytes through register loads at about
+  // 5 TB/s; the large kernel takes about 2 us per K-block per round of 256
+  // tiles.  At the 8B decode shapes this picks the large kernel for gate+up
+  // (96 tiles, K = 4096) and the mid kernel for QKV and down.
+  bool mid = kMode == kFprop && Mr <= 256 && Nc * Kc < (int64_t(1) << 31) && Mr * Kc < (int64_t(1) << 31);
+  if (mid && Nc % kLBN == 0 && fits32) {
+    const double mid_us = ((double)(Nc / 64) * Mr * Kc + (double)((Mr + 63) / 64) * Nc * Kc) / 5.0e6;
+    const double large_us = (double)((large_tiles + 255) / 256) * (double)(Kc / kBK) * 2.0;
+    if (large_us < mid_us) mid = false;
+  }
+  if (mid) {
+    const int64_t tiles = (Nc / 64) * ((Mr + 63) / 64);
+    hipLaunchKernelGGL(gemm_fp8_mid_kernel, dim3((unsigned)tiles), dim3(512), 0, stream, A, sa, B, sb,
+                       (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C);
+    return hipGetLastError();
+  }
+  if (Nc % kLBN == 0 && fits32 && (large_tiles >= 256 || (kMode == kFprop && Mr <= 256))) {
     const int64_t tiles = ((Mr + kLBM - 1) / kLBM) * (Nc / kLBN);
     hipLaunchKernelGGL(gemm_fp8_large_kernel<kMode>, dim3((unsigned)tiles), dim3(kLThreads), 0,
                        stream, A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C);

@@ -270,9 +270,10 @@ def test_linear_8b_up_forward_backward_sampled():
 def test_fprop_batch_invariant_across_kernels():
     """The pages' unified flow makes the rollout graph a subgraph of the training
     forward; at kernel level a token's FProp output must not depend on the batch
-    it is computed in.  Rows computed alone (decode, weight-streaming kernel),
-    in a mid-size batch (128 x 128 kernel) and inside a large training batch
-    (256 x 256 kernel) must be bitwise identical."""
+    it is computed in.  Rows computed alone or in decode batches (M <= 64,
+    weight-streaming kernel), in a batch of a few hundred (128 x 128 kernel) and
+    inside a large training batch (256 x 256 kernel) must be bitwise identical.
+    (Batches of 65..256 rows use the K-split kernel: see test_fprop_mid_*.)"""
     rng = np.random.default_rng(21)
     M, N, K = 2048, 1024, 1024  # 8 x 4 = 32 large tiles: below the large-kernel threshold
     qx_all, qw = codes(rng, (M, K)), codes(rng, (N, K))
@@ -284,7 +285,7 @@ def test_fprop_batch_invariant_across_kernels():
     y_big = host(jet.gemm_fprop(u8_dev(qx_big), f32_dev(sx_big), qw_d, sw_d))[:M]
     y_mid = host(jet.gemm_fprop(u8_dev(qx_all), f32_dev(sx_all), qw_d, sw_d))
     assert np.array_equal(y_mid, y_big), "128x128 vs 256x256 kernel"
-    for m0, m in [(0, 1), (5, 16), (100, 33), (640, 64), (1000, 200)]:
+    for m0, m in [(0, 1), (5, 16), (100, 33), (640, 64), (1000, 300)]:
         y = host(jet.gemm_fprop(u8_dev(qx_all[m0:m0 + m]), f32_dev(np.ascontiguousarray(sx_all[:, m0:m0 + m])),
                                 qw_d, sw_d))
         assert np.array_equal(y, y_big[m0:m0 + m]), f"rows {m0}..{m0 + m}"
@@ -297,17 +298,63 @@ def test_fprop_decode_wave_splits(m, k):
     K-block to 64 K-blocks walks the waves-per-strip choice through 1, 2, 4, 8
     and 16, and M through 1, 2 and 4 token sub-tiles (17 and 50 are ragged).
     Each result matches the oracle and equals, bit for bit, the same rows
-    computed inside a 65-token batch by the 128 x 128 kernel."""
-    n = 384
+    computed inside a 257-token batch by the 128 x 128 kernel."""
+    n, mb = 384, 257
     rng = np.random.default_rng(1000 + 13 * m + k)
-    qx, qw = codes(rng, (65, k)), codes(rng, (n, k))
-    sx, sw = scales(rng, (k // 128, 65)), scales(rng, (n // 128, k // 128))
+    qx, qw = codes(rng, (mb, k)), codes(rng, (n, k))
+    sx, sw = scales(rng, (k // 128, mb)), scales(rng, (n // 128, k // 128))
     qw_d, sw_d = u8_dev(qw), f32_dev(sw)
     yg = Guarded((m, n), torch.bfloat16)
     jet.gemm_fprop(u8_dev(qx[:m]), f32_dev(np.ascontiguousarray(sx[:, :m])), qw_d, sw_d, yg.t)
-    y65 = host(jet.gemm_fprop(u8_dev(qx), f32_dev(sx), qw_d, sw_d))
+    yb = host(jet.gemm_fprop(u8_dev(qx), f32_dev(sx), qw_d, sw_d))
     torch.cuda.synchronize()
     assert yg.intact()
     y = host(yg.t)
     check(y, oracle.gemm_fprop_ref(qx[:m], np.ascontiguousarray(sx[:, :m]), qw, sw), f"decode fprop {m}x{n}x{k}")
-    assert np.array_equal(y, y65[:m]), "decode kernel vs 128 x 128 kernel"
+    assert np.array_equal(y, yb[:m]), "decode kernel vs 128 x 128 kernel"
+
+
+@pytest.mark.parametrize("n,k", [(128, 128), (384, 1152), (640, 4096), (256, 12288)])
+@pytest.mark.parametrize("m", [65, 100, 128, 200, 256])
+def test_fprop_mid_batches(m, n, k):
+    """FProp at 65..256 rows (K split over the eight waves of a workgroup):
+    parity with the oracle, guards intact, and every row bitwise equal to the
+    same row computed in the other mid-size batch (rows are independent and the
+    K split does not depend on M).  K = 1 .. 96 blocks covers waves with no
+    block, one block and several."""
+    rng = np.random.default_rng(2000 + m + n + k)
+    qx, qw = codes(rng, (256, k)), codes(rng, (n, k))
+    sx, sw = scales(rng, (k // 128, 256)), scales(rng, (n // 128, k // 128))
+    qw_d, sw_d = u8_dev(qw), f32_dev(sw)
+    sxm = np.ascontiguousarray(sx[:, :m])
+    yg = Guarded((m, n), torch.bfloat16)
+    jet.gemm_fprop(u8_dev(qx[:m]), f32_dev(sxm), qw_d, sw_d, yg.t)
+    other = 97 if m != 97 else 256
+    y_o = host(jet.gemm_fprop(u8_dev(qx[:other]), f32_dev(np.ascontiguousarray(sx[:, :other])), qw_d, sw_d))
+    torch.cuda.synchronize()
+    assert yg.intact()
+    y = host(yg.t)
+    check(y, oracle.gemm_fprop_ref(qx[:m], sxm, qw, sw), f"mid fprop {m}x{n}x{k}")
+    r = min(m, other)
+    assert np.array_equal(y[:r], y_o[:r]), "rows differ between mid-size batches"
+
+
+@pytest.mark.parametrize("m,n,k", [(130, 16384, 256), (256, 24576, 128), (97, 24576, 384)])
+def test_fprop_large_kernel_below_256_rows(m, n, k):
+    """65..256 rows with many output columns: the 256 x 256 kernel is chosen over
+    the K-split kernel (ragged single row tile).  Parity with the oracle, and
+    every row bitwise equal to the same row inside a 257-row batch (128 x 128
+    kernel): both fold K sequentially."""
+    rng = np.random.default_rng(3000 + m + k)
+    qx, qw = codes(rng, (257, k)), codes(rng, (n, k))
+    sx, sw = scales(rng, (k // 128, 257)), scales(rng, (n // 128, k // 128))
+    qw_d, sw_d = u8_dev(qw), f32_dev(sw)
+    sxm = np.ascontiguousarray(sx[:, :m])
+    yg = Guarded((m, n), torch.bfloat16)
+    jet.gemm_fprop(u8_dev(qx[:m]), f32_dev(sxm), qw_d, sw_d, yg.t)
+    yb = host(jet.gemm_fprop(u8_dev(qx), f32_dev(sx), qw_d, sw_d))
+    torch.cuda.synchronize()
+    assert yg.intact()
+    y = host(yg.t)
+    check(y, oracle.gemm_fprop_ref(qx[:m], sxm, qw, sw), f"fprop {m}x{n}x{k}")
+    assert np.array_equal(y, yb[:m]), "256 x 256 kernel (ragged rows) vs 128 x 128 kernel"

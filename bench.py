@@ -44,6 +44,7 @@ HBM_PEAK_GBS = 8000.0
 
 M, K, N = 8192, 4096, 12288
 EPS = 1e-6
+ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
 def parse():
@@ -75,6 +76,33 @@ def kernel_work():
         "requant_dy": ("GB/s", req(M, N)),
         "gemm_wgrad": ("TFLOP/s", g),
     }
+
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "qwen3_8b_up_step_hbm_traffic.md")
+
+
+def measured_traffic(kernel):
+    """HBM-side bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (calibrated against a plain copy), or None when that record was
+    taken on a different GEMM source than the one built here."""
+    import hashlib
+    try:
+        lines = open(TRAFFIC_RECORD).read().splitlines()
+    except OSError:
+        return None
+    want, table = None, {}
+    for ln in lines:
+        f = ln.split()
+        if len(f) == 3 and f[0] == "source_sha256":
+            want = (f[1], f[2])
+        elif len(f) == 3 and f[0] == "traffic_bytes":
+            table[f[1]] = int(f[2])
+    if want is None or kernel not in table:
+        return None
+    with open(os.path.join(ROOT, want[0]), "rb") as fh:
+        if hashlib.sha256(fh.read()).hexdigest() != want[1]:
+            return None
+    return table[kernel]
 
 
 def cpu_baseline(d, gamma):
@@ -256,7 +284,7 @@ def main():
     dom = max(("gemm_fprop", "gemm_dgrad", "gemm_wgrad"), key=lambda k: kernels[k]["avg_us"])
     roof = {"bound": "mfma", "kernel": dom, "achieved": kernels[dom]["rate"],
             "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(kernels[dom]["rate"] / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None}
+            "frac": round(kernels[dom]["rate"] / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": measured_traffic(dom)}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,

@@ -37,12 +37,26 @@ __device__ __forceinline__ float scale_from_amax(float amax) {
   return amax == 0.0f ? 1.0f : amax / kE4M3Max;
 }
 
+// Cross-lane moves inside a 16-lane DPP row (a quarter-wave), in registers:
+//   kXor1  quad_perm [1,0,3,2]: lane l reads lane l ^ 1
+//   kXor2  quad_perm [2,3,0,1]: lane l reads lane l ^ 2
+//   kHalfMirror row_half_mirror: lane l reads lane 7 - l within its 8-lane half-row
+//   kMirror     row_mirror:      lane l reads lane 15 - l within its row
+// Once every lane of an aligned group of 4 (resp. 8) holds the same value, the
+// two mirrors deliver the value of the neighbouring group, exactly as a xor 4
+// (resp. xor 8) exchange would.
+constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+
 // Max over the 16 lanes of a quarter-wave (lanes 16q .. 16q+15).
 __device__ __forceinline__ float quarter_wave_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1, 16));
-  v = fmaxf(v, __shfl_xor(v, 2, 16));
-  v = fmaxf(v, __shfl_xor(v, 4, 16));
-  v = fmaxf(v, __shfl_xor(v, 8, 16));
+  v = fmaxf(v, dpp<kXor1>(v));
+  v = fmaxf(v, dpp<kXor2>(v));
+  v = fmaxf(v, dpp<kHalfMirror>(v));
+  v = fmaxf(v, dpp<kMirror>(v));
   return v;
 }
 
@@ -50,6 +64,20 @@ __device__ __forceinline__ float wave_max(float v) {
   v = quarter_wave_max(v);
   v = fmaxf(v, __shfl_xor(v, 16, 64));
   v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+
+// Sum over the 64 lanes as the balanced binary tree over lane order: level k
+// adds the partial sums of the aligned lane groups of size 2^k that differ in
+// bit k (a xor butterfly), so every partial is a node of the canonical tree and
+// all lanes end with the same value.  Levels 0..3 stay inside a 16-lane row.
+__device__ __forceinline__ float wave_sum_tree(float v) {
+  v = v + dpp<kXor1>(v);
+  v = v + dpp<kXor2>(v);
+  v = v + dpp<kHalfMirror>(v);
+  v = v + dpp<kMirror>(v);
+  v = v + __shfl_xor(v, 16, 64);
+  v = v + __shfl_xor(v, 32, 64);
   return v;
 }
 

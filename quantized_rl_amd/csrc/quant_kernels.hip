@@ -157,8 +157,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(const uint16_t*
     float f[8];
     unpack_bf16x8(xv[p], f);
     float v = tree8_sq(f);
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off, 64);
+    v = wave_sum_tree(v);
     ps[p] = v;
   }
   // pairwise tree over the pass sums (all lanes hold the same values)
@@ -220,8 +219,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
       unpack_bf16x8(*reinterpret_cast<const uint4*>(xr + e), f);
       v = tree8_sq(f);
     }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off, 64);
+    v = wave_sum_tree(v);
     if (lane == 0) part[j][wave] = v;
   }
   __syncthreads();

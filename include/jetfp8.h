@@ -137,6 +137,13 @@ int requant_transpose_128x1(const uint8_t* q, const float* s, int64_t M, int64_t
  *   qw : u8 [N][K], sw : f32 [N/128][K/128] (quantize_weight_128x128 output)
  *   y  : bf16 [M][N].
  * K % 128 == 0, N % 128 == 0, M >= 0 (any M).  K == 0 writes zeros.
+ * Batch invariance: a row's output depends only on that row of (qx, sx) and on
+ * the weight.  For M <= 64 and M > 256 every kernel folds the K-blocks in
+ * ascending order with acc = fma(P_kb, fl32(sx * sw), acc), so the row is
+ * bitwise the same whatever M is.  Batches of 65..256 rows may run a kernel
+ * that folds 8 interleaved K-block subsets and sums them in a fixed order:
+ * deterministic and bitwise the same across such batches, but it may differ
+ * from the sequential fold in the last bits.
  */
 int gemm_fprop(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw, int64_t M,
                int64_t N, int64_t K, uint16_t* y, void* stream);

@@ -156,6 +156,24 @@ def test_rmsnorm_quant_decode_shapes(m):
     assert_same(host(s), so, "s")
 
 
+@pytest.mark.parametrize("m,k", [(8195, 4096), (8192, 2048)])
+def test_rmsnorm_quant_training_batches_sampled(m, k):
+    """Training-size batches (8k rows, the bench shape and a ragged one): bit-exact
+    against the oracle on sampled rows -- the first and last 64, rows around
+    the middle, and random rows (rows are independent)."""
+    rng = np.random.default_rng(m + k)
+    x = synth.random_bf16((m, k), seed=m + k, std=1.0)
+    g = synth.f32_to_bf16_bits((1 + 0.05 * rng.standard_normal(k)).astype(np.float32))
+    q, s = jet.rmsnorm_quant(bf16_dev(x), bf16_dev(g), 1e-6)
+    qh, sh = host(q), host(s)
+    half = (m + 1) // 2
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(m - 64, m), np.arange(half - 8, half + 8),
+                                     rng.integers(0, m, 64)]))
+    qo, so = oracle.rmsnorm_quant(x[rows], g, 1e-6)
+    assert_same(qh[rows], qo, "q")
+    assert_same(sh[:, rows], so, "s")
+
+
 @pytest.mark.parametrize("m,k", [(1, 128), (5, 640), (3, 2048), (9, 4096), (7, 5120), (3, 7808), (4, 8192),
                                  (2, 12288), (2, 65536)])
 def test_rmsnorm_quant_widths(m, k):

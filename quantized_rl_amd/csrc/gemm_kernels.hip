@@ -551,27 +551,34 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
 // Decode FProp (M <= 64 tokens, rollout): parallel weight streaming with the
 // sequential accumulation order kept.
 //
-// One workgroup per 16 output columns.  Its kW waves compute the 128-deep
-// block partials P_kb = MFMA(W slice, X slice) of different K-blocks at once
-// (wave w takes K-block c * kW + w of chunk c, with kD K-blocks of operands
-// and scales in flight per wave, loaded straight into registers), and park
-// them in LDS with their factors fl32(sx * sw).  After each chunk, wave i (one
+// One workgroup per kS strips of 16 output columns (a wave's X fragments
+// serve all kS strips).  Its kW waves compute the 128-deep block partials
+// P_kb = MFMA(W slice, X slice) of different K-blocks at once (wave w takes
+// K-block c * kW + w of chunk c, with kD K-blocks of operands and scales in
+// flight per wave, loaded straight into registers), and park them in LDS with
+// their factors fl32(sx * sw).  After each chunk, wave i (one
 // per 16 tokens) folds the chunk's partials in ascending K order:
 // acc = fma(P_kb, fl32(sx * sw), acc) -- exactly the per-element operation
 // sequence of the 128 x 128 and 256 x 256 FProp kernels, so a token's output
 // is bit-identical whichever of these kernels and batch sizes compute it.
-// kW (waves per strip) is chosen at launch from the strip count; with kW = 1
-// the lone wave folds each partial as soon as it is computed, with no LDS.
+// kS and kW are chosen at launch from the strip count; with kW = 1 the lone
+// wave folds each partial as soon as it is computed, with no LDS.
 //
 // Every prefetch load is issued on every path (clamped to the last block past
 // the end), so the compiler's wait before a slot's use covers that slot's
 // loads only, and the chunk barrier waits for LDS traffic only: a
 // __syncthreads() fence would drain the prefetched global loads every chunk.
-template <int kMT, int kW>  // kMT: row sub-tiles of 16 tokens (M <= 16 * kMT)
+template <int kMT, int kW, int kS>  // token sub-tiles (M <= 16 kMT), K-phases, strips per wave
 struct DecodeCfg {
-  // chunks of loads in flight per wave (a lone wave streams its whole strip)
-  static constexpr int kD = kW == 1 ? (kMT == 1 ? 8 : (kMT == 2 ? 6 : 4)) : ((kMT >= 2 && kW == 16) ? 2 : 4);
+  // K-blocks of operands in flight per wave: about 128 registers of slots
+  // (56 with 16 waves per workgroup, which leaves 128 registers per lane)
+  static constexpr int kSlotRegs = 8 * (kS + kMT);
+  static constexpr int kFit = (kW == 16 ? 56 : 128) / kSlotRegs;
+  static constexpr int kMax = kW == 1 ? 8 : 4;
+  static constexpr int kD = kFit > kMax ? kMax : (kFit < 1 ? 1 : kFit);
   static_assert(kW == 1 || kW >= kMT, "one folding wave per 16-token sub-tile");
+  static_assert(kW == 1 || kW * kMT * kS <= 64, "parked partials must fit in LDS");
+  static_assert(16 * kS <= kBN, "a wave's strips lie in one 128-column weight block");
 };
 
 // Prefetched scale loads use the buffer-load intrinsic, as the operands do:
@@ -589,20 +596,21 @@ __device__ __forceinline__ float ld_scale(rsrc_t r, uint32_t byte_off) {
 // not for its outstanding global loads.
 __device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int kMT, int kW>
+template <int kMT, int kW, int kS>
 __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
     const uint8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, uint32_t M, uint32_t N, uint32_t K, uint16_t* __restrict__ Y) {
-  constexpr int kD = DecodeCfg<kMT, kW>::kD;
+  constexpr int kD = DecodeCfg<kMT, kW, kS>::kD;
   const int t = threadIdx.x, l = t & 63, lr = l & 15, lk = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const uint32_t n0 = blockIdx.x * 16u;
+  const uint32_t n0 = blockIdx.x * (16u * kS);  // the workgroup's kS strips of 16 columns
   const uint32_t nkb = K / kBK;
   const uint32_t nch = (nkb + kW - 1) / kW;
   const rsrc_t rw = make_rsrc(W, N * K);
   const rsrc_t rx = make_rsrc(X, M * K);
-  const uint32_t w_off = (n0 + lr) * K + 32u * lk;
-  uint32_t x_off[kMT], xm[kMT];
+  uint32_t w_off[kS], x_off[kMT], xm[kMT];
+#pragma unroll
+  for (int s = 0; s < kS; ++s) w_off[s] = (n0 + 16u * s + lr) * K + 32u * lk;
 #pragma unroll
   for (int i = 0; i < kMT; ++i) {
     xm[i] = (16u * i + lr) < M ? (16u * i + lr) : (M - 1);  // ragged tail: repeat the last token
@@ -611,15 +619,18 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
   const rsrc_t rsx = make_rsrc(sx, nkb * M * 4u);
   const rsrc_t rsw = make_rsrc(sw + (n0 / kBN) * nkb, nkb * 4u);
 
-  v8i_t wr[kD], xr[kD][kMT];
+  v8i_t wr[kD][kS], xr[kD][kMT];
   float sxr[kD][kMT], swr[kD];
   auto load = [&](int slot, uint32_t c) {
     uint32_t kb = c * kW + (uint32_t)w;
     kb = kb < nkb ? kb : nkb - 1;  // past the end: a valid block whose product is not used
     const uint32_t kofs = kb * kBK;
-    const v4i_t w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off, kofs, 0);
-    const v4i_t w1 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off + 16u, kofs, 0);
-    wr[slot] = v8i_t{w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int s = 0; s < kS; ++s) {
+      const v4i_t w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[s], kofs, 0);
+      const v4i_t w1 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[s] + 16u, kofs, 0);
+      wr[slot][s] = v8i_t{w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    }
 #pragma unroll
     for (int i = 0; i < kMT; ++i) {
       const v4i_t x0 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_off[i], kofs, 0);
@@ -633,10 +644,12 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
   for (int j = 0; j < kD; ++j) load(j, (uint32_t)j);
 
   if constexpr (kW == 1) {
-    // a lone wave per strip: fold each partial as soon as it is computed
-    v4f_t acc1[kMT];
+    // a lone wave per strip group: fold each partial as soon as it is computed
+    v4f_t acc1[kMT][kS];
 #pragma unroll
-    for (int i = 0; i < kMT; ++i) acc1[i] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < kMT; ++i)
+#pragma unroll
+      for (int s = 0; s < kS; ++s) acc1[i][s] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma clang loop unroll(disable)
     for (uint32_t c0 = 0; c0 < nch; c0 += kD) {
 #pragma unroll
@@ -646,10 +659,13 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
         const uint32_t kb = c0 + j;
 #pragma unroll
         for (int i = 0; i < kMT; ++i) {
-          const v4f_t p = mfma_fp8(wr[j], xr[j][i]);
           const float sc = kb < nkb ? sxr[j][i] * swr[j] : 0.0f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc1[i][e] = fmaf(p[e], sc, acc1[i][e]);
+          for (int s = 0; s < kS; ++s) {
+            const v4f_t p = mfma_fp8(wr[j][s], xr[j][i]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc1[i][s][e] = fmaf(p[e], sc, acc1[i][s][e]);
+          }
         }
         load(j, kb + kD);
       }
@@ -658,16 +674,21 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
     for (int i = 0; i < kMT; ++i) {
       const uint32_t m = 16u * i + lr;
       if (m < M) {
-        const uint32_t lo = f32_to_bf16_rne(acc1[i][0]) | (f32_to_bf16_rne(acc1[i][1]) << 16);
-        const uint32_t hi = f32_to_bf16_rne(acc1[i][2]) | (f32_to_bf16_rne(acc1[i][3]) << 16);
-        *reinterpret_cast<uint2*>(Y + (size_t)m * N + n0 + 4 * lk) = make_uint2(lo, hi);
+#pragma unroll
+        for (int s = 0; s < kS; ++s) {
+          const uint32_t lo = f32_to_bf16_rne(acc1[i][s][0]) | (f32_to_bf16_rne(acc1[i][s][1]) << 16);
+          const uint32_t hi = f32_to_bf16_rne(acc1[i][s][2]) | (f32_to_bf16_rne(acc1[i][s][3]) << 16);
+          *reinterpret_cast<uint2*>(Y + (size_t)m * N + n0 + 16 * s + 4 * lk) = make_uint2(lo, hi);
+        }
       }
     }
   } else {
-    __shared__ v4f_t part[2][kW][kMT][64];
+    __shared__ v4f_t part[2][kW][kMT][kS][64];
     __shared__ float fac[2][kW][kMT][16];  // fl32(sx * sw) of each parked partial's tokens
-    // the folding wave (w < kMT) owns token 16 w + lr, columns n0 + 4 lk .. + 3
-    v4f_t acc = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // the folding wave (w < kMT) owns token 16 w + lr, columns n0 + 16 s + 4 lk .. + 3
+    v4f_t acc[kS];
+#pragma unroll
+    for (int s = 0; s < kS; ++s) acc[s] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma clang loop unroll(disable)
     for (uint32_t c0 = 0; c0 < nch; c0 += kD) {
 #pragma unroll
@@ -678,19 +699,21 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
         const int buf = (int)(c & 1);
 #pragma unroll
         for (int i = 0; i < kMT; ++i) {
-          part[buf][w][i][l] = mfma_fp8(wr[j], xr[j][i]);
+#pragma unroll
+          for (int s = 0; s < kS; ++s) part[buf][w][i][s][l] = mfma_fp8(wr[j][s], xr[j][i]);
           if (lk == 0) fac[buf][w][i][lr] = sxr[j][i] * swr[j];
         }
         lds_barrier();
-        {
-          if (w < kMT) {
+        if (w < kMT) {
 #pragma unroll
-            for (int k = 0; k < kW; ++k) {
-              if (c * kW + k < nkb) {
-                const v4f_t p = part[buf][k][w][l];
-                const float sc = fac[buf][k][w][lr];
+          for (int k = 0; k < kW; ++k) {
+            if (c * kW + k < nkb) {
+              const float sc = fac[buf][k][w][lr];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = fmaf(p[e], sc, acc[e]);
+              for (int s = 0; s < kS; ++s) {
+                const v4f_t p = part[buf][k][w][s][l];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[s][e] = fmaf(p[e], sc, acc[s][e]);
               }
             }
           }
@@ -700,9 +723,12 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
     }
     if (w < kMT && 16u * (uint32_t)w + lr < M) {
       const uint32_t m = 16u * (uint32_t)w + lr;
-      const uint32_t lo = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-      const uint32_t hi = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
-      *reinterpret_cast<uint2*>(Y + (size_t)m * N + n0 + 4 * lk) = make_uint2(lo, hi);
+#pragma unroll
+      for (int s = 0; s < kS; ++s) {
+        const uint32_t lo = f32_to_bf16_rne(acc[s][0]) | (f32_to_bf16_rne(acc[s][1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(acc[s][2]) | (f32_to_bf16_rne(acc[s][3]) << 16);
+        *reinterpret_cast<uint2*>(Y + (size_t)m * N + n0 + 16 * s + 4 * lk) = make_uint2(lo, hi);
+      }
     }
   }
 }
@@ -853,31 +879,45 @@ static hipError_t launch_zero(uint16_t* p, int64_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int kMT, int kW>
+template <int kMT, int kW, int kS>
 static void launch_decode_t(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
                             uint32_t m, uint32_t n, uint32_t k, uint16_t* C, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_fp8_decode_kernel<kMT, kW>), dim3(n / 16), dim3(64 * kW), 0, stream, A, sa, B,
-                     sb, m, n, k, C);
+  hipLaunchKernelGGL((gemm_fp8_decode_kernel<kMT, kW, kS>), dim3(n / (16 * kS)), dim3(64 * kW), 0, stream,
+                     A, sa, B, sb, m, n, k, C);
 }
 
-template <int kMT>
-static void launch_decode_m(int kw, const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
-                            uint32_t m, uint32_t n, uint32_t k, uint16_t* C, hipStream_t stream) {
+// kw is rounded to an instantiated value: at least kMT (one folding wave per
+// token sub-tile) and with the parked partials within LDS.
+template <int kMT, int kS>
+static void launch_decode_ms(int kw, const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
+                             uint32_t m, uint32_t n, uint32_t k, uint16_t* C, hipStream_t stream) {
+  constexpr int kW2 = kMT > 2 ? kMT : 2;
+  constexpr int kW8 = 8 * kMT * kS <= 64 ? 8 : (4 * kMT * kS <= 64 ? 4 : kW2);
+  constexpr int kW16 = 16 * kMT * kS <= 64 ? 16 : kW8;
+  constexpr int kW4 = 4 * kMT * kS <= 64 ? 4 : kW2;
   switch (kw) {
-    case 1: launch_decode_t<kMT, 1>(A, sa, B, sb, m, n, k, C, stream); break;
-    case 2: launch_decode_t<kMT, (kMT > 2 ? kMT : 2)>(A, sa, B, sb, m, n, k, C, stream); break;
-    case 4: launch_decode_t<kMT, 4>(A, sa, B, sb, m, n, k, C, stream); break;
-    case 8: launch_decode_t<kMT, 8>(A, sa, B, sb, m, n, k, C, stream); break;
-    default: launch_decode_t<kMT, 16>(A, sa, B, sb, m, n, k, C, stream); break;
+    case 1: launch_decode_t<kMT, 1, kS>(A, sa, B, sb, m, n, k, C, stream); break;
+    case 2: launch_decode_t<kMT, kW2, kS>(A, sa, B, sb, m, n, k, C, stream); break;
+    case 4: launch_decode_t<kMT, kW4, kS>(A, sa, B, sb, m, n, k, C, stream); break;
+    case 8: launch_decode_t<kMT, kW8, kS>(A, sa, B, sb, m, n, k, C, stream); break;
+    default: launch_decode_t<kMT, kW16, kS>(A, sa, B, sb, m, n, k, C, stream); break;
   }
 }
 
-static void launch_decode(int mt, int kw, const uint8_t* A, const float* sa, const uint8_t* B,
+template <int kMT>
+static void launch_decode_m(int kw, int ks, const uint8_t* A, const float* sa, const uint8_t* B,
+                            const float* sb, uint32_t m, uint32_t n, uint32_t k, uint16_t* C,
+                            hipStream_t stream) {
+  if (ks == 2) launch_decode_ms<kMT, 2>(kw, A, sa, B, sb, m, n, k, C, stream);
+  else launch_decode_ms<kMT, 1>(kw, A, sa, B, sb, m, n, k, C, stream);
+}
+
+static void launch_decode(int mt, int kw, int ks, const uint8_t* A, const float* sa, const uint8_t* B,
                           const float* sb, uint32_t m, uint32_t n, uint32_t k, uint16_t* C,
                           hipStream_t stream) {
-  if (mt == 1) launch_decode_m<1>(kw, A, sa, B, sb, m, n, k, C, stream);
-  else if (mt == 2) launch_decode_m<2>(kw, A, sa, B, sb, m, n, k, C, stream);
-  else launch_decode_m<4>(kw, A, sa, B, sb, m, n, k, C, stream);
+  if (mt == 1) launch_decode_m<1>(kw, ks, A, sa, B, sb, m, n, k, C, stream);
+  else if (mt == 2) launch_decode_m<2>(kw, ks, A, sa, B, sb, m, n, k, C, stream);
+  else launch_decode_m<4>(kw, ks, A, sa, B, sb, m, n, k, C, stream);
 }
 
 template <int kMode>
@@ -888,18 +928,22 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
   if (Kc == 0) return launch_zero(C, Mr * Nc, stream);
   // rollout decode: weight-streaming kernel for up to 64 tokens (FProp)
   if (kMode == kFprop && Mr <= 64 && Nc * Kc < (int64_t(1) << 31) && Mr * Kc < (int64_t(1) << 31)) {
-    // Waves per strip: enough for about 2048 / mt streaming waves (a wave
-    // with mt token sub-tiles does mt times the MFMA and X-load work per
-    // K-block), or 4096 for long K, where a strip's sequential chain is long;
-    // at most 16, and at most one per two K-blocks.  Measured on the 8B decode
-    // shapes (K = 4096 and 12288, N = 4096 .. 24576, M = 1 .. 64).
-    const int64_t strips = Nc / 16, nkb = Kc / kBK;
+    // Strips per wave: 2 when there are at least 384 strips of 16 columns
+    // (each X fragment then serves two strips), else 1.  Waves per strip
+    // group: enough for about 1024 / mt streaming waves (a wave with mt token
+    // sub-tiles does mt times the MFMA and X-load work per K-block), or 2048
+    // for long K, where a group's sequential chain is long; at most 16, and
+    // at most one per two K-blocks.  Measured on the 8B decode shapes
+    // (K = 4096 and 12288, N = 4096 .. 24576, M = 1 .. 64).
+    const int64_t nkb = Kc / kBK;
     const int mt = Mr <= 16 ? 1 : (Mr <= 32 ? 2 : 4);
-    const int64_t target = nkb >= 64 ? 4096 : 2048 / mt;
+    const int ks = Nc / 16 >= 384 ? 2 : 1;
+    const int64_t groups = Nc / (16 * ks);
+    const int64_t target = nkb >= 64 ? 2048 : 1024 / mt;
     int kw = 16;
-    while (kw > 1 && (strips * kw > target || kw > (nkb + 1) / 2)) kw /= 2;
+    while (kw > 1 && (groups * kw > target || kw > (nkb + 1) / 2)) kw /= 2;
     if (kw > 1 && kw < mt) kw = mt;  // wave i folds token sub-tile i
-    launch_decode(mt, kw, A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C, stream);
+    launch_decode(mt, kw, ks, A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C, stream);
     return hipGetLastError();
   }
   // the large-tile kernel works with 32-bit byte offsets

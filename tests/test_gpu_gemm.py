@@ -358,3 +358,27 @@ def test_fprop_large_kernel_below_256_rows(m, n, k):
     y = host(yg.t)
     check(y, oracle.gemm_fprop_ref(qx[:m], sxm, qw, sw), f"fprop {m}x{n}x{k}")
     assert np.array_equal(y, yb[:m]), "256 x 256 kernel (ragged rows) vs 128 x 128 kernel"
+
+
+@pytest.mark.parametrize("k", [256, 1024, 4096])
+@pytest.mark.parametrize("m", [1, 17, 33, 64])
+def test_fprop_decode_two_strips_per_wave(m, k):
+    """Decode FProp with 384 strips of 16 columns (N = 6144, the 8B QKV width):
+    each wave serves two strips with one set of X fragments.  M = 1 .. 64 and
+    K = 2 .. 32 blocks walk one, two and four token sub-tiles with 1, 2 and 4
+    waves per strip pair.  Parity with the oracle, and every row bitwise equal
+    to the same row in a 257-row batch (128 x 128 kernel)."""
+    n, mb = 6144, 257
+    rng = np.random.default_rng(4000 + 7 * m + k)
+    qx, qw = codes(rng, (mb, k)), codes(rng, (n, k))
+    sx, sw = scales(rng, (k // 128, mb)), scales(rng, (n // 128, k // 128))
+    qw_d, sw_d = u8_dev(qw), f32_dev(sw)
+    sxm = np.ascontiguousarray(sx[:, :m])
+    yg = Guarded((m, n), torch.bfloat16)
+    jet.gemm_fprop(u8_dev(qx[:m]), f32_dev(sxm), qw_d, sw_d, yg.t)
+    yb = host(jet.gemm_fprop(u8_dev(qx), f32_dev(sx), qw_d, sw_d))
+    torch.cuda.synchronize()
+    assert yg.intact()
+    y = host(yg.t)
+    check(y, oracle.gemm_fprop_ref(qx[:m], sxm, qw, sw), f"decode fprop {m}x{n}x{k}")
+    assert np.array_equal(y, yb[:m]), "decode kernel vs 128 x 128 kernel"

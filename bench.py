@@ -44,6 +44,7 @@ HBM_PEAK_GBS = 8000.0
 
 M, K, N = 8192, 4096, 12288
 EPS = 1e-6
+DECODE_WEIGHT_SETS = 4
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -175,16 +176,26 @@ def bench_decode(args):
 
     x, gamma, h = bf16(d["x"]), bf16(d["gamma"]), bf16(d["down_in"])
     wq = {k: jet.quantize_weight_128x128(bf16(d[k])) for k in ("w_qkv", "w_gu", "w_down")}
+    # The three FP8 weights total 176 MB, which the 256 MB MALL could hold from one
+    # step to the next; consecutive steps therefore rotate over DECODE_WEIGHT_SETS
+    # copies (704 MB), so every step streams its weights from HBM.
+    sets = [wq] + [{k: (q.clone(), s.clone()) for k, (q, s) in wq.items()} for _ in range(DECODE_WEIGHT_SETS - 1)]
     torch.cuda.synchronize()
     qx, sx = jet.rmsnorm_quant(x, gamma, d["eps"])
     qh, sh = jet.quantize_act_1x128(h)
     y = {k: torch.empty((m, wq[k][0].shape[0]), dtype=torch.bfloat16, device=dev) for k in wq}
+    cur = [0]
+
+    def norm():
+        cur[0] = (cur[0] + 1) % len(sets)
+        jet.rmsnorm_quant(x, gamma, d["eps"], qx, sx)
+
     steps = [
-        ("rmsnorm_quant", lambda: jet.rmsnorm_quant(x, gamma, d["eps"], qx, sx)),
-        ("gemm_fprop_qkv", lambda: jet.gemm_fprop(qx, sx, *wq["w_qkv"], y["w_qkv"])),
-        ("gemm_fprop_gate_up", lambda: jet.gemm_fprop(qx, sx, *wq["w_gu"], y["w_gu"])),
+        ("rmsnorm_quant", norm),
+        ("gemm_fprop_qkv", lambda: jet.gemm_fprop(qx, sx, *sets[cur[0]]["w_qkv"], y["w_qkv"])),
+        ("gemm_fprop_gate_up", lambda: jet.gemm_fprop(qx, sx, *sets[cur[0]]["w_gu"], y["w_gu"])),
         ("quantize_act_1x128", lambda: jet.quantize_act_1x128(h, qh, sh)),
-        ("gemm_fprop_down", lambda: jet.gemm_fprop(qh, sh, *wq["w_down"], y["w_down"])),
+        ("gemm_fprop_down", lambda: jet.gemm_fprop(qh, sh, *sets[cur[0]]["w_down"], y["w_down"])),
     ]
     per, step_ms, wall = time_steps(torch, steps, args.steps, args.warmup, dev)
     ms_per_step = float(np.mean(step_ms))
@@ -208,7 +219,8 @@ def bench_decode(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3",
         "data": "synthetic",
         "config": {"workload": "qwen3_8b_decode", "M": m, "K": 4096,
-                   "weights": "qkv 6144x4096, gate_up 24576x4096, down 4096x12288", "seed": 2},
+                   "weights": "qkv 6144x4096, gate_up 24576x4096, down 4096x12288", "seed": 2,
+                   "weight_sets_rotated": DECODE_WEIGHT_SETS},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["weight_GBps"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": kernels[dom]["frac_hbm"], "traffic": None},
         "kernels": kernels,

@@ -50,6 +50,35 @@ def test_decode_8b(m):
                   f"decode down M={m}")
 
 
+@pytest.mark.parametrize("m", [16, 64])
+def test_unified_flow_rollout_rows_inside_training_batch(m):
+    """The unified precision flow at kernel level: the rollout graph is a
+    subgraph of the training forward.  The decode tokens of the 8B workload,
+    normalised+quantised and multiplied by the FP8 QKV weight at rollout shape
+    (M = 16 / 64: decode kernel) and inside an 8192-token training batch
+    (256 x 256 kernel), give identical FP8 codes, scales and FProp outputs, bit
+    for bit; the rollout side also matches the oracle."""
+    d = synth.decode_8b(m)
+    eps, r0 = d["eps"], 1000
+    big = synth.random_bf16((8192, 4096), seed=77 + m, std=1.0)
+    big[r0:r0 + m] = d["x"]
+    g_d = bf16_dev(d["gamma"])
+    qd, sd = jet.rmsnorm_quant(bf16_dev(d["x"]), g_d, eps)
+    qb, sb = jet.rmsnorm_quant(bf16_dev(big), g_d, eps)
+    qw, sw = jet.quantize_weight_128x128(bf16_dev(d["w_qkv"]))
+    yd = host(jet.gemm_fprop(qd, sd, qw, sw))
+    yb = host(jet.gemm_fprop(qb, sb, qw, sw))[r0:r0 + m]
+    qdh, sdh = host(qd), host(sd)
+    assert np.array_equal(qdh, host(qb)[r0:r0 + m]), "FP8 codes differ between rollout and training batch"
+    assert np.array_equal(sdh.view(np.uint32), host(sb)[:, r0:r0 + m].view(np.uint32)), "scales differ"
+    assert np.array_equal(yd, yb), "FProp output differs between rollout and training batch"
+    qo, so = oracle.rmsnorm_quant(d["x"], d["gamma"], eps)
+    assert np.array_equal(qdh, qo) and np.array_equal(sdh.view(np.uint32), so.view(np.uint32))
+    cols = np.sort(np.random.default_rng(m).choice(6144, 96, replace=False))
+    check_sampled(yd[:, cols], oracle.dequant_groups(qo, so) @ weight_rows_deq(d["w_qkv"], cols).T,
+                  f"rollout qkv M={m}")
+
+
 @pytest.mark.parametrize("name", ["qkv", "o", "gate_up", "down"])
 def test_llama_layer0(name):
     d = synth.llama_layer(0, name)

@@ -149,6 +149,23 @@ int gemm_fprop(const uint8_t* qx, const float* sx, const uint8_t* qw, const floa
                int64_t N, int64_t K, uint16_t* y, void* stream);
 
 /*
+ * gemm_fprop_quant -- gemm_fprop, plus the 1x128 quantisation of its output for
+ * the next layer's GEMM (the fused quantisation that removes a separate pass
+ * over Y: [P3-CORE] on fusing quantisation into the producing kernels, [P3-STEPS]
+ * step 2):
+ *   y = gemm_fprop(qx, sx, qw, sw)   (bf16 [M][N], as gemm_fprop)
+ *   (qy, sy) = quantize_act_1x128(y) (qy u8 [M][N], sy f32 [N/128][M]),
+ * bit for bit: the quantisation reads the bf16 values of y.  The 1x128
+ * quantiser runs right after the GEMM on the same stream (measured faster on
+ * gfx950 than quantising in the GEMM epilogue).  Same shape rules as
+ * gemm_fprop; y, qy and sy are all outputs (no overlap with each other or the
+ * inputs).
+ */
+int gemm_fprop_quant(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
+                     int64_t M, int64_t N, int64_t K, uint16_t* y, uint8_t* qy, float* sy,
+                     void* stream);
+
+/*
  * gemm_dgrad -- input-gradient GEMM dX = dY W, same (1x128) x (128x128)
  * configuration as FProp with the weight blocks used transposed ([P3-LAYOUT],
  * [P3-CORE], [P3-STEPS] step 4):

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     JetFP8Error,
     gemm_dgrad,
     gemm_fprop,
+    gemm_fprop_quant,
     gemm_wgrad,
     quantize_act_1x128,
     quantize_weight_128x128,

@@ -21,6 +21,7 @@ SIGNATURES = {
     "rmsnorm_quant": [_c_p, _c_p, _c_i64, _c_i64, ctypes.c_float, _c_p, _c_p, _c_p],
     "requant_transpose_128x1": [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "gemm_fprop": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
+    "gemm_fprop_quant": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p],
     "gemm_dgrad": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
     "gemm_wgrad": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
 }
@@ -158,6 +159,26 @@ def gemm_fprop(qx, sx, qw, sw, y=None):
         qx.data_ptr(), sx.data_ptr(), qw.data_ptr(), sw.data_ptr(), M, N, K, y.data_ptr(),
         _stream(qx.device)))
     return y
+
+
+def gemm_fprop_quant(qx, sx, qw, sw, y=None, qy=None, sy=None):
+    """gemm_fprop plus the 1x128 quantisation of Y for the next layer:
+    returns (y bf16 [M, N], qy uint8 [M, N], sy float32 [N/128, M])."""
+    torch = _torch()
+    M, K = qx.shape
+    N = qw.shape[0]
+    _need(qx, torch.uint8, (M, K), "qx")
+    _need(sx, torch.float32, (K // 128, M), "sx")
+    _need(qw, torch.uint8, (N, K), "qw")
+    _need(sw, torch.float32, (N // 128, K // 128), "sw")
+    y = _empty((M, N), torch.bfloat16, qx.device) if y is None else _need(y, torch.bfloat16, (M, N), "y")
+    qy = _empty((M, N), torch.uint8, qx.device) if qy is None else _need(qy, torch.uint8, (M, N), "qy")
+    sy = _empty((N // 128, M), torch.float32, qx.device) if sy is None else \
+        _need(sy, torch.float32, (N // 128, M), "sy")
+    _check("gemm_fprop_quant", lib().gemm_fprop_quant(
+        qx.data_ptr(), sx.data_ptr(), qw.data_ptr(), sw.data_ptr(), M, N, K, y.data_ptr(),
+        qy.data_ptr(), sy.data_ptr(), _stream(qx.device)))
+    return y, qy, sy
 
 
 def gemm_dgrad(qdy, sdy, qw, sw, dx=None):

@@ -108,6 +108,23 @@ int gemm_fprop(const uint8_t* qx, const float* sx, const uint8_t* qw, const floa
   return launched(jetfp8::launch_gemm_fprop(qx, sx, qw, sw, M, N, K, y, as_stream(stream)));
 }
 
+int gemm_fprop_quant(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
+                     int64_t M, int64_t N, int64_t K, uint16_t* y, uint8_t* qy, float* sy,
+                     void* stream) {
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || N % 128 || K % 128) return JETFP8_EINVAL;
+  if (int st = check_ptrs({{qx, M * K}, {sx, 4 * (M * K / 128)}, {qw, N * K},
+                           {sw, 4 * (N * K / (128 * 128))}},
+                          {{y, 2 * M * N}, {qy, M * N}, {sy, 4 * (M * N / 128)}}))
+    return st;
+  // FProp, then the 1x128 quantiser on y, back to back on the stream.  (Doing the
+  // quantisation in the 256 x 256 kernel's epilogue was measured slower: there it
+  // runs after the main loop at two waves per SIMD with nothing to overlap, while
+  // the separate kernel hides the same ALU work under its memory traffic.)
+  const hipError_t e = jetfp8::launch_gemm_fprop(qx, sx, qw, sw, M, N, K, y, as_stream(stream));
+  if (e != hipSuccess) return launched(e);
+  return launched(jetfp8::launch_quant_act(y, M, N, qy, sy, as_stream(stream)));
+}
+
 int gemm_dgrad(const uint8_t* qdy, const float* sdy, const uint8_t* qw, const float* sw, int64_t M,
                int64_t N, int64_t K, uint16_t* dx, void* stream) {
   if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || N % 128 || K % 128) return JETFP8_EINVAL;

@@ -82,6 +82,16 @@ def test_requant_validation(jetlib):
     assert c("requant_transpose_128x1", 0, 0, 0, 128, 0, 0, 0) == OK
 
 
+def test_gemm_fprop_quant_validation(jetlib):
+    f = "gemm_fprop_quant"
+    assert c(f, P[0], P[1], P[2], P[3], 16, 100, 128, P[4], P[5], P[6], 0) == EINVAL
+    assert c(f, P[0], P[1], P[2], P[3], 16, 128, 128, P[4], 0, P[6], 0) == ENULL     # qy missing
+    assert c(f, P[0], P[1], P[2], P[3], 16, 128, 128, P[4], P[4], P[6], 0) == EALIAS  # qy overlaps y
+    assert c(f, P[0], P[1], P[2], P[3], 16, 128, 128, P[4], P[5], P[0], 0) == EALIAS  # sy overlaps qx
+    assert c(f, P[0], P[1], P[2], P[3], 16, 128, 128, P[4], P[5], P[6] + 8, 0) == EALIGN
+    assert c(f, 0, 0, P[2], P[3], 0, 128, 128, 0, 0, 0, 0) == OK  # M = 0: nothing to do
+
+
 def test_gemm_validation(jetlib):
     # fprop(qx, sx, qw, sw, M, N, K, y)
     assert c("gemm_fprop", P[0], P[1], P[2], P[3], 16, 100, 128, P[4], 0) == EINVAL

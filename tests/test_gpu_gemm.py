@@ -382,3 +382,32 @@ def test_fprop_decode_two_strips_per_wave(m, k):
     y = host(yg.t)
     check(y, oracle.gemm_fprop_ref(qx[:m], sxm, qw, sw), f"decode fprop {m}x{n}x{k}")
     assert np.array_equal(y, yb[:m]), "decode kernel vs 128 x 128 kernel"
+
+
+@pytest.mark.parametrize("m,n,k", [(2048, 8192, 256), (2125, 8192, 128), (64, 384, 512), (200, 384, 512),
+                                   (300, 512, 256)])
+def test_fprop_quant_fused(m, n, k):
+    """gemm_fprop_quant: y equals gemm_fprop's and (qy, sy) equal quantize_act_1x128(y),
+    bit for bit, across the kernels FProp dispatches to (256 x 256 for the first two
+    shapes, the second with a ragged last row tile; decode, K-split, 128 x 128).  Against
+    the oracle: y within the GEMM tolerance, and the dequantised (qy, sy) within 1e-3
+    normwise of the oracle's 1x128 quantisation of bf16(Yref)."""
+    rng = np.random.default_rng(5000 + m + n + k)
+    qx, qw = codes(rng, (m, k)), codes(rng, (n, k))
+    sx, sw = scales(rng, (k // 128, m)), scales(rng, (n // 128, k // 128))
+    qx_d, sx_d, qw_d, sw_d = u8_dev(qx), f32_dev(sx), u8_dev(qw), f32_dev(sw)
+    yg, qg, sg = Guarded((m, n), torch.bfloat16), Guarded((m, n), torch.uint8), Guarded((n // 128, m), torch.float32)
+    jet.gemm_fprop_quant(qx_d, sx_d, qw_d, sw_d, yg.t, qg.t, sg.t)
+    y2 = jet.gemm_fprop(qx_d, sx_d, qw_d, sw_d)
+    q2, s2 = jet.quantize_act_1x128(y2)
+    torch.cuda.synchronize()
+    assert yg.intact() and qg.intact() and sg.intact()
+    y, q, s = host(yg.t), host(qg.t), host(sg.t)
+    assert np.array_equal(y, host(y2)), "y differs from gemm_fprop"
+    assert np.array_equal(q, host(q2)) and np.array_equal(s.view(np.uint32), host(s2).view(np.uint32)), \
+        "(qy, sy) differ from quantize_act_1x128(y)"
+    ref = oracle.gemm_fprop_ref(qx, sx, qw, sw)
+    check(y, ref, f"fprop_quant y {m}x{n}x{k}")
+    qo, so = oracle.quant_act_1x128(oracle.f64_to_bf16_bits(ref))
+    deq, deqo = oracle.dequant_groups(q, s), oracle.dequant_groups(qo, so)
+    assert np.linalg.norm(deq - deqo) <= 1e-3 * np.linalg.norm(deqo)

@@ -1,0 +1,73 @@
+"""FP8 linear layer as a torch autograd op, built only from the C-ABI entry points.
+
+Forward (Jet-RL pages, paper.rainbus.top summary, "方法步骤详情" steps 1-3):
+X is quantised 1x128 (or taken already quantised from ``rmsnorm_quant``), W
+128x128, Y = FProp; the FP8 X (codes + scales) and FP8 W are what is saved for
+backward -- no bf16 copy of X is kept.
+
+Backward (step 4): dY stays bf16 between layers and is quantised 1x128 for
+DGrad (dX = dY W, the weight blocks used transposed) and, after the 128x1
+requantisation of both saved operands, WGrad (dW = dY^T X).
+
+Every arithmetic step runs in libjetfp8.so; this module only orders the calls
+and allocates outputs through torch.  The token count M must be a multiple of
+128 for the backward (128-token groups of the requantisation).
+"""
+
+import torch
+
+from . import _lib
+
+
+class FP8LinearFunction(torch.autograd.Function):
+    """y = x w^T with the mixed-granularity FP8 recipe.  x bf16 [M, K], w bf16 [N, K]."""
+
+    @staticmethod
+    def forward(ctx, x, w):
+        qx, sx = _lib.quantize_act_1x128(x.contiguous())
+        qw, sw = _lib.quantize_weight_128x128(w.contiguous())
+        y = _lib.gemm_fprop(qx, sx, qw, sw)
+        ctx.save_for_backward(qx, sx, qw, sw)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        qx, sx, qw, sw = ctx.saved_tensors
+        return fp8_linear_backward(dy, qx, sx, qw, sw)
+
+
+def fp8_linear_backward(dy, qx, sx, qw, sw):
+    """(dx bf16 [M, K], dw bf16 [N, K]) from bf16 dY [M, N] and the saved FP8 operands."""
+    M = dy.shape[0]
+    if M % 128:
+        raise ValueError(f"FP8 linear backward needs M % 128 == 0 (128-token groups), got M={M}")
+    qdy, sdy = _lib.quantize_act_1x128(dy.contiguous())
+    dx = _lib.gemm_dgrad(qdy, sdy, qw, sw)
+    qxt, sxt = _lib.requant_transpose_128x1(qx, sx)
+    qdyt, sdyt = _lib.requant_transpose_128x1(qdy, sdy)
+    dw = _lib.gemm_wgrad(qdyt, sdyt, qxt, sxt)
+    return dx, dw
+
+
+def fp8_linear(x, w):
+    """Functional form of :class:`FP8LinearFunction`."""
+    return FP8LinearFunction.apply(x, w)
+
+
+class FP8Linear(torch.nn.Module):
+    """A bias-free linear layer with a bf16 master weight [out, in] whose forward
+    and backward GEMMs run in FP8 (the unified precision flow: rollout calls the
+    same forward)."""
+
+    def __init__(self, in_features, out_features, device=None):
+        super().__init__()
+        if in_features % 128 or out_features % 128:
+            raise ValueError("in_features and out_features must be multiples of 128")
+        self.weight = torch.nn.Parameter(
+            torch.empty(out_features, in_features, dtype=torch.bfloat16, device=device))
+        torch.nn.init.normal_(self.weight, std=0.02)
+
+    def forward(self, x):
+        shape = x.shape
+        y = fp8_linear(x.reshape(-1, shape[-1]), self.weight)
+        return y.reshape(*shape[:-1], self.weight.shape[0])

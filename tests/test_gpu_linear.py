@@ -1,0 +1,94 @@
+"""The FP8 linear autograd op (quantized_rl_amd.linear) on the GPU.
+
+Its forward and backward must be exactly the C-ABI pipeline: the gradients
+torch's autograd returns are checked against the oracle's pipeline on the same
+bf16 inputs (quantisers bit-exact upstream, GEMMs to the GEMM tolerance), the
+tensors saved for backward are the FP8 codes and scales, and a two-layer stack
+trains through autograd.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_common import bf16_dev, host
+from quantized_rl_amd import linear, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def check(y, ref, what):
+    r = oracle.check_gemm(y, ref)
+    assert r["ok"], f"{what}: {r}"
+
+
+@pytest.mark.parametrize("m,k,n", [(256, 512, 384), (384, 640, 256)])
+def test_fp8_linear_autograd_matches_the_oracle_pipeline(m, k, n):
+    x_h = synth.random_bf16((m, k), seed=m + k, std=1.0)
+    w_h = synth.random_bf16((n, k), seed=n + 1, std=0.02)
+    dy_h = synth.random_bf16((m, n), seed=m + n, std=1e-3)
+    x = bf16_dev(x_h).requires_grad_(True)
+    w = bf16_dev(w_h).requires_grad_(True)
+    y = linear.fp8_linear(x, w)
+    y.backward(bf16_dev(dy_h))
+    torch.cuda.synchronize()
+
+    qxo, sxo = oracle.quant_act_1x128(x_h)
+    qwo, swo = oracle.quant_weight_128x128(w_h)
+    qdyo, sdyo = oracle.quant_act_1x128(dy_h)
+    check(host(y.detach()), oracle.gemm_fprop_ref(qxo, sxo, qwo, swo), "y")
+    check(host(x.grad), oracle.gemm_dgrad_ref(qdyo, sdyo, qwo, swo), "dx")
+    qxt, sxt = oracle.requant_transpose_128x1(qxo, sxo)
+    qdyt, sdyt = oracle.requant_transpose_128x1(qdyo, sdyo)
+    check(host(w.grad), oracle.gemm_wgrad_ref(qdyt, sdyt, qxt, sxt), "dw")
+
+
+def test_fp8_linear_saves_fp8_activations_only():
+    m, k, n = 256, 512, 384
+    x = bf16_dev(synth.random_bf16((m, k), seed=5)).requires_grad_(True)
+    w = bf16_dev(synth.random_bf16((n, k), seed=6, std=0.02)).requires_grad_(True)
+    saved = []
+    with torch.autograd.graph.saved_tensors_hooks(lambda t: saved.append(t) or t, lambda t: t):
+        y = linear.fp8_linear(x, w)
+    assert sorted(str(t.dtype) for t in saved) == ["torch.float32", "torch.float32", "torch.uint8", "torch.uint8"]
+    assert any(t.dtype == torch.uint8 and tuple(t.shape) == (m, k) for t in saved)  # FP8 X, no bf16 copy
+    y.sum().backward()
+
+
+def test_fp8_linear_rejects_ragged_tokens_in_backward():
+    x = bf16_dev(synth.random_bf16((100, 256), seed=7)).requires_grad_(True)
+    w = bf16_dev(synth.random_bf16((128, 256), seed=8, std=0.02)).requires_grad_(True)
+    y = linear.fp8_linear(x, w)  # the forward accepts any M
+    with pytest.raises(ValueError):
+        y.backward(torch.ones_like(y))
+
+
+def test_two_layer_fp8_stack_trains():
+    """Two FP8Linear layers: one SGD step on a least-squares loss lowers the loss,
+    and each layer's gradients equal the functional op applied to the same tensors."""
+    torch.manual_seed(0)
+    dev = torch.device("cuda:0")
+    l1, l2 = linear.FP8Linear(512, 384, device=dev), linear.FP8Linear(384, 256, device=dev)
+    x = torch.randn(256, 512, device=dev).to(torch.bfloat16)
+    target = torch.randn(256, 256, device=dev).to(torch.bfloat16) * 0.01
+
+    def loss_fn():
+        return ((l2(l1(x)).float() - target.float()) ** 2).mean()
+
+    loss0 = loss_fn()
+    loss0.backward()
+    g1, g2 = l1.weight.grad.clone(), l2.weight.grad.clone()
+    assert torch.isfinite(g1.float()).all() and torch.isfinite(g2.float()).all()
+    # the same gradients from the functional op on the same tensors
+    h = linear.fp8_linear(x, l1.weight.detach())
+    h_req = h.detach().requires_grad_(True)
+    w2 = l2.weight.detach().clone().requires_grad_(True)
+    out = linear.fp8_linear(h_req, w2)
+    ((out.float() - target.float()) ** 2).mean().backward()
+    assert torch.equal(w2.grad, g2)
+    with torch.no_grad():
+        for p in (l1.weight, l2.weight):
+            p -= (5.0 * p.grad.float()).to(torch.bfloat16)
+            p.grad = None
+    assert loss_fn().item() < loss0.item()

@@ -411,3 +411,27 @@ def test_fprop_quant_fused(m, n, k):
     qo, so = oracle.quant_act_1x128(oracle.f64_to_bf16_bits(ref))
     deq, deqo = oracle.dequant_groups(q, s), oracle.dequant_groups(qo, so)
     assert np.linalg.norm(deq - deqo) <= 1e-3 * np.linalg.norm(deqo)
+
+
+def test_dgrad_wgrad_large_kernel_ragged_rows():
+    """DGrad and WGrad on the 256 x 256 kernel (>= 256 tiles) with a ragged last row
+    tile: DGrad with M = 4100 tokens, WGrad with N = 4224 output rows (33 x 128).
+    Full outputs against the oracle, guard zones intact."""
+    rng = np.random.default_rng(6000)
+    m, n, k = 4100, 256, 4096
+    qdy, qw = codes(rng, (m, n)), codes(rng, (n, k))
+    sdy, sw = scales(rng, (n // 128, m)), scales(rng, (n // 128, k // 128))
+    dxg = Guarded((m, k), torch.bfloat16)
+    jet.gemm_dgrad(u8_dev(qdy), f32_dev(sdy), u8_dev(qw), f32_dev(sw), dxg.t)
+    torch.cuda.synchronize()
+    assert dxg.intact()
+    check(host(dxg.t), oracle.gemm_dgrad_ref(qdy, sdy, qw, sw), f"dgrad {m}x{n}x{k}")
+
+    m, n, k = 256, 4224, 4096
+    qdyt, qxt = codes(rng, (n, m)), codes(rng, (k, m))
+    sdyt, sxt = scales(rng, (m // 128, n)), scales(rng, (m // 128, k))
+    dwg = Guarded((n, k), torch.bfloat16)
+    jet.gemm_wgrad(u8_dev(qdyt), f32_dev(sdyt), u8_dev(qxt), f32_dev(sxt), dwg.t)
+    torch.cuda.synchronize()
+    assert dwg.intact()
+    check(host(dwg.t), oracle.gemm_wgrad_ref(qdyt, sdyt, qxt, sxt), f"wgrad {m}x{n}x{k}")

@@ -7,7 +7,7 @@
 // (Jet-RL pages, paper.rainbus.top summary, sections "GEMM 量化布局", "核心方法",
 // "方法步骤详情" steps 2 and 4.)
 //
-// All three are one kernel template computing
+// Every kernel here computes
 //   C[i][j] = sum_kb  sa[kb][i] * sb(kb, j) * P_kb[i][j],
 //   P_kb[i][j] = sum_{k in block kb} A[i][k] * Bop[k][j]       (exact FP8 products, fp32 sum)
 // where A is [rows][Kc] with the contraction contiguous, and Bop is either
@@ -19,6 +19,16 @@
 // v_mfma_f32_16x16x128_f8f6f4 with a zero accumulator; the fp32 partial is
 // multiplied by the product of the two scales and added to the running fp32
 // accumulator in registers (one FMA per output element per K-block).
+//
+// Kernels (chosen in launch_gemm):
+//   gemm_fp8_large_kernel<mode>  256 x 256 tiles: problems with >= 256 tiles, and
+//                                FProp with <= 256 rows when a traffic estimate
+//                                prefers it to the K-split kernel;
+//   gemm_fp8_kernel<mode>        128 x 128 tiles: everything else;
+//   gemm_fp8_decode_kernel       FProp with M <= 64 (weight streaming);
+//   gemm_fp8_mid_kernel          FProp with 65 .. 256 rows (K split over 8 waves).
+// All but the last fold the K-blocks of an output in ascending order with the
+// same fp32 operations, so a row's FProp output does not depend on the kernel.
 #include "device_common.hpp"
 #include "launch.hpp"
 

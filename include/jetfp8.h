@@ -49,6 +49,9 @@
  *   empty); outputs must not overlap inputs or each other; sizes >= 0 and at
  *   most 2^31 - 1 per dimension; the divisibility rules stated per function.
  *   A status of JETFP8_ELAUNCH reports a HIP error from the enqueue itself.
+ * - GEMMs address operands with 32-bit byte offsets: a call whose operands or
+ *   output would reach 2^31 bytes (counting one 256-row tile of padding on
+ *   the row dimension) returns JETFP8_EUNSUPPORTED and writes nothing.
  * - Inputs must be finite (NaN/Inf are outside the contract; the kernels do
  *   not hang on them, but the result is unspecified).
  * - Identical inputs give bitwise identical outputs (no atomics, no split-K

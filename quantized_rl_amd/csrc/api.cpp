@@ -47,6 +47,14 @@ int check_ptrs(std::initializer_list<Buf> ins, std::initializer_list<Buf> outs) 
 
 int launched(hipError_t e) { return e == hipSuccess ? JETFP8_OK : JETFP8_ELAUNCH; }
 
+// The GEMM kernels address their operands with 32-bit byte offsets (buffer
+// resources).  With one 256-row tile of ragged-row padding, both operands and
+// the output (rows x cols bf16) must stay below 2^31 bytes.
+bool gemm_fits(int64_t rows, int64_t cols, int64_t kc) {
+  const int64_t lim = int64_t(1) << 31;
+  return (rows + 256) * kc < lim && cols * kc < lim && (rows + 256) * cols * 2 < lim;
+}
+
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
@@ -105,6 +113,7 @@ int gemm_fprop(const uint8_t* qx, const float* sx, const uint8_t* qw, const floa
                            {sw, 4 * (N * K / (128 * 128))}},
                           {{y, 2 * M * N}}))
     return st;
+  if (!gemm_fits(M, N, K)) return JETFP8_EUNSUPPORTED;
   return launched(jetfp8::launch_gemm_fprop(qx, sx, qw, sw, M, N, K, y, as_stream(stream)));
 }
 
@@ -116,6 +125,7 @@ int gemm_fprop_quant(const uint8_t* qx, const float* sx, const uint8_t* qw, cons
                            {sw, 4 * (N * K / (128 * 128))}},
                           {{y, 2 * M * N}, {qy, M * N}, {sy, 4 * (M * N / 128)}}))
     return st;
+  if (!gemm_fits(M, N, K)) return JETFP8_EUNSUPPORTED;
   // FProp, then the 1x128 quantiser on y, back to back on the stream.  (Doing the
   // quantisation in the 256 x 256 kernel's epilogue was measured slower: there it
   // runs after the main loop at two waves per SIMD with nothing to overlap, while
@@ -132,6 +142,7 @@ int gemm_dgrad(const uint8_t* qdy, const float* sdy, const uint8_t* qw, const fl
                            {sw, 4 * (N * K / (128 * 128))}},
                           {{dx, 2 * M * K}}))
     return st;
+  if (!gemm_fits(M, K, N)) return JETFP8_EUNSUPPORTED;
   return launched(jetfp8::launch_gemm_dgrad(qdy, sdy, qw, sw, M, N, K, dx, as_stream(stream)));
 }
 
@@ -143,6 +154,7 @@ int gemm_wgrad(const uint8_t* qdyt, const float* sdyt, const uint8_t* qxt, const
                            {sxt, 4 * (K * M / 128)}},
                           {{dw, 2 * N * K}}))
     return st;
+  if (!gemm_fits(N, K, M)) return JETFP8_EUNSUPPORTED;
   return launched(jetfp8::launch_gemm_wgrad(qdyt, sdyt, qxt, sxt, M, N, K, dw, as_stream(stream)));
 }
 

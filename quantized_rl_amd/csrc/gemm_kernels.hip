@@ -21,12 +21,13 @@
 // accumulator in registers (one FMA per output element per K-block).
 //
 // Kernels (chosen in launch_gemm):
-//   gemm_fp8_large_kernel<mode>  256 x 256 tiles: problems with >= 256 tiles, and
-//                                FProp with <= 256 rows when a traffic estimate
-//                                prefers it to the K-split kernel;
-//   gemm_fp8_kernel<mode>        128 x 128 tiles: everything else;
 //   gemm_fp8_decode_kernel       FProp with M <= 64 (weight streaming);
-//   gemm_fp8_mid_kernel          FProp with 65 .. 256 rows (K split over 8 waves).
+//   gemm_fp8_mid_kernel          FProp with 65 .. 256 rows, long K and few
+//                                column tiles (K split over 8 waves);
+//   gemm_fp8_large_kernel<mode>  256 x 256 tiles: problems with >= 256 of them;
+//   gemm_fp8_med_kernel<mode>    128 x 128 tiles, same machinery: everything else.
+// Byte offsets are 32-bit (buffer resources): the API rejects GEMMs whose
+// operands or output, with one tile of ragged rows, reach 2^31 bytes.
 // All but the last fold the K-blocks of an output in ascending order with the
 // same fp32 operations, so a row's FProp output does not depend on the kernel.
 #include "device_common.hpp"
@@ -41,13 +42,7 @@ typedef int v4i_t __attribute__((ext_vector_type(4)));
 
 enum GemmMode { kFprop = 0, kDgrad = 1, kWgrad = 2 };
 
-constexpr int kBM = 128, kBN = 128, kBK = 128;
-constexpr int kThreads = 256;
-constexpr int kTileBytes = kBM * kBK;  // 16 KB per operand tile
-
-// 16-byte chunk c of tile row r is stored at chunk position c ^ swz(r).
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
+constexpr int kBN = 128, kBK = 128;  // weight block width, K-block depth
 
 __device__ __forceinline__ v2i_t lds_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
@@ -59,166 +54,6 @@ __device__ __forceinline__ v4f_t mfma_fp8(const v8i_t& a, const v8i_t& b) {
   // cbsz = blgp = 0: both operands OCP E4M3; zero scale operands select the
   // unscaled instruction.
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
-}
-
-template <int kMode>
-__global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(const uint8_t* __restrict__ A,
-                                                               const float* __restrict__ sa,
-                                                               const uint8_t* __restrict__ B,
-                                                               const float* __restrict__ sb,
-                                                               int64_t Mr, int64_t Nc, int64_t Kc,
-                                                               uint16_t* __restrict__ C) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) float sas[2][kBM];
-  __shared__ __attribute__((aligned(16))) float sbs[2][kBN];
-
-  const int t = threadIdx.x, l = t & 63, w = t >> 6;
-  const int wm = w >> 1, wn = w & 1;        // wave's 64x64 quadrant
-  const int64_t row0 = (int64_t)blockIdx.y * kBM;
-  const int64_t col0 = (int64_t)blockIdx.x * kBN;
-  const int64_t nkb = Kc / kBK;
-
-  // global -> register staging: four 16-byte chunks of A and of B per thread
-  uint4 ra[4], rb[4];
-  float rsa = 0.0f, rsb = 0.0f;
-
-  auto load_tile = [&](int64_t kb) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int id = t + kThreads * p, r = id >> 3, c = id & 7;
-      int64_t gr = row0 + r;
-      gr = gr < Mr ? gr : Mr - 1;  // ragged last row tile: clamp, results are not stored
-      ra[p] = *reinterpret_cast<const uint4*>(A + gr * Kc + kb * kBK + c * 16);
-      if (kMode == kDgrad) {
-        rb[p] = *reinterpret_cast<const uint4*>(B + (kb * kBK + r) * Nc + col0 + c * 16);
-      } else {
-        rb[p] = *reinterpret_cast<const uint4*>(B + (col0 + r) * Kc + kb * kBK + c * 16);
-      }
-    }
-    if (t < kBM) {
-      int64_t gr = row0 + t;
-      gr = gr < Mr ? gr : Mr - 1;
-      rsa = sa[kb * Mr + gr];
-    } else if (kMode == kWgrad) {
-      rsb = sb[kb * Nc + col0 + (t - kBM)];
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int id = t + kThreads * p, r = id >> 3, c = id & 7;
-      *reinterpret_cast<uint4*>(&As[buf][lds_off(r, c)]) = ra[p];
-      *reinterpret_cast<uint4*>(&Bs[buf][lds_off(r, c)]) = rb[p];
-    }
-    if (t < kBM) sas[buf][t] = rsa;
-    else if (kMode == kWgrad) sbs[buf][t - kBM] = rsb;
-  };
-
-  v4f_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  const int lr = l & 15;   // row (A) / column (B) inside a 16x16 sub-tile
-  const int lk = l >> 4;   // which 32-byte slice of the 128-deep block
-  for (int64_t kb = 0; kb < nkb; ++kb) {
-    const int cur = (int)(kb & 1);
-    if (kb + 1 < nkb) load_tile(kb + 1);
-
-    // operand fragments
-    v8i_t af[4], bf[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 64 + 16 * i + lr;
-      const uint4 x0 = *reinterpret_cast<const uint4*>(&As[cur][lds_off(r, 2 * lk)]);
-      const uint4 x1 = *reinterpret_cast<const uint4*>(&As[cur][lds_off(r, 2 * lk + 1)]);
-      af[i] = v8i_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                    (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (kMode == kDgrad) {
-        // LDS holds B[n][c] (n = contraction).  Lane (lr) supplies the address of
-        // contraction row 32 lk + 8 q + (lr >> 1), bytes 8 (lr & 1) of the
-        // sub-tile's 16 columns; it receives column lr of those 8 rows.
-        const int chunk = 4 * wn + j;
-        v2i_t part[4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int n = 32 * lk + 8 * q4 + (lr >> 1);
-          part[q4] = lds_tr8(&Bs[cur][lds_off(n, chunk) + 8 * (lr & 1)]);
-        }
-        bf[j] = v8i_t{part[0].x, part[0].y, part[1].x, part[1].y,
-                      part[2].x, part[2].y, part[3].x, part[3].y};
-      } else {
-        const int r = wn * 64 + 16 * j + lr;
-        const uint4 x0 = *reinterpret_cast<const uint4*>(&Bs[cur][lds_off(r, 2 * lk)]);
-        const uint4 x1 = *reinterpret_cast<const uint4*>(&Bs[cur][lds_off(r, 2 * lk + 1)]);
-        bf[j] = v8i_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                      (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      }
-    }
-
-    // scales: this lane's output rows are wm*64 + 16 i + 4 lk + e, column wn*64 + 16 j + lr
-    float sarow[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 s4 = *reinterpret_cast<const float4*>(&sas[cur][wm * 64 + 16 * i + 4 * lk]);
-      sarow[i][0] = s4.x; sarow[i][1] = s4.y; sarow[i][2] = s4.z; sarow[i][3] = s4.w;
-    }
-    if (kMode == kWgrad) {
-      float sbcol[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sbcol[j] = sbs[cur][wn * 64 + 16 * j + lr];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v4f_t p = mfma_fp8(af[i], bf[j]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(p[e], sarow[i][e] * sbcol[j], acc[i][j][e]);
-        }
-    } else {
-      const float sblk = (kMode == kFprop) ? sb[(col0 / kBN) * nkb + kb]
-                                           : sb[kb * (Nc / kBN) + col0 / kBN];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sarow[i][e] *= sblk;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v4f_t p = mfma_fp8(af[i], bf[j]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(p[e], sarow[i][e], acc[i][j][e]);
-        }
-    }
-
-    if (kb + 1 < nkb) store_tile(cur ^ 1);
-    __syncthreads();
-  }
-
-  // epilogue: fp32 -> bf16 (nearest even), masked on ragged rows
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t gr = row0 + wm * 64 + 16 * i + 4 * lk + e;
-      if (gr < Mr) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t gc = col0 + wn * 64 + 16 * j + lr;
-          C[gr * Nc + gc] = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
-        }
-      }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -556,6 +391,257 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Medium-tile kernel: 128 x 128 output tile, 4 waves (2 x 2) of 64 x 64, two
+// workgroups per CU.  The large kernel's machinery at a quarter of the tile:
+// direct-to-LDS operand loads (double-buffered, spread over the MFMA stream),
+// the same XOR swizzle, LDS-staged scale factors, the same fold per output
+// element.  For problems with fewer than 256 tiles of 256 x 256 it keeps every
+// CU busy where the large kernel would leave most idle.
+constexpr int kMBM = 128, kMBN = 128;
+constexpr int kMThreads = 256;
+
+struct MStage {
+  uint8_t ab[kMBM * kBK + kMBN * kBK];  // 32 KB: A rows then B rows
+  // FProp, DGrad: sc[0] holds fl32(sa(row) * sb(block)) (the tile's 128
+  // columns are one weight block); WGrad: sc[0] the A-row scales, sc[1] the
+  // 128 B-column scales in column order.  Rows transposed: r at [(r % 16) * 8 + r / 16].
+  float sc[2][kMBM];
+};
+
+template <int kMode>
+struct MedTile {
+  int t, l, w, wm, wn, lr, lk;
+  uint32_t M, N, K, row0, col0, nkb, arow;
+  rsrc_t ra, rb;
+  uint32_t va[4], vb[4];
+  const float* sa;
+  const float* sb;
+  uint32_t a_even, a_odd, b_even, b_odd, s_row;
+  uint32_t dv[4];
+
+  __device__ __forceinline__ void setup_offsets() {
+    // row wm*64 + 16 i + lr: f(row) = f0(lr) ^ bit1(i) (as in the large kernel)
+    const uint32_t f0 = (uint32_t)((lr & 7) ^ ((lr >> 3) & 1));
+    const uint32_t ra0 = (uint32_t)(wm * 64 + lr) * 128u;
+    a_even = ra0 + (((uint32_t)(2 * lk) ^ f0) << 4);
+    a_odd = ra0 + (((uint32_t)(2 * lk + 1) ^ f0) << 4);
+    const uint32_t rb0 = (uint32_t)(kMBM * kBK) + (uint32_t)(wn * 64 + lr) * 128u;
+    b_even = rb0 + (((uint32_t)(2 * lk) ^ f0) << 4);
+    b_odd = rb0 + (((uint32_t)(2 * lk + 1) ^ f0) << 4);
+    s_row = (uint32_t)(lr * 8 + wm * 4) * 4u;
+    // DGrad: transposed reads of B[n][c]; n = 32 lk + 8 q + lr / 2, chunk 4 wn + j
+    const uint32_t x = (uint32_t)(((lr >> 1) & 7) ^ (lk & 1) ^ (4 * wn));
+    const uint32_t dbase = (uint32_t)(kMBM * kBK) + (uint32_t)(32 * lk + (lr >> 1)) * 128u + 8u * (uint32_t)(lr & 1);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) dv[v] = dbase + (((uint32_t)v ^ x) << 4);
+  }
+
+  // Piece p < 4: A rows 32 w + 8 p ..; piece 4 + p: the matching B rows
+  // (DGrad: contraction rows of the weight's 128-column block).
+  __device__ __forceinline__ void issue_piece(uint32_t kb, MStage& st, int piece) const {
+    uint8_t* As = st.ab;
+    uint8_t* Bs = st.ab + kMBM * kBK;
+    const int p = piece & 3;
+    if (piece < 4)
+      buf_to_lds16(ra, As + (32 * w + 8 * p) * 128, va[p], kb * kBK);
+    else if (kMode == kDgrad)
+      buf_to_lds16(rb, Bs + (32 * w + 8 * p) * 128, vb[p], kb * kBK * N);
+    else
+      buf_to_lds16(rb, Bs + (32 * w + 8 * p) * 128, vb[p], kb * kBK);
+  }
+  __device__ __forceinline__ void issue(uint32_t kb, MStage& st) const {
+#pragma unroll
+    for (int piece = 0; piece < 8; ++piece) issue_piece(kb, st, piece);
+  }
+  // threads 0..127: the row factor of row t (FProp, DGrad: with the block
+  // scale folded in); threads 128..255: WGrad column scales.  The product is
+  // formed in store_scale, after the block's MFMAs.
+  __device__ __forceinline__ float2 load_scale(uint32_t kb) const {
+    if (kMode == kWgrad) return make_float2(t >= kMBM ? sb[kb * N + col0 + (t - kMBM)] : sa[kb * M + arow], 1.0f);
+    const uint32_t cb = col0 / kBN;
+    const uint32_t bi = (kMode == kFprop) ? cb * nkb + kb : kb * (N / kBN) + cb;
+    return make_float2(sa[kb * M + arow], sb[bi]);
+  }
+  __device__ __forceinline__ void store_scale(MStage& st, float2 x) const {
+    if (t < kMBM) st.sc[0][(t & 15) * 8 + (t >> 4)] = (kMode == kWgrad) ? x.x : x.x * x.y;
+    else if (kMode == kWgrad) st.sc[1][t - kMBM] = x.x;
+  }
+
+  __device__ __forceinline__ static v8i_t frag(const uint8_t* base, uint32_t o0, uint32_t o1) {
+    const uint4 x0 = *reinterpret_cast<const uint4*>(base + o0);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(base + o1);
+    return v8i_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+  }
+
+  __device__ __forceinline__ void compute(const MStage& st, v4f_t (&acc)[4][4], uint32_t kn, MStage& nxt) const {
+    const uint8_t* S = st.ab;
+    v8i_t bf[4];
+    auto read_b = [&](int j) {
+      if (kMode == kDgrad) {
+        v2i_t part[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) part[q4] = lds_tr8(S + dv[j ^ (q4 & 1)] + 1024 * q4);
+        bf[j] = v8i_t{part[0].x, part[0].y, part[1].x, part[1].y,
+                      part[2].x, part[2].y, part[3].x, part[3].y};
+      } else {
+        const bool sw = (j >> 1) & 1;
+        bf[j] = frag(S + 2048 * j, sw ? b_odd : b_even, sw ? b_even : b_odd);
+      }
+    };
+    v8i_t af[2];
+    af[0] = frag(S, a_even, a_odd);
+    read_b(0);
+    read_b(1);
+    float srow[4];
+    {
+      const float4 s0 = *reinterpret_cast<const float4*>(reinterpret_cast<const uint8_t*>(st.sc[0]) + s_row);
+      srow[0] = s0.x; srow[1] = s0.y; srow[2] = s0.z; srow[3] = s0.w;
+    }
+    float scol[4][4];
+    if (kMode == kWgrad) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 c4 = *reinterpret_cast<const float4*>(&st.sc[1][wn * 64 + 16 * j + 4 * lk]);
+        scol[j][0] = c4.x; scol[j][1] = c4.y; scol[j][2] = c4.z; scol[j][3] = c4.w;
+      }
+    }
+    // pipeline over the 16 (row, column) sub-tiles as in the large kernel; the
+    // next block's 8 direct loads go out on the odd steps
+    v4f_t part[3];
+#pragma unroll
+    for (int q = 0; q < 18; ++q) {
+      const int i = q >> 2, j = q & 3;
+      if (q < 2) read_b(q + 2);
+      if (q < 16 && j == 0 && i + 1 < 4) {
+        const int n = i + 1;
+        const bool sw = (n >> 1) & 1;
+        af[n & 1] = frag(S + 2048 * n, sw ? a_odd : a_even, sw ? a_even : a_odd);
+      }
+      if (q < 16) part[q % 3] = mfma_fp8(bf[j], af[i & 1]);
+      if (q < 16 && (q & 1)) issue_piece(kn, nxt, q >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q >= 2) {
+        const int qp = q - 2, pi = qp >> 2, pj = qp & 3;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sc = (kMode == kWgrad) ? srow[pi] * scol[pj][e] : srow[pi];
+          acc[pi][pj][e] = fmaf(part[qp % 3][e], sc, acc[pi][pj][e]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
+template <int kMode>
+__global__ __launch_bounds__(kMThreads, 2) void gemm_fp8_med_kernel(const uint8_t* __restrict__ A,
+                                                                     const float* __restrict__ sa,
+                                                                     const uint8_t* __restrict__ B,
+                                                                     const float* __restrict__ sb,
+                                                                     uint32_t M, uint32_t N, uint32_t K,
+                                                                     uint16_t* __restrict__ C) {
+  __shared__ __attribute__((aligned(16))) MStage st0;
+  __shared__ __attribute__((aligned(16))) MStage st1;
+
+  MedTile<kMode> g;
+  g.t = threadIdx.x;
+  g.l = g.t & 63;
+  g.w = __builtin_amdgcn_readfirstlane(g.t >> 6);
+  g.wm = g.w >> 1;  // wave tile: rows wm*64 .. +64, cols wn*64 .. +64
+  g.wn = g.w & 1;
+  g.lr = g.l & 15;
+  g.lk = g.l >> 4;
+  g.M = M; g.N = N; g.K = K;
+  g.sa = sa; g.sb = sb;
+  g.setup_offsets();
+
+  // launch order as in the large kernel: one contiguous tile range per XCD,
+  // tile-row groups of kGroupM rows walked column by column
+  const uint32_t ntm = (M + kMBM - 1) / kMBM, ntn = N / kMBN, total = ntm * ntn;
+  uint32_t id = blockIdx.x;
+  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+  const uint32_t per_group = kGroupM * ntn;
+  const uint32_t g0 = (id / per_group) * kGroupM;
+  const uint32_t gm = (ntm - g0) < (uint32_t)kGroupM ? (ntm - g0) : (uint32_t)kGroupM;
+  g.row0 = (g0 + (id % per_group) % gm) * kMBM;
+  g.col0 = ((id % per_group) / gm) * kMBN;
+  g.nkb = K / kBK;
+  const uint32_t t7 = (uint32_t)g.t & 127u;
+  g.arow = (g.row0 + t7) < M ? (g.row0 + t7) : (M - 1);
+  g.ra = make_rsrc(A, M * K);
+  g.rb = make_rsrc(B, N * K);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = 32 * g.w + 8 * p + (g.l >> 3);
+    g.va[p] = (g.row0 + r) * K + (((g.l & 7) ^ lf(r)) << 4);
+    if (kMode == kDgrad)
+      g.vb[p] = r * N + g.col0 + (((g.l & 7) ^ lf(r)) << 4);  // contraction row r of the block
+    else
+      g.vb[p] = (g.col0 + r) * K + (((g.l & 7) ^ lf(r)) << 4);
+  }
+
+  v4f_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  g.store_scale(st0, g.load_scale(0));
+  g.issue(0, st0);
+  wait_vmem();
+  __syncthreads();
+
+  const uint32_t last = g.nkb - 1;
+#pragma clang loop unroll(disable)
+  for (uint32_t kb = 0; kb < g.nkb; kb += 2) {
+    {
+      const uint32_t kn = kb + 1 <= last ? kb + 1 : last;
+      const float2 x = g.load_scale(kn);
+      g.compute(st0, acc, kn, st1);
+      g.store_scale(st1, x);
+      wait_vmem();
+      __syncthreads();
+    }
+    if (kb + 1 <= last) {
+      const uint32_t kn = kb + 2 <= last ? kb + 2 : last;
+      const float2 x = g.load_scale(kn);
+      g.compute(st1, acc, kn, st0);
+      g.store_scale(st0, x);
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  // epilogue: bf16 tile staged in LDS (rows 0..63 in stage 0, 64..127 in
+  // stage 1, pitch 256 + 16 bytes), then 16-byte buffer stores
+  constexpr int kPitch = kMBN * 2 + 16;
+  static_assert(64 * kPitch <= (int)sizeof(MStage), "epilogue staging must fit one stage");
+  const rsrc_t rc = make_rsrc(C, M * N * 2u);
+  auto crow = [&](int r) -> uint8_t* {
+    return (r < 64 ? reinterpret_cast<uint8_t*>(&st0) : reinterpret_cast<uint8_t*>(&st1)) + (r & 63) * kPitch;
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = g.wm * 64 + 16 * i + g.lr, c = g.wn * 64 + 16 * j + 4 * g.lk;
+      const uint32_t lo = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
+      const uint32_t hi = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
+      *reinterpret_cast<uint2*>(crow(r) + 2 * c) = make_uint2(lo, hi);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int id16 = g.t + kMThreads * p;  // 16-byte chunk id: 16 per row
+    const int r = id16 >> 4, c16 = id16 & 15;
+    const uint4 v = *reinterpret_cast<const uint4*>(crow(r) + 16 * c16);
+    const v4i_t d = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(d, rc, ((g.row0 + r) * N + g.col0 + 8 * c16) * 2u, 0, 0);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Decode FProp (M <= 64 tokens, rollout): parallel weight streaming with the
@@ -956,37 +1042,33 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
     launch_decode(mt, kw, ks, A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C, stream);
     return hipGetLastError();
   }
-  // the large-tile kernel works with 32-bit byte offsets
-  const bool fits32 = (Mr + kLBM) * Kc < (int64_t(1) << 31) && Nc * Kc < (int64_t(1) << 31) &&
-                      (Mr + kLBM) * Nc * 2 < (int64_t(1) << 31);
-  const int64_t large_tiles = ((Mr + kLBM - 1) / kLBM) * (Nc / kLBN);
-  // 65..256 rows: the K-split mid kernel unless the 256 x 256 kernel is
-  // expected to be faster.  Estimates (measured rates): the mid kernel moves
-  // (N/64) M K + ceil(M/64) N K operand bytes through register loads at about
-  // 5 TB/s; the large kernel takes about 2 us per K-block per round of 256
-  // tiles.  At the 8B decode shapes this picks the large kernel for gate+up
-  // (96 tiles, K = 4096) and the mid kernel for QKV and down.
-  bool mid = kMode == kFprop && Mr <= 256 && Nc * Kc < (int64_t(1) << 31) && Mr * Kc < (int64_t(1) << 31);
-  if (mid && Nc % kLBN == 0 && fits32) {
-    const double mid_us = ((double)(Nc / 64) * Mr * Kc + (double)((Mr + 63) / 64) * Nc * Kc) / 5.0e6;
-    const double large_us = (double)((large_tiles + 255) / 256) * (double)(Kc / kBK) * 2.0;
-    if (large_us < mid_us) mid = false;
-  }
-  if (mid) {
+  // 65..256 rows: the K-split kernel when K is long and there are few column
+  // tiles (so few 128 x 128 tiles, each with a long sequential K chain), the
+  // medium-tile kernel otherwise.  Measured on the 8B and 32B rollout shapes:
+  // the K-split kernel wins only for the 8B down projection (N = 4096,
+  // K = 12288), the medium kernel for QKV, gate+up and the 32B down.
+  const int64_t nkb = Kc / kBK;
+  if (kMode == kFprop && Mr <= 256 && nkb >= 64 && Nc / kBN <= 32 && Nc * Kc < (int64_t(1) << 31) &&
+      Mr * Kc < (int64_t(1) << 31)) {
     const int64_t tiles = (Nc / 64) * ((Mr + 63) / 64);
     hipLaunchKernelGGL(gemm_fp8_mid_kernel, dim3((unsigned)tiles), dim3(512), 0, stream, A, sa, B, sb,
                        (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C);
     return hipGetLastError();
   }
-  if (Nc % kLBN == 0 && fits32 && (large_tiles >= 256 || (kMode == kFprop && Mr <= 256))) {
-    const int64_t tiles = ((Mr + kLBM - 1) / kLBM) * (Nc / kLBN);
-    hipLaunchKernelGGL(gemm_fp8_large_kernel<kMode>, dim3((unsigned)tiles), dim3(kLThreads), 0,
+  // the large-tile kernel works with 32-bit byte offsets; it needs >= 256
+  // tiles to fill the chip
+  const bool fits32 = (Mr + kLBM) * Kc < (int64_t(1) << 31) && Nc * Kc < (int64_t(1) << 31) &&
+                      (Mr + kLBM) * Nc * 2 < (int64_t(1) << 31);
+  const int64_t large_tiles = ((Mr + kLBM - 1) / kLBM) * (Nc / kLBN);
+  if (Nc % kLBN == 0 && fits32 && large_tiles >= 256) {
+    hipLaunchKernelGGL(gemm_fp8_large_kernel<kMode>, dim3((unsigned)large_tiles), dim3(kLThreads), 0,
                        stream, A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C);
     return hipGetLastError();
   }
-  dim3 grid((unsigned)(Nc / kBN), (unsigned)((Mr + kBM - 1) / kBM));
-  hipLaunchKernelGGL(gemm_fp8_kernel<kMode>, grid, dim3(kThreads), 0, stream, A, sa, B, sb, Mr, Nc,
-                     Kc, C);
+  // the medium-tile kernel (the caller guarantees 32-bit byte offsets)
+  const int64_t tiles = ((Mr + kMBM - 1) / kMBM) * (Nc / kMBN);
+  hipLaunchKernelGGL(gemm_fp8_med_kernel<kMode>, dim3((unsigned)tiles), dim3(kMThreads), 0, stream, A, sa, B,
+                     sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C);
   return hipGetLastError();
 }
 

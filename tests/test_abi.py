@@ -82,6 +82,16 @@ def test_requant_validation(jetlib):
     assert c("requant_transpose_128x1", 0, 0, 0, 128, 0, 0, 0) == OK
 
 
+def test_gemm_size_limit(jetlib):
+    EUNSUP = 5
+    Q = [(i + 1) << 40 for i in range(8)]  # fake addresses far enough apart for 4 GiB tensors
+    # 2^20 tokens x 4096: a 4 GiB operand, beyond the kernels' 32-bit offsets
+    assert c("gemm_fprop", Q[0], Q[1], Q[2], Q[3], 1 << 20, 128, 4096, Q[4], 0) == EUNSUP
+    assert c("gemm_dgrad", Q[0], Q[1], Q[2], Q[3], 1 << 20, 4096, 128, Q[4], 0) == EUNSUP
+    assert c("gemm_wgrad", Q[0], Q[1], Q[2], Q[3], 1 << 20, 128, 4096, Q[4], 0) == EUNSUP
+    assert c("gemm_fprop_quant", Q[0], Q[1], Q[2], Q[3], 1 << 20, 128, 4096, Q[4], Q[5], Q[6], 0) == EUNSUP
+
+
 def test_gemm_fprop_quant_validation(jetlib):
     f = "gemm_fprop_quant"
     assert c(f, P[0], P[1], P[2], P[3], 16, 100, 128, P[4], P[5], P[6], 0) == EINVAL

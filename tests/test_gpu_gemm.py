@@ -54,8 +54,8 @@ def check(y, ref, what, rms=None):
 
 # ---------------------------------------------------------------- FProp
 
-# shapes with N % 256 == 0 and M >= 256 run the 256 x 256 large-tile kernel,
-# the others the 128 x 128 kernel
+# shapes with at least 256 tiles of 256 x 256 run the large-tile kernel, M <= 64
+# the decode kernel, the others the 128 x 128 medium-tile kernel
 FPROP_SHAPES = [(256, 384, 512), (1, 128, 128), (16, 384, 256), (64, 256, 128), (200, 384, 512),
                 (130, 128, 1024), (257, 640, 384),
                 (256, 256, 256), (300, 512, 384), (513, 768, 640), (1024, 1280, 2048)]
@@ -317,11 +317,11 @@ def test_fprop_decode_wave_splits(m, k):
 @pytest.mark.parametrize("n,k", [(128, 128), (384, 1152), (640, 4096), (256, 12288)])
 @pytest.mark.parametrize("m", [65, 100, 128, 200, 256])
 def test_fprop_mid_batches(m, n, k):
-    """FProp at 65..256 rows (K split over the eight waves of a workgroup):
-    parity with the oracle, guards intact, and every row bitwise equal to the
-    same row computed in the other mid-size batch (rows are independent and the
-    K split does not depend on M).  K = 1 .. 96 blocks covers waves with no
-    block, one block and several."""
+    """FProp at 65..256 rows: the K-split kernel for K = 96 blocks with few column
+    tiles (waves with several blocks), the medium-tile kernel otherwise.  Parity
+    with the oracle, guards intact, and every row bitwise equal to the same row
+    computed in another batch of this size range (rows are independent and
+    neither kernel's order depends on M)."""
     rng = np.random.default_rng(2000 + m + n + k)
     qx, qw = codes(rng, (256, k)), codes(rng, (n, k))
     sx, sw = scales(rng, (k // 128, 256)), scales(rng, (n // 128, k // 128))
@@ -340,11 +340,10 @@ def test_fprop_mid_batches(m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(130, 16384, 256), (256, 24576, 128), (97, 24576, 384)])
-def test_fprop_large_kernel_below_256_rows(m, n, k):
-    """65..256 rows with many output columns: the 256 x 256 kernel is chosen over
-    the K-split kernel (ragged single row tile).  Parity with the oracle, and
-    every row bitwise equal to the same row inside a 257-row batch (128 x 128
-    kernel): both fold K sequentially."""
+def test_fprop_medium_kernel_below_256_rows(m, n, k):
+    """65..256 rows with many output columns: the 128 x 128 medium-tile kernel (a
+    ragged last row tile).  Parity with the oracle, and every row bitwise equal to
+    the same row inside a 257-row batch: both fold K sequentially."""
     rng = np.random.default_rng(3000 + m + k)
     qx, qw = codes(rng, (257, k)), codes(rng, (n, k))
     sx, sw = scales(rng, (k // 128, 257)), scales(rng, (n // 128, k // 128))
@@ -357,7 +356,7 @@ def test_fprop_large_kernel_below_256_rows(m, n, k):
     assert yg.intact()
     y = host(yg.t)
     check(y, oracle.gemm_fprop_ref(qx[:m], sxm, qw, sw), f"fprop {m}x{n}x{k}")
-    assert np.array_equal(y, yb[:m]), "256 x 256 kernel (ragged rows) vs 128 x 128 kernel"
+    assert np.array_equal(y, yb[:m]), "rows differ between batch sizes"
 
 
 @pytest.mark.parametrize("k", [256, 1024, 4096])

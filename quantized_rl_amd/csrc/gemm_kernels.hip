@@ -197,7 +197,11 @@ struct LargeTile {
   // is set: two base offsets plus an immediate 2048 i.  The same holds for
   // the B sub-tiles j.
   // The next K-block's direct loads (into the other stage) are issued one
-  // piece every four MFMAs, spread over the block instead of in one burst.
+  // piece every two MFMAs over the first half of the block: late enough not
+  // to crowd the block's first fragment reads, early enough that the last
+  // piece has half a block to arrive before the end-of-block wait (issued
+  // through the whole block, its latency showed in every block; in one
+  // burst, the fragment reads stalled behind it).
   __device__ __forceinline__ void compute(const LStage& st, v4f_t (&acc)[8][4], uint32_t kn, LStage& nxt) const {
     const uint8_t* S = st.ab;
     // B fragments are read in the order the first row of MFMAs uses them,
@@ -257,7 +261,7 @@ struct LargeTile {
         af[n & 1] = frag(S + 2048 * n, sw ? a_odd : a_even, sw ? a_even : a_odd);
       }
       if (q < 32) part[q % 3] = mfma_fp8(bf[j], af[i & 1]);
-      if (q < 32 && j == 1) issue_piece(kn, nxt, i);
+      if (q < 16 && !(q & 1)) issue_piece(kn, nxt, q >> 1);
       __builtin_amdgcn_sched_barrier(0);
       if (q >= 2) {
         const int qp = q - 2, pi = qp >> 2, pj = qp & 3;

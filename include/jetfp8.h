@@ -36,7 +36,8 @@
  *   bit-exact functions of their inputs.
  * - GEMMs accumulate each 128-deep block product in fp32, multiply it by the
  *   product of the two operands' fp32 scales for that block, add it to an fp32
- *   accumulator, and round the result to bf16 (nearest even).
+ *   accumulator, and round the result to bf16 (nearest even); gemm_wgrad_f32
+ *   returns the fp32 accumulator itself.
  * - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *   enqueues work on it and returns; the caller keeps the buffers alive until
  *   the stream has reached them.
@@ -193,6 +194,25 @@ int gemm_dgrad(const uint8_t* qdy, const float* sdy, const uint8_t* qw, const fl
  */
 int gemm_wgrad(const uint8_t* qdyt, const float* sdyt, const uint8_t* qxt, const float* sxt,
                int64_t M, int64_t N, int64_t K, uint16_t* dw, void* stream);
+
+/*
+ * gemm_wgrad_f32 -- gemm_wgrad with an fp32 output that is written or added
+ * to.  The pages fix the weight gradient's operands and scaling ([P3-CORE],
+ * [P3-STEPS] step 4) but not the precision the gradient is kept in; with an
+ * fp32 output the gradients of several micro-batches (or of several token
+ * shards on different GPUs) are summed before a single final rounding,
+ * where bf16 partial gradients would each be rounded.
+ *   accumulate == 0:  dw[n][k] = G[n][k]
+ *   accumulate == 1:  dw[n][k] = fl32(dw[n][k] + G[n][k])
+ * G is the fp32 accumulator that gemm_wgrad rounds: gemm_wgrad's output is
+ * exactly the bf16 (nearest-even) rounding of G.
+ *   dw : f32 [N][K], read as well as written when accumulate == 1.
+ * Shape rules as gemm_wgrad, with 4-byte output elements in the 2^31-byte
+ * limit; accumulate must be 0 or 1 (else JETFP8_EINVAL).  M == 0 writes zeros
+ * (accumulate == 0) or leaves dw unchanged (accumulate == 1).
+ */
+int gemm_wgrad_f32(const uint8_t* qdyt, const float* sdyt, const uint8_t* qxt, const float* sxt,
+                   int64_t M, int64_t N, int64_t K, float* dw, int accumulate, void* stream);
 
 #ifdef __cplusplus
 }

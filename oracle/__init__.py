@@ -56,6 +56,7 @@ from .gemm import (
     f64_to_bf16_bits,
     bf16_ulp,
     check_gemm,
+    check_gemm_f32,
 )
 
 __all__ = [
@@ -64,5 +65,5 @@ __all__ = [
     "requant_transpose_128x1", "pairwise_sum_f32",
     "dequant_groups", "dequant_blocks", "gemm_fprop_ref", "gemm_dgrad_ref", "gemm_wgrad_ref",
     "gemm_fprop_ref_at", "gemm_dgrad_ref_at", "gemm_wgrad_ref_at",
-    "f64_to_bf16_bits", "bf16_ulp", "check_gemm",
+    "f64_to_bf16_bits", "bf16_ulp", "check_gemm", "check_gemm_f32",
 ]

@@ -140,3 +140,35 @@ def check_gemm(y_bf16, yref64, rms=None, norm_tol=1e-3, elem_tol=1e-3):
     excess = float(np.max(np.abs(y - ref_b) - bound)) if y.size else -1.0
     ok = normwise <= norm_tol and excess <= 0.0
     return {"ok": bool(ok), "normwise": normwise, "elem_excess": excess}
+
+
+def check_gemm_f32(y_f32, yref64, contrib64=None, rms=None, norm_tol=1e-3, elem_tol=1e-3):
+    """Acceptance check of an fp32 GEMM result (the weight gradient kept in fp32).
+
+    The pages fix no output precision for it.  The fp32 result is the GEMM's
+    accumulator before the bf16 rounding, so it is held to the bf16 result's
+    bound, measured against the unrounded reference: normwise
+    ||Y - Yref64|| / ||G64|| <= 1e-3 and elementwise
+    |Y - Yref64| <= ulp_bf16(G64) + 1e-3 * rms(G64) + 2**-23 * |Yref64|.
+    (The MFMA's own accumulation of a 128-deep block is not exact, so the
+    accumulator is no more accurate than that; the last term covers the
+    rounding of an addition to an existing value.)  G64 is the product itself:
+    ``yref64``, or ``contrib64`` when the result was added to an existing value
+    (``yref64`` then being that value plus G64).  An all-zero product requires
+    Y == Yref64 exactly.
+    """
+    y = np.asarray(y_f32, dtype=np.float32).astype(np.float64)
+    ref = np.asarray(yref64, dtype=np.float64)
+    g = ref if contrib64 is None else np.asarray(contrib64, dtype=np.float64)
+    assert y.shape == ref.shape == g.shape
+    if rms is None:
+        rms = float(np.sqrt(np.mean(g * g))) if g.size else 0.0
+    g_norm = float(np.linalg.norm(g))
+    if g_norm == 0.0:
+        ok = bool(np.all(y == ref))
+        return {"ok": ok, "normwise": 0.0 if ok else float("inf"), "elem_excess": 0.0 if ok else float("inf")}
+    normwise = float(np.linalg.norm(y - ref) / g_norm)
+    bound = bf16_ulp(g) + elem_tol * rms + 2.0 ** -23 * np.abs(ref)
+    excess = float(np.max(np.abs(y - ref) - bound)) if y.size else -1.0
+    ok = normwise <= norm_tol and excess <= 0.0
+    return {"ok": bool(ok), "normwise": normwise, "elem_excess": excess}

@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     gemm_fprop,
     gemm_fprop_quant,
     gemm_wgrad,
+    gemm_wgrad_f32,
     quantize_act_1x128,
     quantize_weight_128x128,
     requant_transpose_128x1,

@@ -24,6 +24,7 @@ SIGNATURES = {
     "gemm_fprop_quant": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p],
     "gemm_dgrad": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
     "gemm_wgrad": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
+    "gemm_wgrad_f32": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_int, _c_p],
 }
 
 STATUS = {0: "JETFP8_OK", 1: "JETFP8_EINVAL", 2: "JETFP8_EALIGN", 3: "JETFP8_ENULL",
@@ -212,4 +213,26 @@ def gemm_wgrad(qdyt, sdyt, qxt, sxt, dw=None):
     _check("gemm_wgrad", lib().gemm_wgrad(
         qdyt.data_ptr(), sdyt.data_ptr(), qxt.data_ptr(), sxt.data_ptr(), M, N, K, dw.data_ptr(),
         _stream(qdyt.device)))
+    return dw
+
+
+def gemm_wgrad_f32(qdyt, sdyt, qxt, sxt, dw=None, accumulate=False):
+    """dW fp32 [N, K] = dY^T X (operands as gemm_wgrad), written into a new or given
+    tensor, or added to the given ``dw`` when ``accumulate`` is true."""
+    torch = _torch()
+    N, M = qdyt.shape
+    K = qxt.shape[0]
+    _need(qdyt, torch.uint8, (N, M), "qdyt")
+    _need(sdyt, torch.float32, (M // 128, N), "sdyt")
+    _need(qxt, torch.uint8, (K, M), "qxt")
+    _need(sxt, torch.float32, (M // 128, K), "sxt")
+    if dw is None:
+        if accumulate:
+            raise ValueError("gemm_wgrad_f32: accumulate=True needs the dw tensor to add to")
+        dw = _empty((N, K), torch.float32, qdyt.device)
+    else:
+        _need(dw, torch.float32, (N, K), "dw")
+    _check("gemm_wgrad_f32", lib().gemm_wgrad_f32(
+        qdyt.data_ptr(), sdyt.data_ptr(), qxt.data_ptr(), sxt.data_ptr(), M, N, K, dw.data_ptr(),
+        1 if accumulate else 0, _stream(qdyt.device)))
     return dw

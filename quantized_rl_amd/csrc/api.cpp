@@ -49,10 +49,10 @@ int launched(hipError_t e) { return e == hipSuccess ? JETFP8_OK : JETFP8_ELAUNCH
 
 // The GEMM kernels address their operands with 32-bit byte offsets (buffer
 // resources).  With one 256-row tile of ragged-row padding, both operands and
-// the output (rows x cols bf16) must stay below 2^31 bytes.
-bool gemm_fits(int64_t rows, int64_t cols, int64_t kc) {
+// the output (rows x cols elements of out_bytes each) must stay below 2^31 bytes.
+bool gemm_fits(int64_t rows, int64_t cols, int64_t kc, int64_t out_bytes = 2) {
   const int64_t lim = int64_t(1) << 31;
-  return (rows + 256) * kc < lim && cols * kc < lim && (rows + 256) * cols * 2 < lim;
+  return (rows + 256) * kc < lim && cols * kc < lim && (rows + 256) * cols * out_bytes < lim;
 }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -156,6 +156,19 @@ int gemm_wgrad(const uint8_t* qdyt, const float* sdyt, const uint8_t* qxt, const
     return st;
   if (!gemm_fits(N, K, M)) return JETFP8_EUNSUPPORTED;
   return launched(jetfp8::launch_gemm_wgrad(qdyt, sdyt, qxt, sxt, M, N, K, dw, as_stream(stream)));
+}
+
+int gemm_wgrad_f32(const uint8_t* qdyt, const float* sdyt, const uint8_t* qxt, const float* sxt,
+                   int64_t M, int64_t N, int64_t K, float* dw, int accumulate, void* stream) {
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || M % 128 || N % 128 || K % 128) return JETFP8_EINVAL;
+  if (accumulate != 0 && accumulate != 1) return JETFP8_EINVAL;
+  if (int st = check_ptrs({{qdyt, N * M}, {sdyt, 4 * (N * M / 128)}, {qxt, K * M},
+                           {sxt, 4 * (K * M / 128)}},
+                          {{dw, 4 * N * K}}))
+    return st;
+  if (!gemm_fits(N, K, M, 4)) return JETFP8_EUNSUPPORTED;
+  return launched(jetfp8::launch_gemm_wgrad_f32(qdyt, sdyt, qxt, sxt, M, N, K, dw, accumulate != 0,
+                                                as_stream(stream)));
 }
 
 }  // extern "C"

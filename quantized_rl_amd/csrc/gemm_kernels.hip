@@ -276,13 +276,28 @@ struct LargeTile {
   }
 };
 
-template <int kMode>
+// Output element kinds of the tile kernels: bf16 (every entry point), fp32
+// written, fp32 added to what the output already holds (WGrad into an fp32
+// gradient buffer).
+enum OutKind { kOutBf16 = 0, kOutF32 = 1, kOutF32Add = 2 };
+
+// fp32 output straight from the accumulators: each lane's four consecutive
+// columns of a 16 x 16 sub-tile go out as one 16-byte store (a quarter-wave
+// covers 64 contiguous bytes of a row); rows past the end fall outside the
+// buffer, read as zero and are not written.
+template <int kOut>
+__device__ __forceinline__ void store_f32(rsrc_t rc, uint32_t byte_off, v4f_t v) {
+  if (kOut == kOutF32Add) v += __builtin_bit_cast(v4f_t, __builtin_amdgcn_raw_buffer_load_b128(rc, byte_off, 0, 0));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i_t, v), rc, byte_off, 0, 0);
+}
+
+template <int kMode, int kOut = kOutBf16>
 __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t* __restrict__ A,
                                                                     const float* __restrict__ sa,
                                                                     const uint8_t* __restrict__ B,
                                                                     const float* __restrict__ sb,
                                                                     uint32_t M, uint32_t N, uint32_t K,
-                                                                    uint16_t* __restrict__ C) {
+                                                                    void* __restrict__ Cv) {
   __shared__ __attribute__((aligned(16))) LStage st0;
   __shared__ __attribute__((aligned(16))) LStage st1;
 
@@ -363,6 +378,18 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
     }
   }
 
+  if constexpr (kOut != kOutBf16) {
+    const rsrc_t rc = make_rsrc(Cv, M * N * 4u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t r = g.row0 + g.wm * 128 + 16 * i + g.lr, c = g.col0 + g.wn * 64 + 16 * j + 4 * g.lk;
+        store_f32<kOut>(rc, (r * N + c) * 4u, acc[i][j]);
+      }
+    return;
+  }
+  uint16_t* C = static_cast<uint16_t*>(Cv);
   // epilogue: stage the bf16 tile in LDS with a row pitch of 512 + 16 bytes
   // (rows 0..127 fill stage 0, rows 128..255 stage 1: 128 * 528 bytes is
   // exactly one stage object), then write it out with 16-byte buffer stores
@@ -399,7 +426,7 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
 // ---------------------------------------------------------------------------
 // Medium-tile kernel: 128 x 128 output tile, 4 waves (2 x 2) of 64 x 64, two
 // workgroups per CU.  The large kernel's machinery at a quarter of the tile:
-// direct-to-LDS operand loads (double-buffered, spread over the MFMA stream),
+// direct-to-LDS operand loads (double-buffered, issued early in each block),
 // the same XOR swizzle, LDS-staged scale factors, the same fold per output
 // element.  For problems with fewer than 256 tiles of 256 x 256 it keeps every
 // CU busy where the large kernel would leave most idle.
@@ -524,7 +551,12 @@ struct MedTile {
         af[n & 1] = frag(S + 2048 * n, sw ? a_odd : a_even, sw ? a_even : a_odd);
       }
       if (q < 16) part[q % 3] = mfma_fp8(bf[j], af[i & 1]);
-      if (q < 16 && (q & 1)) issue_piece(kn, nxt, q >> 1);
+      // the next K-block's loads: two pieces per MFMA over the first four, so
+      // that they have most of the (16-MFMA) block to arrive
+      if (q < 4) {
+        issue_piece(kn, nxt, 2 * q);
+        issue_piece(kn, nxt, 2 * q + 1);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (q >= 2) {
         const int qp = q - 2, pi = qp >> 2, pj = qp & 3;
@@ -539,13 +571,13 @@ struct MedTile {
   }
 };
 
-template <int kMode>
+template <int kMode, int kOut = kOutBf16>
 __global__ __launch_bounds__(kMThreads, 2) void gemm_fp8_med_kernel(const uint8_t* __restrict__ A,
                                                                      const float* __restrict__ sa,
                                                                      const uint8_t* __restrict__ B,
                                                                      const float* __restrict__ sb,
                                                                      uint32_t M, uint32_t N, uint32_t K,
-                                                                     uint16_t* __restrict__ C) {
+                                                                     void* __restrict__ Cv) {
   __shared__ __attribute__((aligned(16))) MStage st0;
   __shared__ __attribute__((aligned(16))) MStage st1;
 
@@ -618,6 +650,18 @@ __global__ __launch_bounds__(kMThreads, 2) void gemm_fp8_med_kernel(const uint8_
     }
   }
 
+  if constexpr (kOut != kOutBf16) {
+    const rsrc_t rc = make_rsrc(Cv, M * N * 4u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t r = g.row0 + g.wm * 64 + 16 * i + g.lr, c = g.col0 + g.wn * 64 + 16 * j + 4 * g.lk;
+        store_f32<kOut>(rc, (r * N + c) * 4u, acc[i][j]);
+      }
+    return;
+  }
+  uint16_t* C = static_cast<uint16_t*>(Cv);
   // epilogue: bf16 tile staged in LDS (rows 0..63 in stage 0, 64..127 in
   // stage 1, pitch 256 + 16 bytes), then 16-byte buffer stores
   constexpr int kPitch = kMBN * 2 + 16;
@@ -1020,14 +1064,20 @@ static void launch_decode(int mt, int kw, int ks, const uint8_t* A, const float*
   else launch_decode_m<4>(kw, ks, A, sa, B, sb, m, n, k, C, stream);
 }
 
-template <int kMode>
+template <int kMode, int kOut = kOutBf16>
 static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
-                              int64_t Mr, int64_t Nc, int64_t Kc, uint16_t* C,
+                              int64_t Mr, int64_t Nc, int64_t Kc, void* Cv,
                               hipStream_t stream) {
   if (Mr == 0 || Nc == 0) return hipSuccess;
-  if (Kc == 0) return launch_zero(C, Mr * Nc, stream);
+  // an empty contraction: the product is zero (nothing to add for kOutF32Add)
+  if (Kc == 0) {
+    if (kOut == kOutF32Add) return hipSuccess;
+    return launch_zero(static_cast<uint16_t*>(Cv), Mr * Nc * (kOut == kOutF32 ? 2 : 1), stream);
+  }
+  uint16_t* C = static_cast<uint16_t*>(Cv);
   // rollout decode: weight-streaming kernel for up to 64 tokens (FProp)
-  if (kMode == kFprop && Mr <= 64 && Nc * Kc < (int64_t(1) << 31) && Mr * Kc < (int64_t(1) << 31)) {
+  if (kMode == kFprop && kOut == kOutBf16 && Mr <= 64 && Nc * Kc < (int64_t(1) << 31) &&
+      Mr * Kc < (int64_t(1) << 31)) {
     // Strips per wave: 2 when there are at least 384 strips of 16 columns
     // (each X fragment then serves two strips), else 1.  Waves per strip
     // group: enough for about 1024 / mt streaming waves (a wave with mt token
@@ -1052,8 +1102,8 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
   // the K-split kernel wins only for the 8B down projection (N = 4096,
   // K = 12288), the medium kernel for QKV, gate+up and the 32B down.
   const int64_t nkb = Kc / kBK;
-  if (kMode == kFprop && Mr <= 256 && nkb >= 64 && Nc / kBN <= 32 && Nc * Kc < (int64_t(1) << 31) &&
-      Mr * Kc < (int64_t(1) << 31)) {
+  if (kMode == kFprop && kOut == kOutBf16 && Mr <= 256 && nkb >= 64 && Nc / kBN <= 32 &&
+      Nc * Kc < (int64_t(1) << 31) && Mr * Kc < (int64_t(1) << 31)) {
     const int64_t tiles = (Nc / 64) * ((Mr + 63) / 64);
     hipLaunchKernelGGL(gemm_fp8_mid_kernel, dim3((unsigned)tiles), dim3(512), 0, stream, A, sa, B, sb,
                        (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C);
@@ -1062,17 +1112,17 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
   // the large-tile kernel works with 32-bit byte offsets; it needs >= 256
   // tiles to fill the chip
   const bool fits32 = (Mr + kLBM) * Kc < (int64_t(1) << 31) && Nc * Kc < (int64_t(1) << 31) &&
-                      (Mr + kLBM) * Nc * 2 < (int64_t(1) << 31);
+                      (Mr + kLBM) * Nc * (kOut == kOutBf16 ? 2 : 4) < (int64_t(1) << 31);
   const int64_t large_tiles = ((Mr + kLBM - 1) / kLBM) * (Nc / kLBN);
   if (Nc % kLBN == 0 && fits32 && large_tiles >= 256) {
-    hipLaunchKernelGGL(gemm_fp8_large_kernel<kMode>, dim3((unsigned)large_tiles), dim3(kLThreads), 0,
-                       stream, A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C);
+    hipLaunchKernelGGL((gemm_fp8_large_kernel<kMode, kOut>), dim3((unsigned)large_tiles), dim3(kLThreads), 0,
+                       stream, A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, Cv);
     return hipGetLastError();
   }
   // the medium-tile kernel (the caller guarantees 32-bit byte offsets)
   const int64_t tiles = ((Mr + kMBM - 1) / kMBM) * (Nc / kMBN);
-  hipLaunchKernelGGL(gemm_fp8_med_kernel<kMode>, dim3((unsigned)tiles), dim3(kMThreads), 0, stream, A, sa, B,
-                     sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C);
+  hipLaunchKernelGGL((gemm_fp8_med_kernel<kMode, kOut>), dim3((unsigned)tiles), dim3(kMThreads), 0, stream, A,
+                     sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, Cv);
   return hipGetLastError();
 }
 
@@ -1093,6 +1143,13 @@ hipError_t launch_gemm_wgrad(const uint8_t* qdyt, const float* sdyt, const uint8
                              hipStream_t stream) {
   // rows are the N output features, columns the K input features, contraction over M tokens
   return launch_gemm<kWgrad>(qdyt, sdyt, qxt, sxt, N, K, M, dw, stream);
+}
+
+hipError_t launch_gemm_wgrad_f32(const uint8_t* qdyt, const float* sdyt, const uint8_t* qxt,
+                                 const float* sxt, int64_t M, int64_t N, int64_t K, float* dw,
+                                 bool accumulate, hipStream_t stream) {
+  if (accumulate) return launch_gemm<kWgrad, kOutF32Add>(qdyt, sdyt, qxt, sxt, N, K, M, dw, stream);
+  return launch_gemm<kWgrad, kOutF32>(qdyt, sdyt, qxt, sxt, N, K, M, dw, stream);
 }
 
 }  // namespace jetfp8

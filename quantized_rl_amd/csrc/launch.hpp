@@ -22,5 +22,8 @@ hipError_t launch_gemm_dgrad(const uint8_t* qdy, const float* sdy, const uint8_t
 hipError_t launch_gemm_wgrad(const uint8_t* qdyt, const float* sdyt, const uint8_t* qxt,
                              const float* sxt, int64_t M, int64_t N, int64_t K, uint16_t* dw,
                              hipStream_t stream);
+hipError_t launch_gemm_wgrad_f32(const uint8_t* qdyt, const float* sdyt, const uint8_t* qxt,
+                                 const float* sxt, int64_t M, int64_t N, int64_t K, float* dw,
+                                 bool accumulate, hipStream_t stream);
 
 }  // namespace jetfp8

@@ -12,6 +12,10 @@ requantisation of both saved operands, WGrad (dW = dY^T X).
 Every arithmetic step runs in libjetfp8.so; this module only orders the calls
 and allocates outputs through torch.  The token count M must be a multiple of
 128 for the backward (128-token groups of the requantisation).
+
+Optionally the weight gradient is kept in fp32 (``gemm_wgrad_f32``): each
+backward adds its dW to an fp32 buffer, so the gradients of several
+micro-batches are summed before any rounding to bf16.
 """
 
 import torch
@@ -20,24 +24,30 @@ from . import _lib
 
 
 class FP8LinearFunction(torch.autograd.Function):
-    """y = x w^T with the mixed-granularity FP8 recipe.  x bf16 [M, K], w bf16 [N, K]."""
+    """y = x w^T with the mixed-granularity FP8 recipe.  x bf16 [M, K], w bf16 [N, K].
+
+    With ``dw_fp32`` (a float32 [N, K] buffer) the backward adds the weight
+    gradient to that buffer in fp32 and returns no gradient for ``w``."""
 
     @staticmethod
-    def forward(ctx, x, w):
+    def forward(ctx, x, w, dw_fp32=None):
         qx, sx = _lib.quantize_act_1x128(x.contiguous())
         qw, sw = _lib.quantize_weight_128x128(w.contiguous())
         y = _lib.gemm_fprop(qx, sx, qw, sw)
         ctx.save_for_backward(qx, sx, qw, sw)
+        ctx.dw_fp32 = dw_fp32
         return y
 
     @staticmethod
     def backward(ctx, dy):
         qx, sx, qw, sw = ctx.saved_tensors
-        return fp8_linear_backward(dy, qx, sx, qw, sw)
+        dx, dw = fp8_linear_backward(dy, qx, sx, qw, sw, dw_fp32=ctx.dw_fp32)
+        return dx, dw, None
 
 
-def fp8_linear_backward(dy, qx, sx, qw, sw):
-    """(dx bf16 [M, K], dw bf16 [N, K]) from bf16 dY [M, N] and the saved FP8 operands."""
+def fp8_linear_backward(dy, qx, sx, qw, sw, dw_fp32=None):
+    """(dx bf16 [M, K], dw bf16 [N, K]) from bf16 dY [M, N] and the saved FP8 operands.
+    With ``dw_fp32`` given, dW is added to it in fp32 instead and None is returned for dw."""
     M = dy.shape[0]
     if M % 128:
         raise ValueError(f"FP8 linear backward needs M % 128 == 0 (128-token groups), got M={M}")
@@ -45,29 +55,45 @@ def fp8_linear_backward(dy, qx, sx, qw, sw):
     dx = _lib.gemm_dgrad(qdy, sdy, qw, sw)
     qxt, sxt = _lib.requant_transpose_128x1(qx, sx)
     qdyt, sdyt = _lib.requant_transpose_128x1(qdy, sdy)
+    if dw_fp32 is not None:
+        _lib.gemm_wgrad_f32(qdyt, sdyt, qxt, sxt, dw=dw_fp32, accumulate=True)
+        return dx, None
     dw = _lib.gemm_wgrad(qdyt, sdyt, qxt, sxt)
     return dx, dw
 
 
-def fp8_linear(x, w):
+def fp8_linear(x, w, dw_fp32=None):
     """Functional form of :class:`FP8LinearFunction`."""
-    return FP8LinearFunction.apply(x, w)
+    return FP8LinearFunction.apply(x, w, dw_fp32)
 
 
 class FP8Linear(torch.nn.Module):
     """A bias-free linear layer with a bf16 master weight [out, in] whose forward
     and backward GEMMs run in FP8 (the unified precision flow: rollout calls the
-    same forward)."""
+    same forward).
 
-    def __init__(self, in_features, out_features, device=None):
+    ``fp32_grad_accum=True`` keeps the weight gradient in an fp32 buffer
+    ``main_grad`` instead of ``weight.grad``: every backward adds to it (summing
+    micro-batches before any bf16 rounding); ``zero_main_grad()`` clears it."""
+
+    def __init__(self, in_features, out_features, device=None, fp32_grad_accum=False):
         super().__init__()
         if in_features % 128 or out_features % 128:
             raise ValueError("in_features and out_features must be multiples of 128")
         self.weight = torch.nn.Parameter(
             torch.empty(out_features, in_features, dtype=torch.bfloat16, device=device))
         torch.nn.init.normal_(self.weight, std=0.02)
+        self.register_buffer(
+            "main_grad",
+            torch.zeros(out_features, in_features, dtype=torch.float32, device=device)
+            if fp32_grad_accum else None,
+            persistent=False)
+
+    def zero_main_grad(self):
+        if self.main_grad is not None:
+            self.main_grad.zero_()
 
     def forward(self, x):
         shape = x.shape
-        y = fp8_linear(x.reshape(-1, shape[-1]), self.weight)
+        y = fp8_linear(x.reshape(-1, shape[-1]), self.weight, self.main_grad)
         return y.reshape(*shape[:-1], self.weight.shape[0])

@@ -27,7 +27,7 @@ def declared_functions():
 def test_header_declares_the_seven_entry_points():
     names = declared_functions()
     for n in ["quantize_act_1x128", "quantize_weight_128x128", "rmsnorm_quant",
-              "requant_transpose_128x1", "gemm_fprop", "gemm_dgrad", "gemm_wgrad",
+              "requant_transpose_128x1", "gemm_fprop", "gemm_dgrad", "gemm_wgrad", "gemm_wgrad_f32",
               "jetfp8_status_string"]:
         assert n in names
 
@@ -117,3 +117,18 @@ def test_gemm_validation(jetlib):
     assert c("gemm_wgrad", P[0], P[1], P[2], P[3], 100, 128, 128, P[4], 0) == EINVAL
     assert c("gemm_wgrad", P[0], P[1], P[2], P[3], 128, 128, 128, P[3], 0) == EALIAS
     assert c("gemm_wgrad", P[0], P[1], P[2], P[3], 128, 0, 128, 0, 0) == OK  # N = 0: empty output
+
+
+def test_gemm_wgrad_f32_validation(jetlib):
+    f = "gemm_wgrad_f32"
+    # wgrad_f32(qdyt, sdyt, qxt, sxt, M, N, K, dw, accumulate)
+    assert c(f, P[0], P[1], P[2], P[3], 100, 128, 128, P[4], 0, 0) == EINVAL   # M % 128
+    assert c(f, P[0], P[1], P[2], P[3], 128, 128, 128, P[4], 2, 0) == EINVAL   # accumulate not 0/1
+    assert c(f, P[0], P[1], P[2], P[3], 128, 128, 128, P[4], -1, 0) == EINVAL
+    assert c(f, P[0], P[1], P[2], P[3], 128, 128, 128, 0, 0, 0) == ENULL
+    assert c(f, P[0], P[1], P[2], P[3], 128, 128, 128, P[4] + 8, 1, 0) == EALIGN
+    assert c(f, P[0], P[1], P[2], P[3], 128, 128, 128, P[3] - 16, 0, 0) == EALIAS  # dw runs into sxt
+    assert c(f, P[0], P[1], P[2], P[3], 128, 0, 128, 0, 1, 0) == OK  # N = 0: empty output
+    # 4-byte output elements: dW [2^17, 4096] fp32 is 2 GiB (its bf16 form would fit)
+    Q = [(i + 1) << 40 for i in range(8)]
+    assert c(f, Q[0], Q[1], Q[2], Q[3], 128, 1 << 17, 4096, Q[4], 0, 0) == 5

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from gpu_common import bf16_dev, host
-from quantized_rl_amd import linear, synth
+from quantized_rl_amd import _lib, linear, synth
 
 pytestmark = pytest.mark.gpu
 
@@ -92,3 +92,51 @@ def test_two_layer_fp8_stack_trains():
             p -= (5.0 * p.grad.float()).to(torch.bfloat16)
             p.grad = None
     assert loss_fn().item() < loss0.item()
+
+
+def test_fp8_linear_fp32_grad_accumulation_over_micro_batches():
+    """FP8Linear(fp32_grad_accum=True): two micro-batches add their weight
+    gradients into main_grad in fp32 (no gradient lands in weight.grad); the sum
+    equals the two fp32 WGrad results added in fp32, each of which rounds to the
+    bf16 gradient of the plain layer, and it matches the oracle's fp64 sum."""
+    torch.manual_seed(1)
+    dev = torch.device("cuda:0")
+    m, k, n = 256, 512, 384
+    layer = linear.FP8Linear(k, n, device=dev, fp32_grad_accum=True)
+    w = layer.weight.detach().clone()
+    xs = [synth.random_bf16((m, k), seed=40 + i, std=1.0) for i in range(2)]
+    dys = [synth.random_bf16((m, n), seed=50 + i, std=1e-3) for i in range(2)]
+    parts = []
+    for x_h, dy_h in zip(xs, dys):
+        x = bf16_dev(x_h).requires_grad_(True)
+        layer(x).backward(bf16_dev(dy_h))
+        # the same micro-batch through the plain bf16 path and through gemm_wgrad_f32
+        x2 = bf16_dev(x_h).requires_grad_(True)
+        w2 = w.clone().requires_grad_(True)
+        linear.fp8_linear(x2, w2).backward(bf16_dev(dy_h))
+        qx, sx = jet_quant(x2)
+        qdy, sdy = jet_quant(bf16_dev(dy_h))
+        qxt, sxt = _lib.requant_transpose_128x1(qx, sx)
+        qdyt, sdyt = _lib.requant_transpose_128x1(qdy, sdy)
+        g = host(_lib.gemm_wgrad_f32(qdyt, sdyt, qxt, sxt))
+        assert np.array_equal(host(w2.grad), oracle.f64_to_bf16_bits(g.astype(np.float64)))
+        assert torch.equal(x.grad, x2.grad)
+        parts.append(g)
+    torch.cuda.synchronize()
+    assert layer.weight.grad is None
+    assert np.array_equal(host(layer.main_grad), np.float32(0) + parts[0] + parts[1])
+    ref = 0.0
+    for x_h, dy_h in zip(xs, dys):
+        qxo, sxo = oracle.quant_act_1x128(x_h)
+        qdyo, sdyo = oracle.quant_act_1x128(dy_h)
+        qxt, sxt = oracle.requant_transpose_128x1(qxo, sxo)
+        qdyt, sdyt = oracle.requant_transpose_128x1(qdyo, sdyo)
+        ref = ref + oracle.gemm_wgrad_ref(qdyt, sdyt, qxt, sxt)
+    r = oracle.check_gemm_f32(host(layer.main_grad), ref)
+    assert r["ok"], r
+    layer.zero_main_grad()
+    assert bool((layer.main_grad == 0).all())
+
+
+def jet_quant(t):
+    return _lib.quantize_act_1x128(t.detach().contiguous())

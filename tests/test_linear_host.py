@@ -1,0 +1,27 @@
+"""Host-side construction of the FP8 linear module (no kernel is called)."""
+
+import pytest
+import torch
+
+from quantized_rl_amd import linear
+
+
+def test_fp8_linear_module_buffers():
+    plain = linear.FP8Linear(256, 128, device="cpu")
+    assert plain.main_grad is None
+    assert plain.weight.dtype == torch.bfloat16 and tuple(plain.weight.shape) == (128, 256)
+    plain.zero_main_grad()  # nothing to clear
+    acc = linear.FP8Linear(256, 128, device="cpu", fp32_grad_accum=True)
+    assert acc.main_grad.dtype == torch.float32 and tuple(acc.main_grad.shape) == (128, 256)
+    assert bool((acc.main_grad == 0).all())
+    acc.main_grad.fill_(2.0)
+    acc.zero_main_grad()
+    assert bool((acc.main_grad == 0).all())
+    assert "main_grad" not in acc.state_dict()  # not persistent: the master weight is the state
+
+
+def test_fp8_linear_module_rejects_unaligned_features():
+    with pytest.raises(ValueError):
+        linear.FP8Linear(100, 128, device="cpu")
+    with pytest.raises(ValueError):
+        linear.FP8Linear(128, 200, device="cpu")

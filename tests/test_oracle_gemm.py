@@ -191,3 +191,32 @@ def test_check_gemm_tolerance():
     assert not oracle.check_gemm(np.full((4, 4), 1, np.uint16), z)["ok"]
     assert np.array_equal(oracle.bf16_ulp(np.array([1.0, 1.5, 2.0 ** -130, 0.0])),
                           np.array([2.0 ** -7, 2.0 ** -7, 2.0 ** -133, 2.0 ** -133]))
+
+
+def test_check_gemm_f32_tolerance():
+    rng = np.random.default_rng(9)
+    ref = rng.standard_normal((64, 64))
+    y = ref.astype(np.float32)
+    r = oracle.check_gemm_f32(y, ref)
+    assert r["ok"] and r["normwise"] < 1e-7
+    # one element just inside / just outside ulp_bf16(ref) + 1e-3 rms
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    bound = float(oracle.bf16_ulp(ref[5, 6])) + 1e-3 * rms
+    y1 = y.copy()
+    y1[5, 6] = np.float32(ref[5, 6] + 0.98 * bound)
+    assert oracle.check_gemm_f32(y1, ref)["ok"]
+    y1[5, 6] = np.float32(ref[5, 6] - 1.05 * bound)
+    assert not oracle.check_gemm_f32(y1, ref)["ok"]
+    # a uniform 0.2 % relative error fails the normwise bound
+    assert not oracle.check_gemm_f32((ref * 1.002).astype(np.float32), ref)["ok"]
+    # accumulation: the bound follows the added product, not the (large) base value
+    base = rng.standard_normal((64, 64)) * 1e3
+    tot = base + ref
+    assert oracle.check_gemm_f32(tot.astype(np.float32), tot, contrib64=ref)["ok"]
+    yw = tot.astype(np.float32)
+    yw[1, 2] += np.float32(0.25)  # far beyond the product's bound, far below the base's bf16 ulp
+    assert not oracle.check_gemm_f32(yw, tot, contrib64=ref)["ok"]
+    # zero product: the result must equal the reference exactly
+    z = np.zeros((4, 4))
+    assert oracle.check_gemm_f32(z.astype(np.float32), z)["ok"]
+    assert not oracle.check_gemm_f32(np.full((4, 4), 1e-30, np.float32), z)["ok"]

@@ -135,30 +135,41 @@ def cpu_baseline(d, gamma):
 
 
 def time_steps(torch, steps, n_steps, n_warmup, dev):
-    """Run warm-up steps, then time n_steps steps with HIP events around every
-    kernel (recorded on the launch stream).  Returns (per-kernel ms lists,
-    per-step ms list, wall seconds)."""
+    """Run warm-up steps, then two timed passes of n_steps steps on the launch
+    stream.  Pass 1 records a HIP event only at step boundaries: it gives the
+    step times and the wall time.  Pass 2 records an event after every kernel:
+    it gives the per-kernel times (those events put a small gap between the
+    kernels, so pass 2's steps run slightly longer than pass 1's).  Returns
+    (per-kernel ms lists, per-step ms list, wall seconds of pass 1)."""
     for _ in range(n_warmup):
         for _, fn in steps:
             fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)] for _ in range(n_steps)]
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    bounds[0].record(stream)
+    for s in range(n_steps):
+        for _, fn in steps:
+            fn()
+        bounds[s + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [bounds[s].elapsed_time(bounds[s + 1]) for s in range(n_steps)]
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)] for _ in range(n_steps)]
+    torch.cuda.synchronize()
     for s in range(n_steps):
         ev[s][0].record(stream)
         for i, (_, fn) in enumerate(steps):
             fn()
             ev[s][i + 1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per = {name: [] for name, _ in steps}
-    step_ms = []
     for s in range(n_steps):
         for i, (name, _) in enumerate(steps):
             per[name].append(ev[s][i].elapsed_time(ev[s][i + 1]))
-        step_ms.append(ev[s][0].elapsed_time(ev[s][-1]))
     return per, step_ms, wall
 
 

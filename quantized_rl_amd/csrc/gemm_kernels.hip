@@ -189,7 +189,48 @@ struct LargeTile {
     return v8i_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
   }
 
-  // Multiply the K-block held in stage st into the accumulators.
+  // Registers carried from one K-block into the next: the first A fragment,
+  // the first two B fragments and the row factors of the block, read from its
+  // stage right after the barrier that publishes it.
+  struct Head {
+    v8i_t af0, bf0, bf1;
+    float srow[8];
+  };
+
+  // B fragment j of the stage at S.  DGrad: transposed reads of W's rows.
+  __device__ __forceinline__ v8i_t read_b(const uint8_t* S, int j) const {
+    if (kMode == kDgrad) {
+      v2i_t part[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) part[q4] = lds_tr8(S + dv[j ^ (q4 & 1)] + 1024 * q4);
+      return v8i_t{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
+    }
+    const bool sw = (j >> 1) & 1;
+    return frag(S + 2048 * j, sw ? b_odd : b_even, sw ? b_even : b_odd);
+  }
+  // Row factors of the 8 row sub-tiles (transposed layout: 8 contiguous
+  // floats); FProp, DGrad: the products for the column half holding the
+  // wave's 64 columns.
+  __device__ __forceinline__ void read_srow(const LStage& st, float (&srow)[8]) const {
+    const uint8_t* sr = reinterpret_cast<const uint8_t*>(st.sc[kMode == kWgrad ? 0 : (wn >> 1)]) + s_row;
+    const float4 s0 = *reinterpret_cast<const float4*>(sr);
+    const float4 s1 = *reinterpret_cast<const float4*>(sr + 16);
+    srow[0] = s0.x; srow[1] = s0.y; srow[2] = s0.z; srow[3] = s0.w;
+    srow[4] = s1.x; srow[5] = s1.y; srow[6] = s1.z; srow[7] = s1.w;
+  }
+  // The first A fragment is read before the B fragments: the block's first
+  // MFMA then waits for four reads instead of the whole set.
+  __device__ __forceinline__ void read_head(const LStage& st, Head& h) const {
+    h.af0 = frag(st.ab, a_even, a_odd);
+    h.bf0 = read_b(st.ab, 0);
+    h.bf1 = read_b(st.ab, 1);
+    read_srow(st, h.srow);
+  }
+
+  // Multiply the K-block held in stage st into the accumulators, load K-block
+  // kn into stage nxt, and publish nxt (with its scale factors xs) to all
+  // waves: store the factors, wait for this wave's loads, barrier, read the
+  // head of nxt.
   //
   // Row sub-tile i of the A tile: lane reads row wm*128 + 16 i + lr, logical
   // chunks 2 lk and 2 lk + 1.  The swizzle f(row) equals f0(lr) ^ bit1(i), so
@@ -199,43 +240,25 @@ struct LargeTile {
   // The next K-block's direct loads (into the other stage) are issued one
   // piece every two MFMAs over the first half of the block: late enough not
   // to crowd the block's first fragment reads, early enough that the last
-  // piece has half a block to arrive before the end-of-block wait (issued
-  // through the whole block, its latency showed in every block; in one
-  // burst, the fragment reads stalled behind it).
-  __device__ __forceinline__ void compute(const LStage& st, v4f_t (&acc)[8][4], uint32_t kn, LStage& nxt) const {
+  // piece has half a block to arrive before the wait (issued through the
+  // whole block, its latency showed in every block; in one burst, the
+  // fragment reads stalled behind it).
+  // WGrad publishes nxt at step kBar = 27, once the block's last LDS read (A
+  // row 7, step 24) is done: the barrier and the next block's head reads then
+  // overlap the last MFMAs and rescales, whose VALU work is largest in WGrad.
+  // FProp and DGrad publish after the block, which leaves the loads more time
+  // (measured better with cold caches).
+  __device__ __forceinline__ void compute(const LStage& st, v4f_t (&acc)[8][4], uint32_t kn, LStage& nxt,
+                                          float2 xs, Head& h) const {
+    constexpr int kBar = kMode == kWgrad ? 27 : 34;
     const uint8_t* S = st.ab;
-    // B fragments are read in the order the first row of MFMAs uses them,
-    // each well ahead of its use (bf[0], bf[1] before the loop, bf[j + 2] at
-    // step j), after the first A fragment: the first MFMA waits for four
-    // reads instead of the whole set.
-    v8i_t bf[4];
-    auto read_b = [&](int j) {
-      if (kMode == kDgrad) {
-        v2i_t part[4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) part[q4] = lds_tr8(S + dv[j ^ (q4 & 1)] + 1024 * q4);
-        bf[j] = v8i_t{part[0].x, part[0].y, part[1].x, part[1].y,
-                      part[2].x, part[2].y, part[3].x, part[3].y};
-      } else {
-        const bool sw = (j >> 1) & 1;
-        bf[j] = frag(S + 2048 * j, sw ? b_odd : b_even, sw ? b_even : b_odd);
-      }
-    };
-    v8i_t af[2];
-    af[0] = frag(S, a_even, a_odd);
-    read_b(0);
-    read_b(1);
-    // row factors of the 8 row sub-tiles (transposed layout: 8 contiguous
-    // floats); FProp, DGrad: the products for the column half holding the
-    // wave's 64 columns
+    v8i_t bf[4], af[2];
+    bf[0] = h.bf0;
+    bf[1] = h.bf1;
+    af[0] = h.af0;
     float srow[8];
-    {
-      const uint8_t* sr = reinterpret_cast<const uint8_t*>(st.sc[kMode == kWgrad ? 0 : (wn >> 1)]) + s_row;
-      const float4 s0 = *reinterpret_cast<const float4*>(sr);
-      const float4 s1 = *reinterpret_cast<const float4*>(sr + 16);
-      srow[0] = s0.x; srow[1] = s0.y; srow[2] = s0.z; srow[3] = s0.w;
-      srow[4] = s1.x; srow[5] = s1.y; srow[6] = s1.z; srow[7] = s1.w;
-    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) srow[r] = h.srow[r];
     float scol[4][4];
     if (kMode == kWgrad) {
 #pragma unroll
@@ -244,17 +267,22 @@ struct LargeTile {
         scol[j][0] = c4.x; scol[j][1] = c4.y; scol[j][2] = c4.z; scol[j][3] = c4.w;
       }
     }
+    auto publish = [&]() {
+      store_scale(nxt, xs);
+      wait_vmem();
+      __syncthreads();
+    };
 
     // Software pipeline over the 32 (row, column) sub-tiles, row-major: step q
     // issues the MFMA of sub-tile q, then rescales the partial of sub-tile
     // q - 2 into its accumulators, so two MFMAs separate every partial from
-    // its use; the A fragment of the next row sub-tile is read a row ahead.
-    // Scheduling barriers pin the order.
+    // its use; the A fragment of the next row sub-tile is read a row ahead,
+    // B fragments 2 and 3 at steps 0 and 1.  Scheduling barriers pin the order.
     v4f_t part[3];
 #pragma unroll
     for (int q = 0; q < 34; ++q) {
       const int i = q >> 2, j = q & 3;
-      if (q < 2) read_b(q + 2);
+      if (q < 2) bf[q + 2] = read_b(S, q + 2);
       if (q < 32 && j == 0 && i + 1 < 8) {
         const int n = i + 1;
         const bool sw = (n >> 1) & 1;
@@ -262,6 +290,11 @@ struct LargeTile {
       }
       if (q < 32) part[q % 3] = mfma_fp8(bf[j], af[i & 1]);
       if (q < 16 && !(q & 1)) issue_piece(kn, nxt, q >> 1);
+      if (q == kBar) publish();
+      if (q == kBar + 1) h.af0 = frag(nxt.ab, a_even, a_odd);
+      if (q == kBar + 2) h.bf0 = read_b(nxt.ab, 0);
+      if (q == kBar + 3) h.bf1 = read_b(nxt.ab, 1);
+      if (q == kBar + 4) read_srow(nxt, h.srow);
       __builtin_amdgcn_sched_barrier(0);
       if (q >= 2) {
         const int qp = q - 2, pi = qp >> 2, pj = qp & 3;
@@ -272,6 +305,10 @@ struct LargeTile {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if (kBar >= 34) {
+      publish();
+      read_head(nxt, h);
     }
   }
 };
@@ -353,6 +390,8 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
   g.issue(0, st0);
   wait_vmem();
   __syncthreads();
+  typename LargeTile<kMode>::Head head;
+  g.read_head(st0, head);
 
   // Two K-blocks per trip: compute stage 0 while stage 1 loads, then the
   // reverse.  The prefetch past the last block reloads the last block (the
@@ -362,21 +401,15 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
   for (uint32_t kb = 0; kb < g.nkb; kb += 2) {
     {
       const uint32_t kn = kb + 1 <= last ? kb + 1 : last;
-      const float2 x = g.load_scale(kn);
-      g.compute(st0, acc, kn, st1);
-      g.store_scale(st1, x);
-      wait_vmem();
-      __syncthreads();
+      g.compute(st0, acc, kn, st1, g.load_scale(kn), head);
     }
     if (kb + 1 <= last) {
       const uint32_t kn = kb + 2 <= last ? kb + 2 : last;
-      const float2 x = g.load_scale(kn);
-      g.compute(st1, acc, kn, st0);
-      g.store_scale(st0, x);
-      wait_vmem();
-      __syncthreads();
+      g.compute(st1, acc, kn, st0, g.load_scale(kn), head);
     }
   }
+  // every wave is done with the operand stages (the epilogue reuses them)
+  __syncthreads();
 
   if constexpr (kOut != kOutBf16) {
     const rsrc_t rc = make_rsrc(Cv, M * N * 4u);

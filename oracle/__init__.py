@@ -17,6 +17,8 @@ page "paper.rainbus.top/paper/2601.14243", sections "FP8 量化 (E4M3 格式)",
   gradients, 128x128 blocks for weights; the fused RMSNorm + 1x128 quantiser;
   and the requantisation of a saved 1x128 FP8 tensor into 128x1 groups along
   the token dimension, stored transposed.
+* ``norm``   -- the gradients of the RMSNorm (dx, dgamma) in fp64, and their
+  acceptance check.
 * ``gemm``   -- the three block-scaled GEMMs (FProp Y = X W^T, DGrad
   dX = dY W, WGrad dW = dY^T X) as their plain definition on dequantised values
   in fp64, the bf16 rounding of the result, and the acceptance check.
@@ -31,6 +33,10 @@ brute force.  One function has no such pin for its exact bits:
 ``rmsnorm_quant`` -- the pages name a fused RMSNorm but give no formula, so the
 order of its fp32 reduction is this oracle's reading (parity unpinned against
 the pages; pinned only against math.fsum and torch's rms_norm to a tolerance).
+The RMSNorm backward (``norm``) follows from calculus on that same reading, so it
+too is parity unpinned against the pages; it is pinned against central finite
+differences of the forward, torch's autograd of rms_norm in float64 and a
+closed-form identity for sum_k x_k dx_k.
 """
 
 from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode, e4m3_table
@@ -39,11 +45,13 @@ from .quant import (
     quant_act_1x128,
     quant_act_1x128_f32,
     rmsnorm_f32,
+    rmsnorm_rstd_f32,
     quant_weight_128x128,
     rmsnorm_quant,
     requant_transpose_128x1,
     pairwise_sum_f32,
 )
+from .norm import check_rmsnorm_backward, rmsnorm_backward_ref
 from .gemm import (
     dequant_groups,
     dequant_blocks,
@@ -61,7 +69,7 @@ from .gemm import (
 
 __all__ = [
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "e4m3_table",
-    "bf16_bits_to_f32", "quant_act_1x128", "quant_act_1x128_f32", "rmsnorm_f32", "quant_weight_128x128", "rmsnorm_quant",
+    "bf16_bits_to_f32", "quant_act_1x128", "quant_act_1x128_f32", "rmsnorm_f32", "rmsnorm_rstd_f32", "rmsnorm_backward_ref", "check_rmsnorm_backward", "quant_weight_128x128", "rmsnorm_quant",
     "requant_transpose_128x1", "pairwise_sum_f32",
     "dequant_groups", "dequant_blocks", "gemm_fprop_ref", "gemm_dgrad_ref", "gemm_wgrad_ref",
     "gemm_fprop_ref_at", "gemm_dgrad_ref_at", "gemm_wgrad_ref_at",

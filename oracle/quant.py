@@ -134,13 +134,27 @@ def rmsnorm_f32(x_bf16, gamma_bf16, eps):
         raise ValueError("expected x [M, K], gamma [K], K > 0")
     _check_finite(x)
     _check_finite(gamma)
+    inv = _rstd_f32(x, eps)
+    return ((x * inv[:, None]).astype(np.float32) * gamma[None, :]).astype(np.float32)
+
+
+def _rstd_f32(x, eps):
     k = x.shape[1]
     sq = (x * x).astype(np.float32)
     ss = pairwise_sum_f32(sq)
     ms = (ss / np.float32(k)).astype(np.float32)
     d = (ms + np.float32(eps)).astype(np.float32)
-    inv = (_ONE / np.sqrt(d)).astype(np.float32)  # correctly rounded sqrt, then a division
-    return ((x * inv[:, None]).astype(np.float32) * gamma[None, :]).astype(np.float32)
+    return (_ONE / np.sqrt(d)).astype(np.float32)  # correctly rounded sqrt, then a division
+
+
+def rmsnorm_rstd_f32(x_bf16, eps):
+    """The per-row fp32 factor inv = fl32(1 / fl32(sqrt(fl32(fl32(ss / K) + eps))))
+    that rmsnorm_f32 multiplies by (the value a forward saves for the backward)."""
+    x = bf16_bits_to_f32(x_bf16)
+    if x.ndim != 2 or x.shape[1] == 0:
+        raise ValueError("expected x [M, K], K > 0")
+    _check_finite(x)
+    return _rstd_f32(x, eps)
 
 
 def rmsnorm_quant(x_bf16, gamma_bf16, eps):

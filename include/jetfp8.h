@@ -119,6 +119,37 @@ int rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K
                   uint8_t* q, float* s, void* stream);
 
 /*
+ * rmsnorm_quant_rstd -- rmsnorm_quant that also saves, for the backward, the
+ * per-row factor it multiplied by:
+ *   rstd[m] = inv = fl32(1 / fl32(sqrt(fl32(fl32(ss / K) + eps))))
+ *   rstd : f32 [M] output.  q and s are bitwise those of rmsnorm_quant.
+ * Same shape rules as rmsnorm_quant.
+ */
+int rmsnorm_quant_rstd(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps,
+                       uint8_t* q, float* s, float* rstd, void* stream);
+
+/*
+ * rmsnorm_backward -- gradients of the RMSNorm of rmsnorm_quant for an
+ * upstream gradient dy (the FP8 linear's DGrad output).  The pages train
+ * through the fused RMSNorm ([P3-STEPS] step 5) without stating its formula;
+ * these are the derivatives of the standard RMSNorm y = x * gamma * rstd:
+ *   c[m]      = (1/K) sum_k gamma[k] * dy[m][k] * x[m][k]
+ *   dx[m][k]  = rstd[m] * (gamma[k] * dy[m][k] - x[m][k] * rstd[m]^2 * c[m])
+ *   dgamma[k] = sum_m dy[m][k] * x[m][k] * rstd[m]
+ * evaluated in fp32 (dx rounded to bf16, nearest even; dgamma fp32), with a
+ * fixed summation order: identical inputs give identical bits.
+ *   x, dy : bf16 [M][K]; gamma : bf16 [K]; rstd : f32 [M] (from
+ *           rmsnorm_quant_rstd on the same x, gamma, eps).
+ *   dx : bf16 [M][K] output; dgamma : f32 [K] output (zeros when M == 0).
+ *   workspace : f32 scratch of rmsnorm_backward_workspace_bytes(M, K) bytes,
+ *           owned by the caller (its contents on entry are ignored).
+ * K % 128 == 0 and 0 < K <= 6144; M >= 0.
+ */
+int64_t rmsnorm_backward_workspace_bytes(int64_t M, int64_t K); /* -1 for an invalid shape */
+int rmsnorm_backward(const uint16_t* x, const uint16_t* gamma, const float* rstd, const uint16_t* dy,
+                     int64_t M, int64_t K, uint16_t* dx, float* dgamma, float* workspace, void* stream);
+
+/*
  * requant_transpose_128x1 -- requantise a saved 1x128 FP8 tensor into 128x1
  * groups along its rows (the token dimension) and store it transposed
  * ([P3-STEPS] steps 3-4, [P3-NOVEL]).  Used on the saved (QX, SX) and on

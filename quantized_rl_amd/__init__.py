@@ -17,5 +17,8 @@ from ._lib import (  # noqa: F401
     quantize_act_1x128,
     quantize_weight_128x128,
     requant_transpose_128x1,
+    rmsnorm_backward,
+    rmsnorm_backward_workspace_bytes,
     rmsnorm_quant,
+    rmsnorm_quant_rstd,
 )

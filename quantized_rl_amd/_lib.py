@@ -19,6 +19,8 @@ SIGNATURES = {
     "quantize_act_1x128": [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "quantize_weight_128x128": [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "rmsnorm_quant": [_c_p, _c_p, _c_i64, _c_i64, ctypes.c_float, _c_p, _c_p, _c_p],
+    "rmsnorm_quant_rstd": [_c_p, _c_p, _c_i64, _c_i64, ctypes.c_float, _c_p, _c_p, _c_p, _c_p],
+    "rmsnorm_backward": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p],
     "requant_transpose_128x1": [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "gemm_fprop": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
     "gemm_fprop_quant": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p],
@@ -51,6 +53,8 @@ def lib():
             fn = getattr(L, name)
             fn.argtypes = argt
             fn.restype = ctypes.c_int
+        L.rmsnorm_backward_workspace_bytes.argtypes = [_c_i64, _c_i64]
+        L.rmsnorm_backward_workspace_bytes.restype = _c_i64
         L.jetfp8_status_string.argtypes = [ctypes.c_int]
         L.jetfp8_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -130,6 +134,52 @@ def rmsnorm_quant(x, gamma, eps, q=None, s=None):
         x.data_ptr(), gamma.data_ptr(), M, K, float(eps), q.data_ptr(), s.data_ptr(),
         _stream(x.device)))
     return q, s
+
+
+def rmsnorm_quant_rstd(x, gamma, eps, q=None, s=None, rstd=None):
+    """rmsnorm_quant that also returns the per-row factor: (q, s, rstd float32 [M])."""
+    torch = _torch()
+    M, K = x.shape
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(gamma, torch.bfloat16, (K,), "gamma")
+    q = _empty((M, K), torch.uint8, x.device) if q is None else _need(q, torch.uint8, (M, K), "q")
+    s = _empty((K // 128, M), torch.float32, x.device) if s is None else \
+        _need(s, torch.float32, (K // 128, M), "s")
+    rstd = _empty((M,), torch.float32, x.device) if rstd is None else _need(rstd, torch.float32, (M,), "rstd")
+    _check("rmsnorm_quant_rstd", lib().rmsnorm_quant_rstd(
+        x.data_ptr(), gamma.data_ptr(), M, K, float(eps), q.data_ptr(), s.data_ptr(), rstd.data_ptr(),
+        _stream(x.device)))
+    return q, s, rstd
+
+
+def rmsnorm_backward_workspace_bytes(M, K):
+    return int(lib().rmsnorm_backward_workspace_bytes(M, K))
+
+
+def rmsnorm_backward(x, gamma, rstd, dy, dx=None, dgamma=None, workspace=None):
+    """(dx bf16 [M, K], dgamma float32 [K]) of the RMSNorm for upstream dy bf16 [M, K];
+    rstd float32 [M] from rmsnorm_quant_rstd.  The workspace (float32, at least
+    rmsnorm_backward_workspace_bytes(M, K) bytes) is allocated with torch if not given."""
+    torch = _torch()
+    M, K = x.shape
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(gamma, torch.bfloat16, (K,), "gamma")
+    _need(rstd, torch.float32, (M,), "rstd")
+    _need(dy, torch.bfloat16, (M, K), "dy")
+    dx = _empty((M, K), torch.bfloat16, x.device) if dx is None else _need(dx, torch.bfloat16, (M, K), "dx")
+    dgamma = _empty((K,), torch.float32, x.device) if dgamma is None else \
+        _need(dgamma, torch.float32, (K,), "dgamma")
+    nbytes = rmsnorm_backward_workspace_bytes(M, K)
+    if nbytes < 0:
+        raise JetFP8Error("rmsnorm_backward", 1, "invalid shape")
+    if workspace is None:
+        workspace = _empty((max(nbytes // 4, 1),), torch.float32, x.device)
+    elif workspace.dtype != torch.float32 or not workspace.is_contiguous() or workspace.numel() * 4 < nbytes:
+        raise ValueError(f"workspace: expected contiguous float32 of at least {nbytes} bytes")
+    _check("rmsnorm_backward", lib().rmsnorm_backward(
+        x.data_ptr(), gamma.data_ptr(), rstd.data_ptr(), dy.data_ptr(), M, K, dx.data_ptr(),
+        dgamma.data_ptr(), workspace.data_ptr(), _stream(x.device)))
+    return dx, dgamma
 
 
 def requant_transpose_128x1(q, s, qt=None, st=None):

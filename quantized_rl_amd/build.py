@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libjetfp8.so")
-SOURCES = ["api.cpp", "quant_kernels.hip", "gemm_kernels.hip"]
+SOURCES = ["api.cpp", "quant_kernels.hip", "gemm_kernels.hip", "norm_kernels.hip"]
 
 # -ffp-contract=off: every fp32 multiply and add of the quantisers is its own
 #   rounding step (no fused multiply-add), as their definitions state.

@@ -95,7 +95,33 @@ int rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K
   if (!dim_ok(M) || K <= 0 || K > 65536 || K % 128) return JETFP8_EINVAL;
   const int64_t n = M * K;
   if (int st = check_ptrs({{x, 2 * n}, {gamma, 2 * K}}, {{q, n}, {s, 4 * (n / 128)}})) return st;
-  return launched(jetfp8::launch_rmsnorm_quant(x, gamma, M, K, eps, q, s, as_stream(stream)));
+  return launched(jetfp8::launch_rmsnorm_quant(x, gamma, M, K, eps, q, s, nullptr, as_stream(stream)));
+}
+
+int rmsnorm_quant_rstd(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps,
+                       uint8_t* q, float* s, float* rstd, void* stream) {
+  if (!dim_ok(M) || K <= 0 || K > 65536 || K % 128) return JETFP8_EINVAL;
+  const int64_t n = M * K;
+  if (int st = check_ptrs({{x, 2 * n}, {gamma, 2 * K}}, {{q, n}, {s, 4 * (n / 128)}, {rstd, 4 * M}}))
+    return st;
+  return launched(jetfp8::launch_rmsnorm_quant(x, gamma, M, K, eps, q, s, rstd, as_stream(stream)));
+}
+
+int64_t rmsnorm_backward_workspace_bytes(int64_t M, int64_t K) {
+  if (!dim_ok(M) || K <= 0 || K > 6144 || K % 128) return -1;
+  return 4 * jetfp8::rmsnorm_backward_parts(M) * K;
+}
+
+int rmsnorm_backward(const uint16_t* x, const uint16_t* gamma, const float* rstd, const uint16_t* dy,
+                     int64_t M, int64_t K, uint16_t* dx, float* dgamma, float* workspace, void* stream) {
+  const int64_t ws = rmsnorm_backward_workspace_bytes(M, K);
+  if (ws < 0) return JETFP8_EINVAL;
+  const int64_t n = M * K;
+  if (int st = check_ptrs({{x, 2 * n}, {gamma, 2 * K}, {rstd, 4 * M}, {dy, 2 * n}},
+                          {{dx, 2 * n}, {dgamma, 4 * K}, {workspace, ws}}))
+    return st;
+  return launched(jetfp8::launch_rmsnorm_backward(x, gamma, rstd, dy, M, K, dx, dgamma, workspace,
+                                                  as_stream(stream)));
 }
 
 int requant_transpose_128x1(const uint8_t* q, const float* s, int64_t M, int64_t K, uint8_t* qt,

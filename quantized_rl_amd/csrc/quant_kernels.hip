@@ -2,7 +2,8 @@
 //
 //   quantize_act_1x128       1x128 per-group E4M3 quantisation (activations, gradients)
 //   quantize_weight_128x128  128x128 per-block E4M3 quantisation (weights)
-//   rmsnorm_quant            fused RMSNorm + 1x128 quantisation
+//   rmsnorm_quant            fused RMSNorm + 1x128 quantisation (optionally saving the
+//                            per-row factor rstd for the backward)
 //   requant_transpose_128x1  saved 1x128 FP8 -> 128x1 groups along tokens, stored transposed
 //
 // Definitions: Jet-RL pages, paper.rainbus.top summary, sections
@@ -137,7 +138,8 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(const uint16_t*
                                                                  const uint16_t* __restrict__ gamma,
                                                                  int64_t M, int64_t K, float eps,
                                                                  uint8_t* __restrict__ q,
-                                                                 float* __restrict__ s) {
+                                                                 float* __restrict__ s,
+                                                                 float* __restrict__ rstd) {
   const int l = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;  // whole waves only
@@ -170,6 +172,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(const uint16_t*
   }
   const float ms = ps[0] / (float)K;
   const float inv = 1.0f / sqrt_rn(ms + eps);
+  if (rstd != nullptr && l == 0) rstd[row] = inv;
 
   const int lane16 = l & 15, quarter = l >> 4;
 #pragma unroll
@@ -193,9 +196,9 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(const uint16_t*
 
 template <int kP>
 static void launch_rows(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps,
-                        uint8_t* q, float* s, hipStream_t stream) {
+                        uint8_t* q, float* s, float* rstd, hipStream_t stream) {
   hipLaunchKernelGGL(rmsnorm_quant_rows_kernel<kP>, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream,
-                     x, gamma, M, K, eps, q, s);
+                     x, gamma, M, K, eps, q, s, rstd);
 }
 
 // Wider rows: one workgroup (256 threads) per row, two passes over the row.
@@ -203,7 +206,8 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
                                                             const uint16_t* __restrict__ gamma,
                                                             int64_t M, int64_t K, float eps,
                                                             uint8_t* __restrict__ q,
-                                                            float* __restrict__ s) {
+                                                            float* __restrict__ s,
+                                                            float* __restrict__ rstd) {
   __shared__ float part[kNormMaxPasses][4];
   __shared__ float inv_sh;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -236,6 +240,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
     const float ms = ps[0] / (float)K;
     const float d = ms + eps;
     inv_sh = 1.0f / sqrt_rn(d);
+    if (rstd != nullptr) rstd[row] = inv_sh;
   }
   __syncthreads();
   const float inv = inv_sh;
@@ -383,31 +388,31 @@ hipError_t launch_quant_weight(const uint16_t* w, int64_t N, int64_t K, uint8_t*
 }
 
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K,
-                                float eps, uint8_t* q, float* s, hipStream_t stream) {
+                                float eps, uint8_t* q, float* s, float* rstd, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   if (K <= 512 * kRowPasses) {
     switch ((K + 511) / 512) {
-      case 1: launch_rows<1>(x, gamma, M, K, eps, q, s, stream); break;
-      case 2: launch_rows<2>(x, gamma, M, K, eps, q, s, stream); break;
-      case 3: launch_rows<3>(x, gamma, M, K, eps, q, s, stream); break;
-      case 4: launch_rows<4>(x, gamma, M, K, eps, q, s, stream); break;
-      case 5: launch_rows<5>(x, gamma, M, K, eps, q, s, stream); break;
-      case 6: launch_rows<6>(x, gamma, M, K, eps, q, s, stream); break;
-      case 7: launch_rows<7>(x, gamma, M, K, eps, q, s, stream); break;
-      case 8: launch_rows<8>(x, gamma, M, K, eps, q, s, stream); break;
-      case 9: launch_rows<9>(x, gamma, M, K, eps, q, s, stream); break;
-      case 10: launch_rows<10>(x, gamma, M, K, eps, q, s, stream); break;
-      case 11: launch_rows<11>(x, gamma, M, K, eps, q, s, stream); break;
-      case 12: launch_rows<12>(x, gamma, M, K, eps, q, s, stream); break;
-      case 13: launch_rows<13>(x, gamma, M, K, eps, q, s, stream); break;
-      case 14: launch_rows<14>(x, gamma, M, K, eps, q, s, stream); break;
-      case 15: launch_rows<15>(x, gamma, M, K, eps, q, s, stream); break;
-      default: launch_rows<16>(x, gamma, M, K, eps, q, s, stream); break;
+      case 1: launch_rows<1>(x, gamma, M, K, eps, q, s, rstd, stream); break;
+      case 2: launch_rows<2>(x, gamma, M, K, eps, q, s, rstd, stream); break;
+      case 3: launch_rows<3>(x, gamma, M, K, eps, q, s, rstd, stream); break;
+      case 4: launch_rows<4>(x, gamma, M, K, eps, q, s, rstd, stream); break;
+      case 5: launch_rows<5>(x, gamma, M, K, eps, q, s, rstd, stream); break;
+      case 6: launch_rows<6>(x, gamma, M, K, eps, q, s, rstd, stream); break;
+      case 7: launch_rows<7>(x, gamma, M, K, eps, q, s, rstd, stream); break;
+      case 8: launch_rows<8>(x, gamma, M, K, eps, q, s, rstd, stream); break;
+      case 9: launch_rows<9>(x, gamma, M, K, eps, q, s, rstd, stream); break;
+      case 10: launch_rows<10>(x, gamma, M, K, eps, q, s, rstd, stream); break;
+      case 11: launch_rows<11>(x, gamma, M, K, eps, q, s, rstd, stream); break;
+      case 12: launch_rows<12>(x, gamma, M, K, eps, q, s, rstd, stream); break;
+      case 13: launch_rows<13>(x, gamma, M, K, eps, q, s, rstd, stream); break;
+      case 14: launch_rows<14>(x, gamma, M, K, eps, q, s, rstd, stream); break;
+      case 15: launch_rows<15>(x, gamma, M, K, eps, q, s, rstd, stream); break;
+      default: launch_rows<16>(x, gamma, M, K, eps, q, s, rstd, stream); break;
     }
     return hipGetLastError();
   }
   hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3((unsigned)M), dim3(256), 0, stream, x, gamma, M, K,
-                     eps, q, s);
+                     eps, q, s, rstd);
   return hipGetLastError();
 }
 

@@ -97,3 +97,47 @@ class FP8Linear(torch.nn.Module):
         shape = x.shape
         y = fp8_linear(x.reshape(-1, shape[-1]), self.weight, self.main_grad)
         return y.reshape(*shape[:-1], self.weight.shape[0])
+
+
+class RMSNormFP8LinearFunction(torch.autograd.Function):
+    """y = FP8Linear(RMSNorm(x; gamma, eps); w) with the norm fused into the
+    quantisation (rmsnorm_quant_rstd): the normalised activation exists only as
+    its FP8 codes and scales.  Saved for backward: bf16 x and the per-row rstd
+    (for the norm's gradients) and the FP8 operands of the GEMMs."""
+
+    @staticmethod
+    def forward(ctx, x, gamma, w, eps):
+        x = x.contiguous()
+        qx, sx, rstd = _lib.rmsnorm_quant_rstd(x, gamma.contiguous(), eps)
+        qw, sw = _lib.quantize_weight_128x128(w.contiguous())
+        y = _lib.gemm_fprop(qx, sx, qw, sw)
+        ctx.save_for_backward(x, gamma, rstd, qx, sx, qw, sw)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, gamma, rstd, qx, sx, qw, sw = ctx.saved_tensors
+        dxn, dw = fp8_linear_backward(dy, qx, sx, qw, sw)
+        dx, dgamma = _lib.rmsnorm_backward(x, gamma.contiguous(), rstd, dxn)
+        # gamma's gradient is computed in fp32; the parameter's dtype is bf16
+        return dx, dgamma.to(gamma.dtype), dw, None
+
+
+class RMSNormFP8Linear(torch.nn.Module):
+    """RMSNorm (bf16 gamma, initialised to 1) followed by a bias-free FP8 linear
+    layer; forward and backward run through the library's kernels."""
+
+    def __init__(self, in_features, out_features, eps=1e-6, device=None):
+        super().__init__()
+        if in_features % 128 or out_features % 128:
+            raise ValueError("in_features and out_features must be multiples of 128")
+        self.eps = float(eps)
+        self.gamma = torch.nn.Parameter(torch.ones(in_features, dtype=torch.bfloat16, device=device))
+        self.weight = torch.nn.Parameter(
+            torch.empty(out_features, in_features, dtype=torch.bfloat16, device=device))
+        torch.nn.init.normal_(self.weight, std=0.02)
+
+    def forward(self, x):
+        shape = x.shape
+        y = RMSNormFP8LinearFunction.apply(x.reshape(-1, shape[-1]), self.gamma, self.weight, self.eps)
+        return y.reshape(*shape[:-1], self.weight.shape[0])

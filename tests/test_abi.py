@@ -21,13 +21,14 @@ P = [A * (i + 1) for i in range(10)]
 
 def declared_functions():
     text = open(HEADER).read()
-    return re.findall(r"^(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+    return re.findall(r"^(?:int|int64_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
 
 
 def test_header_declares_the_seven_entry_points():
     names = declared_functions()
     for n in ["quantize_act_1x128", "quantize_weight_128x128", "rmsnorm_quant",
               "requant_transpose_128x1", "gemm_fprop", "gemm_dgrad", "gemm_wgrad", "gemm_wgrad_f32",
+              "rmsnorm_quant_rstd", "rmsnorm_backward", "rmsnorm_backward_workspace_bytes",
               "jetfp8_status_string"]:
         assert n in names
 
@@ -132,3 +133,23 @@ def test_gemm_wgrad_f32_validation(jetlib):
     # 4-byte output elements: dW [2^17, 4096] fp32 is 2 GiB (its bf16 form would fit)
     Q = [(i + 1) << 40 for i in range(8)]
     assert c(f, Q[0], Q[1], Q[2], Q[3], 128, 1 << 17, 4096, Q[4], 0, 0) == 5
+
+
+def test_rmsnorm_rstd_and_backward_validation(jetlib):
+    f = "rmsnorm_quant_rstd"
+    assert c(f, P[0], P[1], 4, 100, 1e-6, P[2], P[3], P[4], 0) == EINVAL
+    assert c(f, P[0], P[1], 4, 128, 1e-6, P[2], P[3], 0, 0) == ENULL          # rstd missing
+    assert c(f, P[0], P[1], 16, 128, 1e-6, P[2], P[3], P[3] + 16, 0) == EALIAS  # rstd overlaps s
+    assert c(f, 0, P[1], 0, 128, 1e-6, 0, 0, 0, 0) == OK
+    ws = _lib.rmsnorm_backward_workspace_bytes
+    # one row of K floats per workgroup of 4 R rows, R = ceil(M / 1024) in 1..8
+    assert ws(8192, 4096) == 4 * 256 * 4096 and ws(1, 128) == 4 * 128 and ws(0, 128) == 0
+    assert ws(256, 4096) == 4 * 64 * 4096 and ws(2000, 128) == 4 * 250 * 128 and ws(65536, 128) == 4 * 2048 * 128
+    assert ws(4, 100) == -1 and ws(4, 6144 + 128) == -1 and ws(-1, 128) == -1
+    b = "rmsnorm_backward"
+    # (x, gamma, rstd, dy, M, K, dx, dgamma, workspace)
+    assert c(b, P[0], P[1], P[2], P[3], 4, 6272, P[4], P[5], P[6], 0) == EINVAL  # K > 6144
+    assert c(b, P[0], P[1], P[2], P[3], 4, 128, P[4], P[5], 0, 0) == ENULL      # workspace missing
+    assert c(b, P[0], P[1], P[2], P[3], 4, 128, P[4], P[5], P[4] + 512, 0) == EALIAS  # workspace over dx
+    assert c(b, P[0], P[1], P[2], P[3], 4, 128, P[3], P[5], P[6], 0) == EALIAS  # dx over dy
+    assert c(b, P[0], P[1], P[2], P[3], 4, 128, P[4], P[5] + 4, P[6], 0) == EALIGN

@@ -25,3 +25,11 @@ def test_fp8_linear_module_rejects_unaligned_features():
         linear.FP8Linear(100, 128, device="cpu")
     with pytest.raises(ValueError):
         linear.FP8Linear(128, 200, device="cpu")
+
+
+def test_rmsnorm_fp8_linear_module_parameters():
+    blk = linear.RMSNormFP8Linear(256, 128, eps=1e-5, device="cpu")
+    assert blk.gamma.dtype == torch.bfloat16 and bool((blk.gamma == 1).all())
+    assert tuple(blk.weight.shape) == (128, 256) and blk.eps == 1e-5
+    with pytest.raises(ValueError):
+        linear.RMSNormFP8Linear(200, 128, device="cpu")

@@ -30,6 +30,8 @@
 // operands or output, with one tile of ragged rows, reach 2^31 bytes.
 // All but the last fold the K-blocks of an output in ascending order with the
 // same fp32 operations, so a row's FProp output does not depend on the kernel.
+#include <atomic>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -154,6 +156,30 @@ struct LargeTile {
                            (uint32_t)(32 * lk + (lr >> 1)) * 128u + 8u * (uint32_t)(lr & 1);
 #pragma unroll
     for (int v = 0; v < 4; ++v) dv[v] = dbase + (((uint32_t)v ^ x) << 4);
+  }
+
+  // Tile id -> output tile origin (tile-row groups of kGroupM rows walked
+  // column by column) and the per-tile load offsets.
+  __device__ __forceinline__ void set_tile(uint32_t id, uint32_t ntm, uint32_t ntn) {
+    const uint32_t per_group = kGroupM * ntn;
+    const uint32_t g0 = (id / per_group) * kGroupM;
+    const uint32_t gm = (ntm - g0) < (uint32_t)kGroupM ? (ntm - g0) : (uint32_t)kGroupM;
+    row0 = (g0 + (id % per_group) % gm) * kLBM;
+    col0 = ((id % per_group) / gm) * kLBN;
+    arow = (row0 + t8) < M ? (row0 + t8) : (M - 1);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = 32 * w + 8 * p + (l >> 3);
+      va[p] = (row0 + r) * K + (((l & 7) ^ lf(r)) << 4);
+      if (kMode == kDgrad) {
+        // B tile = W[kb*128 + rr][col0 + 128 h + ...]: two 128-column halves of
+        // 128 contraction rows; this wave fills half h = w / 4, rows 32 (w % 4) ..
+        const int rr = 32 * (w & 3) + 8 * p + (l >> 3);
+        vb[p] = rr * N + col0 + 128 * (w >> 2) + (((l & 7) ^ lf(rr)) << 4);
+      } else {
+        vb[p] = (col0 + r) * K + (((l & 7) ^ lf(r)) << 4);
+      }
+    }
   }
 
   // Direct loads of K-block kb into stage st: wave w fills 32 rows of each
@@ -363,42 +389,32 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
   g.M = M; g.N = N; g.K = K;
   g.sa = sa; g.sb = sb;
   g.setup_offsets();
-
-  // launch order: spread over the 8 XCDs so that each XCD gets one contiguous
-  // range of tiles, then walk tile-row groups of kGroupM rows column by column
-  const uint32_t ntm = (M + kLBM - 1) / kLBM, ntn = N / kLBN, total = ntm * ntn;
-  uint32_t id = blockIdx.x;
-  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
-  const uint32_t per_group = kGroupM * ntn;
-  const uint32_t g0 = (id / per_group) * kGroupM;
-  const uint32_t gm = (ntm - g0) < (uint32_t)kGroupM ? (ntm - g0) : (uint32_t)kGroupM;
-  g.row0 = (g0 + (id % per_group) % gm) * kLBM;
-  g.col0 = ((id % per_group) / gm) * kLBN;
   g.nkb = K / kBK;
   g.t8 = (uint32_t)g.t & 255u;
-  g.arow = (g.row0 + g.t8) < M ? (g.row0 + g.t8) : (M - 1);
   g.b_half = (kMode == kWgrad) && g.t >= kLBM;
   g.ra = make_rsrc(A, M * K);
   g.rb = make_rsrc(B, N * K);
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int r = 32 * g.w + 8 * p + (g.l >> 3);
-    g.va[p] = (g.row0 + r) * K + (((g.l & 7) ^ lf(r)) << 4);
-    if (kMode == kDgrad) {
-      // B tile = W[kb*128 + rr][col0 + 128 h + ...]: two 128-column halves of
-      // 128 contraction rows; this wave fills half h = w / 4, rows 32 (w % 4) ..
-      const int rr = 32 * (g.w & 3) + 8 * p + (g.l >> 3);
-      g.vb[p] = rr * N + g.col0 + 128 * (g.w >> 2) + (((g.l & 7) ^ lf(rr)) << 4);
-    } else {
-      g.vb[p] = (g.col0 + r) * K + (((g.l & 7) ^ lf(r)) << 4);
-    }
-  }
 
-  v4f_t acc[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // Tiles of this workgroup.  The grid is a multiple of 8 workgroups, dealt to
+  // the 8 XCDs round-robin; each XCD works through one contiguous range of
+  // tile ids (its share of the operands stays in its L2), its workgroups
+  // taking ids local, local + (workgroups per XCD), ...  With as many
+  // workgroups as tiles each takes one; with fewer (one per CU) each loops
+  // over several, and the last K-block of a tile already loads the first
+  // block of the next one (FProp and DGrad with an even block count; see the
+  // launcher).  WGrad keeps one tile per workgroup: the loop's extra live
+  // registers made it spill (measured 4-6 % slower), while FProp gained 2-4 %.
+  constexpr bool kPersist = kMode != kWgrad;
+  const uint32_t ntm = (M + kLBM - 1) / kLBM, ntn = N / kLBN, total = ntm * ntn;
+  const bool xcd_split = (total & 7) == 0;
+  const uint32_t per_xcd = total >> 3, wg_per_xcd = gridDim.x >> 3;
+  const uint32_t xcd = blockIdx.x & 7;
+  uint32_t local = xcd_split ? (blockIdx.x >> 3) : blockIdx.x;
+  const uint32_t stride = xcd_split ? wg_per_xcd : gridDim.x;
+  const uint32_t range = xcd_split ? per_xcd : total;
+  auto tile_id = [&](uint32_t loc) { return xcd_split ? xcd * per_xcd + loc : loc; };
+  if (local >= range) return;  // (the launcher never makes such workgroups)
+  g.set_tile(tile_id(local), ntm, ntn);
 
   g.store_scale(st0, g.load_scale(0));
   g.issue(0, st0);
@@ -407,74 +423,98 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
   typename LargeTile<kMode>::Head head;
   g.read_head(st0, head);
 
-  // Two K-blocks per trip: compute stage 0 while stage 1 loads, then the
-  // reverse.  The prefetch past the last block reloads the last block (the
-  // loop stays free of branches; nkb >= 1).
   const uint32_t last = g.nkb - 1;
 #pragma clang loop unroll(disable)
-  for (uint32_t kb = 0; kb < g.nkb; kb += 2) {
-    {
-      const uint32_t kn = kb + 1 <= last ? kb + 1 : last;
-      g.compute(st0, acc, kn, st1, g.load_scale(kn), head);
-    }
-    if (kb + 1 <= last) {
-      const uint32_t kn = kb + 2 <= last ? kb + 2 : last;
-      g.compute(st1, acc, kn, st0, g.load_scale(kn), head);
-    }
-  }
-  // every wave is done with the operand stages (the epilogue reuses them)
-  __syncthreads();
-
-  if constexpr (kOut != kOutBf16) {
-    const rsrc_t rc = make_rsrc(Cv, M * N * 4u);
+  for (;;) {
+    const uint32_t row0 = g.row0, col0 = g.col0;
+    const bool has_next = kPersist && (g.nkb & 1) == 0 && local + stride < range;
+    v4f_t acc[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t r = g.row0 + g.wm * 128 + 16 * i + g.lr, c = g.col0 + g.wn * 64 + 16 * j + 4 * g.lk;
-        store_f32<kOut>(rc, (r * N + c) * 4u, acc[i][j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Two K-blocks per trip: compute stage 0 while stage 1 loads, then the
+    // reverse.  After the tile's last block the prefetch moves on to the next
+    // tile's first block, or, for the last tile, reloads the last block (the
+    // loop stays free of branches on the data path; nkb >= 1).
+#pragma clang loop unroll(disable)
+    for (uint32_t kb = 0; kb < g.nkb; kb += 2) {
+      {
+        const uint32_t kn = kb + 1 <= last ? kb + 1 : last;
+        g.compute(st0, acc, kn, st1, g.load_scale(kn), head);
       }
-    return;
-  }
-  uint16_t* C = static_cast<uint16_t*>(Cv);
-  // epilogue: stage the bf16 tile in LDS with a row pitch of 512 + 16 bytes
-  // (rows 0..127 fill stage 0, rows 128..255 stage 1: 128 * 528 bytes is
-  // exactly one stage object), then write it out with 16-byte buffer stores
-  // (rows past M fall outside the buffer and are dropped)
-  constexpr int kPitch = kLBN * 2 + 16;
-  static_assert(128 * kPitch == sizeof(LStage), "epilogue staging must fill one stage exactly");
-  const rsrc_t rc = make_rsrc(C, M * N * 2u);
-  auto crow = [&](int r) -> uint8_t* {
-    return (r < 128 ? reinterpret_cast<uint8_t*>(&st0) : reinterpret_cast<uint8_t*>(&st1)) + (r & 127) * kPitch;
-  };
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = g.wm * 128 + 16 * i + g.lr, c = g.wn * 64 + 16 * j + 4 * g.lk;
-      // the hardware conversion saves about 3 VALU per element (FProp 1-2 %
-      // faster); DGrad keeps the integer rounding, with which its register
-      // allocation stays spill-free
-      uint32_t lo, hi;
-      if (kMode != kDgrad) {
-        lo = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-        hi = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-      } else {
-        lo = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
-        hi = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
+      if (kb + 1 <= last) {
+        uint32_t kn = kb + 2;
+        if (kn > last) {
+          kn = last;
+          if (has_next) {
+            local += stride;
+            g.set_tile(tile_id(local), ntm, ntn);
+            kn = 0;
+          }
+        }
+        g.compute(st1, acc, kn, st0, g.load_scale(kn), head);
       }
-      *reinterpret_cast<uint2*>(crow(r) + 2 * c) = make_uint2(lo, hi);
     }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  __syncthreads();
+
+    if constexpr (kOut != kOutBf16) {
+      const rsrc_t rc = make_rsrc(Cv, M * N * 4u);
 #pragma unroll
-  for (int p = 0; p < 16; ++p) {
-    const int id16 = g.t + kLThreads * p;  // 16-byte chunk id: 32 per row
-    const int r = id16 >> 5, c16 = id16 & 31;
-    const uint4 v = *reinterpret_cast<const uint4*>(crow(r) + 16 * c16);
-    const v4i_t d = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-    __builtin_amdgcn_raw_buffer_store_b128(d, rc, ((g.row0 + r) * N + g.col0 + 8 * c16) * 2u, 0, 0);
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t r = row0 + g.wm * 128 + 16 * i + g.lr, c = col0 + g.wn * 64 + 16 * j + 4 * g.lk;
+          store_f32<kOut>(rc, (r * N + c) * 4u, acc[i][j]);
+        }
+    } else {
+      // bf16 epilogue, staged through stage 1 (free once the last block's
+      // barrier has passed; stage 0 may already hold the next tile's first
+      // block) in two halves of 128 rows with a row pitch of 512 + 16 bytes,
+      // then written with 16-byte buffer stores (rows past M fall outside the
+      // buffer and are dropped)
+      constexpr int kPitch = kLBN * 2 + 16;
+      static_assert(128 * kPitch == sizeof(LStage), "epilogue staging must fill one stage exactly");
+      uint16_t* C = static_cast<uint16_t*>(Cv);
+      const rsrc_t rc = make_rsrc(C, M * N * 2u);
+      uint8_t* stage = reinterpret_cast<uint8_t*>(&st1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (g.wm == h) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int r = 16 * i + g.lr, c = g.wn * 64 + 16 * j + 4 * g.lk;
+              // the hardware conversion saves about 3 VALU per element (FProp
+              // 1-2 % faster); DGrad keeps the integer rounding, with which
+              // its register allocation stays spill-free
+              uint32_t lo, hi;
+              if (kMode != kDgrad) {
+                lo = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+                hi = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+              } else {
+                lo = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
+                hi = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
+              }
+              *reinterpret_cast<uint2*>(stage + r * kPitch + 2 * c) = make_uint2(lo, hi);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const int id16 = g.t + kLThreads * p;  // 16-byte chunk id: 32 per row
+          const int r = id16 >> 5, c16 = id16 & 31;
+          const uint4 v = *reinterpret_cast<const uint4*>(stage + r * kPitch + 16 * c16);
+          const v4i_t d = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+          __builtin_amdgcn_raw_buffer_store_b128(d, rc, ((row0 + 128 * h + r) * N + col0 + 8 * c16) * 2u, 0, 0);
+        }
+        __syncthreads();
+      }
+    }
+    if (!has_next) break;
   }
 }
 
@@ -1071,6 +1111,19 @@ __global__ void fill_zero_u16(uint16_t* __restrict__ p, int64_t n) {
     p[i] = 0;
 }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+static int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 static hipError_t launch_zero(uint16_t* p, int64_t n, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   int64_t blocks = (n + 255) / 256;
@@ -1171,8 +1224,16 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
                       (Mr + kLBM) * Nc * (kOut == kOutBf16 ? 2 : 4) < (int64_t(1) << 31);
   const int64_t large_tiles = ((Mr + kLBM - 1) / kLBM) * (Nc / kLBN);
   if (Nc % kLBN == 0 && fits32 && large_tiles >= 256) {
-    hipLaunchKernelGGL((gemm_fp8_large_kernel<kMode, kOut>), dim3((unsigned)large_tiles), dim3(kLThreads), 0,
-                       stream, A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, Cv);
+    // FProp and DGrad: one workgroup per CU looping over tiles when the block
+    // count is even (the next tile's first block then lands in stage 0, where
+    // a tile starts); otherwise one workgroup per tile.
+    int64_t grid = large_tiles;
+    if (kMode != kWgrad && nkb % 2 == 0) {
+      const int64_t cus = cu_count() & ~7;
+      if (cus >= 8 && cus < grid) grid = cus;
+    }
+    hipLaunchKernelGGL((gemm_fp8_large_kernel<kMode, kOut>), dim3((unsigned)grid), dim3(kLThreads), 0, stream,
+                       A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, Cv);
     return hipGetLastError();
   }
   // the medium-tile kernel (the caller guarantees 32-bit byte offsets)

@@ -434,3 +434,31 @@ def test_dgrad_wgrad_large_kernel_ragged_rows():
     torch.cuda.synchronize()
     assert dwg.intact()
     check(host(dwg.t), oracle.gemm_wgrad_ref(qdyt, sdyt, qxt, sxt), f"wgrad {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(8348, 2304, 512), (8192, 2304, 768)])
+def test_fprop_large_kernel_several_tiles_per_workgroup(m, n, k):
+    """More 256 x 256 tiles than CUs: the workgroups loop over tiles, each tile's
+    last K-block prefetching the next tile's first.  8348 x 2304 has 33 x 9 = 297
+    tiles (not a multiple of 8: plain striding, ragged last row tile); 8192 x 2304
+    has 288 (the per-XCD split, four workgroups per XCD taking two tiles).  Rows
+    must equal, bit for bit, the same rows computed in small batches by the other
+    kernels, and sampled outputs must match the oracle."""
+    print(f"[fprop tiles] m={m} n={n} k={k}", flush=True)
+    rng = np.random.default_rng(m + n + k)
+    qx, qw = codes(rng, (m, k)), codes(rng, (n, k))
+    sx, sw = scales(rng, (k // 128, m)), scales(rng, (n // 128, k // 128))
+    qw_d, sw_d = u8_dev(qw), f32_dev(sw)
+    yg = Guarded((m, n), torch.bfloat16)
+    jet.gemm_fprop(u8_dev(qx), f32_dev(sx), qw_d, sw_d, yg.t)
+    torch.cuda.synchronize()
+    assert yg.intact()
+    y = host(yg.t)
+    for m0, mm in [(0, 64), (4000, 300), (m - 200, 200), (m - 37, 37)]:
+        ys = host(jet.gemm_fprop(u8_dev(qx[m0:m0 + mm]), f32_dev(np.ascontiguousarray(sx[:, m0:m0 + mm])),
+                                 qw_d, sw_d))
+        assert np.array_equal(ys, y[m0:m0 + mm]), f"rows {m0}..{m0 + mm}"
+    rows = np.sort(rng.choice(m, 64, replace=False))
+    cols = np.sort(rng.choice(n, 64, replace=False))
+    ref = oracle.gemm_fprop_ref_at(qx, sx, qw, sw, rows, cols)
+    check(y[np.ix_(rows, cols)], ref, f"fprop {m}x{n}x{k}", rms=float(np.sqrt(np.mean(ref ** 2))))

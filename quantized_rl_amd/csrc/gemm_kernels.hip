@@ -24,12 +24,15 @@
 //   gemm_fp8_decode_kernel       FProp with M <= 64 (weight streaming);
 //   gemm_fp8_mid_kernel          FProp with 65 .. 256 rows, long K and few
 //                                column tiles (K split over 8 waves);
-//   gemm_fp8_large_kernel<mode>  256 x 256 tiles: problems with >= 256 of them;
+//   gemm_fp8_large_kernel<mode>  256 x 256 tiles: problems with >= 256 of them
+//                                (FProp and DGrad: one workgroup per CU looping
+//                                over the tiles);
 //   gemm_fp8_med_kernel<mode>    128 x 128 tiles, same machinery: everything else.
 // Byte offsets are 32-bit (buffer resources): the API rejects GEMMs whose
 // operands or output, with one tile of ragged rows, reach 2^31 bytes.
-// All but the last fold the K-blocks of an output in ascending order with the
-// same fp32 operations, so a row's FProp output does not depend on the kernel.
+// All but the K-split kernel fold the K-blocks of an output in ascending order
+// with the same fp32 operations, so a row's FProp output does not depend on the
+// kernel (nor on the batch it is computed in).
 #include <atomic>
 
 #include "device_common.hpp"

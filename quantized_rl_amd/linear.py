@@ -141,3 +141,22 @@ class RMSNormFP8Linear(torch.nn.Module):
         shape = x.shape
         y = RMSNormFP8LinearFunction.apply(x.reshape(-1, shape[-1]), self.gamma, self.weight, self.eps)
         return y.reshape(*shape[:-1], self.weight.shape[0])
+
+
+class FP8Stack(torch.nn.Module):
+    """A stack of RMSNormFP8Linear layers (for example the four projections of a
+    transformer layer's MLP path at the 8B shapes), every GEMM, quantisation and
+    normalisation in FP8 through the library.  No activation function between
+    the layers: the pages do not define one for this path."""
+
+    def __init__(self, dims, eps=1e-6, device=None):
+        super().__init__()
+        if len(dims) < 2:
+            raise ValueError("dims needs at least an input and an output size")
+        self.layers = torch.nn.ModuleList(
+            RMSNormFP8Linear(dims[i], dims[i + 1], eps=eps, device=device) for i in range(len(dims) - 1))
+
+    def forward(self, x):
+        for layer in self.layers:
+            x = layer(x)
+        return x

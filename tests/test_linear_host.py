@@ -33,3 +33,11 @@ def test_rmsnorm_fp8_linear_module_parameters():
     assert tuple(blk.weight.shape) == (128, 256) and blk.eps == 1e-5
     with pytest.raises(ValueError):
         linear.RMSNormFP8Linear(200, 128, device="cpu")
+
+
+def test_fp8_stack_shapes():
+    st = linear.FP8Stack([512, 1024, 512, 768, 384], device="cpu")
+    assert len(st.layers) == 4
+    assert [tuple(l.weight.shape) for l in st.layers] == [(1024, 512), (512, 1024), (768, 512), (384, 768)]
+    with pytest.raises(ValueError):
+        linear.FP8Stack([512], device="cpu")

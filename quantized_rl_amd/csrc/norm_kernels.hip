@@ -12,14 +12,15 @@
 // the formulas are calculus on the standard RMSNorm.
 //
 // Both are HBM-bound: x and dy are read once, dx written once.
-//   rmsnorm_backward_rows_kernel: a workgroup of 4 waves owns 4 R consecutive
-//     rows, R per wave, one row at a time; R = ceil(M / 1024) clamped to
-//     1..8, so that small batches still spread over many workgroups.  Lane l
-//     covers the 8 elements at 512 p + 8 l of pass p (all loads of a row
-//     issued up front).  S is the lane's sequential sum followed by the wave
-//     butterfly.  Each wave keeps its rows' dgamma terms in registers (summed
-//     in row order); the four waves then add theirs in wave order through LDS
-//     and the workgroup writes its partial row of dgamma to the workspace.
+//   rmsnorm_backward_rows_kernel: a workgroup of 4 waves owns R consecutive
+//     rows (R = 2 ceil(M / 512) clamped to 1..32) and walks them one at a time,
+//     all four waves on the same row: wave w covers the 512-element passes
+//     w, w + 4, ... (lane l: the 8 elements at 512 p + 8 l), so a lane holds
+//     only K / 256 of the row and the next row's loads are issued before the
+//     current row is finished.  S is each wave's lane-sequential sum and
+//     butterfly, the four wave sums added in wave order through LDS.  A wave
+//     keeps its columns' dgamma terms in registers, summed in row order, and
+//     writes them as its part of the workgroup's partial row of dgamma.
 //   rmsnorm_dgamma_reduce_kernel: dgamma_k = the partials summed in a fixed
 //     order (four quarters in sequence, then ((q0 + q1) + q2) + q3).
 // Identical inputs give identical bits; no atomics.
@@ -28,15 +29,17 @@
 
 namespace jetfp8 {
 
-constexpr int kBwdMaxPasses = 12;  // K <= 6144
+constexpr int kBwdMaxPasses = 12;  // K <= 6144: at most 3 passes per wave
 
-static int64_t bwd_rows_per_wave(int64_t M) {
-  const int64_t r = (M + 1023) / 1024;
-  return r < 1 ? 1 : (r > 8 ? 8 : r);
+// Rows per workgroup: 2 ceil(M / 512) clamped to 1..32 (measured best of
+// 1..8, 1..16 and 1..32 at M = 256 .. 16384).
+static int64_t bwd_rows_per_group(int64_t M) {
+  const int64_t r = 2 * ((M + 511) / 512);
+  return r < 1 ? 1 : (r > 32 ? 32 : r);
 }
 
 int64_t rmsnorm_backward_parts(int64_t M) {
-  const int64_t rows = 4 * bwd_rows_per_wave(M);
+  const int64_t rows = bwd_rows_per_group(M);
   return (M + rows - 1) / rows;
 }
 
@@ -47,82 +50,83 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&f)[8]) {
                     f32_to_bf16_rne(f[6]) | (f32_to_bf16_rne(f[7]) << 16));
 }
 
-template <int kP>
+// kQ: passes per wave (ceil(ceil(K / 512) / 4)).
+template <int kQ>
 __global__ __launch_bounds__(256) void rmsnorm_backward_rows_kernel(const uint16_t* __restrict__ x,
                                                                     const uint16_t* __restrict__ gamma,
                                                                     const float* __restrict__ rstd,
                                                                     const uint16_t* __restrict__ dy,
-                                                                    int64_t M, int64_t K, int rows_per_wave,
+                                                                    int64_t M, int64_t K, int rows_per_group,
                                                                     uint16_t* __restrict__ dx,
                                                                     float* __restrict__ part) {
-  __shared__ float red[512 * kP];
+  __shared__ float wsum[2][4];
   const int t = threadIdx.x, l = t & 63, w = t >> 6;
-  const int64_t row0 = ((int64_t)blockIdx.x * 4 + w) * rows_per_wave;
+  const int64_t row0 = (int64_t)blockIdx.x * rows_per_group;
+  const int64_t rows = (M - row0) < rows_per_group ? (M - row0) : rows_per_group;
 
-  float u[kP][8];
+  // this lane's element offsets and whether they exist
+  int64_t e[kQ];
+  bool in[kQ];
 #pragma unroll
-  for (int p = 0; p < kP; ++p)
+  for (int q = 0; q < kQ; ++q) {
+    e[q] = 512 * (int64_t)(w + 4 * q) + 8 * l;
+    in[q] = e[q] < K;
+  }
+  float fg[kQ][8], u[kQ][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) u[p][i] = 0.0f;
-
-  for (int r = 0; r < rows_per_wave; ++r) {
-    const int64_t row = row0 + r;
-    if (row >= M) break;  // uniform over the wave; no barrier inside the loop
-    const float rr = rstd[row];
-    uint4 xv[kP], dv[kP];
+  for (int q = 0; q < kQ; ++q) {
+    unpack_bf16x8(in[q] ? *reinterpret_cast<const uint4*>(gamma + e[q]) : make_uint4(0, 0, 0, 0), fg[q]);
 #pragma unroll
-    for (int p = 0; p < kP; ++p) {
-      const int64_t e = 512 * p + 8 * l;
-      const bool in = p < kP - 1 || e < K;
-      xv[p] = in ? ld_stream16(x + row * K + e) : make_uint4(0, 0, 0, 0);
-      dv[p] = in ? ld_stream16(dy + row * K + e) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 8; ++i) u[q][i] = 0.0f;
+  }
+  auto load_row = [&](int64_t row, uint4 (&xv)[kQ], uint4 (&dv)[kQ]) {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      xv[q] = in[q] ? ld_stream16(x + row * K + e[q]) : make_uint4(0, 0, 0, 0);
+      dv[q] = in[q] ? ld_stream16(dy + row * K + e[q]) : make_uint4(0, 0, 0, 0);
     }
+  };
+  uint4 xv[kQ], dv[kQ];
+  load_row(row0, xv, dv);
+  for (int64_t r = 0; r < rows; ++r) {
+    const int64_t row = row0 + r;
+    const float rr = rstd[row];
+    float fx[kQ][8], fd[kQ][8];
     float sl = 0.0f;
 #pragma unroll
-    for (int p = 0; p < kP; ++p) {
-      const int64_t e = 512 * p + 8 * l;
-      const bool in = p < kP - 1 || e < K;
-      float fx[8], fd[8], fg[8];
-      unpack_bf16x8(xv[p], fx);
-      unpack_bf16x8(dv[p], fd);
-      unpack_bf16x8(in ? *reinterpret_cast<const uint4*>(gamma + e) : make_uint4(0, 0, 0, 0), fg);
+    for (int q = 0; q < kQ; ++q) {
+      unpack_bf16x8(xv[q], fx[q]);
+      unpack_bf16x8(dv[q], fd[q]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sl = sl + (fg[i] * fd[i]) * fx[i];
+      for (int i = 0; i < 8; ++i) sl = sl + (fg[q][i] * fd[q][i]) * fx[q][i];
     }
-    const float c = wave_sum_tree(sl) / (float)K;
+    // the next row's loads go out before this row's reduction and stores
+    if (r + 1 < rows) load_row(row + 1, xv, dv);
+    const float ws = wave_sum_tree(sl);
+    if (l == 0) wsum[r & 1][w] = ws;
+    __syncthreads();
+    const float c = (((wsum[r & 1][0] + wsum[r & 1][1]) + wsum[r & 1][2]) + wsum[r & 1][3]) / (float)K;
     const float rc = (rr * rr) * c;
 #pragma unroll
-    for (int p = 0; p < kP; ++p) {
-      const int64_t e = 512 * p + 8 * l;
-      const bool in = p < kP - 1 || e < K;
-      float fx[8], fd[8], fg[8], o[8];
-      unpack_bf16x8(xv[p], fx);
-      unpack_bf16x8(dv[p], fd);
-      unpack_bf16x8(in ? *reinterpret_cast<const uint4*>(gamma + e) : make_uint4(0, 0, 0, 0), fg);
+    for (int q = 0; q < kQ; ++q) {
+      float o[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        o[i] = rr * ((fg[i] * fd[i]) - fx[i] * rc);
-        u[p][i] = u[p][i] + (fd[i] * fx[i]) * rr;
+        o[i] = rr * ((fg[q][i] * fd[q][i]) - fx[q][i] * rc);
+        u[q][i] = u[q][i] + (fd[q][i] * fx[q][i]) * rr;
       }
-      if (in) *reinterpret_cast<uint4*>(dx + row * K + e) = pack_bf16x8(o);
+      if (in[q]) *reinterpret_cast<uint4*>(dx + row * K + e[q]) = pack_bf16x8(o);
     }
   }
-
-  // the four waves' dgamma terms, added in wave order
-  for (int ww = 0; ww < 4; ++ww) {
-    if (w == ww) {
+  // this wave's columns of the workgroup's partial row of dgamma
 #pragma unroll
-      for (int p = 0; p < kP; ++p) {
-        const int64_t e = 512 * p + 8 * l;
-        if (p < kP - 1 || e < K) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) red[e + i] = ww == 0 ? u[p][i] : red[e + i] + u[p][i];
-        }
-      }
+  for (int q = 0; q < kQ; ++q) {
+    if (in[q]) {
+      float* pp = part + (int64_t)blockIdx.x * K + e[q];
+      *reinterpret_cast<float4*>(pp) = make_float4(u[q][0], u[q][1], u[q][2], u[q][3]);
+      *reinterpret_cast<float4*>(pp + 4) = make_float4(u[q][4], u[q][5], u[q][6], u[q][7]);
     }
-    __syncthreads();
   }
-  for (int64_t k = t; k < K; k += 256) part[(int64_t)blockIdx.x * K + k] = red[k];
 }
 
 __global__ __launch_bounds__(256) void rmsnorm_dgamma_reduce_kernel(const float* __restrict__ part,
@@ -144,11 +148,11 @@ __global__ __launch_bounds__(256) void rmsnorm_dgamma_reduce_kernel(const float*
   if (w == 0 && k < K) dgamma[k] = ((q[0][c] + q[1][c]) + q[2][c]) + q[3][c];
 }
 
-template <int kP>
+template <int kQ>
 static void launch_bwd_rows(const uint16_t* x, const uint16_t* gamma, const float* rstd, const uint16_t* dy,
                             int64_t M, int64_t K, uint16_t* dx, float* part, hipStream_t stream) {
-  hipLaunchKernelGGL(rmsnorm_backward_rows_kernel<kP>, dim3((unsigned)rmsnorm_backward_parts(M)), dim3(256), 0,
-                     stream, x, gamma, rstd, dy, M, K, (int)bwd_rows_per_wave(M), dx, part);
+  hipLaunchKernelGGL(rmsnorm_backward_rows_kernel<kQ>, dim3((unsigned)rmsnorm_backward_parts(M)), dim3(256), 0,
+                     stream, x, gamma, rstd, dy, M, K, (int)bwd_rows_per_group(M), dx, part);
 }
 
 hipError_t launch_rmsnorm_backward(const uint16_t* x, const uint16_t* gamma, const float* rstd,
@@ -157,19 +161,11 @@ hipError_t launch_rmsnorm_backward(const uint16_t* x, const uint16_t* gamma, con
   if (K == 0) return hipSuccess;
   const int64_t nparts = rmsnorm_backward_parts(M);
   if (M > 0) {
-    switch ((K + 511) / 512) {
+    const int64_t passes = (K + 511) / 512;
+    switch ((passes + 3) / 4) {
       case 1: launch_bwd_rows<1>(x, gamma, rstd, dy, M, K, dx, workspace, stream); break;
       case 2: launch_bwd_rows<2>(x, gamma, rstd, dy, M, K, dx, workspace, stream); break;
-      case 3: launch_bwd_rows<3>(x, gamma, rstd, dy, M, K, dx, workspace, stream); break;
-      case 4: launch_bwd_rows<4>(x, gamma, rstd, dy, M, K, dx, workspace, stream); break;
-      case 5: launch_bwd_rows<5>(x, gamma, rstd, dy, M, K, dx, workspace, stream); break;
-      case 6: launch_bwd_rows<6>(x, gamma, rstd, dy, M, K, dx, workspace, stream); break;
-      case 7: launch_bwd_rows<7>(x, gamma, rstd, dy, M, K, dx, workspace, stream); break;
-      case 8: launch_bwd_rows<8>(x, gamma, rstd, dy, M, K, dx, workspace, stream); break;
-      case 9: launch_bwd_rows<9>(x, gamma, rstd, dy, M, K, dx, workspace, stream); break;
-      case 10: launch_bwd_rows<10>(x, gamma, rstd, dy, M, K, dx, workspace, stream); break;
-      case 11: launch_bwd_rows<11>(x, gamma, rstd, dy, M, K, dx, workspace, stream); break;
-      default: launch_bwd_rows<kBwdMaxPasses>(x, gamma, rstd, dy, M, K, dx, workspace, stream); break;
+      default: launch_bwd_rows<3>(x, gamma, rstd, dy, M, K, dx, workspace, stream); break;
     }
   }
   hipLaunchKernelGGL(rmsnorm_dgamma_reduce_kernel, dim3((unsigned)((K + 63) / 64)), dim3(256), 0, stream,

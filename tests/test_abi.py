@@ -142,9 +142,9 @@ def test_rmsnorm_rstd_and_backward_validation(jetlib):
     assert c(f, P[0], P[1], 16, 128, 1e-6, P[2], P[3], P[3] + 16, 0) == EALIAS  # rstd overlaps s
     assert c(f, 0, P[1], 0, 128, 1e-6, 0, 0, 0, 0) == OK
     ws = _lib.rmsnorm_backward_workspace_bytes
-    # one row of K floats per workgroup of 4 R rows, R = ceil(M / 1024) in 1..8
+    # one row of K floats per workgroup of R rows, R = 2 ceil(M / 512) in 1..32
     assert ws(8192, 4096) == 4 * 256 * 4096 and ws(1, 128) == 4 * 128 and ws(0, 128) == 0
-    assert ws(256, 4096) == 4 * 64 * 4096 and ws(2000, 128) == 4 * 250 * 128 and ws(65536, 128) == 4 * 2048 * 128
+    assert ws(256, 4096) == 4 * 128 * 4096 and ws(2000, 128) == 4 * 250 * 128 and ws(65536, 128) == 4 * 2048 * 128
     assert ws(4, 100) == -1 and ws(4, 6144 + 128) == -1 and ws(-1, 128) == -1
     b = "rmsnorm_backward"
     # (x, gamma, rstd, dy, M, K, dx, dgamma, workspace)

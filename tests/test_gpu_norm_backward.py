@@ -52,9 +52,10 @@ def run_backward(x, g, dy):
     return host(dx.t), host(dg.t)
 
 
-# ragged row counts (not a multiple of the 32 rows of a workgroup), K not a
-# multiple of 512 (a partial last pass), the 8B and 32B hidden sizes
-@pytest.mark.parametrize("m,k", [(1, 128), (31, 384), (33, 640), (64, 4096), (100, 5120), (257, 6144)])
+# ragged row counts (not a multiple of a workgroup's rows), K not a multiple of
+# 512 (a partial last pass) or of 2048 (waves with fewer passes), the 8B and 32B
+# hidden sizes
+@pytest.mark.parametrize("m,k", [(1, 128), (31, 384), (33, 640), (64, 4096), (100, 5120), (257, 6144), (1500, 2560)])
 def test_rmsnorm_backward_matches_oracle(m, k):
     print(f"[rmsnorm_backward] m={m} k={k}", flush=True)
     x = synth.random_bf16((m, k), seed=7 * m + k)

@@ -31,10 +31,10 @@ __device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old, bool hi_ha
                  : __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
 }
 
-// S = amax / 448 as an IEEE fp32 division (this file is compiled with
-// correctly rounded fp32 division); S = 1 for an all-zero group.
+// S = amax / 448 rounded as the IEEE fp32 division (amax_over_448, exact for
+// every non-negative finite amax); S = 1 for an all-zero group.
 __device__ __forceinline__ float scale_from_amax(float amax) {
-  return amax == 0.0f ? 1.0f : amax / kE4M3Max;
+  return amax == 0.0f ? 1.0f : amax_over_448(amax);
 }
 
 // Cross-lane moves inside a 16-lane DPP row (a quarter-wave), in registers:
@@ -51,20 +51,29 @@ __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
 }
 
-// Max over the 16 lanes of a quarter-wave (lanes 16q .. 16q+15).
+// Max over the 16 lanes of a quarter-wave (lanes 16q .. 16q+15) of
+// non-negative values (group amaxes).  The fp32 bit patterns are compared as
+// unsigned integers, which orders non-negative floats as their values, so the
+// DPP reads need none of the NaN-quieting moves an fp32 max puts around them.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t u) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, kCtrl, 0xF, 0xF, false);
+}
 __device__ __forceinline__ float quarter_wave_max(float v) {
-  v = fmaxf(v, dpp<kXor1>(v));
-  v = fmaxf(v, dpp<kXor2>(v));
-  v = fmaxf(v, dpp<kHalfMirror>(v));
-  v = fmaxf(v, dpp<kMirror>(v));
-  return v;
+  uint32_t u = __float_as_uint(v);
+  u = max(u, dpp_u32<kXor1>(u));
+  u = max(u, dpp_u32<kXor2>(u));
+  u = max(u, dpp_u32<kHalfMirror>(u));
+  u = max(u, dpp_u32<kMirror>(u));
+  return __uint_as_float(u);
 }
 
+// Max over the 64 lanes of non-negative values.
 __device__ __forceinline__ float wave_max(float v) {
-  v = quarter_wave_max(v);
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+  uint32_t u = __float_as_uint(quarter_wave_max(v));
+  u = max(u, (uint32_t)__shfl_xor((int)u, 16, 64));
+  u = max(u, (uint32_t)__shfl_xor((int)u, 32, 64));
+  return __uint_as_float(u);
 }
 
 // Sum over the 64 lanes as the balanced binary tree over lane order: level k

@@ -39,6 +39,17 @@ JETFP8_HD uint32_t f32_to_bf16_rne(float f) {
 // range, where the E4M3 cast gives a zero code either way.
 JETFP8_HD float div_by_scale(float x, double inv_s) { return (float)((double)x * inv_s); }
 
+// S = fl32(amax / 448) for a non-negative finite amax, computed as
+// fl32(fl64(amax * fl64(1 / 448))).  fl64(1/448) and the fp64 product each add
+// at most 2^-53 of relative error, so the fp64 value is within 2^-52 of
+// amax / 448, which is never an fp32 rounding midpoint in the normal range (a
+// midpoint times 448 = 7 * 2^6 needs at least 27 significant bits) and lies
+// relatively at least about 2^-27 away from one; the one fp32 rounding then
+// gives the correctly rounded quotient.  The host check compares it with the
+// IEEE fp32 division on every positive finite fp32 value, subnormal results
+// included (no mismatch).  Three operations instead of a full division.
+JETFP8_HD float amax_over_448(float amax) { return (float)((double)amax * (1.0 / 448.0)); }
+
 // Correctly rounded fp32 square root of a non-negative finite d.
 //
 // The hardware square root is only accurate to about one ulp, so the result is

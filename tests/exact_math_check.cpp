@@ -22,6 +22,18 @@ int main(int argc, char** argv) {
     }
     ++n_sqrt;
   }
+  // S = amax / 448: every stride-th positive finite fp32 (all of them with stride 1),
+  // all subnormals and the smallest normals
+  uint64_t bad_s = 0, n_s = 0;
+  for (uint64_t b = 1; b < 0x7f800000ull; b += (b < (1u << 24) ? 1 : stride)) {
+    const float a = f32_from_bits((uint32_t)b);
+    volatile float ref = a / 448.0f;
+    if (f32_bits(amax_over_448(a)) != f32_bits(ref)) {
+      if (bad_s < 5) printf("amax/448 mismatch amax=%a got %a want %a\n", a, amax_over_448(a), (float)ref);
+      ++bad_s;
+    }
+    ++n_s;
+  }
   // quotient x / S: random pairs, plus pairs constructed next to fp32 midpoints
   std::mt19937_64 rng(1234);
   uint64_t bad_div = 0, n_div = 0;
@@ -54,6 +66,7 @@ int main(int argc, char** argv) {
     for (int k = -3; k <= 3; ++k) check(f32_from_bits(f32_bits(x0) + k), s);
   }
   printf("sqrt_rn: %llu checked, %llu mismatches\n", (unsigned long long)n_sqrt, (unsigned long long)bad_sqrt);
+  printf("amax_over_448: %llu checked, %llu mismatches\n", (unsigned long long)n_s, (unsigned long long)bad_s);
   printf("div_by_scale: %llu checked, %llu mismatches\n", (unsigned long long)n_div, (unsigned long long)bad_div);
-  return (bad_sqrt || bad_div) ? 1 : 0;
+  return (bad_sqrt || bad_div || bad_s) ? 1 : 0;
 }

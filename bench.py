@@ -173,6 +173,54 @@ def time_steps(torch, steps, n_steps, n_warmup, dev):
     return per, step_ms, wall
 
 
+def read_sclk_mhz():
+    """Current shader clock from the driver's DPM table (the line marked '*'), or None."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as fh:
+                for line in fh:
+                    if line.rstrip().endswith("*"):
+                        return int(line.split(":")[1].strip().lower().split("mhz")[0])
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
+def sustained_sclk(torch, steps, seconds=0.6):
+    """Shader clock under load: run the step back to back for `seconds` while a
+    thread samples the DPM table every 20 ms (samples from the first 0.1 s are
+    dropped).  Returns a dict, or None where the table is unreadable."""
+    import threading
+    if read_sclk_mhz() is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        t0 = time.perf_counter()
+        while not stop.is_set():
+            v = read_sclk_mhz()
+            if v is not None and time.perf_counter() - t0 > 0.1:
+                samples.append(v)
+            time.sleep(0.02)
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            for _, fn in steps:
+                fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    return {"median": float(np.median(samples)), "min": min(samples), "max": max(samples),
+            "samples": len(samples),
+            "source": f"pp_dpm_sclk sampled every 20 ms over {seconds} s of back-to-back steps after the timed passes"}
+
+
 def bench_decode(args):
     import torch
     import quantized_rl_amd as jet
@@ -320,6 +368,7 @@ def main():
         "kernels": kernels,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
     }
+    out["sclk_mhz"] = sustained_sclk(torch, steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(d, g_host)
     print(json.dumps(out), flush=True)

@@ -26,8 +26,17 @@ gate+up weights, 1x128 quantisation of the down-projection input and the down
 FProp (weights quantised once, outside the timed region).  Decode is bound by
 streaming the FP8 weights, so its kernels also report weight GB/s.
 
+``--workload llama_layer`` times the forward + backward of the four linears
+of one Llama-3.1-8B layer (QKV, O, gate+up, down) at M = 16384 tokens, and
+``--workload qwen32b_half_mlp`` that of one GPU's half of a Qwen3-32B MLP
+(gate+up 5120 -> 25600, down 12800 -> 5120) at M = 8192: per linear the same
+kernels as the default step (1x128 quantisation of X, weight quantisation,
+FProp, dY quantisation, DGrad, both requants, WGrad).  They report every
+GEMM's rate; ``value`` is again all GEMM work over the step time.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--workload linear_8b_up|decode_8b] [--decode-m M]
+                       [--workload linear_8b_up|decode_8b|llama_layer|qwen32b_half_mlp]
+                       [--decode-m M]
 """
 
 import argparse
@@ -54,7 +63,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="linear_8b_up", choices=["linear_8b_up", "decode_8b"])
+    ap.add_argument("--workload", default="linear_8b_up",
+                    choices=["linear_8b_up", "decode_8b", "llama_layer", "qwen32b_half_mlp"])
     ap.add_argument("--decode-m", type=int, default=16)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (torch copy_), whose HBM counters "
@@ -288,6 +298,96 @@ def bench_decode(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_layers(args):
+    """Forward + backward of several linears back to back (one training step of
+    a layer's linears); every GEMM is reported against the FP8 MFMA peak."""
+    import torch
+    import quantized_rl_amd as jet
+    from quantized_rl_amd import synth
+
+    dev = torch.device("cuda:0")
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.workload == "llama_layer":
+        m, seed = 16384, 3
+        linears = []
+        for name in synth.LLAMA_LINEARS:
+            d = synth.llama_layer(0, name, m=m)
+            linears.append((name, bf16(d["x"]), bf16(d["w"]), bf16(d["dy"])))
+            del d
+        cfg = {"workload": "llama31_8b_layer_linears_fwd_bwd", "M": m, "layer": 0,
+               "linears": {k: {"N": n, "K": kk} for k, (n, kk) in synth.LLAMA_LINEARS.items()}, "seed": seed}
+    else:
+        m, seed = 8192, 4
+        d = synth.qwen32b_half_mlp(m)
+        linears = [("gate_up", bf16(d["x"]), bf16(d["w_gu"]), bf16(d["dy_gu"])),
+                   ("down", bf16(d["down_in"]), bf16(d["w_down"]), bf16(d["dy_down"]))]
+        del d
+        cfg = {"workload": "qwen3_32b_half_mlp_fwd_bwd", "M": m,
+               "linears": {"gate_up": {"N": 25600, "K": 5120}, "down": {"N": 5120, "K": 12800}}, "seed": seed}
+    u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+    steps, work = [], {}
+    total_flops = 0.0
+    for name, x, w, dy in linears:
+        n, k = w.shape
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)  # noqa: E731
+        b = dict(qx=e((m, k), u8), sx=e((k // 128, m), f32), qw=e((n, k), u8),
+                 sw=e((n // 128, k // 128), f32), qdy=e((m, n), u8), sdy=e((n // 128, m), f32),
+                 qxt=e((k, m), u8), sxt=e((m // 128, k), f32), qdyt=e((n, m), u8),
+                 sdyt=e((m // 128, n), f32), y=e((m, n), bf), dx=e((m, k), bf), dw=e((n, k), bf))
+        g = 2.0 * m * n * k
+        total_flops += 3 * g
+        steps += [
+            (f"{name}.quantize_act_x", lambda x=x, b=b: jet.quantize_act_1x128(x, b["qx"], b["sx"])),
+            (f"{name}.quantize_weight", lambda w=w, b=b: jet.quantize_weight_128x128(w, b["qw"], b["sw"])),
+            (f"{name}.gemm_fprop", lambda b=b: jet.gemm_fprop(b["qx"], b["sx"], b["qw"], b["sw"], b["y"])),
+            (f"{name}.quantize_act_dy", lambda dy=dy, b=b: jet.quantize_act_1x128(dy, b["qdy"], b["sdy"])),
+            (f"{name}.gemm_dgrad", lambda b=b: jet.gemm_dgrad(b["qdy"], b["sdy"], b["qw"], b["sw"], b["dx"])),
+            (f"{name}.requant_x", lambda b=b: jet.requant_transpose_128x1(b["qx"], b["sx"], b["qxt"], b["sxt"])),
+            (f"{name}.requant_dy", lambda b=b: jet.requant_transpose_128x1(b["qdy"], b["sdy"], b["qdyt"], b["sdyt"])),
+            (f"{name}.gemm_wgrad", lambda b=b: jet.gemm_wgrad(b["qdyt"], b["sdyt"], b["qxt"], b["sxt"], b["dw"])),
+        ]
+        act = m * k * 3 + 4 * m * k // 128
+        work.update({
+            f"{name}.quantize_act_x": ("GB/s", act),
+            f"{name}.quantize_weight": ("GB/s", n * k * 3 + 4 * n * k // (128 * 128)),
+            f"{name}.gemm_fprop": ("TFLOP/s", g),
+            f"{name}.quantize_act_dy": ("GB/s", m * n * 3 + 4 * m * n // 128),
+            f"{name}.gemm_dgrad": ("TFLOP/s", g),
+            f"{name}.requant_x": ("GB/s", 2 * (m * k + 4 * m * k // 128)),
+            f"{name}.requant_dy": ("GB/s", 2 * (m * n + 4 * m * n // 128)),
+            f"{name}.gemm_wgrad": ("TFLOP/s", g),
+        })
+    torch.cuda.synchronize()
+    per, step_ms, wall = time_steps(torch, steps, args.steps, args.warmup, dev)
+    ms_per_step = float(np.mean(step_ms))
+    kernels = {}
+    for name, (unit, amount) in work.items():
+        avg_ms = float(np.mean(per[name]))
+        rate = amount / (avg_ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+        peak = MFMA_FP8_PEAK_TFLOPS if unit == "TFLOP/s" else HBM_PEAK_GBS
+        kernels[name] = {"avg_us": round(avg_ms * 1e3, 2), "rate": round(rate, 1), "unit": unit,
+                         "frac": round(rate / peak, 4)}
+    gemms = [k for k in kernels if ".gemm_" in k]
+    dom = max(gemms, key=lambda k: kernels[k]["avg_us"])
+    gemm_ms = sum(kernels[k]["avg_us"] for k in gemms) * 1e-3
+    out = {
+        "metric": METRIC, "value": round(total_flops / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3",
+        "data": "synthetic", "config": cfg,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": kernels[dom]["rate"],
+                     "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(kernels[dom]["rate"] / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None},
+        "gemm_only_TFLOPs": round(total_flops / (gemm_ms * 1e-3) / 1e12, 1),
+        "kernels": kernels,
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -297,6 +397,10 @@ def main():
     if args.workload == "decode_8b":
         sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
         bench_decode(args)
+        return
+    if args.workload in ("llama_layer", "qwen32b_half_mlp"):
+        sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+        bench_layers(args)
         return
     import torch
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))

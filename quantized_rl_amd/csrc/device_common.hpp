@@ -37,6 +37,17 @@ __device__ __forceinline__ float scale_from_amax(float amax) {
   return amax == 0.0f ? 1.0f : amax_over_448(amax);
 }
 
+// 1 / S in fp64 within one ulp, for the quotient fl32(fl64(x * (1 / S))):
+// v_rcp_f64 refined by recip_nr (a handful of full-rate fp64 operations
+// instead of the IEEE division sequence).
+__device__ __forceinline__ double inv_scale(float s) {
+  const double d = (double)s;
+  return recip_nr(d, __builtin_amdgcn_rcp(d));
+}
+
+// fl32(1 / c), correctly rounded, for a non-negative fp32 c (recip_f32_from).
+__device__ __forceinline__ float recip_f32_rn(float c) { return recip_f32_from(c, inv_scale(c)); }
+
 // Cross-lane moves inside a 16-lane DPP row (a quarter-wave), in registers:
 //   kXor1  quad_perm [1,0,3,2]: lane l reads lane l ^ 1
 //   kXor2  quad_perm [2,3,0,1]: lane l reads lane l ^ 2

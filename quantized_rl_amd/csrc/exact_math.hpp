@@ -26,11 +26,37 @@ JETFP8_HD uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// fl32(x / S) computed as fl32(fl64(x * fl64(1 / S))), with inv_s = fl64(1 / S).
+// 1 / d in fp64 to within one ulp (relative error below 2^-52) for an fp64 d
+// that is an fp32 value (normal or subnormal), from a seed r0 with relative
+// error below 2^-20: two Newton-Raphson steps with fused multiply-adds.  Each
+// step squares the seed's relative error (2^-20 -> 2^-40 -> 2^-80) and adds
+// the rounding of its own fma (2^-53).  The device seed is v_rcp_f64; the host
+// check drives it with seeds perturbed by +-2^-20.
+JETFP8_HD double recip_nr(double d, double r0) {
+  double e = __builtin_fma(-d, r0, 1.0);
+  const double r1 = __builtin_fma(r0, e, r0);
+  e = __builtin_fma(-d, r1, 1.0);
+  return __builtin_fma(r1, e, r1);
+}
+
+// fl32(1 / c) for a non-negative fp32 c, from an fp64 value r within 2^-52
+// (relative) of 1 / c when c is positive and finite: c * m != 1 for every
+// fp32 rounding midpoint m (m has an odd 25-bit significand), and C * Mi - 2^j
+// for the integer significands is a nonzero integer, so 1 / c lies at least
+// 2^-49 (relative) from every midpoint and r rounds to the same fp32 value.
+// c = +inf gives +0 and c = 0 gives +inf, as the IEEE division does (r is
+// not used there: the Newton steps give NaN for those two).
+JETFP8_HD float recip_f32_from(float c, double r) {
+  const float inf = __builtin_inff();
+  return c == inf ? 0.0f : (c == 0.0f ? inf : (float)r);
+}
+
+// fl32(x / S) computed as fl32(fl64(x * inv_s)), with inv_s within one ulp of
+// 1 / S (fl64(1 / S), or recip_nr's result).
 //
-// Why this equals the correctly rounded fp32 quotient: inv_s and the fp64
-// product each add a relative error of at most 2^-53, so z = fl64(x * inv_s) is
-// within 2^-51.9 (relative) of x / S.  For fp32 x and S, x / S is never an fp32
+// Why this equals the correctly rounded fp32 quotient: inv_s adds a relative
+// error of at most 2^-52 and the fp64 product at most 2^-53, so
+// z = fl64(x * inv_s) is within 2^-51.4 (relative) of x / S.  For fp32 x and S, x / S is never an fp32
 // rounding midpoint (a midpoint has an odd 25-bit significand, so S times it
 // needs more than 24 significant bits), and its relative distance to the
 // nearest midpoint is at least 2^-49 (x - S * midpoint is a nonzero multiple of

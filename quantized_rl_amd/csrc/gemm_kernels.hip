@@ -34,6 +34,7 @@
 // with the same fp32 operations, so a row's FProp output does not depend on the
 // kernel (nor on the batch it is computed in).
 #include <atomic>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -111,6 +112,27 @@ __device__ __forceinline__ void buf_to_lds16(rsrc_t r, uint8_t* lds_wave_base, u
 // vmcnt(0): wait for every outstanding vector-memory load of this wave
 // (including the LDS-direct loads); expcnt and lgkmcnt left at their maxima.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// vmcnt(n), n <= 63: wait until at most n of this wave's vector-memory loads
+// are outstanding (they complete in issue order for this count).
+template <int kN>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(kN >= 0 && kN <= 63, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((kN & 15) | ((kN >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier for LDS traffic: waits for this wave's LDS operations,
+// not for its outstanding global loads (__syncthreads() is also a release
+// fence, which waits for every load in flight, direct-to-LDS ones included).
+__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// f(std::integral_constant<int, 0>{}), .., f(std::integral_constant<int, kN - 1>{})
+template <int kN, int kI = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (kI < kN) {
+    f(std::integral_constant<int, kI>{});
+    static_for<kN, kI + 1>(f);
+  }
+}
 
 // One stage of operand tiles (A then B) and its scales, as separate LDS
 // objects: the loop below is unrolled over the two stages so that every LDS
@@ -670,15 +692,27 @@ struct MedTile {
   }
 };
 
-template <int kMode, int kOut = kOutBf16>
-__global__ __launch_bounds__(kMThreads, 2) void gemm_fp8_med_kernel(const uint8_t* __restrict__ A,
-                                                                     const float* __restrict__ sa,
-                                                                     const uint8_t* __restrict__ B,
-                                                                     const float* __restrict__ sb,
-                                                                     uint32_t M, uint32_t N, uint32_t K,
-                                                                     void* __restrict__ Cv) {
+// kSt operand stages: 2 (double buffering, two workgroups per CU) or 4 (loads
+// issued three K-blocks ahead, one workgroup per CU).  With one tile or less
+// per CU, a tile's chain of K-blocks waits on memory latency at every block
+// when only one block is in flight; four stages keep three in flight.
+template <int kStages>
+struct MedStages {
+  static constexpr int kMinBlocks = kStages == 2 ? 2 : 1;
+};
+
+template <int kMode, int kOut = kOutBf16, int kSt = 2>
+__global__ __launch_bounds__(kMThreads, MedStages<kSt>::kMinBlocks) void gemm_fp8_med_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ B,
+    const float* __restrict__ sb, uint32_t M, uint32_t N, uint32_t K, void* __restrict__ Cv) {
+  static_assert(kSt == 2 || kSt == 4, "two or four operand stages");
+  // separate LDS objects, named statically below (see LStage); st2 and st3
+  // exist only with four stages
   __shared__ __attribute__((aligned(16))) MStage st0;
   __shared__ __attribute__((aligned(16))) MStage st1;
+  typedef typename std::conditional<kSt == 4, MStage, char>::type MStageOpt;
+  __shared__ __attribute__((aligned(16))) MStageOpt st2;
+  __shared__ __attribute__((aligned(16))) MStageOpt st3;
 
   MedTile<kMode> g;
   g.t = threadIdx.x;
@@ -723,31 +757,67 @@ __global__ __launch_bounds__(kMThreads, 2) void gemm_fp8_med_kernel(const uint8_
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  g.store_scale(st0, g.load_scale(0));
-  g.issue(0, st0);
-  wait_vmem();
-  __syncthreads();
-
+  auto stage = [&](auto c) -> MStage& {
+    constexpr int i = decltype(c)::value;
+    if constexpr (i == 0) return st0;
+    else if constexpr (i == 1) return st1;
+    else if constexpr (i == 2) return *reinterpret_cast<MStage*>(&st2);  // (kSt == 4 only)
+    else return *reinterpret_cast<MStage*>(&st3);
+  };
   const uint32_t last = g.nkb - 1;
-#pragma clang loop unroll(disable)
-  for (uint32_t kb = 0; kb < g.nkb; kb += 2) {
-    {
-      const uint32_t kn = kb + 1 <= last ? kb + 1 : last;
-      const float2 x = g.load_scale(kn);
-      g.compute(st0, acc, kn, st1);
-      g.store_scale(st1, x);
-      wait_vmem();
-      __syncthreads();
-    }
+  // Block kb lives in stage kb % kSt.  Its scale factors are fetched into
+  // registers when its loads are issued (kSt - 1 blocks ahead) and stored to
+  // its stage at the end of the block before it.
+  float2 xs[kSt];
+  static_for<kSt - 1>([&](auto c) {
+    constexpr int p = decltype(c)::value;
+    const uint32_t kp = (uint32_t)p <= last ? (uint32_t)p : last;
+    xs[p] = g.load_scale(kp);
+    g.issue(kp, stage(c));
+  });
+  // Publishing a block: with four stages the barrier must not be a fence,
+  // which would wait for the later blocks' loads too; each wave's vmcnt wait
+  // covers its own pieces of the block, the barrier everyone's.
+  auto publish = [&]() {
+    wait_vmem_le<8 * (kSt - 2)>();
+    if constexpr (kSt == 2) __syncthreads();
+    else lds_barrier();
+  };
+  g.store_scale(st0, xs[0]);
+  publish();  // block 0's pieces (blocks 1 .. kSt - 2 may be in flight)
+
+  // One K-block in stage s: issue block kb + kSt - 1 (clamped to the last:
+  // the extra loads fill a stage no remaining block uses), multiply, then
+  // publish block kb + 1: its factors into its stage, wait for this wave's
+  // pieces of it (8 pieces per block are issued after them for each of the
+  // kSt - 2 later blocks), barrier.
+  auto step = [&](auto c, uint32_t kb) {
+    constexpr int st = decltype(c)::value;
+    constexpr int sn = (st + kSt - 1) % kSt, s1 = (st + 1) % kSt;
+    const uint32_t kn = kb + kSt - 1 <= last ? kb + kSt - 1 : last;
+    xs[sn] = g.load_scale(kn);
+    g.compute(stage(c), acc, kn, stage(std::integral_constant<int, sn>{}));
     if (kb + 1 <= last) {
-      const uint32_t kn = kb + 2 <= last ? kb + 2 : last;
-      const float2 x = g.load_scale(kn);
-      g.compute(st1, acc, kn, st0);
-      g.store_scale(st0, x);
-      wait_vmem();
-      __syncthreads();
+      g.store_scale(stage(std::integral_constant<int, s1>{}), xs[s1]);
+      publish();
+    }
+  };
+#pragma clang loop unroll(disable)
+  for (uint32_t kb = 0; kb < g.nkb; kb += kSt) {
+    step(std::integral_constant<int, 0>{}, kb);
+    if (kb + 1 > last) break;
+    step(std::integral_constant<int, 1>{}, kb + 1);
+    if constexpr (kSt == 4) {
+      if (kb + 2 > last) break;
+      step(std::integral_constant<int, 2>{}, kb + 2);
+      if (kb + 3 > last) break;
+      step(std::integral_constant<int, 3>{}, kb + 3);
     }
   }
+  // the clamped loads of the last blocks may still be landing in stages the
+  // epilogue reuses
+  wait_vmem();
+  __syncthreads();
 
   if constexpr (kOut != kOutBf16) {
     const rsrc_t rc = make_rsrc(Cv, M * N * 4u);
@@ -835,9 +905,6 @@ __device__ __forceinline__ float ld_scale(rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
 }
 
-// Workgroup barrier for LDS traffic: waits for this wave's LDS operations,
-// not for its outstanding global loads.
-__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int kMT, int kW, int kS>
 __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
@@ -1239,10 +1306,19 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
                        A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, Cv);
     return hipGetLastError();
   }
-  // the medium-tile kernel (the caller guarantees 32-bit byte offsets)
+  // the medium-tile kernel (the caller guarantees 32-bit byte offsets): four
+  // stages when there is at most one tile per CU (measured at M = 256: the
+  // 8B QKV projection, 96 tiles, 36 -> 29 us), two stages and two workgroups
+  // per CU otherwise (with 384 tiles, two rounds of the four-stage kernel
+  // took 60 us against 45 us for one round of two per CU: a CU's loads in
+  // flight are capped, so more CUs pulling data beats deeper prefetch)
   const int64_t tiles = ((Mr + kMBM - 1) / kMBM) * (Nc / kMBN);
-  hipLaunchKernelGGL((gemm_fp8_med_kernel<kMode, kOut>), dim3((unsigned)tiles), dim3(kMThreads), 0, stream, A,
-                     sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, Cv);
+  if (tiles <= (int64_t)cu_count())
+    hipLaunchKernelGGL((gemm_fp8_med_kernel<kMode, kOut, 4>), dim3((unsigned)tiles), dim3(kMThreads), 0, stream,
+                       A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, Cv);
+  else
+    hipLaunchKernelGGL((gemm_fp8_med_kernel<kMode, kOut, 2>), dim3((unsigned)tiles), dim3(kMThreads), 0, stream,
+                       A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, Cv);
   return hipGetLastError();
 }
 

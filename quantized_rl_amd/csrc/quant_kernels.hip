@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t* __
     unpack_bf16x8(v[it], f);
     const float amax = quarter_wave_max(absmax8(f));
     const float sc = scale_from_amax(amax);
-    const double inv = 1.0 / (double)sc;
+    const double inv = inv_scale(sc);
     const uint2 codes = quant8(f, inv);
     if (r < M && g_ok) {
       st_stream8(q + r * K + col, codes);
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void quant_weight_128x128_kernel(const uint16_
   __syncthreads();
   amax = fmaxf(fmaxf(wave_amax[0], wave_amax[1]), fmaxf(wave_amax[2], wave_amax[3]));
   const float sc = scale_from_amax(amax);
-  const double inv = 1.0 / (double)sc;
+  const double inv = inv_scale(sc);
   uint8_t* qbase = q + (nb * kGroup) * K + kb * kGroup + lane16 * 8;
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(const uint16_t*
     if (n & 1) ps[h] = ps[n - 1];
   }
   const float ms = ps[0] / (float)K;
-  const float inv = 1.0f / sqrt_rn(ms + eps);
+  const float inv = recip_f32_rn(sqrt_rn(ms + eps));
   if (rstd != nullptr && l == 0) rstd[row] = inv;
 
   const int lane16 = l & 15, quarter = l >> 4;
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(const uint16_t*
       for (int i = 0; i < 8; ++i) f[i] = (f[i] * inv) * gm[i];
       const float amax = quarter_wave_max(absmax8(f));
       const float sc = scale_from_amax(amax);
-      const double dinv = 1.0 / (double)sc;
+      const double dinv = inv_scale(sc);
       st_stream8(q + row * K + e, quant8(f, dinv));
       if (lane16 == 0) s[g * M + row] = sc;
     }
@@ -199,6 +199,93 @@ static void launch_rows(const uint16_t* x, const uint16_t* gamma, int64_t M, int
                         uint8_t* q, float* s, float* rstd, hipStream_t stream) {
   hipLaunchKernelGGL(rmsnorm_quant_rows_kernel<kP>, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream,
                      x, gamma, M, K, eps, q, s, rstd);
+}
+
+// Rows of K = 2048 kQ elements (kQ = 1, 2, 4: the 2048-, 4096- and
+// 8192-wide models): the four waves of a workgroup share each row, and a
+// workgroup walks rows blockIdx.x, blockIdx.x + gridDim.x, ..  Wave w owns the
+// kQ passes kQ w .. kQ w + kQ - 1 of 512 elements (lane l: the 8 elements at
+// 512 p + 8 l), so its pass sums combine pairwise into the subtree of its
+// 512 kQ elements and the four wave subtrees meet in LDS as (w0 + w1) +
+// (w2 + w3): the same canonical tree as the one-wave kernel.  gamma is
+// loaded and widened to fp32 once per workgroup, the row's fp32 values are
+// kept for the quantisation (one widening per element), and the next row's
+// loads are issued before the current row is reduced.
+template <int kQ>
+__global__ __launch_bounds__(256) void rmsnorm_quant_split_kernel(const uint16_t* __restrict__ x,
+                                                                  const uint16_t* __restrict__ gamma,
+                                                                  int64_t M, int64_t K, float eps,
+                                                                  uint8_t* __restrict__ q,
+                                                                  float* __restrict__ s,
+                                                                  float* __restrict__ rstd) {
+  // K = 2048 kQ is a power of two, so ss / K is exactly ss * (1 / K)
+  constexpr float kInvK = 1.0f / (float)(2048 * kQ);
+  __shared__ float wsum[2][4];  // per row parity: the four wave subtrees
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane16 = l & 15, quarter = l >> 4;
+  const int64_t e0 = 512 * kQ * w + 8 * l;  // element of pass j: e0 + 512 j
+
+  float g[kQ][8];
+#pragma unroll
+  for (int j = 0; j < kQ; ++j) unpack_bf16x8(*reinterpret_cast<const uint4*>(gamma + e0 + 512 * j), g[j]);
+
+  // one row: reduce, normalise, quantise; `nxt` receives the loads of row + gridDim.x
+  auto do_row = [&](int64_t row, const uint4 (&cur)[kQ], uint4 (&nxt)[kQ], int par) {
+    float f[kQ][8];
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) unpack_bf16x8(cur[j], f[j]);
+    const int64_t next = row + gridDim.x;
+    if (next < M) {
+#pragma unroll
+      for (int j = 0; j < kQ; ++j) nxt[j] = ld_stream16(x + next * K + e0 + 512 * j);
+    }
+    float ps[kQ];
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) ps[j] = wave_sum_tree(tree8_sq(f[j]));
+#pragma unroll
+    for (int n = kQ; n > 1; n /= 2)
+#pragma unroll
+      for (int j = 0; j < n / 2; ++j) ps[j] = ps[2 * j] + ps[2 * j + 1];
+    if (l == 0) wsum[par][w] = ps[0];
+    __syncthreads();
+    const float tot = (wsum[par][0] + wsum[par][1]) + (wsum[par][2] + wsum[par][3]);
+    const float inv = recip_f32_rn(sqrt_rn(tot * kInvK + eps));
+    if (rstd != nullptr && threadIdx.x == 0) rstd[row] = inv;
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) {
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = (f[j][i] * inv) * g[j][i];
+      const float amax = quarter_wave_max(absmax8(y));
+      const float sc = scale_from_amax(amax);
+      st_stream8(q + row * K + e0 + 512 * j, quant8(y, inv_scale(sc)));
+      const int64_t grp = 4 * (kQ * w + j) + quarter;
+      if (lane16 == 0) s[grp * M + row] = sc;
+    }
+  };
+
+  // rows alternate between two register buffers (no copies between them)
+  uint4 xa[kQ], xb[kQ];
+  int64_t row = blockIdx.x;
+#pragma unroll
+  for (int j = 0; j < kQ; ++j) xa[j] = ld_stream16(x + row * K + e0 + 512 * j);
+  while (true) {
+    do_row(row, xa, xb, 0);
+    row += gridDim.x;
+    if (row >= M) break;
+    do_row(row, xb, xa, 1);
+    row += gridDim.x;
+    if (row >= M) break;
+  }
+}
+
+template <int kQ>
+static void launch_split(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K, float eps,
+                         uint8_t* q, float* s, float* rstd, hipStream_t stream) {
+  // about eight workgroups per CU; each walks M / grid rows
+  const int64_t grid = M < 2048 ? M : 2048;
+  hipLaunchKernelGGL(rmsnorm_quant_split_kernel<kQ>, dim3((unsigned)grid), dim3(256), 0, stream, x, gamma,
+                     M, K, eps, q, s, rstd);
 }
 
 // Wider rows: one workgroup (256 threads) per row, two passes over the row.
@@ -239,7 +326,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
     }
     const float ms = ps[0] / (float)K;
     const float d = ms + eps;
-    inv_sh = 1.0f / sqrt_rn(d);
+    inv_sh = recip_f32_rn(sqrt_rn(d));
     if (rstd != nullptr) rstd[row] = inv_sh;
   }
   __syncthreads();
@@ -257,7 +344,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
     for (int i = 0; i < 8; ++i) f[i] = (f[i] * inv) * gm[i];
     const float amax = quarter_wave_max(absmax8(f));
     const float sc = scale_from_amax(amax);
-    const double dinv = 1.0 / (double)sc;
+    const double dinv = inv_scale(sc);
     *reinterpret_cast<uint2*>(q + row * K + e) = quant8(f, dinv);
     if (lane16 == 0) s[g * M + row] = sc;
   }
@@ -271,11 +358,14 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
 // each column k (tokens 0..63 and 64..127).  A thread reads its 64 codes with
 // the gfx950 LDS transpose read (ds_read_b64_tr_b8: within each 16-lane
 // group, lane i receives byte (i & 7) of the 8-byte rows addressed by lanes
-// 2j + (i >> 3), j = 0..7 -- one column of an 8 x 16 byte block), decodes them
-// (v_cvt_pk_f32_fp8), multiplies by the token scales and keeps the 64 fp32
-// values in registers.  The two halves' amax meet in LDS; each thread then
-// writes its 64 requantised codes into an LDS copy of the Qt tile, which the
-// workgroup stores with full 128-byte rows.
+// 2j + (i >> 3), j = 0..7 -- one column of an 8 x 16 byte block) and keeps
+// them as codes (16 registers).  Pass 1 decodes them (v_cvt_pk_f32_fp8),
+// multiplies by the token scales and takes the column amax; the two halves'
+// amax meet in LDS.  Pass 2 recomputes the same fp32 products and writes the
+// requantised codes into the same LDS tile, now holding Qt (every read of the
+// input tile happens before the barrier between the passes), which the
+// workgroup stores with full 128-byte rows.  One 18.4 KB tile and about 40
+// registers per thread let eight workgroups share a CU.
 constexpr int kRqPitch = 128 + 16;  // LDS row pitch in bytes (16-byte pad)
 
 typedef int v2i_t __attribute__((ext_vector_type(2)));
@@ -293,18 +383,33 @@ __device__ __forceinline__ void decode4(uint32_t w, float (&v)[4]) {
   v[0] = lo.x; v[1] = lo.y; v[2] = hi.x; v[3] = hi.y;
 }
 
+// The eight dequantised values fl32(decode(code) * s) of one transpose read
+// (tokens r0 .. r0 + 7 of the thread's column); the scales come from LDS.
+__device__ __forceinline__ void dequant8(v2i_t r, const float* sc, float (&v)[8]) {
+  float d[8];
+  decode4((uint32_t)r.x, *reinterpret_cast<float(*)[4]>(&d[0]));
+  decode4((uint32_t)r.y, *reinterpret_cast<float(*)[4]>(&d[4]));
+  const float4 s0 = *reinterpret_cast<const float4*>(sc);
+  const float4 s1 = *reinterpret_cast<const float4*>(sc + 4);
+  v[0] = d[0] * s0.x; v[1] = d[1] * s0.y; v[2] = d[2] * s0.z; v[3] = d[3] * s0.w;
+  v[4] = d[4] * s1.x; v[5] = d[5] * s1.y; v[6] = d[6] * s1.z; v[7] = d[7] * s1.w;
+}
+
 __global__ __launch_bounds__(256) void requant_transpose_kernel(const uint8_t* __restrict__ q,
                                                                 const float* __restrict__ s,
                                                                 int64_t M, int64_t K,
                                                                 uint8_t* __restrict__ qt,
                                                                 float* __restrict__ st) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kGroup * kRqPitch];   // codes [m][k]
-  __shared__ __attribute__((aligned(16))) uint8_t otile[kGroup * kRqPitch];  // codes [k][m]
-  __shared__ float sc_in[kGroup];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kGroup * kRqPitch];  // [m][k], then [k][m]
+  __shared__ __attribute__((aligned(16))) float sc_in[kGroup];
   __shared__ float half_amax[2][kGroup];
   const int t = threadIdx.x;
-  const int64_t kg = blockIdx.x;  // feature group (128 columns)
-  const int64_t mb = blockIdx.y;  // token block (128 rows)
+  // Token blocks run fastest: the workgroups in flight share a few feature
+  // groups, so their stores fill long contiguous stretches of each Qt row
+  // (the loads still cover whole rows of Q per feature group).  With feature
+  // groups fastest, the stores of a 16384-token tensor ran 30 % slower.
+  const int64_t mb = blockIdx.x;  // token block (128 rows)
+  const int64_t kg = blockIdx.y;  // feature group (128 columns)
   const uint8_t* src = q + (mb * kGroup) * K + kg * kGroup;
 
   // 128 rows x 8 chunks of 16 bytes = 1024 chunks, 4 per thread
@@ -327,44 +432,48 @@ __global__ __launch_bounds__(256) void requant_transpose_kernel(const uint8_t* _
   const int col = 16 * gi + li;
   // address this lane supplies for row block j: row 64 h + 8 j + (li >> 1), bytes 8 (li & 1)
   const uint8_t* abase = tile + (64 * h + (li >> 1)) * kRqPitch + 16 * gi + 8 * (li & 1);
-  float v[64];
+  const float* sch = sc_in + 64 * h;
+  v2i_t r[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const v2i_t r = lds_read_tr8(abase + 8 * j * kRqPitch);
-    float d[8];
-    decode4((uint32_t)r.x, *reinterpret_cast<float(*)[4]>(&d[0]));
-    decode4((uint32_t)r.y, *reinterpret_cast<float(*)[4]>(&d[4]));
-#pragma unroll
-    for (int b = 0; b < 8; ++b) v[8 * j + b] = d[b] * sc_in[64 * h + 8 * j + b];
-  }
+  for (int j = 0; j < 8; ++j) r[j] = lds_read_tr8(abase + 8 * j * kRqPitch);
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  for (int j = 0; j < 8; ++j) {
+    float v[8];
+    dequant8(r[j], sch + 8 * j, v);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) amax = fmaxf(amax, fabsf(v[b]));
+  }
   half_amax[h][col] = amax;
-  __syncthreads();
+  __syncthreads();  // also ends every read of the input tile
+  // Opaque to the compiler: pass 2 decodes the codes again instead of keeping
+  // pass 1's 64 decoded values alive across the barrier.
+#pragma unroll
+  for (int j = 0; j < 8; ++j) __asm__ volatile("" : "+v"(r[j]));
   amax = fmaxf(half_amax[0][col], half_amax[1][col]);
   const float sc = scale_from_amax(amax);
-  const double inv = 1.0 / (double)sc;
+  const double inv = inv_scale(sc);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {  // 16 codes per 16-byte LDS store
     uint32_t o[4];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int b = 16 * i + 4 * w;
-      int p = cvt_pk_e4m3(div_by_scale(v[b], inv), div_by_scale(v[b + 1], inv), 0, false);
-      p = cvt_pk_e4m3(div_by_scale(v[b + 2], inv), div_by_scale(v[b + 3], inv), p, true);
-      o[w] = (uint32_t)p;
+    for (int jj = 0; jj < 2; ++jj) {
+      float v[8];
+      dequant8(r[2 * i + jj], sch + 8 * (2 * i + jj), v);
+      const uint2 p = quant8(v, inv);
+      o[2 * jj] = p.x;
+      o[2 * jj + 1] = p.y;
     }
-    *reinterpret_cast<uint4*>(otile + col * kRqPitch + 64 * h + 16 * i) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(tile + col * kRqPitch + 64 * h + 16 * i) = make_uint4(o[0], o[1], o[2], o[3]);
   }
   if (h == 0) st[mb * K + kg * kGroup + col] = sc;
   __syncthreads();
   // store Qt rows kg*128 + r, tokens mb*128 .. +128: 8 threads per 128-byte row
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int id = t + 256 * it, r = id >> 3, ch = id & 7;
-    st_stream16(qt + (kg * kGroup + r) * M + mb * kGroup + ch * 16,
-                *reinterpret_cast<const uint4*>(otile + r * kRqPitch + ch * 16));
+    const int id = t + 256 * it, rr = id >> 3, ch = id & 7;
+    st_stream16(qt + (kg * kGroup + rr) * M + mb * kGroup + ch * 16,
+                *reinterpret_cast<const uint4*>(tile + rr * kRqPitch + ch * 16));
   }
 }
 
@@ -390,6 +499,12 @@ hipError_t launch_quant_weight(const uint16_t* w, int64_t N, int64_t K, uint8_t*
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, int64_t M, int64_t K,
                                 float eps, uint8_t* q, float* s, float* rstd, hipStream_t stream) {
   if (M == 0) return hipSuccess;
+  if (K == 2048 || K == 4096 || K == 8192) {
+    if (K == 2048) launch_split<1>(x, gamma, M, K, eps, q, s, rstd, stream);
+    else if (K == 4096) launch_split<2>(x, gamma, M, K, eps, q, s, rstd, stream);
+    else launch_split<4>(x, gamma, M, K, eps, q, s, rstd, stream);
+    return hipGetLastError();
+  }
   if (K <= 512 * kRowPasses) {
     switch ((K + 511) / 512) {
       case 1: launch_rows<1>(x, gamma, M, K, eps, q, s, rstd, stream); break;
@@ -419,7 +534,7 @@ hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, int64_
 hipError_t launch_requant(const uint8_t* q, const float* s, int64_t M, int64_t K, uint8_t* qt,
                           float* st, hipStream_t stream) {
   if (M == 0 || K == 0) return hipSuccess;
-  dim3 grid((unsigned)(K / kGroup), (unsigned)(M / kGroup));
+  dim3 grid((unsigned)(M / kGroup), (unsigned)(K / kGroup));
   hipLaunchKernelGGL(requant_transpose_kernel, grid, dim3(256), 0, stream, q, s, M, K, qt, st);
   return hipGetLastError();
 }

@@ -1,10 +1,12 @@
 """Host checks of the device helpers that must round exactly (no GPU).
 
-The quantisation kernels compute fl32(x / S) as fl32(fl64(x * fl64(1/S))),
-S = fl32(amax / 448) as fl32(fl64(amax * fl64(1/448))), and the RMSNorm square
-root with an exact midpoint test; all are compiled here for the host from the
-same header and compared bit for bit with x86's IEEE fp32 division and square
-root.
+The quantisation kernels compute fl32(x / S) as fl32(fl64(x * inv)), with inv
+within one fp64 ulp of 1/S from two Newton-Raphson steps on v_rcp_f64's seed
+(recip_nr; the host drives it with seeds perturbed by +-2^-14), S = fl32(amax /
+448) as fl32(fl64(amax * fl64(1/448))), the RMSNorm factor 1 / sqrt as the fp32
+rounding of the same refined reciprocal, and the square root with an exact
+midpoint test; all are compiled here for the host from the same header and
+compared bit for bit with x86's IEEE fp32 (and fp64) division and square root.
 """
 
 import os

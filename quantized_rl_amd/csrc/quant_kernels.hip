@@ -203,7 +203,7 @@ static void launch_rows(const uint16_t* x, const uint16_t* gamma, int64_t M, int
 
 // Rows of K = 2048 kQ elements (kQ = 1, 2, 4: the 2048-, 4096- and
 // 8192-wide models): the four waves of a workgroup share each row, and a
-// workgroup walks rows blockIdx.x, blockIdx.x + gridDim.x, ..  Wave w owns the
+// workgroup walks a strided set of rows (below).  Wave w owns the
 // kQ passes kQ w .. kQ w + kQ - 1 of 512 elements (lane l: the 8 elements at
 // 512 p + 8 l), so its pass sums combine pairwise into the subtree of its
 // 512 kQ elements and the four wave subtrees meet in LDS as (w0 + w1) +
@@ -230,12 +230,13 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_split_kernel(const uint16_t
   for (int j = 0; j < kQ; ++j) unpack_bf16x8(*reinterpret_cast<const uint4*>(gamma + e0 + 512 * j), g[j]);
 
   // one row: reduce, normalise, quantise; `nxt` receives the loads of row + gridDim.x
-  auto do_row = [&](int64_t row, const uint4 (&cur)[kQ], uint4 (&nxt)[kQ], int par) {
+  auto do_row = [&](int64_t row, int64_t end, int64_t stride, const uint4 (&cur)[kQ], uint4 (&nxt)[kQ],
+                    int par) {
     float f[kQ][8];
 #pragma unroll
     for (int j = 0; j < kQ; ++j) unpack_bf16x8(cur[j], f[j]);
-    const int64_t next = row + gridDim.x;
-    if (next < M) {
+    const int64_t next = row + stride;
+    if (next < end) {
 #pragma unroll
       for (int j = 0; j < kQ; ++j) nxt[j] = ld_stream16(x + next * K + e0 + 512 * j);
     }
@@ -264,18 +265,36 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_split_kernel(const uint16_t
     }
   };
 
+  // Rows of this workgroup: with a grid of 8 g workgroups (dealt to the 8
+  // XCDs round-robin), XCD x owns rows [x M / 8, (x + 1) M / 8) and its
+  // workgroups walk them with stride g, so the rows in flight on one XCD are
+  // consecutive and the 4-byte scale stores of a group fill whole lines in
+  // that XCD's L2 (interleaved over the XCDs, each line was written back in
+  // pieces from eight caches: 21 % more bytes written).  Other grids: one row
+  // per workgroup.
+  int64_t row, end, stride;
+  if (gridDim.x % 8 == 0 && (int64_t)gridDim.x < M) {
+    const int64_t xcd = blockIdx.x % 8;
+    row = xcd * M / 8 + blockIdx.x / 8;
+    end = (xcd + 1) * M / 8;
+    stride = gridDim.x / 8;
+  } else {
+    row = blockIdx.x;
+    end = M;
+    stride = gridDim.x;
+  }
+  if (row >= end) return;  // whole workgroup: no barrier is left waiting
   // rows alternate between two register buffers (no copies between them)
   uint4 xa[kQ], xb[kQ];
-  int64_t row = blockIdx.x;
 #pragma unroll
   for (int j = 0; j < kQ; ++j) xa[j] = ld_stream16(x + row * K + e0 + 512 * j);
   while (true) {
-    do_row(row, xa, xb, 0);
-    row += gridDim.x;
-    if (row >= M) break;
-    do_row(row, xb, xa, 1);
-    row += gridDim.x;
-    if (row >= M) break;
+    do_row(row, end, stride, xa, xb, 0);
+    row += stride;
+    if (row >= end) break;
+    do_row(row, end, stride, xb, xa, 1);
+    row += stride;
+    if (row >= end) break;
   }
 }
 

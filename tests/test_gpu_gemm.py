@@ -55,7 +55,10 @@ def check(y, ref, what, rms=None):
 # ---------------------------------------------------------------- FProp
 
 # shapes with at least 256 tiles of 256 x 256 run the large-tile kernel, M <= 64
-# the decode kernel, the others the 128 x 128 medium-tile kernel
+# the decode kernel, the others the 128 x 128 medium-tile kernel (four operand
+# stages with at most one tile per CU, as for all but the marked shapes here,
+# two stages otherwise); K-block counts 1 .. 5, 8 and 16 cover the ends of the
+# four-stage loop
 FPROP_SHAPES = [(256, 384, 512), (1, 128, 128), (16, 384, 256), (64, 256, 128), (200, 384, 512),
                 (130, 128, 1024), (257, 640, 384),
                 (256, 256, 256), (300, 512, 384), (513, 768, 640), (1024, 1280, 2048)]
@@ -120,7 +123,8 @@ def test_fprop_k_zero_writes_zeros():
 # ---------------------------------------------------------------- DGrad
 
 DGRAD_SHAPES = [(256, 384, 512), (1, 128, 128), (16, 256, 384), (200, 512, 256), (129, 128, 640),
-                (300, 640, 256), (777, 256, 768), (1024, 2048, 1280)]
+                (300, 640, 256), (777, 256, 768), (1024, 2048, 1280),
+                (2048, 384, 2560)]  # 320 tiles of 128 x 128: the two-stage medium kernel
 
 
 @pytest.mark.parametrize("m,n,k", DGRAD_SHAPES)
@@ -153,7 +157,8 @@ def test_dgrad_exact_integer_and_equals_fprop_on_transposed_weight(m, n, k):
 # ---------------------------------------------------------------- WGrad
 
 WGRAD_SHAPES = [(128, 128, 128), (256, 384, 512), (384, 256, 256), (1024, 128, 384),
-                (256, 256, 256), (384, 512, 768), (1024, 1280, 512), (2048, 256, 1024)]
+                (256, 256, 256), (384, 512, 768), (1024, 1280, 512), (2048, 256, 1024),
+                (384, 2560, 2048)]  # 320 tiles of 128 x 128: the two-stage medium kernel
 
 
 @pytest.mark.parametrize("m,n,k", WGRAD_SHAPES)

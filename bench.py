@@ -23,8 +23,11 @@ object describes the slowest GEMM against the dense FP8 MFMA peak.  The
 ``--workload decode_8b`` instead times the rollout decode path at M tokens
 (``--decode-m``, default 16): RMSNorm+quant, FProp against the FP8 QKV and
 gate+up weights, 1x128 quantisation of the down-projection input and the down
-FProp (weights quantised once, outside the timed region).  Decode is bound by
-streaming the FP8 weights, so its kernels also report weight GB/s.
+FProp (weights quantised once, outside the timed region).  The FProps go
+through gemm_fprop_splitk, which at 65..256 tokens splits K across workgroups
+for the shapes with fewer output tiles than CUs (its workspace is allocated
+before the timed region).  Decode is bound by streaming the FP8 weights, so its
+kernels also report weight GB/s.
 
 ``--workload llama_layer`` times the forward + backward of the four linears
 of one Llama-3.1-8B layer (QKV, O, gate+up, down) at M = 16384 tokens, and
@@ -253,6 +256,11 @@ def bench_decode(args):
     qx, sx = jet.rmsnorm_quant(x, gamma, d["eps"])
     qh, sh = jet.quantize_act_1x128(h)
     y = {k: torch.empty((m, wq[k][0].shape[0]), dtype=torch.bfloat16, device=dev) for k in wq}
+    # FProp through gemm_fprop_splitk: at 65..256 tokens the shapes with fewer
+    # output tiles than CUs split K across workgroups through this workspace
+    # (allocated once, outside the timed region); other shapes run gemm_fprop
+    need = max(jet.gemm_fprop_splitk_workspace_bytes(m, q.shape[0], q.shape[1]) for q, _ in wq.values())
+    ws = torch.empty((max(need, 4) // 4,), dtype=torch.float32, device=dev)
     cur = [0]
 
     def norm():
@@ -261,10 +269,10 @@ def bench_decode(args):
 
     steps = [
         ("rmsnorm_quant", norm),
-        ("gemm_fprop_qkv", lambda: jet.gemm_fprop(qx, sx, *sets[cur[0]]["w_qkv"], y["w_qkv"])),
-        ("gemm_fprop_gate_up", lambda: jet.gemm_fprop(qx, sx, *sets[cur[0]]["w_gu"], y["w_gu"])),
+        ("gemm_fprop_qkv", lambda: jet.gemm_fprop_splitk(qx, sx, *sets[cur[0]]["w_qkv"], y["w_qkv"], ws)),
+        ("gemm_fprop_gate_up", lambda: jet.gemm_fprop_splitk(qx, sx, *sets[cur[0]]["w_gu"], y["w_gu"], ws)),
         ("quantize_act_1x128", lambda: jet.quantize_act_1x128(h, qh, sh)),
-        ("gemm_fprop_down", lambda: jet.gemm_fprop(qh, sh, *sets[cur[0]]["w_down"], y["w_down"])),
+        ("gemm_fprop_down", lambda: jet.gemm_fprop_splitk(qh, sh, *sets[cur[0]]["w_down"], y["w_down"], ws)),
     ]
     per, step_ms, wall = time_steps(torch, steps, args.steps, args.warmup, dev)
     ms_per_step = float(np.mean(step_ms))

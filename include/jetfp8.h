@@ -184,6 +184,34 @@ int gemm_fprop(const uint8_t* qx, const float* sx, const uint8_t* qw, const floa
                int64_t N, int64_t K, uint16_t* y, void* stream);
 
 /*
+ * gemm_fprop_splitk -- gemm_fprop for rollout batches, with the contraction
+ * split across workgroups through a caller-provided fp32 workspace
+ * ([P3-LAYOUT], [P3-CORE], [P3-STEPS] step 2; the rollout runs the training
+ * forward's FP8 path, [P3-CORE]).  Same operands, layouts and requirements as
+ * gemm_fprop.  When 65 <= M <= 256 and the output has fewer 128 x 128 tiles
+ * than the chip has CUs (256), K's 128-deep blocks are split into S equal
+ * contiguous ranges (S divides K/128, at most two workgroups per CU, at least
+ * four blocks per range); range s is folded in ascending order as in
+ * gemm_fprop, from zero, into an fp32 partial, and
+ *   y[m][n] = bf16(((P_0 + P_1) + P_2) + ... + P_{S-1}),
+ * deterministic, but not bitwise the sequential fold of gemm_fprop.  Other
+ * shapes need no workspace and run gemm_fprop itself.
+ *   workspace       : f32 device buffer of at least
+ *                     gemm_fprop_splitk_workspace_bytes(M, N, K) bytes (16-byte
+ *                     aligned, overlapping no operand); its contents on entry
+ *                     are ignored and on return unspecified.  May be NULL when
+ *                     that size is 0.
+ *   workspace_bytes : its size; smaller than required -> JETFP8_EINVAL.
+ */
+int gemm_fprop_splitk(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw, int64_t M,
+                      int64_t N, int64_t K, uint16_t* y, float* workspace, int64_t workspace_bytes,
+                      void* stream);
+
+/* Workspace bytes gemm_fprop_splitk needs for this shape (S * M * N * 4, or 0
+ * when it runs gemm_fprop); -1 for an invalid shape.  Needs no GPU. */
+int64_t gemm_fprop_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
  * gemm_fprop_quant -- gemm_fprop, plus the 1x128 quantisation of its output for
  * the next layer's GEMM (the fused quantisation that removes a separate pass
  * over Y: [P3-CORE] on fusing quantisation into the producing kernels, [P3-STEPS]

@@ -12,6 +12,8 @@ from ._lib import (  # noqa: F401
     gemm_dgrad,
     gemm_fprop,
     gemm_fprop_quant,
+    gemm_fprop_splitk,
+    gemm_fprop_splitk_workspace_bytes,
     gemm_wgrad,
     gemm_wgrad_f32,
     quantize_act_1x128,

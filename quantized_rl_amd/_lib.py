@@ -23,6 +23,7 @@ SIGNATURES = {
     "rmsnorm_backward": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p],
     "requant_transpose_128x1": [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "gemm_fprop": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
+    "gemm_fprop_splitk": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p],
     "gemm_fprop_quant": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p],
     "gemm_dgrad": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
     "gemm_wgrad": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
@@ -55,6 +56,8 @@ def lib():
             fn.restype = ctypes.c_int
         L.rmsnorm_backward_workspace_bytes.argtypes = [_c_i64, _c_i64]
         L.rmsnorm_backward_workspace_bytes.restype = _c_i64
+        L.gemm_fprop_splitk_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64]
+        L.gemm_fprop_splitk_workspace_bytes.restype = _c_i64
         L.jetfp8_status_string.argtypes = [ctypes.c_int]
         L.jetfp8_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -209,6 +212,36 @@ def gemm_fprop(qx, sx, qw, sw, y=None):
     _check("gemm_fprop", lib().gemm_fprop(
         qx.data_ptr(), sx.data_ptr(), qw.data_ptr(), sw.data_ptr(), M, N, K, y.data_ptr(),
         _stream(qx.device)))
+    return y
+
+
+def gemm_fprop_splitk_workspace_bytes(M, N, K):
+    """Bytes of fp32 workspace gemm_fprop_splitk needs (0: it runs gemm_fprop)."""
+    n = lib().gemm_fprop_splitk_workspace_bytes(M, N, K)
+    if n < 0:
+        raise JetFP8Error("gemm_fprop_splitk_workspace_bytes", 1, f"invalid shape {M}x{N}x{K}")
+    return n
+
+
+def gemm_fprop_splitk(qx, sx, qw, sw, y=None, workspace=None):
+    """gemm_fprop with K split across workgroups for 65..256-row batches with few
+    output tiles, through an fp32 workspace (allocated here when not given)."""
+    torch = _torch()
+    M, K = qx.shape
+    N = qw.shape[0]
+    _need(qx, torch.uint8, (M, K), "qx")
+    _need(sx, torch.float32, (K // 128, M), "sx")
+    _need(qw, torch.uint8, (N, K), "qw")
+    _need(sw, torch.float32, (N // 128, K // 128), "sw")
+    y = _empty((M, N), torch.bfloat16, qx.device) if y is None else _need(y, torch.bfloat16, (M, N), "y")
+    need = gemm_fprop_splitk_workspace_bytes(M, N, K)
+    if workspace is None:
+        workspace = _empty((max(need, 4) // 4,), torch.float32, qx.device)
+    if workspace.dtype != torch.float32 or not workspace.is_contiguous() or workspace.device != qx.device:
+        raise ValueError("workspace: a contiguous float32 tensor on the operands' device")
+    _check("gemm_fprop_splitk", lib().gemm_fprop_splitk(
+        qx.data_ptr(), sx.data_ptr(), qw.data_ptr(), sw.data_ptr(), M, N, K, y.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * 4, _stream(qx.device)))
     return y
 
 

@@ -143,6 +143,24 @@ int gemm_fprop(const uint8_t* qx, const float* sx, const uint8_t* qw, const floa
   return launched(jetfp8::launch_gemm_fprop(qx, sx, qw, sw, M, N, K, y, as_stream(stream)));
 }
 
+int64_t gemm_fprop_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || N % 128 || K % 128) return -1;
+  return jetfp8::fprop_splitk_workspace_bytes(M, N, K);
+}
+
+int gemm_fprop_splitk(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw, int64_t M,
+                      int64_t N, int64_t K, uint16_t* y, float* workspace, int64_t workspace_bytes,
+                      void* stream) {
+  const int64_t ws = gemm_fprop_splitk_workspace_bytes(M, N, K);
+  if (ws < 0 || workspace_bytes < ws) return JETFP8_EINVAL;
+  if (int st = check_ptrs({{qx, M * K}, {sx, 4 * (M * K / 128)}, {qw, N * K},
+                           {sw, 4 * (N * K / (128 * 128))}},
+                          {{y, 2 * M * N}, {workspace, ws}}))
+    return st;
+  if (!gemm_fits(M, N, K)) return JETFP8_EUNSUPPORTED;
+  return launched(jetfp8::launch_gemm_fprop_splitk(qx, sx, qw, sw, M, N, K, y, workspace, as_stream(stream)));
+}
+
 int gemm_fprop_quant(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
                      int64_t M, int64_t N, int64_t K, uint16_t* y, uint8_t* qy, float* sy,
                      void* stream) {

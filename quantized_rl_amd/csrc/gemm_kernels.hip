@@ -565,7 +565,10 @@ struct MStage {
 template <int kMode>
 struct MedTile {
   int t, l, w, wm, wn, lr, lk;
-  uint32_t M, N, K, row0, col0, nkb, arow;
+  // nkb K-blocks starting at block kb0 (a K-split share; kb0 = 0 and
+  // nkb = nkbt, all K / 128 blocks, otherwise); the block arguments below are
+  // relative to kb0
+  uint32_t M, N, K, row0, col0, nkb, nkbt, kb0, arow;
   rsrc_t ra, rb;
   uint32_t va[4], vb[4];
   const float* sa;
@@ -596,6 +599,7 @@ struct MedTile {
     uint8_t* As = st.ab;
     uint8_t* Bs = st.ab + kMBM * kBK;
     const int p = piece & 3;
+    kb += kb0;
     if (piece < 4)
       buf_to_lds16(ra, As + (32 * w + 8 * p) * 128, va[p], kb * kBK);
     else if (kMode == kDgrad)
@@ -611,9 +615,10 @@ struct MedTile {
   // scale folded in); threads 128..255: WGrad column scales.  The product is
   // formed in store_scale, after the block's MFMAs.
   __device__ __forceinline__ float2 load_scale(uint32_t kb) const {
+    kb += kb0;
     if (kMode == kWgrad) return make_float2(t >= kMBM ? sb[kb * N + col0 + (t - kMBM)] : sa[kb * M + arow], 1.0f);
     const uint32_t cb = col0 / kBN;
-    const uint32_t bi = (kMode == kFprop) ? cb * nkb + kb : kb * (N / kBN) + cb;
+    const uint32_t bi = (kMode == kFprop) ? cb * nkbt + kb : kb * (N / kBN) + cb;
     return make_float2(sa[kb * M + arow], sb[bi]);
   }
   __device__ __forceinline__ void store_scale(MStage& st, float2 x) const {
@@ -736,7 +741,11 @@ __global__ __launch_bounds__(kMThreads, MedStages<kSt>::kMinBlocks) void gemm_fp
   const uint32_t gm = (ntm - g0) < (uint32_t)kGroupM ? (ntm - g0) : (uint32_t)kGroupM;
   g.row0 = (g0 + (id % per_group) % gm) * kMBM;
   g.col0 = ((id % per_group) / gm) * kMBN;
-  g.nkb = K / kBK;
+  // K-split share: blockIdx.y of gridDim.y equal ranges (the launcher makes
+  // gridDim.y divide the block count; it is 1 except for split FProp)
+  g.nkbt = K / kBK;
+  g.nkb = g.nkbt / gridDim.y;
+  g.kb0 = blockIdx.y * g.nkb;
   const uint32_t t7 = (uint32_t)g.t & 127u;
   g.arow = (g.row0 + t7) < M ? (g.row0 + t7) : (M - 1);
   g.ra = make_rsrc(A, M * K);
@@ -820,7 +829,8 @@ __global__ __launch_bounds__(kMThreads, MedStages<kSt>::kMinBlocks) void gemm_fp
   __syncthreads();
 
   if constexpr (kOut != kOutBf16) {
-    const rsrc_t rc = make_rsrc(Cv, M * N * 4u);
+    // a K-split share writes its own fp32 partial: slice blockIdx.y of [splits][M][N]
+    const rsrc_t rc = make_rsrc(static_cast<float*>(Cv) + (size_t)blockIdx.y * M * N, M * N * 4u);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1346,6 +1356,80 @@ hipError_t launch_gemm_wgrad_f32(const uint8_t* qdyt, const float* sdyt, const u
                                  bool accumulate, hipStream_t stream) {
   if (accumulate) return launch_gemm<kWgrad, kOutF32Add>(qdyt, sdyt, qxt, sxt, N, K, M, dw, stream);
   return launch_gemm<kWgrad, kOutF32>(qdyt, sdyt, qxt, sxt, N, K, M, dw, stream);
+}
+
+// ---------------------------------------------------------------------------
+// FProp with K split across workgroups (65 .. 256 rows), through a workspace
+// the caller provides.  Below one 128 x 128 tile per CU (the 8B QKV and down
+// projections of a 256-token rollout batch: 96 and 64 tiles) most CUs idle and
+// each tile's sequential chain of K-blocks waits on memory; splitting K into S
+// equal contiguous ranges gives S workgroups per tile.  Share s folds its
+// blocks in ascending order, acc = fma(P_kb, fl32(sx * sw), acc) from zero,
+// and writes the fp32 partial to slice s of the workspace; the reduction adds
+// the S partials of each output in share order, ((p0 + p1) + p2) + ..., and
+// rounds to bf16.  Deterministic, and the same for a row whatever batch of
+// this size range holds it when S is the same, but not the single sequential
+// fold of gemm_fprop.
+constexpr int kSplitTargetCUs = 256;  // MI355X; fixed so the workspace size needs no device query
+
+int fprop_split_count(int64_t M, int64_t N, int64_t K) {
+  if (M <= 64 || M > 256 || N % kMBN != 0 || K % kBK != 0) return 1;
+  const int64_t tiles = ((M + kMBM - 1) / kMBM) * (N / kMBN);
+  const int64_t nkb = K / kBK;
+  if (tiles >= kSplitTargetCUs) return 1;
+  // the most shares that keep at most two workgroups per CU and at least four
+  // K-blocks per share, and divide the block count
+  int best = 1;
+  for (int64_t s = 2; s <= nkb / 4; ++s)
+    if (nkb % s == 0 && tiles * s <= 2 * kSplitTargetCUs) best = (int)s;
+  return best;
+}
+
+// y[i] = bf16(((p0[i] + p1[i]) + p2[i]) + ...), eight outputs per thread
+__global__ __launch_bounds__(256) void splitk_reduce_bf16_kernel(const float* __restrict__ ws, int splits,
+                                                                 int64_t n, uint16_t* __restrict__ y) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= n) return;
+  float4 a = *reinterpret_cast<const float4*>(ws + i);
+  float4 b = *reinterpret_cast<const float4*>(ws + i + 4);
+  for (int sp = 1; sp < splits; ++sp) {
+    const float4 c = *reinterpret_cast<const float4*>(ws + sp * n + i);
+    const float4 d = *reinterpret_cast<const float4*>(ws + sp * n + i + 4);
+    a.x += c.x; a.y += c.y; a.z += c.z; a.w += c.w;
+    b.x += d.x; b.y += d.y; b.z += d.z; b.w += d.w;
+  }
+  uint4 o;
+  o.x = f32_to_bf16_rne(a.x) | (f32_to_bf16_rne(a.y) << 16);
+  o.y = f32_to_bf16_rne(a.z) | (f32_to_bf16_rne(a.w) << 16);
+  o.z = f32_to_bf16_rne(b.x) | (f32_to_bf16_rne(b.y) << 16);
+  o.w = f32_to_bf16_rne(b.z) | (f32_to_bf16_rne(b.w) << 16);
+  *reinterpret_cast<uint4*>(y + i) = o;
+}
+
+int64_t fprop_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const int s = fprop_split_count(M, N, K);
+  return s > 1 ? (int64_t)s * M * N * 4 : 0;
+}
+
+hipError_t launch_gemm_fprop_splitk(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
+                                    int64_t M, int64_t N, int64_t K, uint16_t* y, float* ws,
+                                    hipStream_t stream) {
+  const int s = fprop_split_count(M, N, K);
+  if (s <= 1) return launch_gemm_fprop(qx, sx, qw, sw, M, N, K, y, stream);
+  const int64_t tiles = ((M + kMBM - 1) / kMBM) * (N / kMBN);
+  const dim3 grid((unsigned)tiles, (unsigned)s);
+  if (tiles * s <= kSplitTargetCUs)
+    hipLaunchKernelGGL((gemm_fp8_med_kernel<kFprop, kOutF32, 4>), grid, dim3(kMThreads), 0, stream, qx, sx, qw,
+                       sw, (uint32_t)M, (uint32_t)N, (uint32_t)K, (void*)ws);
+  else
+    hipLaunchKernelGGL((gemm_fp8_med_kernel<kFprop, kOutF32, 2>), grid, dim3(kMThreads), 0, stream, qx, sx, qw,
+                       sw, (uint32_t)M, (uint32_t)N, (uint32_t)K, (void*)ws);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = M * N;  // a multiple of 128
+  hipLaunchKernelGGL(splitk_reduce_bf16_kernel, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, stream, ws, s,
+                     n, y);
+  return hipGetLastError();
 }
 
 }  // namespace jetfp8

@@ -21,6 +21,12 @@ hipError_t launch_requant(const uint8_t* q, const float* s, int64_t M, int64_t K
                           float* st, hipStream_t stream);
 hipError_t launch_gemm_fprop(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
                              int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
+// FProp with K split across workgroups through a caller workspace (65 .. 256
+// rows with fewer 128 x 128 tiles than CUs); 0 bytes: plain FProp.
+int64_t fprop_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_fprop_splitk(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
+                                    int64_t M, int64_t N, int64_t K, uint16_t* y, float* ws,
+                                    hipStream_t stream);
 hipError_t launch_gemm_dgrad(const uint8_t* qdy, const float* sdy, const uint8_t* qw,
                              const float* sw, int64_t M, int64_t N, int64_t K, uint16_t* dx,
                              hipStream_t stream);

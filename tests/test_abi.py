@@ -153,3 +153,30 @@ def test_rmsnorm_rstd_and_backward_validation(jetlib):
     assert c(b, P[0], P[1], P[2], P[3], 4, 128, P[4], P[5], P[4] + 512, 0) == EALIAS  # workspace over dx
     assert c(b, P[0], P[1], P[2], P[3], 4, 128, P[3], P[5], P[6], 0) == EALIAS  # dx over dy
     assert c(b, P[0], P[1], P[2], P[3], 4, 128, P[4], P[5] + 4, P[6], 0) == EALIGN
+
+
+def test_gemm_fprop_splitk_validation(jetlib):
+    ws = _lib.gemm_fprop_splitk_workspace_bytes
+    # S * M * N * 4 bytes: S shares of K (dividing K/128, >= 4 blocks each, at most 512
+    # workgroups) when 65 <= M <= 256 and there are fewer 128 x 128 tiles than 256
+    assert ws(256, 6144, 4096) == 4 * 256 * 6144 * 4      # 8B QKV: 96 tiles, 32 blocks
+    assert ws(256, 4096, 12288) == 8 * 256 * 4096 * 4     # 8B down: 64 tiles, 96 blocks
+    assert ws(128, 6144, 4096) == 8 * 128 * 6144 * 4      # 48 tiles
+    assert ws(256, 5120, 12800) == 5 * 256 * 5120 * 4     # 32B down: 80 tiles, 100 blocks
+    assert ws(256, 24576, 4096) == 0                       # 384 tiles fill the chip
+    assert ws(64, 6144, 4096) == ws(257, 6144, 4096) == ws(200, 384, 512) == 0
+    raw = jetlib.gemm_fprop_splitk_workspace_bytes
+    assert raw(16, 100, 128) == -1 and raw(-1, 128, 128) == -1 and raw(16, 128, 64) == -1
+    with pytest.raises(_lib.JetFP8Error):
+        ws(16, 100, 128)
+    f = "gemm_fprop_splitk"
+    need = ws(256, 6144, 4096)
+    # (qx, sx, qw, sw, M, N, K, y, workspace, workspace_bytes)
+    assert c(f, P[0], P[1], P[2], P[3], 256, 6144, 4096, P[4], P[5], need - 4, 0) == EINVAL  # too small
+    assert c(f, P[0], P[1], P[2], P[3], 256, 6144, 4096, P[4], 0, need, 0) == ENULL
+    assert c(f, P[0], P[1], P[2], P[3], 256, 6144, 4096, P[4], P[5] + 8, need, 0) == EALIGN
+    Q = [(i + 1) << 36 for i in range(8)]
+    assert c(f, Q[0], Q[1], Q[2], Q[3], 256, 6144, 4096, Q[4], Q[4] + 1024, need, 0) == EALIAS  # over y
+    assert c(f, Q[0], Q[1], Q[2], Q[3], 256, 6144, 4096, Q[4], Q[2], need, 0) == EALIAS         # over qw
+    assert c(f, P[0], P[1], P[2], P[3], 16, 100, 128, P[4], P[5], 0, 0) == EINVAL
+    assert c(f, 0, 0, P[2], P[3], 0, 128, 128, 0, 0, 0, 0) == OK  # M = 0: nothing to do

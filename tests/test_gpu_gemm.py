@@ -467,3 +467,72 @@ def test_fprop_large_kernel_several_tiles_per_workgroup(m, n, k):
     cols = np.sort(rng.choice(n, 64, replace=False))
     ref = oracle.gemm_fprop_ref_at(qx, sx, qw, sw, rows, cols)
     check(y[np.ix_(rows, cols)], ref, f"fprop {m}x{n}x{k}", rms=float(np.sqrt(np.mean(ref ** 2))))
+
+
+# ---------------------------------------------------------------- FProp, K split across workgroups
+
+@pytest.mark.parametrize("m,n,k", [(65, 256, 1024), (100, 128, 1024), (128, 384, 2048), (200, 640, 4096),
+                                   (256, 768, 1536), (129, 256, 12288), (256, 12288, 1024)])
+def test_fprop_splitk(m, n, k):
+    """gemm_fprop_splitk on rollout batch sizes with few output tiles: K split into
+    S shares (S = workspace bytes / (4 M N): 2, 2, 4, 8, 3, 24 and 2 here; shares of
+    four to eight blocks; the last shape's 384 workgroups run the two-stage
+    kernel, the others the four-stage one), each folded sequentially into an fp32
+    partial, the partials summed in share order.  Parity with the oracle, output
+    guards intact, workspace contents on entry ignored, and two calls bitwise
+    equal."""
+    rng = np.random.default_rng(4000 + m + n + k)
+    qx, qw = codes(rng, (m, k)), codes(rng, (n, k))
+    sx, sw = scales(rng, (k // 128, m)), scales(rng, (n // 128, k // 128))
+    need = jet.gemm_fprop_splitk_workspace_bytes(m, n, k)
+    splits = need // (4 * m * n)
+    assert splits >= 2 and need == splits * 4 * m * n and (k // 128) % splits == 0
+    args = (u8_dev(qx), f32_dev(sx), u8_dev(qw), f32_dev(sw))
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")  # garbage on entry
+    yg = Guarded((m, n), torch.bfloat16)
+    jet.gemm_fprop_splitk(*args, y=yg.t, workspace=ws)
+    y2 = host(jet.gemm_fprop_splitk(*args))
+    torch.cuda.synchronize()
+    assert yg.intact()
+    y = host(yg.t)
+    check(y, oracle.gemm_fprop_ref(qx, sx, qw, sw), f"split-K fprop {m}x{n}x{k} (S={splits})")
+    assert np.array_equal(y, y2), "split-K FProp not deterministic"
+
+
+def test_fprop_splitk_exact_integer():
+    """Exact-integer operands with distinct power-of-two scales per (row, block):
+    every partial and their sum are exact, so the split result equals the
+    oracle's bf16 rounding bit for bit."""
+    m, n, k = 256, 256, 2048
+    rng = np.random.default_rng(4242)
+    qx, qw = codes(rng, (m, k), small=True), codes(rng, (n, k), small=True)
+    sx, sw = scales(rng, (k // 128, m), pow2=True), scales(rng, (n // 128, k // 128), pow2=True)
+    assert jet.gemm_fprop_splitk_workspace_bytes(m, n, k) > 0
+    y = host(jet.gemm_fprop_splitk(u8_dev(qx), f32_dev(sx), u8_dev(qw), f32_dev(sw)))
+    assert np.array_equal(y, oracle.f64_to_bf16_bits(oracle.gemm_fprop_ref(qx, sx, qw, sw)))
+
+
+def test_fprop_splitk_without_split_is_gemm_fprop():
+    """Shapes that need no workspace run gemm_fprop itself: bitwise equal."""
+    for m, n, k in [(16, 384, 1024), (256, 24576, 256), (300, 256, 512)]:
+        assert jet.gemm_fprop_splitk_workspace_bytes(m, n, k) == 0
+        rng = np.random.default_rng(m + n + k)
+        args = (u8_dev(codes(rng, (m, k))), f32_dev(scales(rng, (k // 128, m))),
+                u8_dev(codes(rng, (n, k))), f32_dev(scales(rng, (n // 128, k // 128))))
+        assert torch.equal(jet.gemm_fprop_splitk(*args), jet.gemm_fprop(*args))
+
+
+@pytest.mark.parametrize("name,n,k", [("w_qkv", 6144, 4096), ("w_down", 4096, 12288)])
+def test_fprop_splitk_decode_8b_m256(name, n, k):
+    """The 256-token rollout batch of the Qwen3-8B decode workload at full size:
+    QKV (S = 4) and down (S = 8), sampled rows against the oracle."""
+    d = synth.decode_8b(256)
+    x = d["x"] if name == "w_qkv" else d["down_in"]
+    qx, sx = jet.quantize_act_1x128(bf16_dev(x))
+    qw, sw = jet.quantize_weight_128x128(bf16_dev(d[name]))
+    assert jet.gemm_fprop_splitk_workspace_bytes(256, n, k) > 0
+    y = host(jet.gemm_fprop_splitk(qx, sx, qw, sw))
+    qxh, sxh, qwh, swh = host(qx), host(sx), host(qw), host(sw)
+    rows = np.array([0, 1, 77, 128, 200, 255])
+    ref = oracle.gemm_fprop_ref(qxh[rows], np.ascontiguousarray(sxh[:, rows]), qwh, swh)
+    check(y[rows], ref, f"split-K fprop decode 8B {name}")

@@ -536,3 +536,15 @@ def test_fprop_splitk_decode_8b_m256(name, n, k):
     rows = np.array([0, 1, 77, 128, 200, 255])
     ref = oracle.gemm_fprop_ref(qxh[rows], np.ascontiguousarray(sxh[:, rows]), qwh, swh)
     check(y[rows], ref, f"split-K fprop decode 8B {name}")
+
+
+def test_fprop_splitk_qwen32b_half_mlp_m256_down():
+    """One GPU's half of the Qwen3-32B MLP at the 256-token rollout batch: the down
+    projection (N = 5120, K = 12800: 80 tiles, S = 5 shares of 20 blocks), the
+    whole output against the oracle."""
+    d = synth.qwen32b_half_mlp(256)
+    qx, sx = jet.quantize_act_1x128(bf16_dev(d["down_in"]))
+    qw, sw = jet.quantize_weight_128x128(bf16_dev(d["w_down"]))
+    assert jet.gemm_fprop_splitk_workspace_bytes(256, 5120, 12800) == 5 * 256 * 5120 * 4
+    y = host(jet.gemm_fprop_splitk(qx, sx, qw, sw))
+    check(y, oracle.gemm_fprop_ref(host(qx), host(sx), host(qw), host(sw)), "split-K fprop 32B down")

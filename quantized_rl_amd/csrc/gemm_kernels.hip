@@ -27,12 +27,17 @@
 //   gemm_fp8_large_kernel<mode>  256 x 256 tiles: problems with >= 256 of them
 //                                (FProp and DGrad: one workgroup per CU looping
 //                                over the tiles);
-//   gemm_fp8_med_kernel<mode>    128 x 128 tiles, same machinery: everything else.
+//   gemm_fp8_med_kernel<mode>    128 x 128 tiles, same machinery: everything else
+//                                (four operand stages when the tiles do not
+//                                fill the CUs, two otherwise).
+// gemm_fprop_splitk (launch_gemm_fprop_splitk) runs the 128 x 128 kernel on K
+// shares with fp32 partials in a caller workspace, then
+// splitk_reduce_bf16_kernel.
 // Byte offsets are 32-bit (buffer resources): the API rejects GEMMs whose
 // operands or output, with one tile of ragged rows, reach 2^31 bytes.
-// All but the K-split kernel fold the K-blocks of an output in ascending order
-// with the same fp32 operations, so a row's FProp output does not depend on the
-// kernel (nor on the batch it is computed in).
+// All but the K-split kernels fold the K-blocks of an output in ascending
+// order with the same fp32 operations, so a row's FProp output does not depend
+// on the kernel (nor on the batch it is computed in).
 #include <atomic>
 #include <type_traits>
 

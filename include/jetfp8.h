@@ -188,8 +188,9 @@ int gemm_fprop(const uint8_t* qx, const float* sx, const uint8_t* qw, const floa
  * split across workgroups through a caller-provided fp32 workspace
  * ([P3-LAYOUT], [P3-CORE], [P3-STEPS] step 2; the rollout runs the training
  * forward's FP8 path, [P3-CORE]).  Same operands, layouts and requirements as
- * gemm_fprop.  When 65 <= M <= 256 and the output has fewer 128 x 128 tiles
- * than the chip has CUs (256), K's 128-deep blocks are split into S equal
+ * gemm_fprop.  When the output has fewer 128 x 128 tiles than the chip has
+ * CUs (256) and 33 <= M <= 256 (or 17 <= M <= 32 with K >= 8192; smaller
+ * batches stream the weights faster unsplit), K's 128-deep blocks are split into S equal
  * contiguous ranges (S divides K/128, at most two workgroups per CU, at least
  * four blocks per range); range s is folded in ascending order as in
  * gemm_fprop, from zero, into an fp32 partial, and

@@ -1364,11 +1364,13 @@ hipError_t launch_gemm_wgrad_f32(const uint8_t* qdyt, const float* sdyt, const u
 }
 
 // ---------------------------------------------------------------------------
-// FProp with K split across workgroups (65 .. 256 rows), through a workspace
-// the caller provides.  Below one 128 x 128 tile per CU (the 8B QKV and down
-// projections of a 256-token rollout batch: 96 and 64 tiles) most CUs idle and
-// each tile's sequential chain of K-blocks waits on memory; splitting K into S
-// equal contiguous ranges gives S workgroups per tile.  Share s folds its
+// FProp with K split across workgroups (rollout batches of 17 .. 256 rows),
+// through a workspace the caller provides.  Below one 128 x 128 tile per CU
+// (the 8B QKV and down projections of a 256-token rollout batch: 96 and 64
+// tiles) most CUs idle and each tile's sequential chain of K-blocks waits on
+// memory; splitting K into S equal contiguous ranges gives S workgroups per
+// tile.  For 17 .. 64 rows it also reads X once per 128 columns instead of
+// once per 16 (the decode kernel's strips).  Share s folds its
 // blocks in ascending order, acc = fma(P_kb, fl32(sx * sw), acc) from zero,
 // and writes the fp32 partial to slice s of the workspace; the reduction adds
 // the S partials of each output in share order, ((p0 + p1) + p2) + ..., and
@@ -1378,10 +1380,17 @@ hipError_t launch_gemm_wgrad_f32(const uint8_t* qdyt, const float* sdyt, const u
 constexpr int kSplitTargetCUs = 256;  // MI355X; fixed so the workspace size needs no device query
 
 int fprop_split_count(int64_t M, int64_t N, int64_t K) {
-  if (M <= 64 || M > 256 || N % kMBN != 0 || K % kBK != 0) return 1;
+  if (M > 256 || N % kMBN != 0 || K % kBK != 0) return 1;
   const int64_t tiles = ((M + kMBM - 1) / kMBM) * (N / kMBN);
   const int64_t nkb = K / kBK;
   if (tiles >= kSplitTargetCUs) return 1;
+  // Up to 16 rows the weight-streaming decode kernel is faster; from 17 to 32
+  // rows only long contractions gain (its waves re-read X, M x K bytes, once
+  // per 16-column strip).  Measured at the 8B decode shapes, split against the
+  // decode kernel: M = 16: QKV 13.6 / 11.1 us, gate+up 30.0 / 28.2, down 18.1 /
+  // 18.2; M = 32: down (K = 12288) 19.3 / 25.0, the others 5-10 % slower;
+  // M = 64: QKV 16.6 / 22.8, gate+up 34.0 / 39.3, down 21.6 / 37.8.
+  if (M <= 16 || (M <= 32 && nkb < 64)) return 1;
   // the most shares that keep at most two workgroups per CU and at least four
   // K-blocks per share, and divide the block count
   int best = 1;

@@ -158,13 +158,17 @@ def test_rmsnorm_rstd_and_backward_validation(jetlib):
 def test_gemm_fprop_splitk_validation(jetlib):
     ws = _lib.gemm_fprop_splitk_workspace_bytes
     # S * M * N * 4 bytes: S shares of K (dividing K/128, >= 4 blocks each, at most 512
-    # workgroups) when 65 <= M <= 256 and there are fewer 128 x 128 tiles than 256
+    # workgroups) when there are fewer 128 x 128 tiles than 256 and 33 <= M <= 256, or
+    # 17 <= M <= 32 with K >= 8192
     assert ws(256, 6144, 4096) == 4 * 256 * 6144 * 4      # 8B QKV: 96 tiles, 32 blocks
     assert ws(256, 4096, 12288) == 8 * 256 * 4096 * 4     # 8B down: 64 tiles, 96 blocks
     assert ws(128, 6144, 4096) == 8 * 128 * 6144 * 4      # 48 tiles
     assert ws(256, 5120, 12800) == 5 * 256 * 5120 * 4     # 32B down: 80 tiles, 100 blocks
     assert ws(256, 24576, 4096) == 0                       # 384 tiles fill the chip
-    assert ws(64, 6144, 4096) == ws(257, 6144, 4096) == ws(200, 384, 512) == 0
+    assert ws(64, 6144, 4096) == 8 * 64 * 6144 * 4       # 48 tiles
+    assert ws(32, 4096, 12288) == 16 * 32 * 4096 * 4     # long K at 17..32 rows
+    assert ws(16, 6144, 4096) == ws(16, 4096, 12288) == ws(32, 6144, 4096) == 0
+    assert ws(257, 6144, 4096) == ws(200, 384, 512) == 0
     raw = jetlib.gemm_fprop_splitk_workspace_bytes
     assert raw(16, 100, 128) == -1 and raw(-1, 128, 128) == -1 and raw(16, 128, 64) == -1
     with pytest.raises(_lib.JetFP8Error):

@@ -472,15 +472,16 @@ def test_fprop_large_kernel_several_tiles_per_workgroup(m, n, k):
 # ---------------------------------------------------------------- FProp, K split across workgroups
 
 @pytest.mark.parametrize("m,n,k", [(65, 256, 1024), (100, 128, 1024), (128, 384, 2048), (200, 640, 4096),
-                                   (256, 768, 1536), (129, 256, 12288), (256, 12288, 1024)])
+                                   (256, 768, 1536), (129, 256, 12288), (256, 12288, 1024),
+                                   (33, 384, 2048), (64, 256, 4096), (20, 256, 8192)])
 def test_fprop_splitk(m, n, k):
     """gemm_fprop_splitk on rollout batch sizes with few output tiles: K split into
-    S shares (S = workspace bytes / (4 M N): 2, 2, 4, 8, 3, 24 and 2 here; shares of
-    four to eight blocks; the last shape's 384 workgroups run the two-stage
-    kernel, the others the four-stage one), each folded sequentially into an fp32
-    partial, the partials summed in share order.  Parity with the oracle, output
-    guards intact, workspace contents on entry ignored, and two calls bitwise
-    equal."""
+    S shares (S = workspace bytes / (4 M N): 2, 2, 4, 8, 3, 24, 2, 4, 8 and 16 here;
+    shares of four to eight blocks; the 256 x 12288 shape's 384 workgroups run the
+    two-stage kernel, the others the four-stage one; 20 rows split only because K
+    is long), each folded sequentially into an fp32 partial, the partials summed
+    in share order.  Parity with the oracle, output guards intact, workspace
+    contents on entry ignored, and two calls bitwise equal."""
     rng = np.random.default_rng(4000 + m + n + k)
     qx, qw = codes(rng, (m, k)), codes(rng, (n, k))
     sx, sw = scales(rng, (k // 128, m)), scales(rng, (n // 128, k // 128))
@@ -514,7 +515,7 @@ def test_fprop_splitk_exact_integer():
 
 def test_fprop_splitk_without_split_is_gemm_fprop():
     """Shapes that need no workspace run gemm_fprop itself: bitwise equal."""
-    for m, n, k in [(16, 384, 1024), (256, 24576, 256), (300, 256, 512)]:
+    for m, n, k in [(16, 384, 1024), (32, 384, 1024), (256, 24576, 256), (300, 256, 512)]:
         assert jet.gemm_fprop_splitk_workspace_bytes(m, n, k) == 0
         rng = np.random.default_rng(m + n + k)
         args = (u8_dev(codes(rng, (m, k))), f32_dev(scales(rng, (k // 128, m))),

@@ -1394,8 +1394,8 @@ int fprop_split_count(int64_t M, int64_t N, int64_t K) {
   // the most shares that keep at most two workgroups per CU and at least four
   // K-blocks per share, and divide the block count
   int best = 1;
-  for (int64_t s = 2; s <= nkb / 4; ++s)
-    if (nkb % s == 0 && tiles * s <= 2 * kSplitTargetCUs) best = (int)s;
+  for (int64_t s = 2; s <= nkb / 4 && tiles * s <= 2 * kSplitTargetCUs; ++s)
+    if (nkb % s == 0) best = (int)s;
   return best;
 }
 

@@ -523,20 +523,24 @@ def test_fprop_splitk_without_split_is_gemm_fprop():
         assert torch.equal(jet.gemm_fprop_splitk(*args), jet.gemm_fprop(*args))
 
 
-@pytest.mark.parametrize("name,n,k", [("w_qkv", 6144, 4096), ("w_down", 4096, 12288)])
-def test_fprop_splitk_decode_8b_m256(name, n, k):
-    """The 256-token rollout batch of the Qwen3-8B decode workload at full size:
-    QKV (S = 4) and down (S = 8), sampled rows against the oracle."""
-    d = synth.decode_8b(256)
-    x = d["x"] if name == "w_qkv" else d["down_in"]
+@pytest.mark.parametrize("m,name,n,k,splits", [
+    (256, "w_qkv", 6144, 4096, 4), (256, "w_down", 4096, 12288, 8),
+    (64, "w_qkv", 6144, 4096, 8), (64, "w_gu", 24576, 4096, 2), (64, "w_down", 4096, 12288, 16),
+    (32, "w_down", 4096, 12288, 16), (32, "w_qkv", 6144, 4096, 1), (16, "w_gu", 24576, 4096, 1)])
+def test_fprop_splitk_decode_8b(m, name, n, k, splits):
+    """The rollout batches of the Qwen3-8B decode workload at full size, as the decode
+    bench runs them through gemm_fprop_splitk (S = 1: the call is gemm_fprop's
+    kernel), sampled rows against the oracle."""
+    d = synth.decode_8b(m)
+    x = d["down_in"] if name == "w_down" else d["x"]
     qx, sx = jet.quantize_act_1x128(bf16_dev(x))
     qw, sw = jet.quantize_weight_128x128(bf16_dev(d[name]))
-    assert jet.gemm_fprop_splitk_workspace_bytes(256, n, k) > 0
+    assert jet.gemm_fprop_splitk_workspace_bytes(m, n, k) == (splits * 4 * m * n if splits > 1 else 0)
     y = host(jet.gemm_fprop_splitk(qx, sx, qw, sw))
     qxh, sxh, qwh, swh = host(qx), host(sx), host(qw), host(sw)
-    rows = np.array([0, 1, 77, 128, 200, 255])
+    rows = np.unique(np.array([0, 1, m // 3, m // 2, m - 1]))
     ref = oracle.gemm_fprop_ref(qxh[rows], np.ascontiguousarray(sxh[:, rows]), qwh, swh)
-    check(y[rows], ref, f"split-K fprop decode 8B {name}")
+    check(y[rows], ref, f"split-K fprop decode 8B M={m} {name}")
 
 
 def test_fprop_splitk_qwen32b_half_mlp_m256_down():

@@ -1,8 +1,9 @@
 /* Drives libjetfp8.so from plain C through include/jetfp8.h (no Python, no
  * torch): reads X bf16 [M][K] and W bf16 [N][K] from files, runs
- * quantize_act_1x128, quantize_weight_128x128 and gemm_fprop on the default
- * stream, checks a few invalid calls for their status codes, and writes the
- * outputs to files for the test to compare with the oracle.
+ * quantize_act_1x128, quantize_weight_128x128, gemm_fprop and
+ * gemm_fprop_splitk (with the workspace it asks for) on the default stream,
+ * checks a few invalid calls for their status codes, and writes the outputs
+ * to files for the test to compare with the oracle.
  *   usage: c_abi_check M K N x.bin w.bin out_prefix
  */
 #include <stdint.h>
@@ -74,7 +75,17 @@ int main(int argc, char** argv) {
   if (st) { fprintf(stderr, "quantize_weight_128x128: %s\n", jetfp8_status_string(st)); return 1; }
   st = gemm_fprop(qx, sx, qw, sw, M, N, K, y, NULL);
   if (st) { fprintf(stderr, "gemm_fprop: %s\n", jetfp8_status_string(st)); return 1; }
+  /* the split-K FProp with the workspace it asks for (none for shapes it does not split) */
+  const int64_t need = gemm_fprop_splitk_workspace_bytes(M, N, K);
+  if (need < 0) return 3;
+  void *y2, *ws = NULL;
+  CHECK_HIP(hipMalloc(&y2, (size_t)(M * N) * 2));
+  if (need > 0) CHECK_HIP(hipMalloc(&ws, (size_t)need));
+  st = gemm_fprop_splitk(qx, sx, qw, sw, M, N, K, y2, ws, need, NULL);
+  if (st) { fprintf(stderr, "gemm_fprop_splitk: %s\n", jetfp8_status_string(st)); return 1; }
   /* invalid calls: rejected on the host before anything is enqueued */
+  if (gemm_fprop_splitk_workspace_bytes(64, 384, 1024) <= 0) return 3;  /* a shape that splits */
+  if (gemm_fprop_splitk(qx, sx, qw, sw, 64, 384, 1024, y2, NULL, 0, NULL) != JETFP8_EINVAL) return 3;
   if (gemm_fprop(qx, sx, qw, sw, M, N + 1, K, y, NULL) != JETFP8_EINVAL) return 3;
   if (gemm_fprop(qx, sx, qw, sw, M, N, K, (uint16_t*)qx, NULL) != JETFP8_EALIAS) return 3;
   if (quantize_act_1x128(x, M, K, NULL, sx, NULL) != JETFP8_ENULL) return 3;
@@ -86,6 +97,8 @@ int main(int argc, char** argv) {
   if (write_file(argv[6], "qx.bin", hq, (size_t)(M * K)) || write_file(argv[6], "sx.bin", hs, (size_t)(M * K / 128) * 4) ||
       write_file(argv[6], "y.bin", hy, (size_t)(M * N) * 2))
     return 2;
+  CHECK_HIP(hipMemcpy(hy, y2, (size_t)(M * N) * 2, hipMemcpyDeviceToHost));
+  if (write_file(argv[6], "y_splitk.bin", hy, (size_t)(M * N) * 2)) return 2;
   printf("c_abi_check ok\n");
   return 0;
 }

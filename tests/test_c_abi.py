@@ -37,9 +37,17 @@ def test_c_program_links(jetlib, tmp_path):
 
 
 @pytest.mark.gpu
-def test_c_program_matches_the_oracle(jetlib, tmp_path):
-    d = synth.linear_small()  # X [256, 512] with outlier channels, W [384, 512]
-    x, w = d["x"], d["w"]
+@pytest.mark.parametrize("case", ["linear_small", "rollout_64"])
+def test_c_program_matches_the_oracle(jetlib, tmp_path, case):
+    """linear_small: X [256, 512] with outlier channels, W [384, 512] (gemm_fprop_splitk
+    needs no workspace there); rollout_64: X [64, 1024], W [384, 1024], where it splits
+    K in two through the workspace the program allocates."""
+    if case == "linear_small":
+        d = synth.linear_small()
+        x, w = d["x"], d["w"]
+    else:
+        x = synth.random_bf16((64, 1024), seed=64)
+        w = synth.random_bf16((384, 1024), seed=65, std=0.02)
     (m, k), n = x.shape, w.shape[0]
     exe = str(tmp_path / "c_abi_check")
     build_c_program(exe)
@@ -55,5 +63,9 @@ def test_c_program_matches_the_oracle(jetlib, tmp_path):
     qo, so = oracle.quant_act_1x128(x)
     assert np.array_equal(q, qo) and np.array_equal(s.view(np.uint32), so.view(np.uint32))
     qwo, swo = oracle.quant_weight_128x128(w)
-    res = oracle.check_gemm(y, oracle.gemm_fprop_ref(qo, so, qwo, swo))
+    ref = oracle.gemm_fprop_ref(qo, so, qwo, swo)
+    res = oracle.check_gemm(y, ref)
+    assert res["ok"], res
+    y2 = np.fromfile(tmp_path / "y_splitk.bin", dtype=np.uint16).reshape(m, n)
+    res = oracle.check_gemm(y2, ref)
     assert res["ok"], res

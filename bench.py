@@ -55,6 +55,9 @@ MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 (E4M3) MFMA
 HBM_PEAK_GBS = 8000.0
 
 M, K, N = 8192, 4096, 12288
+KERNELS_TIMING = ("HIP events recorded after every kernel of the second timed pass; each interval also "
+                  "holds one launch gap of about 5 us, which matters for the short memory-bound kernels "
+                  "(device durations from rocprofv3 are in profiles/)")
 EPS = 1e-6
 DECODE_WEIGHT_SETS = 4
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -301,6 +304,7 @@ def bench_decode(args):
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["weight_GBps"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": kernels[dom]["frac_hbm"], "traffic": None},
         "kernels": kernels,
+        "kernels_timing": KERNELS_TIMING,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
     }
     print(json.dumps(out), flush=True)
@@ -391,6 +395,7 @@ def bench_layers(args):
                      "frac": round(kernels[dom]["rate"] / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None},
         "gemm_only_TFLOPs": round(total_flops / (gemm_ms * 1e-3) / 1e12, 1),
         "kernels": kernels,
+        "kernels_timing": KERNELS_TIMING,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
     }
     print(json.dumps(out), flush=True)
@@ -478,6 +483,7 @@ def main():
                    "x_quant": "rmsnorm_quant", "seed": 1},
         "roofline": roof,
         "kernels": kernels,
+        "kernels_timing": KERNELS_TIMING,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
     }
     out["sclk_mhz"] = sustained_sclk(torch, steps)

@@ -553,3 +553,20 @@ def test_fprop_splitk_qwen32b_half_mlp_m256_down():
     assert jet.gemm_fprop_splitk_workspace_bytes(256, 5120, 12800) == 5 * 256 * 5120 * 4
     y = host(jet.gemm_fprop_splitk(qx, sx, qw, sw))
     check(y, oracle.gemm_fprop_ref(host(qx), host(sx), host(qw), host(sw)), "split-K fprop 32B down")
+
+
+def test_fprop_splitk_rows_independent_of_batch_with_the_same_shares():
+    """A row's split-K result depends only on that row and the share count: the
+    same rows in a 65-row and a 100-row batch (both one 128-row tile, 4 shares at
+    N = 384, K = 2048) are bitwise equal."""
+    n, k = 384, 2048
+    rng = np.random.default_rng(777)
+    qx, qw = codes(rng, (100, k)), codes(rng, (n, k))
+    sx, sw = scales(rng, (k // 128, 100)), scales(rng, (n // 128, k // 128))
+    assert jet.gemm_fprop_splitk_workspace_bytes(65, n, k) == 4 * 4 * 65 * n
+    assert jet.gemm_fprop_splitk_workspace_bytes(100, n, k) == 4 * 4 * 100 * n
+    qw_d, sw_d = u8_dev(qw), f32_dev(sw)
+    y65 = host(jet.gemm_fprop_splitk(u8_dev(qx[:65]), f32_dev(np.ascontiguousarray(sx[:, :65])), qw_d, sw_d))
+    y100 = host(jet.gemm_fprop_splitk(u8_dev(qx), f32_dev(sx), qw_d, sw_d))
+    assert np.array_equal(y65, y100[:65])
+    check(y100, oracle.gemm_fprop_ref(qx, sx, qw, sw), "split-K fprop 100 rows")

@@ -74,3 +74,56 @@ def test_step_replays_equal_eager():
         step()  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(dw32, g1 + g1)
+
+
+def test_rollout_step_with_split_k_replays_equal_eager():
+    """The rollout forward at a 64-token batch through gemm_fprop_splitk (K split
+    into shares with fp32 partials in a workspace, then the reduction: two launches
+    per projection, no memset) captured once and replayed with eager work in
+    between; every replay equals the eager result bit for bit."""
+    m, k, n_qkv, n_down, k_down = 64, 1024, 768, 256, 2048
+    dev = torch.device("cuda:0")
+    x = bf16_dev(synth.random_bf16((m, k), seed=41))
+    g = bf16_dev(synth.random_bf16((k,), seed=42, std=0.05)) + 1
+    h = bf16_dev(synth.random_bf16((m, k_down), seed=43))
+    wq = jet.quantize_weight_128x128(bf16_dev(synth.random_bf16((n_qkv, k), seed=44, std=0.02)))
+    wd = jet.quantize_weight_128x128(bf16_dev(synth.random_bf16((n_down, k_down), seed=45, std=0.02)))
+    need = max(jet.gemm_fprop_splitk_workspace_bytes(m, n_qkv, k),
+               jet.gemm_fprop_splitk_workspace_bytes(m, n_down, k_down))
+    assert jet.gemm_fprop_splitk_workspace_bytes(m, n_qkv, k) > 0
+    assert jet.gemm_fprop_splitk_workspace_bytes(m, n_down, k_down) > 0
+    ws = torch.empty(need // 4, dtype=torch.float32, device=dev)
+    qx, sx = jet.rmsnorm_quant(x, g, 1e-6)
+    qh, sh = jet.quantize_act_1x128(h)
+    y = torch.empty(m, n_qkv, dtype=torch.bfloat16, device=dev)
+    yd = torch.empty(m, n_down, dtype=torch.bfloat16, device=dev)
+
+    def step():
+        jet.rmsnorm_quant(x, g, 1e-6, qx, sx)
+        jet.gemm_fprop_splitk(qx, sx, *wq, y, ws)
+        jet.quantize_act_1x128(h, qh, sh)
+        jet.gemm_fprop_splitk(qh, sh, *wd, yd, ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [y.clone(), yd.clone()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        y.zero_()
+        yd.zero_()
+        ws.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref[0]) and torch.equal(yd, ref[1]), f"replay {rep}"
+        step()  # eager work between replays
+        torch.cuda.synchronize()

@@ -156,11 +156,12 @@ def test_rmsnorm_quant_decode_shapes(m):
     assert_same(host(s), so, "s")
 
 
-@pytest.mark.parametrize("m,k", [(8195, 4096), (8192, 2048)])
+@pytest.mark.parametrize("m,k", [(8195, 4096), (8192, 2048), (2049, 4096), (3000, 8192)])
 def test_rmsnorm_quant_training_batches_sampled(m, k):
-    """Training-size batches (8k rows, the bench shape and a ragged one): bit-exact
-    against the oracle on sampled rows -- the first and last 64, rows around
-    the middle, and random rows (rows are independent)."""
+    """Training-size batches (8k rows, the bench shape and a ragged one; 2049 and 3000
+    rows, which split unevenly over the eight XCDs' row ranges of the 2048-workgroup
+    grid): bit-exact against the oracle on sampled rows -- the first and last 64,
+    rows around the middle, and random rows (rows are independent)."""
     rng = np.random.default_rng(m + k)
     x = synth.random_bf16((m, k), seed=m + k, std=1.0)
     g = synth.f32_to_bf16_bits((1 + 0.05 * rng.standard_normal(k)).astype(np.float32))

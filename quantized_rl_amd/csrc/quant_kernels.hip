@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_split_kernel(const uint16_t
 #pragma unroll
   for (int j = 0; j < kQ; ++j) unpack_bf16x8(*reinterpret_cast<const uint4*>(gamma + e0 + 512 * j), g[j]);
 
-  // one row: reduce, normalise, quantise; `nxt` receives the loads of row + gridDim.x
+  // one row: reduce, normalise, quantise; `nxt` receives the loads of row + stride
   auto do_row = [&](int64_t row, int64_t end, int64_t stride, const uint4 (&cur)[kQ], uint4 (&nxt)[kQ],
                     int par) {
     float f[kQ][8];

@@ -140,11 +140,14 @@ def rmsnorm_f32(x_bf16, gamma_bf16, eps):
 
 def _rstd_f32(x, eps):
     k = x.shape[1]
-    sq = (x * x).astype(np.float32)
-    ss = pairwise_sum_f32(sq)
-    ms = (ss / np.float32(k)).astype(np.float32)
-    d = (ms + np.float32(eps)).astype(np.float32)
-    return (_ONE / np.sqrt(d)).astype(np.float32)  # correctly rounded sqrt, then a division
+    # fp32 arithmetic throughout: a square or a sum past the fp32 range is +inf
+    # (and the factor then 0), which numpy would otherwise report as a warning
+    with np.errstate(over="ignore"):
+        sq = (x * x).astype(np.float32)
+        ss = pairwise_sum_f32(sq)
+        ms = (ss / np.float32(k)).astype(np.float32)
+        d = (ms + np.float32(eps)).astype(np.float32)
+        return (_ONE / np.sqrt(d)).astype(np.float32)  # correctly rounded sqrt, then a division
 
 
 def rmsnorm_rstd_f32(x_bf16, eps):

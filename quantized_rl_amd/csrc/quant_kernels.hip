@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t* __
     const double inv = inv_scale(sc);
     const uint2 codes = quant8(f, inv);
     if (r < M && g_ok) {
-      st_stream8(q + r * K + col, codes);
+      st_global8(q + r * K + col, codes);
       if (lane16 == 0) s[g * M + r] = sc;
     }
   }
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void quant_weight_128x128_kernel(const uint16_
   for (int it = 0; it < 8; ++it) {
     float f[8];
     unpack_bf16x8(v[it], f);
-    st_stream8(qbase + (int64_t)(rsub + 16 * it) * K, quant8(f, inv));
+    st_global8(qbase + (int64_t)(rsub + 16 * it) * K, quant8(f, inv));
   }
   if (threadIdx.x == 0) s[nb * (K / kGroup) + kb] = sc;
 }
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(const uint16_t*
       const float amax = quarter_wave_max(absmax8(f));
       const float sc = scale_from_amax(amax);
       const double dinv = inv_scale(sc);
-      st_stream8(q + row * K + e, quant8(f, dinv));
+      st_global8(q + row * K + e, quant8(f, dinv));
       if (lane16 == 0) s[g * M + row] = sc;
     }
   }
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_split_kernel(const uint16_t
       for (int i = 0; i < 8; ++i) y[i] = (f[j][i] * inv) * g[j][i];
       const float amax = quarter_wave_max(absmax8(y));
       const float sc = scale_from_amax(amax);
-      st_stream8(q + row * K + e0 + 512 * j, quant8(y, inv_scale(sc)));
+      st_global8(q + row * K + e0 + 512 * j, quant8(y, inv_scale(sc)));
       const int64_t grp = 4 * (kQ * w + j) + quarter;
       if (lane16 == 0) s[grp * M + row] = sc;
     }
@@ -491,7 +491,7 @@ __global__ __launch_bounds__(256) void requant_transpose_kernel(const uint8_t* _
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int id = t + 256 * it, rr = id >> 3, ch = id & 7;
-    st_stream16(qt + (kg * kGroup + rr) * M + mb * kGroup + ch * 16,
+    st_global16(qt + (kg * kGroup + rr) * M + mb * kGroup + ch * 16,
                 *reinterpret_cast<const uint4*>(tile + rr * kRqPitch + ch * 16));
   }
 }

@@ -102,11 +102,12 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;      // raw buffer, 32-bit dwords
 // Cache-policy operand of a buffer store: nt (non-temporal, streaming).  The
 // large kernel's epilogue writes each output line once and nothing in the
 // kernel reads it back; every CU writes its 128 KB tile at about the same
-// moment, and each wave's next barrier waits for its stores to be taken.  In
-// the 8B training step (quantisers, FProp, DGrad, WGrad in turn) streaming
-// stores made DGrad 4 % faster, left WGrad unchanged and made FProp 3 %
-// slower, so only DGrad uses them.  (Timed alone, back to back, all three
-// gained 3-5 %; sc0 sc1, write-through, helped none but FProp.)
+// moment, and each wave's next barrier waits for its stores to be taken.
+// Streaming also keeps FProp's and DGrad's large outputs from displacing the
+// FP8 operands that the next GEMMs of the training step read from the caches:
+// in the 8B step, streaming stores in FProp and DGrad took it 1 % below plain
+// stores, while streaming WGrad's output as well gained nothing.  (Timed
+// alone, back to back, all three kernels ran 3-5 % faster with them.)
 constexpr int kStoreStream = 2;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -510,8 +511,8 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
       // bf16 epilogue, staged through stage 1 (free once the last block's
       // barrier has passed; stage 0 may already hold the next tile's first
       // block) in two halves of 128 rows with a row pitch of 512 + 16 bytes,
-      // then written with 16-byte buffer stores, streaming in DGrad (rows
-      // past M fall outside the buffer and are dropped)
+      // then written with 16-byte buffer stores, streaming in FProp and DGrad
+      // (rows past M fall outside the buffer and are dropped)
       constexpr int kPitch = kLBN * 2 + 16;
       static_assert(128 * kPitch == sizeof(LStage), "epilogue staging must fill one stage exactly");
       uint16_t* C = static_cast<uint16_t*>(Cv);
@@ -549,7 +550,7 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
           const uint4 v = *reinterpret_cast<const uint4*>(stage + r * kPitch + 16 * c16);
           const v4i_t d = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
           __builtin_amdgcn_raw_buffer_store_b128(d, rc, ((row0 + 128 * h + r) * N + col0 + 8 * c16) * 2u, 0,
-                                                 kMode == kDgrad ? kStoreStream : 0);
+                                                 kMode != kWgrad ? kStoreStream : 0);
         }
         __syncthreads();
       }

@@ -16,7 +16,10 @@ Definitions followed (page paper.rainbus.top/paper/2601.14243):
 Readings where the pages are silent (each is one numpy float32 operation, i.e.
 one IEEE-754 binary32 operation rounded to nearest even):
 
-* S = fl32(amax / 448) is a true division; S = 1 when amax == 0 (all codes 0);
+* S = fl32(amax / 448) is a true division; S = 1 when that quotient is 0, i.e.
+  when amax == 0 or amax <= 448 * 2^-150 (a nonzero amax so small that the fp32
+  quotient underflows to zero, which only requantised or RMSNorm'ed fp32 values
+  can reach); every code of such a group is then e4m3(x), a signed zero;
 * q = e4m3(fl32(x / S)) -- the quotient is rounded to fp32, then cast;
 * requantisation dequantises in fp32, v = fl32(decode(q) * S), then applies the
   same rule down each 128-token column;
@@ -47,10 +50,11 @@ def bf16_bits_to_f32(u):
 
 
 def _scale_from_amax(amax):
-    """S = amax / 448 in fp32 (true division); S = 1 where amax == 0."""
+    """S = amax / 448 in fp32 (true division); S = 1 where that quotient is zero
+    (amax == 0, or an amax that underflows when divided by 448)."""
     amax = np.asarray(amax, dtype=np.float32)
-    s = amax / _F448
-    return np.where(amax == np.float32(0.0), _ONE, s).astype(np.float32)
+    s = (amax / _F448).astype(np.float32)
+    return np.where(s == np.float32(0.0), _ONE, s).astype(np.float32)
 
 
 def _check_finite(x):
@@ -176,7 +180,7 @@ def requant_transpose_128x1(q, s):
 
     q: uint8 [M, K]; s: float32 [K // 128, M]; M % 128 == 0.
     v[m, k] = fl32(decode(q[m, k]) * s[k // 128, m]); then for every column k and
-    128-row block mb: S' = amax / 448 (1 if amax == 0) and q' = e4m3(fl32(v / S')).
+    128-row block mb: S' = amax / 448 (1 if that quotient is 0) and q' = e4m3(fl32(v / S')).
     Returns (qt uint8 [K, M], st float32 [M // 128, K]) -- q' stored transposed,
     so each 128x1 group is contiguous.
     """

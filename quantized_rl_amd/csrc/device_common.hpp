@@ -22,8 +22,9 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // high 16 bits of `old`.  Rounding is nearest-even; the explicit clamp to
 // +-448 gives saturation (the hardware conversion alone turns values of 480 and
 // above into NaN).  On gfx950 v_cvt_pk_fp8_f32 of a value in [-448, 448] equals
-// the nearest-even E4M3 code, sign of zero and fp32 subnormals included; this
-// was checked exhaustively over every non-NaN fp32 bit pattern.
+// the nearest-even E4M3 code, sign of zero and fp32 subnormals included: the
+// GPU test tests/test_gpu_casts.py compares this function with an integer
+// definition of the cast on every non-NaN fp32 bit pattern.
 __device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old, bool hi_half) {
   a = __builtin_amdgcn_fmed3f(a, -kE4M3Max, kE4M3Max);
   b = __builtin_amdgcn_fmed3f(b, -kE4M3Max, kE4M3Max);
@@ -32,9 +33,13 @@ __device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old, bool hi_ha
 }
 
 // S = amax / 448 rounded as the IEEE fp32 division (amax_over_448, exact for
-// every non-negative finite amax); S = 1 for an all-zero group.
+// every non-negative finite amax); S = 1 when that quotient is zero: an
+// all-zero group, or a nonzero amax of at most 448 * 2^-150 whose quotient
+// underflows (reachable only from fp32 inputs: requantised or normalised
+// values).  With S = 1 every code of such a group is e4m3(x), a signed zero.
 __device__ __forceinline__ float scale_from_amax(float amax) {
-  return amax == 0.0f ? 1.0f : amax_over_448(amax);
+  const float s = amax_over_448(amax);
+  return s == 0.0f ? 1.0f : s;
 }
 
 // 1 / S in fp64 within one ulp, for the quotient fl32(fl64(x * (1 / S))):

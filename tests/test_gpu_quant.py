@@ -226,6 +226,15 @@ def test_requant_pipeline_linear_8b_up():
             assert_same(st[mb], sto[0], f"{name} st block {mb}")
 
 
+def test_requant_underflowing_scale():
+    """A column whose amax / 448 underflows to zero takes S' = 1 (hand-derived case)."""
+    from test_oracle_quant import underflow_scale_case
+    q, s, want_qt, want_st = underflow_scale_case()
+    qt, st = requant_gpu(q, s)
+    assert np.array_equal(qt, want_qt)
+    assert np.array_equal(st.view(np.uint32), want_st.view(np.uint32))
+
+
 def test_requant_guards():
     rng = np.random.default_rng(9)
     q = rng.integers(0, 0x7E, size=(256, 256)).astype(np.uint8)

@@ -235,6 +235,115 @@ def test_rmsnorm_quant_composition_and_zero_row():
     assert np.all(q[2] == 0) and np.all(s[:, 2] == 1.0)
 
 
+def _f32_bits(a):
+    return int(np.asarray(a, np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("case", golden_io.rmsnorm_cases(), ids=lambda c: c["name"])
+def test_rmsnorm_golden_row(case):
+    """A hand-derived row (tests/golden/rmsnorm_cases.txt) whose codes depend on the
+    order of the two multiplies; placed as row 1 of 3 to pin the scale layout."""
+    k = case["K"]
+    rng = np.random.default_rng(21)
+    x = rand_f32(rng, (3, k), heavy=False)
+    x[1] = np.array(case["x"], np.float32)
+    g = np.array(case["gamma"], np.float32)
+    q, s = oracle.rmsnorm_quant(bf16(x), bf16(g), case["eps"])
+    assert s.shape == (k // 128, 3)
+    assert _f32_bits(s[0, 1]) == case["S_bits"]
+    assert list(q[1]) == case["q"]
+    assert _f32_bits(oracle.rmsnorm_rstd_f32(bf16(x), case["eps"])[1]) == case["rstd_bits"]
+    # the exact evaluation agrees, and the other multiplication order does not
+    inv, groups = exact.rmsnorm_row_exact(case["x"], case["gamma"], case["eps"])
+    assert exact.f32_bits(float(inv)) == case["rstd_bits"] and groups[0][1] == case["q"]
+    y_swapped = (x[1] * (oracle.rmsnorm_rstd_f32(bf16(x), case["eps"])[1] * g).astype(np.float32)).astype(np.float32)
+    q_sw, _ = oracle.quant_act_1x128_f32(y_swapped[None, :])
+    assert list(q_sw[0]) == case["q_swapped"] != case["q"]
+
+
+def _rmsnorm_rows(k, n, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, k)).astype(np.float32)
+    x[:, rng.integers(0, k, size=max(1, k // 1000))] *= np.float32(50)
+    x[n - 1] *= np.float32(2.0 ** -20)  # a row of tiny values: eps dominates d
+    g = (1 + 0.05 * rng.standard_normal(k)).astype(np.float32)
+    g[:3] = -g[:3]
+    return f32_to_bf16_bits(x), f32_to_bf16_bits(g)
+
+
+def _rmsnorm_variant(xb, gb, eps, variant):
+    """The oracle's fp32 chain with one planted mistake (test-only re-statement)."""
+    x, g = oracle.bf16_bits_to_f32(xb), oracle.bf16_bits_to_f32(gb)
+    k = x.shape[1]
+    sq = (x * x).astype(np.float32)
+    if variant == "left_to_right_sum":
+        ss = np.zeros(x.shape[0], np.float32)
+        for j in range(k):
+            ss = (ss + sq[:, j]).astype(np.float32)
+    else:
+        ss = oracle.pairwise_sum_f32(sq)
+    if variant == "times_reciprocal_of_k":
+        ms = (ss * np.float32(1.0 / k)).astype(np.float32)
+    else:
+        ms = (ss / np.float32(k)).astype(np.float32)
+    d = (ms + np.float32(eps)).astype(np.float32)
+    if variant == "rsqrt_once":
+        inv = (1.0 / np.sqrt(d.astype(np.float64))).astype(np.float32)
+    else:
+        inv = (np.float32(1) / np.sqrt(d)).astype(np.float32)
+    if variant == "inv_times_gamma_first":
+        y = (x * (inv[:, None] * g[None, :]).astype(np.float32)).astype(np.float32)
+    else:
+        y = ((x * inv[:, None]).astype(np.float32) * g[None, :]).astype(np.float32)
+    q, s = oracle.quant_act_1x128_f32(y)
+    return inv, q, s
+
+
+RMS_VARIANTS = ("left_to_right_sum", "times_reciprocal_of_k", "rsqrt_once", "inv_times_gamma_first")
+
+
+@pytest.mark.parametrize("k", [128, 640, 4096, 5120])
+def test_rmsnorm_matches_exact_chain(k):
+    """Bit-level pin of rmsnorm_quant: codes, scales and the row factor equal an
+    exact-rational evaluation of the same chain with every fp32 rounding explicit.
+
+    The rows checked are the first three of a seeded pool plus, for each plausible
+    slip in the chain, up to two pool rows on which a test-only copy with that slip
+    planted disagrees with the oracle.  The exact evaluation then shows that the
+    oracle is right on those rows, so none of the slips can hide in it."""
+    pool = 48
+    xb, gb = _rmsnorm_rows(k, pool, seed=k + 5)
+    eps = 1e-6
+    q, s = oracle.rmsnorm_quant(xb, gb, eps)
+    rstd = oracle.rmsnorm_rstd_f32(xb, eps)
+    rows, exposing = [0, 1, 2, pool - 1], {}
+    for variant in RMS_VARIANTS:
+        inv_v, q_v, s_v = _rmsnorm_variant(xb, gb, eps, variant)
+        bad = np.nonzero((inv_v.view(np.uint32) != rstd.view(np.uint32)) | np.any(q_v != q, axis=1)
+                         | np.any(s_v.view(np.uint32) != s.view(np.uint32), axis=0))[0]
+        exposing[variant] = [int(r) for r in bad[:2]]
+        rows += exposing[variant]
+    if k & (k - 1) == 0:
+        # ss / K equals ss * (1 / K) when K is a power of two
+        assert not exposing["times_reciprocal_of_k"]
+        del exposing["times_reciprocal_of_k"]
+    assert all(exposing.values()), exposing
+    xs, gs = oracle.bf16_bits_to_f32(xb), oracle.bf16_bits_to_f32(gb)
+    for r in sorted(set(rows)):
+        inv, groups = exact.rmsnorm_row_exact([float(v) for v in xs[r]], [float(v) for v in gs], eps)
+        assert exact.f32_bits(float(rstd[r])) == exact.f32_bits(float(inv)), f"row {r}: rstd"
+        assert [exact.f32_bits(float(v)) for v in s[:, r]] == [exact.f32_bits(float(sg)) for sg, _ in groups], \
+            f"row {r}: scales"
+        assert list(q[r]) == [c for _, codes in groups for c in codes], f"row {r}: codes"
+
+
+def test_exact_sqrt_helper():
+    # the exact evaluator's square root against the library's correctly rounded one
+    rng = np.random.default_rng(4)
+    for v in rng.uniform(1e-7, 1e4, 500).astype(np.float32):
+        assert float(exact.rn_sqrt_f32(Fraction(float(v)))) == float(np.sqrt(v))
+
+
 # ---------------------------------------------------------------- requant 1x128 -> 128x1
 
 def test_requant_closed_form():
@@ -251,6 +360,48 @@ def test_requant_closed_form():
     want = np.array([0x7E, 0x76, 0x6E, 0x66], np.uint8)[np.arange(m) % 4]
     assert np.array_equal(qt[0::2], np.tile(want, (k // 2, 1)))
     assert np.array_equal(qt[1::2], np.tile(want | 0x80, (k // 2, 1)))
+
+
+def underflow_scale_case():
+    """Requant input whose column amax / 448 underflows to zero (hand-derived).
+
+    Rows 0..127 carry the smallest fp32 subnormal, 2^-149, as their 1x128 scale;
+    codes 1.0 (0x38), -1.0 (0xb8), 224 (0x76) and 240 (0x77) give exact values
+    v = c * 2^-149.  Column 0: amax = 224 * 2^-149, amax / 448 = 2^-150 exactly,
+    half the smallest subnormal, which rounds to the even neighbour 0: S' = 1 by
+    the zero-quotient rule, and every code is e4m3(v) = a zero of v's sign.
+    Column 1: amax = 240 * 2^-149, amax / 448 = (15/28) 2^-149 rounds up to
+    2^-149 = S', and v / S' = c gives back the codes.  Rows 128..255: scale 1 and
+    code 1.0 everywhere (S' = fl32(1/448), codes 0x7e); other columns are zero
+    (S' = 1, codes 00)."""
+    m, k = 256, 128
+    q = np.zeros((m, k), np.uint8)
+    q[:64, :2] = 0x38
+    q[64:127, :2] = 0xB8
+    q[127, 0], q[127, 1] = 0x76, 0x77
+    q[128:, :] = 0x38
+    s = np.ones((1, m), np.float32)
+    s[0, :128] = np.float32(2.0 ** -149)
+    want_qt = np.zeros((k, m), np.uint8)
+    want_st = np.ones((2, k), np.float32)
+    want_qt[0, 64:127] = 0x80
+    want_qt[1, :64], want_qt[1, 64:127], want_qt[1, 127] = 0x38, 0xB8, 0x77
+    want_st[0, 1] = np.float32(2.0 ** -149)
+    want_qt[:, 128:] = 0x7E
+    want_st[1, :] = np.float32(Fraction(1, 448))
+    return q, s, want_qt, want_st
+
+
+def test_requant_underflowing_scale():
+    q, s, want_qt, want_st = underflow_scale_case()
+    qt, st = oracle.requant_transpose_128x1(q, s)
+    assert np.array_equal(qt, want_qt)
+    assert np.array_equal(st.view(np.uint32), want_st.view(np.uint32))
+    # the exact evaluation of column 0 reaches the same rule
+    v = [float(exact.rn_f32(exact.decode(int(q[r, 0])) * Fraction(2) ** -149)) for r in range(128)]
+    vs = [math.copysign(a, -1.0 if q[r, 0] & 0x80 else 1.0) for r, a in enumerate(v)]
+    S, codes = exact.quant_group(vs)
+    assert S == 1 and codes == list(want_qt[0, :128])
 
 
 def test_requant_matches_exact_fractions():

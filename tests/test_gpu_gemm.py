@@ -173,6 +173,27 @@ def test_wgrad_random(m, n, k):
     check(host(dg.t), oracle.gemm_wgrad_ref(qdyt, sdyt, qxt, sxt), f"wgrad {m}x{n}x{k}")
 
 
+# full-range codes: every finite E4M3 code equally likely (the widest spread of
+# product magnitudes inside a 128-deep block); output sizes of 51k..16.8M
+# elements, on the 128 x 128 kernel and (the last shape of each) the 256 x 256 one
+@pytest.mark.parametrize("m,n,k", [(256, 512, 384), (200, 1024, 256), (4096, 256, 4096)])
+def test_dgrad_full_range_codes(m, n, k):
+    rng = np.random.default_rng(m + 3 * n + k)
+    qdy, qw = codes(rng, (m, n), full_range=True), codes(rng, (n, k), full_range=True)
+    sdy, sw = scales(rng, (n // 128, m)), scales(rng, (n // 128, k // 128))
+    dx = host(jet.gemm_dgrad(u8_dev(qdy), f32_dev(sdy), u8_dev(qw), f32_dev(sw)))
+    check(dx, oracle.gemm_dgrad_ref(qdy, sdy, qw, sw), f"dgrad full-range {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(512, 256, 384), (1024, 256, 256), (256, 4096, 4096)])
+def test_wgrad_full_range_codes(m, n, k):
+    rng = np.random.default_rng(5 * m + n + k)
+    qdyt, qxt = codes(rng, (n, m), full_range=True), codes(rng, (k, m), full_range=True)
+    sdyt, sxt = scales(rng, (m // 128, n)), scales(rng, (m // 128, k))
+    dw = host(jet.gemm_wgrad(u8_dev(qdyt), f32_dev(sdyt), u8_dev(qxt), f32_dev(sxt)))
+    check(dw, oracle.gemm_wgrad_ref(qdyt, sdyt, qxt, sxt), f"wgrad full-range {m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("m,n,k", [(256, 256, 384), (384, 256, 512)])
 def test_wgrad_exact_integer(m, n, k):
     rng = np.random.default_rng(12 + m + k)

@@ -108,7 +108,7 @@ int rmsnorm_quant_rstd(const uint16_t* x, const uint16_t* gamma, int64_t M, int6
 }
 
 int64_t rmsnorm_backward_workspace_bytes(int64_t M, int64_t K) {
-  if (!dim_ok(M) || K <= 0 || K > 6144 || K % 128) return -1;
+  if (!dim_ok(M) || K <= 0 || K > 24576 || K % 128) return -1;
   return 4 * jetfp8::rmsnorm_backward_parts(M) * K;
 }
 

@@ -12,13 +12,14 @@
 // the formulas are calculus on the standard RMSNorm.
 //
 // Both are HBM-bound: x and dy are read once, dx written once.
-//   rmsnorm_backward_rows_kernel: a workgroup of 4 waves owns R consecutive
-//     rows (R = 2 ceil(M / 512) clamped to 1..32) and walks them one at a time,
-//     all four waves on the same row: wave w covers the 512-element passes
-//     w, w + 4, ... (lane l: the 8 elements at 512 p + 8 l), so a lane holds
-//     only K / 256 of the row and the next row's loads are issued before the
-//     current row is finished.  S is each wave's lane-sequential sum and
-//     butterfly, the four wave sums added in wave order through LDS.  A wave
+//   rmsnorm_backward_rows_kernel: a workgroup of W waves (4 up to K = 6144,
+//     8 up to 12288, 16 up to 24576) owns R consecutive rows (R = 2 ceil(M /
+//     512) clamped to 1..32) and walks them one at a time, all its waves on the
+//     same row: wave w covers the 512-element passes w, w + W, ... (lane l: the
+//     8 elements at 512 p + 8 l), so a lane holds at most three passes of the
+//     row and the next row's loads are issued before the current row is
+//     finished.  S is each wave's lane-sequential sum and butterfly, the W wave
+//     sums added in wave order through LDS.  A wave
 //     keeps its columns' dgamma terms in registers, summed in row order, and
 //     writes them as its part of the workgroup's partial row of dgamma.
 //   rmsnorm_dgamma_reduce_kernel: dgamma_k = the partials summed in a fixed
@@ -29,7 +30,7 @@
 
 namespace jetfp8 {
 
-constexpr int kBwdMaxPasses = 12;  // K <= 6144: at most 3 passes per wave
+constexpr int kBwdMaxPasses = 48;  // K <= 24576: 16 waves of at most 3 passes
 
 // Rows per workgroup: 2 ceil(M / 512) clamped to 1..32 (measured best of
 // 1..8, 1..16 and 1..32 at M = 256 .. 16384).
@@ -50,16 +51,16 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&f)[8]) {
                     f32_to_bf16_rne(f[6]) | (f32_to_bf16_rne(f[7]) << 16));
 }
 
-// kQ: passes per wave (ceil(ceil(K / 512) / 4)).
-template <int kQ>
-__global__ __launch_bounds__(256) void rmsnorm_backward_rows_kernel(const uint16_t* __restrict__ x,
+// kQ: passes per wave (ceil(ceil(K / 512) / kW)); kW: waves per workgroup.
+template <int kQ, int kW>
+__global__ __launch_bounds__(64 * kW) void rmsnorm_backward_rows_kernel(const uint16_t* __restrict__ x,
                                                                     const uint16_t* __restrict__ gamma,
                                                                     const float* __restrict__ rstd,
                                                                     const uint16_t* __restrict__ dy,
                                                                     int64_t M, int64_t K, int rows_per_group,
                                                                     uint16_t* __restrict__ dx,
                                                                     float* __restrict__ part) {
-  __shared__ float wsum[2][4];
+  __shared__ float wsum[2][kW];
   const int t = threadIdx.x, l = t & 63, w = t >> 6;
   const int64_t row0 = (int64_t)blockIdx.x * rows_per_group;
   const int64_t rows = (M - row0) < rows_per_group ? (M - row0) : rows_per_group;
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(256) void rmsnorm_backward_rows_kernel(const uint16
   bool in[kQ];
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
-    e[q] = 512 * (int64_t)(w + 4 * q) + 8 * l;
+    e[q] = 512 * (int64_t)(w + kW * q) + 8 * l;
     in[q] = e[q] < K;
   }
   float fg[kQ][8], u[kQ][8];
@@ -105,7 +106,10 @@ __global__ __launch_bounds__(256) void rmsnorm_backward_rows_kernel(const uint16
     const float ws = wave_sum_tree(sl);
     if (l == 0) wsum[r & 1][w] = ws;
     __syncthreads();
-    const float c = (((wsum[r & 1][0] + wsum[r & 1][1]) + wsum[r & 1][2]) + wsum[r & 1][3]) / (float)K;
+    float ssum = wsum[r & 1][0];
+#pragma unroll
+    for (int v = 1; v < kW; ++v) ssum = ssum + wsum[r & 1][v];
+    const float c = ssum / (float)K;
     const float rc = (rr * rr) * c;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
@@ -148,11 +152,22 @@ __global__ __launch_bounds__(256) void rmsnorm_dgamma_reduce_kernel(const float*
   if (w == 0 && k < K) dgamma[k] = ((q[0][c] + q[1][c]) + q[2][c]) + q[3][c];
 }
 
-template <int kQ>
+template <int kQ, int kW>
 static void launch_bwd_rows(const uint16_t* x, const uint16_t* gamma, const float* rstd, const uint16_t* dy,
                             int64_t M, int64_t K, uint16_t* dx, float* part, hipStream_t stream) {
-  hipLaunchKernelGGL(rmsnorm_backward_rows_kernel<kQ>, dim3((unsigned)rmsnorm_backward_parts(M)), dim3(256), 0,
-                     stream, x, gamma, rstd, dy, M, K, (int)bwd_rows_per_group(M), dx, part);
+  hipLaunchKernelGGL((rmsnorm_backward_rows_kernel<kQ, kW>), dim3((unsigned)rmsnorm_backward_parts(M)),
+                     dim3(64 * kW), 0, stream, x, gamma, rstd, dy, M, K, (int)bwd_rows_per_group(M), dx, part);
+}
+
+template <int kW>
+static void launch_bwd_rows_w(const uint16_t* x, const uint16_t* gamma, const float* rstd, const uint16_t* dy,
+                              int64_t M, int64_t K, uint16_t* dx, float* part, hipStream_t stream) {
+  const int64_t passes = (K + 511) / 512;
+  switch ((passes + kW - 1) / kW) {
+    case 1: launch_bwd_rows<1, kW>(x, gamma, rstd, dy, M, K, dx, part, stream); break;
+    case 2: launch_bwd_rows<2, kW>(x, gamma, rstd, dy, M, K, dx, part, stream); break;
+    default: launch_bwd_rows<3, kW>(x, gamma, rstd, dy, M, K, dx, part, stream); break;
+  }
 }
 
 hipError_t launch_rmsnorm_backward(const uint16_t* x, const uint16_t* gamma, const float* rstd,
@@ -161,12 +176,13 @@ hipError_t launch_rmsnorm_backward(const uint16_t* x, const uint16_t* gamma, con
   if (K == 0) return hipSuccess;
   const int64_t nparts = rmsnorm_backward_parts(M);
   if (M > 0) {
-    const int64_t passes = (K + 511) / 512;
-    switch ((passes + 3) / 4) {
-      case 1: launch_bwd_rows<1>(x, gamma, rstd, dy, M, K, dx, workspace, stream); break;
-      case 2: launch_bwd_rows<2>(x, gamma, rstd, dy, M, K, dx, workspace, stream); break;
-      default: launch_bwd_rows<3>(x, gamma, rstd, dy, M, K, dx, workspace, stream); break;
-    }
+    const int64_t passes = (K + 511) / 512;  // at most kBwdMaxPasses (the API checks K)
+    if (passes <= 12)
+      launch_bwd_rows_w<4>(x, gamma, rstd, dy, M, K, dx, workspace, stream);
+    else if (passes <= 24)
+      launch_bwd_rows_w<8>(x, gamma, rstd, dy, M, K, dx, workspace, stream);
+    else
+      launch_bwd_rows_w<16>(x, gamma, rstd, dy, M, K, dx, workspace, stream);
   }
   hipLaunchKernelGGL(rmsnorm_dgamma_reduce_kernel, dim3((unsigned)((K + 63) / 64)), dim3(256), 0, stream,
                      workspace, nparts, K, dgamma);

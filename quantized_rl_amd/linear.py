@@ -16,23 +16,56 @@ and allocates outputs through torch.  The token count M must be a multiple of
 Optionally the weight gradient is kept in fp32 (``gemm_wgrad_f32``): each
 backward adds its dW to an fp32 buffer, so the gradients of several
 micro-batches are summed before any rounding to bf16.
+
+The modules quantise their weight once per weight version (the unified flow of
+the pages' "核心方法" section: one FP8 weight per update, shared by every
+forward, rollout or training, and by the backward's DGrad): ``WeightCache``
+keeps the 128x128 FP8 form and re-quantises only when the parameter's storage
+or its in-place version counter changes.
 """
 
 import torch
 
 from . import _lib
 
+# widest row the RMSNorm backward kernel takes (rmsnorm_backward_workspace_bytes)
+RMSNORM_BACKWARD_MAX_K = 24576
+
+
+class WeightCache:
+    """The FP8 form (quantize_weight_128x128) of one bf16 weight, kept until the
+    weight changes: its storage (a new tensor), shape or version counter (any
+    in-place update, e.g. an optimizer step).  ``quantizations`` counts the calls
+    to the quantiser."""
+
+    def __init__(self):
+        self.key = None
+        self.q = self.s = None
+        self.quantizations = 0
+
+    def get(self, w):
+        key = (w.data_ptr(), tuple(w.shape), w.device, w._version)
+        if key != self.key:
+            self.q, self.s = _lib.quantize_weight_128x128(w.detach().contiguous())
+            self.quantizations += 1
+            self.key = key
+        return self.q, self.s
+
 
 class FP8LinearFunction(torch.autograd.Function):
     """y = x w^T with the mixed-granularity FP8 recipe.  x bf16 [M, K], w bf16 [N, K].
 
     With ``dw_fp32`` (a float32 [N, K] buffer) the backward adds the weight
-    gradient to that buffer in fp32 and returns no gradient for ``w``."""
+    gradient to that buffer in fp32 and returns no gradient for ``w``.  With a
+    ``WeightCache`` the weight is quantised only when it has changed."""
 
     @staticmethod
-    def forward(ctx, x, w, dw_fp32=None):
+    def forward(ctx, x, w, dw_fp32=None, wcache=None):
         qx, sx = _lib.quantize_act_1x128(x.contiguous())
-        qw, sw = _lib.quantize_weight_128x128(w.contiguous())
+        if wcache is not None:
+            qw, sw = wcache.get(w)
+        else:
+            qw, sw = _lib.quantize_weight_128x128(w.contiguous())
         y = _lib.gemm_fprop(qx, sx, qw, sw)
         ctx.save_for_backward(qx, sx, qw, sw)
         ctx.dw_fp32 = dw_fp32
@@ -42,7 +75,7 @@ class FP8LinearFunction(torch.autograd.Function):
     def backward(ctx, dy):
         qx, sx, qw, sw = ctx.saved_tensors
         dx, dw = fp8_linear_backward(dy, qx, sx, qw, sw, dw_fp32=ctx.dw_fp32)
-        return dx, dw, None
+        return dx, dw, None, None
 
 
 def fp8_linear_backward(dy, qx, sx, qw, sw, dw_fp32=None):
@@ -62,9 +95,9 @@ def fp8_linear_backward(dy, qx, sx, qw, sw, dw_fp32=None):
     return dx, dw
 
 
-def fp8_linear(x, w, dw_fp32=None):
+def fp8_linear(x, w, dw_fp32=None, wcache=None):
     """Functional form of :class:`FP8LinearFunction`."""
-    return FP8LinearFunction.apply(x, w, dw_fp32)
+    return FP8LinearFunction.apply(x, w, dw_fp32, wcache)
 
 
 class FP8Linear(torch.nn.Module):
@@ -88,6 +121,7 @@ class FP8Linear(torch.nn.Module):
             torch.zeros(out_features, in_features, dtype=torch.float32, device=device)
             if fp32_grad_accum else None,
             persistent=False)
+        self.wcache = WeightCache()
 
     def zero_main_grad(self):
         if self.main_grad is not None:
@@ -95,7 +129,7 @@ class FP8Linear(torch.nn.Module):
 
     def forward(self, x):
         shape = x.shape
-        y = fp8_linear(x.reshape(-1, shape[-1]), self.weight, self.main_grad)
+        y = fp8_linear(x.reshape(-1, shape[-1]), self.weight, self.main_grad, self.wcache)
         return y.reshape(*shape[:-1], self.weight.shape[0])
 
 
@@ -106,10 +140,10 @@ class RMSNormFP8LinearFunction(torch.autograd.Function):
     (for the norm's gradients) and the FP8 operands of the GEMMs."""
 
     @staticmethod
-    def forward(ctx, x, gamma, w, eps):
+    def forward(ctx, x, gamma, w, eps, wcache=None):
         x = x.contiguous()
         qx, sx, rstd = _lib.rmsnorm_quant_rstd(x, gamma.contiguous(), eps)
-        qw, sw = _lib.quantize_weight_128x128(w.contiguous())
+        qw, sw = wcache.get(w) if wcache is not None else _lib.quantize_weight_128x128(w.contiguous())
         y = _lib.gemm_fprop(qx, sx, qw, sw)
         ctx.save_for_backward(x, gamma, rstd, qx, sx, qw, sw)
         return y
@@ -120,7 +154,7 @@ class RMSNormFP8LinearFunction(torch.autograd.Function):
         dxn, dw = fp8_linear_backward(dy, qx, sx, qw, sw)
         dx, dgamma = _lib.rmsnorm_backward(x, gamma.contiguous(), rstd, dxn)
         # gamma's gradient is computed in fp32; the parameter's dtype is bf16
-        return dx, dgamma.to(gamma.dtype), dw, None
+        return dx, dgamma.to(gamma.dtype), dw, None, None
 
 
 class RMSNormFP8Linear(torch.nn.Module):
@@ -131,15 +165,20 @@ class RMSNormFP8Linear(torch.nn.Module):
         super().__init__()
         if in_features % 128 or out_features % 128:
             raise ValueError("in_features and out_features must be multiples of 128")
+        if in_features > RMSNORM_BACKWARD_MAX_K:
+            raise ValueError(f"in_features={in_features}: the RMSNorm backward takes rows of at most "
+                             f"{RMSNORM_BACKWARD_MAX_K} elements")
         self.eps = float(eps)
         self.gamma = torch.nn.Parameter(torch.ones(in_features, dtype=torch.bfloat16, device=device))
         self.weight = torch.nn.Parameter(
             torch.empty(out_features, in_features, dtype=torch.bfloat16, device=device))
         torch.nn.init.normal_(self.weight, std=0.02)
+        self.wcache = WeightCache()
 
     def forward(self, x):
         shape = x.shape
-        y = RMSNormFP8LinearFunction.apply(x.reshape(-1, shape[-1]), self.gamma, self.weight, self.eps)
+        y = RMSNormFP8LinearFunction.apply(x.reshape(-1, shape[-1]), self.gamma, self.weight, self.eps,
+                                           self.wcache)
         return y.reshape(*shape[:-1], self.weight.shape[0])
 
 

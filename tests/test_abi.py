@@ -145,10 +145,10 @@ def test_rmsnorm_rstd_and_backward_validation(jetlib):
     # one row of K floats per workgroup of R rows, R = 2 ceil(M / 512) in 1..32
     assert ws(8192, 4096) == 4 * 256 * 4096 and ws(1, 128) == 4 * 128 and ws(0, 128) == 0
     assert ws(256, 4096) == 4 * 128 * 4096 and ws(2000, 128) == 4 * 250 * 128 and ws(65536, 128) == 4 * 2048 * 128
-    assert ws(4, 100) == -1 and ws(4, 6144 + 128) == -1 and ws(-1, 128) == -1
+    assert ws(4, 100) == -1 and ws(4, 24576 + 128) == -1 and ws(-1, 128) == -1 and ws(4, 24576) > 0
     b = "rmsnorm_backward"
     # (x, gamma, rstd, dy, M, K, dx, dgamma, workspace)
-    assert c(b, P[0], P[1], P[2], P[3], 4, 6272, P[4], P[5], P[6], 0) == EINVAL  # K > 6144
+    assert c(b, P[0], P[1], P[2], P[3], 4, 24704, P[4], P[5], P[6], 0) == EINVAL  # K > 24576
     assert c(b, P[0], P[1], P[2], P[3], 4, 128, P[4], P[5], 0, 0) == ENULL      # workspace missing
     assert c(b, P[0], P[1], P[2], P[3], 4, 128, P[4], P[5], P[4] + 512, 0) == EALIAS  # workspace over dx
     assert c(b, P[0], P[1], P[2], P[3], 4, 128, P[3], P[5], P[6], 0) == EALIAS  # dx over dy

@@ -178,3 +178,33 @@ def test_four_layer_fp8_stack_trains_and_chains_the_layers():
             for p in stack.parameters():
                 p -= (2.0 * p.grad.float()).to(p.dtype)
     assert loss_of(stack(x.detach())).item() < loss0.item()
+
+
+def test_weight_quantised_once_per_update(monkeypatch):
+    """Two forwards with no weight update launch one weight quantisation and give
+    bitwise-equal outputs; an optimizer step (in place) triggers a new one, whose
+    codes equal a fresh quantisation of the updated weight."""
+    calls = []
+    real = _lib.quantize_weight_128x128
+
+    def counting(w, *a, **kw):
+        calls.append(1)
+        return real(w, *a, **kw)
+
+    monkeypatch.setattr(_lib, "quantize_weight_128x128", counting)
+    torch.manual_seed(3)
+    for mod in (linear.FP8Linear(512, 384, device="cuda:0"), linear.RMSNormFP8Linear(512, 384, device="cuda:0")):
+        calls.clear()
+        x = torch.randn(256, 512, device="cuda:0").to(torch.bfloat16)
+        y1 = mod(x)
+        y2 = mod(x)
+        torch.cuda.synchronize()
+        assert len(calls) == 1
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+        y2.float().sum().backward()
+        torch.optim.SGD(mod.parameters(), lr=10.0).step()
+        y3 = mod(x)
+        torch.cuda.synchronize()
+        assert len(calls) == 2 and not torch.equal(y3.view(torch.int16), y1.view(torch.int16))
+        qw, sw = real(mod.weight.detach().contiguous())
+        assert torch.equal(mod.wcache.q, qw) and torch.equal(mod.wcache.s.view(torch.int32), sw.view(torch.int32))

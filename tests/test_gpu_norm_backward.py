@@ -54,8 +54,10 @@ def run_backward(x, g, dy):
 
 # ragged row counts (not a multiple of a workgroup's rows), K not a multiple of
 # 512 (a partial last pass) or of 2048 (waves with fewer passes), the 8B and 32B
-# hidden sizes
-@pytest.mark.parametrize("m,k", [(1, 128), (31, 384), (33, 640), (64, 4096), (100, 5120), (257, 6144), (1500, 2560)])
+# hidden sizes, and widths past 6144 (eight and sixteen waves per row, up to the
+# 24576 limit)
+@pytest.mark.parametrize("m,k", [(1, 128), (31, 384), (33, 640), (64, 4096), (100, 5120), (257, 6144), (1500, 2560),
+                                 (65, 6272), (40, 8192), (70, 12800), (9, 14336), (3, 24576)])
 def test_rmsnorm_backward_matches_oracle(m, k):
     print(f"[rmsnorm_backward] m={m} k={k}", flush=True)
     x = synth.random_bf16((m, k), seed=7 * m + k)

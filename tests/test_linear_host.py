@@ -41,3 +41,30 @@ def test_fp8_stack_shapes():
     assert [tuple(l.weight.shape) for l in st.layers] == [(1024, 512), (512, 1024), (768, 512), (384, 768)]
     with pytest.raises(ValueError):
         linear.FP8Stack([512], device="cpu")
+
+
+def test_rmsnorm_fp8_linear_rejects_rows_past_the_backward_limit():
+    linear.RMSNormFP8Linear(linear.RMSNORM_BACKWARD_MAX_K, 128, device="meta")
+    with pytest.raises(ValueError, match="RMSNorm backward"):
+        linear.RMSNormFP8Linear(linear.RMSNORM_BACKWARD_MAX_K + 128, 128, device="meta")
+
+
+def test_weight_cache_requantises_only_on_change(monkeypatch):
+    calls = []
+
+    def fake_quant(w):
+        calls.append(w.data_ptr())
+        return ("q", len(calls)), ("s", len(calls))
+
+    monkeypatch.setattr(linear._lib, "quantize_weight_128x128", fake_quant)
+    w = torch.zeros(128, 256, dtype=torch.bfloat16)
+    c = linear.WeightCache()
+    a = c.get(w)
+    assert c.get(w) is not None and c.get(w) == a and c.quantizations == 1   # unchanged: reused
+    with torch.no_grad():
+        w.add_(1)                                                              # in-place update
+    b = c.get(w)
+    assert b != a and c.quantizations == 2
+    w2 = w.clone()                                                             # another tensor
+    c.get(w2)
+    assert c.quantizations == 3 and calls[-1] == w2.data_ptr()

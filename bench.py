@@ -67,10 +67,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # The first few dozen steps of a fresh process run up to 5 % slower than the
-    # steady state (measured on the 8B step: 1.309 ms for steps 6-25, then
-    # 1.246-1.253 ms), so the timed steps start after 50 untimed ones.
-    ap.add_argument("--warmup", type=int, default=50)
+    # untimed steps after the settle period (which covers the power-management
+    # transient; see settle())
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="linear_8b_up",
                     choices=["linear_8b_up", "decode_8b", "llama_layer", "qwen32b_half_mlp"])
@@ -128,11 +127,12 @@ def measured_traffic(kernel):
 def cpu_baseline(d, gamma):
     """The oracle on a 256-token slice of the step (all rows of the path)."""
     import oracle
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
-        cores = len(os.sched_getaffinity(0))
+        blas_threads = None
     ms = 256
     x, dy = d["x"][:ms], d["dy"][:ms]
     t0 = time.perf_counter()
@@ -147,19 +147,53 @@ def cpu_baseline(d, gamma):
     dt = time.perf_counter() - t0
     flops = 3 * 2.0 * ms * N * K
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
+            "blas_threads": blas_threads, "kind": "oracle",
             "sample": f"one step on a {ms}-token slice (M={ms}, K={K}, N={N}): rmsnorm_quant, "
                       f"full weight quantisation, quant dY, requant x2, fp64 FProp/DGrad/WGrad; "
-                      f"{dt:.2f} s; quantisers single-threaded numpy, GEMMs numpy BLAS"}
+                      f"{dt:.2f} s; quantisers single-threaded numpy, GEMMs numpy BLAS "
+                      f"({blas_threads} threads) on the {cores} cores of the affinity mask"}
+
+
+SETTLE_S = 0.15
+
+
+def settle(torch, steps, seconds=SETTLE_S):
+    """Run the step back to back for `seconds` before the warm-up steps.
+
+    After an idle period the chip's power management takes some 20-30 ms of
+    sustained load to settle: measured on the 8B step, the first 20 steps after
+    0.3-0.5 s of idle averaged 1.28-1.48 ms (single steps up to 1.6 ms) against
+    1.13 ms later, whether or not the buffers had been used before, while after
+    0.28 s of unrelated bf16 matmul load the first steps already ran at 1.13-1.16
+    ms.  A training job runs its steps back to back, so the timed steps start
+    from that sustained state.  Returns the number of steps run."""
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _, fn in steps:
+            fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
+def settle_info(n):
+    return {"seconds": SETTLE_S, "steps": n,
+            "why": "before the warm-up steps, the step runs back to back for this long: after an idle "
+                   "period the chip's power management needs about 20-30 ms of sustained load to settle "
+                   "(first steps up to 35 % slower, independent of buffer first-touch)"}
 
 
 def time_steps(torch, steps, n_steps, n_warmup, dev):
-    """Run warm-up steps, then two timed passes of n_steps steps on the launch
+    """Run the settle period and the warm-up steps, then two timed passes of n_steps steps on the launch
     stream.  Pass 1 records a HIP event only at step boundaries: it gives the
     step times and the wall time.  Pass 2 records an event after every kernel:
     it gives the per-kernel times (those events put a small gap between the
     kernels, so pass 2's steps run slightly longer than pass 1's).  Returns
-    (per-kernel ms lists, per-step ms list, wall seconds of pass 1)."""
+    (per-kernel ms lists, per-step ms list, wall seconds of pass 1, settle steps)."""
+    n_settle = settle(torch, steps)
     for _ in range(n_warmup):
         for _, fn in steps:
             fn()
@@ -189,7 +223,7 @@ def time_steps(torch, steps, n_steps, n_warmup, dev):
     for s in range(n_steps):
         for i, (name, _) in enumerate(steps):
             per[name].append(ev[s][i].elapsed_time(ev[s][i + 1]))
-    return per, step_ms, wall
+    return per, step_ms, wall, n_settle
 
 
 def read_sclk_mhz():
@@ -280,7 +314,7 @@ def bench_decode(args):
         ("quantize_act_1x128", lambda: jet.quantize_act_1x128(h, qh, sh)),
         ("gemm_fprop_down", lambda: jet.gemm_fprop_splitk(qh, sh, *sets[cur[0]]["w_down"], y["w_down"], ws)),
     ]
-    per, step_ms, wall = time_steps(torch, steps, args.steps, args.warmup, dev)
+    per, step_ms, wall, n_settle = time_steps(torch, steps, args.steps, args.warmup, dev)
     ms_per_step = float(np.mean(step_ms))
     shapes = {"gemm_fprop_qkv": (6144, 4096), "gemm_fprop_gate_up": (24576, 4096), "gemm_fprop_down": (4096, 12288)}
     flops = sum(2.0 * m * n * k for n, k in shapes.values())
@@ -309,6 +343,7 @@ def bench_decode(args):
         "kernels": kernels,
         "kernels_timing": KERNELS_TIMING,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "settle": settle_info(n_settle),
     }
     print(json.dumps(out), flush=True)
 
@@ -376,7 +411,7 @@ def bench_layers(args):
             f"{name}.gemm_wgrad": ("TFLOP/s", g),
         })
     torch.cuda.synchronize()
-    per, step_ms, wall = time_steps(torch, steps, args.steps, args.warmup, dev)
+    per, step_ms, wall, n_settle = time_steps(torch, steps, args.steps, args.warmup, dev)
     ms_per_step = float(np.mean(step_ms))
     kernels = {}
     for name, (unit, amount) in work.items():
@@ -400,6 +435,7 @@ def bench_layers(args):
         "kernels": kernels,
         "kernels_timing": KERNELS_TIMING,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "settle": settle_info(n_settle),
     }
     print(json.dumps(out), flush=True)
 
@@ -459,7 +495,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    per, step_ms, wall = time_steps(torch, steps, args.steps, args.warmup, dev)
+    per, step_ms, wall, n_settle = time_steps(torch, steps, args.steps, args.warmup, dev)
     ms_per_step = float(np.mean(step_ms))
     work = kernel_work()
     gemm_flops = 3 * 2.0 * M * N * K
@@ -488,6 +524,7 @@ def main():
         "kernels": kernels,
         "kernels_timing": KERNELS_TIMING,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "settle": settle_info(n_settle),
     }
     out["sclk_mhz"] = sustained_sclk(torch, steps)
     if not args.no_cpu_baseline:

@@ -52,6 +52,25 @@ def check(y, ref, what, rms=None):
     return r
 
 
+def check_full_range(y, ref, absref, what):
+    """Acceptance for arbitrary (full-range) codes.  The FP8 matrix instruction
+    sums each 32-product slice with reduced precision: a product below about
+    2^-14 of the slice's largest can be lost, at most 31 of them per slice, so a
+    slice's error stays below 2^-9 of its largest product and an output's below
+    2^-9 * sum_k |a_k b_k| (absref, the product of the dequantised magnitudes).
+    Where large products cancel, that exceeds 1e-3 rms; the normwise bound holds
+    regardless."""
+    r = oracle.check_gemm(y, ref)
+    assert r["normwise"] <= 1e-3, f"{what}: {r}"
+    yv = oracle.bf16_bits_to_f32(y).astype(np.float64)
+    ref_b = oracle.bf16_bits_to_f32(oracle.f64_to_bf16_bits(ref)).astype(np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    bound = oracle.bf16_ulp(ref_b) + 1e-3 * rms + 2.0 ** -9 * absref
+    excess = float(np.max(np.abs(yv - ref_b) - bound))
+    assert excess <= 0, f"{what}: elementwise excess {excess} over the slice-truncation bound ({r})"
+    return r
+
+
 # ---------------------------------------------------------------- FProp
 
 # shapes with at least 256 tiles of 256 x 256 run the large-tile kernel, M <= 64
@@ -84,7 +103,8 @@ def test_fprop_full_range_codes(m, n, k):
     qx, qw = codes(rng, (m, k), full_range=True), codes(rng, (n, k), full_range=True)
     sx, sw = scales(rng, (k // 128, m)), scales(rng, (n // 128, k // 128))
     y = host(jet.gemm_fprop(u8_dev(qx), f32_dev(sx), u8_dev(qw), f32_dev(sw)))
-    check(y, oracle.gemm_fprop_ref(qx, sx, qw, sw), f"fprop full-range {m}x{n}x{k}")
+    check_full_range(y, oracle.gemm_fprop_ref(qx, sx, qw, sw), oracle.gemm_fprop_ref(qx & 0x7F, sx, qw & 0x7F, sw),
+                     f"fprop full-range {m}x{n}x{k}")
 
 
 @pytest.mark.parametrize("m,n,k", [(64, 256, 256), (33, 384, 128), (256, 256, 256), (300, 512, 256)])
@@ -174,15 +194,16 @@ def test_wgrad_random(m, n, k):
 
 
 # full-range codes: every finite E4M3 code equally likely (the widest spread of
-# product magnitudes inside a 128-deep block); output sizes of 51k..16.8M
-# elements, on the 128 x 128 kernel and (the last shape of each) the 256 x 256 one
+# product magnitudes inside a 128-deep block), on the 128 x 128 kernel and (the
+# last shape of each) the 256 x 256 one; held to the slice-truncation bound
 @pytest.mark.parametrize("m,n,k", [(256, 512, 384), (200, 1024, 256), (4096, 256, 4096)])
 def test_dgrad_full_range_codes(m, n, k):
     rng = np.random.default_rng(m + 3 * n + k)
     qdy, qw = codes(rng, (m, n), full_range=True), codes(rng, (n, k), full_range=True)
     sdy, sw = scales(rng, (n // 128, m)), scales(rng, (n // 128, k // 128))
     dx = host(jet.gemm_dgrad(u8_dev(qdy), f32_dev(sdy), u8_dev(qw), f32_dev(sw)))
-    check(dx, oracle.gemm_dgrad_ref(qdy, sdy, qw, sw), f"dgrad full-range {m}x{n}x{k}")
+    check_full_range(dx, oracle.gemm_dgrad_ref(qdy, sdy, qw, sw),
+                     oracle.gemm_dgrad_ref(qdy & 0x7F, sdy, qw & 0x7F, sw), f"dgrad full-range {m}x{n}x{k}")
 
 
 @pytest.mark.parametrize("m,n,k", [(512, 256, 384), (1024, 256, 256), (256, 4096, 4096)])
@@ -191,7 +212,8 @@ def test_wgrad_full_range_codes(m, n, k):
     qdyt, qxt = codes(rng, (n, m), full_range=True), codes(rng, (k, m), full_range=True)
     sdyt, sxt = scales(rng, (m // 128, n)), scales(rng, (m // 128, k))
     dw = host(jet.gemm_wgrad(u8_dev(qdyt), f32_dev(sdyt), u8_dev(qxt), f32_dev(sxt)))
-    check(dw, oracle.gemm_wgrad_ref(qdyt, sdyt, qxt, sxt), f"wgrad full-range {m}x{n}x{k}")
+    check_full_range(dw, oracle.gemm_wgrad_ref(qdyt, sdyt, qxt, sxt),
+                     oracle.gemm_wgrad_ref(qdyt & 0x7F, sdyt, qxt & 0x7F, sxt), f"wgrad full-range {m}x{n}x{k}")
 
 
 @pytest.mark.parametrize("m,n,k", [(256, 256, 384), (384, 256, 512)])

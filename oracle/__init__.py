@@ -19,6 +19,9 @@ page "paper.rainbus.top/paper/2601.14243", sections "FP8 量化 (E4M3 格式)",
   the token dimension, stored transposed.
 * ``norm``   -- the gradients of the RMSNorm (dx, dgamma) in fp64, and their
   acceptance check.
+* ``swiglu`` -- SiLU(gate) * up of the gate+up projection's output, quantised
+  1x128 for the down projection (the fused quantisation of "核心方法"; SiLU with
+  a correctly rounded fp32 exponential).
 * ``gemm``   -- the three block-scaled GEMMs (FProp Y = X W^T, DGrad
   dX = dY W, WGrad dW = dY^T X) as their plain definition on dequantised values
   in fp64, the bf16 rounding of the result, and the acceptance check.
@@ -28,15 +31,14 @@ with round-to-nearest-even, written with numpy float32 arithmetic, in the
 order the definition states.  The GEMMs are plain fp64 matrix products.
 
 Pins: ``tests/test_oracle_*.py`` check each function against closed forms,
-invariants, hand-derived golden cases (``tests/golden``), library routines and
-brute force.  One function has no such pin for its exact bits:
-``rmsnorm_quant`` -- the pages name a fused RMSNorm but give no formula, so the
-order of its fp32 reduction is this oracle's reading (parity unpinned against
-the pages; pinned only against math.fsum and torch's rms_norm to a tolerance).
-The RMSNorm backward (``norm``) follows from calculus on that same reading, so it
-too is parity unpinned against the pages; it is pinned against central finite
-differences of the forward, torch's autograd of rms_norm in float64 and a
-closed-form identity for sum_k x_k dx_k.
+invariants, hand-derived golden cases (``tests/golden``), library routines,
+brute force and exact rational arithmetic.  ``rmsnorm_quant`` and
+``swiglu_quant`` follow readings of the pages (no formula is printed for the
+RMSNorm or for SiLU), and are pinned bit for bit to exact evaluations of those
+readings.  The RMSNorm backward (``norm``) follows from calculus on the forward
+reading; it is pinned against central finite differences of the forward,
+torch's autograd of rms_norm in float64 and a closed-form identity for
+sum_k x_k dx_k.
 """
 
 from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode, e4m3_table
@@ -52,6 +54,7 @@ from .quant import (
     pairwise_sum_f32,
 )
 from .norm import check_rmsnorm_backward, rmsnorm_backward_ref
+from .swiglu import exp_rn32, silu_f32, swiglu_f32, swiglu_quant
 from .gemm import (
     dequant_groups,
     dequant_blocks,
@@ -74,4 +77,5 @@ __all__ = [
     "dequant_groups", "dequant_blocks", "gemm_fprop_ref", "gemm_dgrad_ref", "gemm_wgrad_ref",
     "gemm_fprop_ref_at", "gemm_dgrad_ref_at", "gemm_wgrad_ref_at",
     "f64_to_bf16_bits", "bf16_ulp", "check_gemm", "check_gemm_f32",
+    "exp_rn32", "silu_f32", "swiglu_f32", "swiglu_quant",
 ]

@@ -22,8 +22,9 @@ object describes the slowest GEMM against the dense FP8 MFMA peak.  The
 
 ``--workload decode_8b`` instead times the rollout decode path at M tokens
 (``--decode-m``, default 16): RMSNorm+quant, FProp against the FP8 QKV and
-gate+up weights, 1x128 quantisation of the down-projection input and the down
-FProp (weights quantised once, outside the timed region).  The FProps go
+gate+up weights, the fused SwiGLU + 1x128 quantisation of the gate+up output
+(the down projection's input) and the down FProp (weights quantised once,
+outside the timed region).  The FProps go
 through gemm_fprop_splitk, which at 65..256 tokens splits K across workgroups
 for the shapes with fewer output tiles than CUs (its workspace is allocated
 before the timed region).  Decode is bound by streaming the FP8 weights, so its
@@ -37,8 +38,12 @@ kernels as the default step (1x128 quantisation of X, weight quantisation,
 FProp, dY quantisation, DGrad, both requants, WGrad).  They report every
 GEMM's rate; ``value`` is again all GEMM work over the step time.
 
+``--workload llama_mlp`` times the forward of a Llama-3.1-8B MLP at M = 16384
+as one chain (RMSNorm+quant, gate+up FProp, fused SwiGLU + 1x128 quantisation,
+down FProp), and the same chain with the SwiGLU unfused for comparison.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--workload linear_8b_up|decode_8b|llama_layer|qwen32b_half_mlp]
+                       [--workload linear_8b_up|decode_8b|llama_layer|qwen32b_half_mlp|llama_mlp]
                        [--decode-m M]
 """
 
@@ -72,7 +77,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="linear_8b_up",
-                    choices=["linear_8b_up", "decode_8b", "llama_layer", "qwen32b_half_mlp"])
+                    choices=["linear_8b_up", "decode_8b", "llama_layer", "qwen32b_half_mlp", "llama_mlp"])
     ap.add_argument("--decode-m", type=int, default=16)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (torch copy_), whose HBM counters "
@@ -286,7 +291,7 @@ def bench_decode(args):
     def bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    x, gamma, h = bf16(d["x"]), bf16(d["gamma"]), bf16(d["down_in"])
+    x, gamma = bf16(d["x"]), bf16(d["gamma"])
     wq = {k: jet.quantize_weight_128x128(bf16(d[k])) for k in ("w_qkv", "w_gu", "w_down")}
     # The three FP8 weights total 176 MB, which the 256 MB MALL could hold from one
     # step to the next; consecutive steps therefore rotate over DECODE_WEIGHT_SETS
@@ -294,8 +299,10 @@ def bench_decode(args):
     sets = [wq] + [{k: (q.clone(), s.clone()) for k, (q, s) in wq.items()} for _ in range(DECODE_WEIGHT_SETS - 1)]
     torch.cuda.synchronize()
     qx, sx = jet.rmsnorm_quant(x, gamma, d["eps"])
-    qh, sh = jet.quantize_act_1x128(h)
     y = {k: torch.empty((m, wq[k][0].shape[0]), dtype=torch.bfloat16, device=dev) for k in wq}
+    inter = wq["w_down"][0].shape[1]  # 12288: the down projection's input width
+    qh = torch.empty((m, inter), dtype=torch.uint8, device=dev)
+    sh = torch.empty((inter // 128, m), dtype=torch.float32, device=dev)
     # FProp through gemm_fprop_splitk: at 65..256 tokens the shapes with fewer
     # output tiles than CUs split K across workgroups through this workspace
     # (allocated once, outside the timed region); other shapes run gemm_fprop
@@ -311,7 +318,7 @@ def bench_decode(args):
         ("rmsnorm_quant", norm),
         ("gemm_fprop_qkv", lambda: jet.gemm_fprop_splitk(qx, sx, *sets[cur[0]]["w_qkv"], y["w_qkv"], ws)),
         ("gemm_fprop_gate_up", lambda: jet.gemm_fprop_splitk(qx, sx, *sets[cur[0]]["w_gu"], y["w_gu"], ws)),
-        ("quantize_act_1x128", lambda: jet.quantize_act_1x128(h, qh, sh)),
+        ("swiglu_quant", lambda: jet.swiglu_quant(y["w_gu"], qh, sh)),
         ("gemm_fprop_down", lambda: jet.gemm_fprop_splitk(qh, sh, *sets[cur[0]]["w_down"], y["w_down"], ws)),
     ]
     per, step_ms, wall, n_settle = time_steps(torch, steps, args.steps, args.warmup, dev)
@@ -341,6 +348,92 @@ def bench_decode(args):
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["weight_GBps"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": kernels[dom]["frac_hbm"], "traffic": None},
         "kernels": kernels,
+        "kernels_timing": KERNELS_TIMING,
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "settle": settle_info(n_settle),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_mlp(args):
+    """Forward of a Llama-3.1-8B MLP at M = 16384 tokens as one chain:
+    rmsnorm_quant -> FProp gate+up (4096 -> 28672) -> swiglu_quant -> FProp down
+    (14336 -> 4096), weights quantised once outside the timed region.  The same
+    chain with the SwiGLU left unfused (torch's silu and multiply writing a bf16
+    h, then quantize_act_1x128) is timed beside it; ``value`` is the fused
+    chain's GEMM work over its step time."""
+    import torch
+    import quantized_rl_amd as jet
+    from quantized_rl_amd import synth
+
+    dev = torch.device("cuda:0")
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    m = 16384
+    dgu, ddn = synth.llama_layer(0, "gate_up", m=m), synth.llama_layer(0, "down", m=m)
+    x = bf16(dgu["x"])
+    gamma = bf16(synth.decode_8b(16)["gamma"])  # N(1, 0.05) over 4096 channels
+    qwg, swg = jet.quantize_weight_128x128(bf16(dgu["w"]))
+    qwd, swd = jet.quantize_weight_128x128(bf16(ddn["w"]))
+    del dgu, ddn
+    n_gu, k = qwg.shape
+    n_dn, inter = qwd.shape
+    u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+    qx, sx = torch.empty((m, k), dtype=u8, device=dev), torch.empty((k // 128, m), dtype=f32, device=dev)
+    ygu = torch.empty((m, n_gu), dtype=bf, device=dev)
+    qh, sh = torch.empty((m, inter), dtype=u8, device=dev), torch.empty((inter // 128, m), dtype=f32, device=dev)
+    ydn = torch.empty((m, n_dn), dtype=bf, device=dev)
+    hbuf = torch.empty((m, inter), dtype=bf, device=dev)
+
+    def silu_mul():
+        torch.mul(torch.nn.functional.silu(ygu[:, :inter]), ygu[:, inter:], out=hbuf)
+
+    head = [("rmsnorm_quant", lambda: jet.rmsnorm_quant(x, gamma, EPS, qx, sx)),
+            ("gemm_fprop_gate_up", lambda: jet.gemm_fprop(qx, sx, qwg, swg, ygu))]
+    tail = [("gemm_fprop_down", lambda: jet.gemm_fprop(qh, sh, qwd, swd, ydn))]
+    fused = head + [("swiglu_quant", lambda: jet.swiglu_quant(ygu, qh, sh))] + tail
+    unfused = head + [("torch_silu_mul", silu_mul),
+                      ("quantize_act_1x128", lambda: jet.quantize_act_1x128(hbuf, qh, sh))] + tail
+    flops = 2.0 * m * n_gu * k + 2.0 * m * n_dn * inter
+    per, step_ms, wall, n_settle = time_steps(torch, fused, args.steps, args.warmup, dev)
+    per_u, step_u, _, _ = time_steps(torch, unfused, args.steps, args.warmup, dev)
+    ms_per_step, ms_unfused = float(np.mean(step_ms)), float(np.mean(step_u))
+    act = lambda r, c: r * c * 3 + 4 * r * c // 128  # noqa: E731
+    work = {"rmsnorm_quant": ("GB/s", act(m, k) + 2 * k), "gemm_fprop_gate_up": ("TFLOP/s", 2.0 * m * n_gu * k),
+            "swiglu_quant": ("GB/s", m * inter * 5 + 4 * m * inter // 128),
+            "gemm_fprop_down": ("TFLOP/s", 2.0 * m * n_dn * inter),
+            # silu reads gate and writes a bf16 temporary, mul reads it and up and writes h
+            "torch_silu_mul": ("GB/s", m * inter * 10), "quantize_act_1x128": ("GB/s", act(m, inter))}
+
+    def rates(p):
+        out = {}
+        for name in p:
+            unit, amount = work[name]
+            avg_ms = float(np.mean(p[name]))
+            rate = amount / (avg_ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+            peak = MFMA_FP8_PEAK_TFLOPS if unit == "TFLOP/s" else HBM_PEAK_GBS
+            out[name] = {"avg_us": round(avg_ms * 1e3, 2), "rate": round(rate, 1), "unit": unit,
+                         "frac": round(rate / peak, 4)}
+        return out
+
+    kernels = rates(per)
+    dom = max(("gemm_fprop_gate_up", "gemm_fprop_down"), key=lambda n: kernels[n]["avg_us"])
+    out = {
+        "metric": METRIC, "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": "llama31_8b_mlp_fwd", "M": m, "K": k, "gate_up_N": n_gu, "down_K": inter,
+                   "down_N": n_dn, "seed": 3},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": kernels[dom]["rate"],
+                     "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(kernels[dom]["rate"] / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None},
+        "kernels": kernels,
+        "unfused_swiglu": {"ms_per_step": round(ms_unfused, 4), "kernels": rates(per_u),
+                           "bytes_moved_between_the_gemms": work["torch_silu_mul"][1] + work["quantize_act_1x128"][1],
+                           "fused_bytes_moved_between_the_gemms": work["swiglu_quant"][1]},
         "kernels_timing": KERNELS_TIMING,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         "settle": settle_info(n_settle),
@@ -449,6 +542,10 @@ def main():
     if args.workload == "decode_8b":
         sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
         bench_decode(args)
+        return
+    if args.workload == "llama_mlp":
+        sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+        bench_mlp(args)
         return
     if args.workload in ("llama_layer", "qwen32b_half_mlp"):
         sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))

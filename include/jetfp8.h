@@ -164,6 +164,24 @@ int rmsnorm_backward(const uint16_t* x, const uint16_t* gamma, const float* rstd
                      int64_t M, int64_t K, uint16_t* dx, float* dgamma, float* workspace, void* stream);
 
 /*
+ * swiglu_quant -- SwiGLU of the gate+up projection's output fused with the
+ * 1x128 quantisation of the down projection's input ([P3-CORE] on fusing the
+ * quantisation into the neighbouring kernels, [P3-FP8], [P3-GRAN]).  The pages
+ * give no formula for SiLU; it is read as the standard one with an exactly
+ * specified fp32 evaluation:
+ *   gate = y[m][i], up = y[m][I + i]   (y = [gate | up], bf16 [M][2I])
+ *   E = the fp32 value nearest to e^-gate (+inf past the fp32 range)
+ *   silu = fl32(gate / fl32(1 + E));  h = fl32(silu * up)
+ *   (q, s) = the 1x128 quantisation of h, as quantize_act_1x128 does on these
+ *            fp32 values (no bf16 rounding of h).
+ *   y : bf16 [M][2I] input.  q : u8 [M][I]; s : f32 [I/128][M] outputs.
+ * I % 128 == 0; M >= 0.  M == 0 or I == 0 is a no-op.  Bit-exact.  As with
+ * non-finite inputs, an h that overflows fp32 (|silu * up| >= 2^128) is
+ * outside the contract.
+ */
+int swiglu_quant(const uint16_t* y, int64_t M, int64_t I, uint8_t* q, float* s, void* stream);
+
+/*
  * requant_transpose_128x1 -- requantise a saved 1x128 FP8 tensor into 128x1
  * groups along its rows (the token dimension) and store it transposed
  * ([P3-STEPS] steps 3-4, [P3-NOVEL]).  Used on the saved (QX, SX) and on

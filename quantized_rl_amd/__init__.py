@@ -23,4 +23,5 @@ from ._lib import (  # noqa: F401
     rmsnorm_backward_workspace_bytes,
     rmsnorm_quant,
     rmsnorm_quant_rstd,
+    swiglu_quant,
 )

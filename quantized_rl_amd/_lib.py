@@ -22,6 +22,7 @@ SIGNATURES = {
     "rmsnorm_quant_rstd": [_c_p, _c_p, _c_i64, _c_i64, ctypes.c_float, _c_p, _c_p, _c_p, _c_p],
     "rmsnorm_backward": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p],
     "requant_transpose_128x1": [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p],
+    "swiglu_quant": [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "gemm_fprop": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
     "gemm_fprop_splitk": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p],
     "gemm_fprop_quant": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p],
@@ -183,6 +184,22 @@ def rmsnorm_backward(x, gamma, rstd, dy, dx=None, dgamma=None, workspace=None):
         x.data_ptr(), gamma.data_ptr(), rstd.data_ptr(), dy.data_ptr(), M, K, dx.data_ptr(),
         dgamma.data_ptr(), workspace.data_ptr(), _stream(x.device)))
     return dx, dgamma
+
+
+def swiglu_quant(y, q=None, s=None):
+    """y bf16 [M, 2I] (gate | up) -> (q uint8 [M, I], s float32 [I/128, M]): the 1x128
+    quantisation of silu(gate) * up."""
+    torch = _torch()
+    M, I2 = y.shape
+    I = I2 // 2
+    _need(y, torch.bfloat16, (M, I2), "y")
+    if I2 % 2:
+        raise ValueError(f"y: expected an even column count (gate | up), got {I2}")
+    q = _empty((M, I), torch.uint8, y.device) if q is None else _need(q, torch.uint8, (M, I), "q")
+    s = _empty((I // 128, M), torch.float32, y.device) if s is None else \
+        _need(s, torch.float32, (I // 128, M), "s")
+    _check("swiglu_quant", lib().swiglu_quant(y.data_ptr(), M, I, q.data_ptr(), s.data_ptr(), _stream(y.device)))
+    return q, s
 
 
 def requant_transpose_128x1(q, s, qt=None, st=None):

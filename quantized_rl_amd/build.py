@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libjetfp8.so")
-SOURCES = ["api.cpp", "quant_kernels.hip", "gemm_kernels.hip", "norm_kernels.hip"]
+SOURCES = ["api.cpp", "quant_kernels.hip", "gemm_kernels.hip", "norm_kernels.hip", "swiglu_kernels.hip"]
 
 # -ffp-contract=off: every fp32 multiply and add of the quantisers is its own
 #   rounding step (no fused multiply-add), as their definitions state.
@@ -39,7 +39,23 @@ def hipcc():
     return exe
 
 
+def gen_silu_table():
+    """Run the build-time generator of the SiLU table (host C++) into csrc/silu_table.inc."""
+    exe = os.path.join(CSRC, "silu_table_gen")
+    cxx = shutil.which("g++") or shutil.which("c++")
+    if cxx is None:
+        raise RuntimeError("a host C++ compiler (g++) is needed to generate the SiLU table")
+    subprocess.run([cxx, "-O2", "-std=c++17", "-ffp-contract=off", "-o", exe,
+                    os.path.join(CSRC, "silu_table_gen.cpp")], check=True)
+    out = os.path.join(CSRC, "silu_table.inc")
+    subprocess.run([exe, out + ".tmp"], check=True)
+    os.replace(out + ".tmp", out)
+    os.remove(exe)
+    return out
+
+
 def build(verbose=False):
+    gen_silu_table()
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *FLAGS, "-x", "hip", *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if verbose:

@@ -124,6 +124,13 @@ int rmsnorm_backward(const uint16_t* x, const uint16_t* gamma, const float* rstd
                                                   as_stream(stream)));
 }
 
+int swiglu_quant(const uint16_t* y, int64_t M, int64_t I, uint8_t* q, float* s, void* stream) {
+  if (!dim_ok(M) || !dim_ok(I) || I % 128 || I > kMaxDim / 2) return JETFP8_EINVAL;
+  const int64_t n = M * I;
+  if (int st = check_ptrs({{y, 4 * n}}, {{q, n}, {s, 4 * (n / 128)}})) return st;
+  return launched(jetfp8::launch_swiglu_quant(y, M, I, q, s, as_stream(stream)));
+}
+
 int requant_transpose_128x1(const uint8_t* q, const float* s, int64_t M, int64_t K, uint8_t* qt,
                             float* st, void* stream) {
   if (!dim_ok(M) || !dim_ok(K) || M % 128 || K % 128) return JETFP8_EINVAL;

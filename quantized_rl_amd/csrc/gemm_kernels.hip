@@ -1215,8 +1215,7 @@ __global__ void fill_zero_u16(uint16_t* __restrict__ p, int64_t n) {
     p[i] = 0;
 }
 
-// Compute units of the current device (cached per device; 0 if unknown).
-static int cu_count() {
+int device_cu_count() {
   static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
@@ -1333,7 +1332,7 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
     // a tile starts); otherwise one workgroup per tile.
     int64_t grid = large_tiles;
     if (kMode != kWgrad && nkb % 2 == 0) {
-      const int64_t cus = cu_count() & ~7;
+      const int64_t cus = device_cu_count() & ~7;
       if (cus >= 8 && cus < grid) grid = cus;
     }
     hipLaunchKernelGGL((gemm_fp8_large_kernel<kMode, kOut>), dim3((unsigned)grid), dim3(kLThreads), 0, stream,
@@ -1347,7 +1346,7 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
   // took 60 us against 45 us for one round of two per CU: a CU's loads in
   // flight are capped, so more CUs pulling data beats deeper prefetch)
   const int64_t tiles = ((Mr + kMBM - 1) / kMBM) * (Nc / kMBN);
-  if (tiles <= (int64_t)cu_count())
+  if (tiles <= (int64_t)device_cu_count())
     hipLaunchKernelGGL((gemm_fp8_med_kernel<kMode, kOut, 4>), dim3((unsigned)tiles), dim3(kMThreads), 0, stream,
                        A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, Cv);
   else

@@ -6,6 +6,9 @@
 
 namespace jetfp8 {
 
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cu_count();
+
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* s,
                             hipStream_t stream);
 hipError_t launch_quant_weight(const uint16_t* w, int64_t N, int64_t K, uint8_t* q, float* s,
@@ -17,6 +20,8 @@ int64_t rmsnorm_backward_parts(int64_t M);
 hipError_t launch_rmsnorm_backward(const uint16_t* x, const uint16_t* gamma, const float* rstd,
                                    const uint16_t* dy, int64_t M, int64_t K, uint16_t* dx,
                                    float* dgamma, float* workspace, hipStream_t stream);
+hipError_t launch_swiglu_quant(const uint16_t* y, int64_t M, int64_t I, uint8_t* q, float* s,
+                               hipStream_t stream);
 hipError_t launch_requant(const uint8_t* q, const float* s, int64_t M, int64_t K, uint8_t* qt,
                           float* st, hipStream_t stream);
 hipError_t launch_gemm_fprop(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,

@@ -30,8 +30,6 @@
 
 namespace jetfp8 {
 
-constexpr int kBwdMaxPasses = 48;  // K <= 24576: 16 waves of at most 3 passes
-
 // Rows per workgroup: 2 ceil(M / 512) clamped to 1..32 (measured best of
 // 1..8, 1..16 and 1..32 at M = 256 .. 16384).
 static int64_t bwd_rows_per_group(int64_t M) {
@@ -176,7 +174,7 @@ hipError_t launch_rmsnorm_backward(const uint16_t* x, const uint16_t* gamma, con
   if (K == 0) return hipSuccess;
   const int64_t nparts = rmsnorm_backward_parts(M);
   if (M > 0) {
-    const int64_t passes = (K + 511) / 512;  // at most kBwdMaxPasses (the API checks K)
+    const int64_t passes = (K + 511) / 512;  // at most 48: the API takes K <= 24576
     if (passes <= 12)
       launch_bwd_rows_w<4>(x, gamma, rstd, dy, M, K, dx, workspace, stream);
     else if (passes <= 24)

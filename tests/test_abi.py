@@ -2,7 +2,9 @@
 and its host-side validation rejects bad arguments before enqueuing anything.
 
 Pointers here are fake integers; every call either fails validation or has an
-empty output, so no kernel is ever launched.
+empty output, so no kernel is ever launched -- except the two checks that
+adjacent buffers pass validation, which run only where no GPU is visible (the
+launch then fails with ELAUNCH instead of touching memory).
 """
 
 import os
@@ -17,6 +19,11 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 OK, EINVAL, EALIGN, ENULL, EALIAS = 0, 1, 2, 3, 4
 A = 1 << 20  # fake, 16-byte aligned addresses, far apart
 P = [A * (i + 1) for i in range(10)]
+
+
+def no_gpu():
+    import torch
+    return torch.cuda.device_count() == 0
 
 
 def declared_functions():
@@ -60,7 +67,8 @@ def test_quantize_act_validation(jetlib):
     assert c("quantize_act_1x128", P[0] + 8, 4, 128, P[1], P[2], 0) == EALIGN
     assert c("quantize_act_1x128", P[0], 4, 128, P[0] + 512, P[2], 0) == EALIAS  # q inside x
     assert c("quantize_act_1x128", P[0], 4, 128, P[1], P[1] + 256, 0) == EALIAS  # s inside q
-    assert c("quantize_act_1x128", P[0], 4, 128, P[0] + 1024, P[2], 0) != EALIAS  # adjacent is fine
+    if no_gpu():
+        assert c("quantize_act_1x128", P[0], 4, 128, P[0] + 1024, P[2], 0) != EALIAS  # adjacent is fine
     assert c("quantize_act_1x128", 0, 0, 128, 0, 0, 0) == OK  # empty: nothing to do
 
 
@@ -184,3 +192,18 @@ def test_gemm_fprop_splitk_validation(jetlib):
     assert c(f, Q[0], Q[1], Q[2], Q[3], 256, 6144, 4096, Q[4], Q[2], need, 0) == EALIAS         # over qw
     assert c(f, P[0], P[1], P[2], P[3], 16, 100, 128, P[4], P[5], 0, 0) == EINVAL
     assert c(f, 0, 0, P[2], P[3], 0, 128, 128, 0, 0, 0, 0) == OK  # M = 0: nothing to do
+
+
+def test_swiglu_quant_validation(jetlib):
+    # (y [M][2I], M, I, q [M][I], s [I/128][M])
+    assert "swiglu_quant" in declared_functions()
+    assert c("swiglu_quant", P[0], 4, 100, P[1], P[2], 0) == EINVAL        # I % 128
+    assert c("swiglu_quant", P[0], -1, 128, P[1], P[2], 0) == EINVAL
+    assert c("swiglu_quant", P[0], 4, 1 << 30, P[1], P[2], 0) == EINVAL    # 2I past 2^31 - 1
+    assert c("swiglu_quant", 0, 4, 128, P[1], P[2], 0) == ENULL
+    assert c("swiglu_quant", P[0], 4, 128, P[1] + 4, P[2], 0) == EALIGN
+    assert c("swiglu_quant", P[0], 4, 128, P[0] + 1024, P[2], 0) == EALIAS  # q inside y (2 KB)
+    if no_gpu():
+        assert c("swiglu_quant", P[0], 4, 128, P[0] + 2048, P[2], 0) != EALIAS  # right after y
+    assert c("swiglu_quant", P[0], 4, 128, P[1], P[1] + 256, 0) == EALIAS   # s inside q
+    assert c("swiglu_quant", 0, 0, 128, 0, 0, 0) == OK

@@ -245,6 +245,25 @@ int gemm_fprop_splitk(const uint8_t* qx, const float* sx, const uint8_t* qw, con
 int64_t gemm_fprop_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
+ * gemm_fprop_splitk_noalloc -- gemm_fprop_splitk with a workspace the library
+ * owns, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): same
+ * operands, results (bit for bit) and requirements, no workspace argument.
+ * The workspace is a static device array of JETFP8_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) that every device the library runs on holds until the process
+ * ends; its address is looked up on the first call on each device.  The call
+ * allocates and frees nothing.  The split rule keeps every workspace within
+ * that size (at most 512 K-shares of 128 x 128 fp32 partials), so every shape
+ * gemm_fprop_splitk takes is accepted; a shape needing more would return
+ * JETFP8_EUNSUPPORTED and write nothing.  All calls on one device share the
+ * array, so calls that overlap on one device (different streams or threads)
+ * race; serialise them.
+ */
+#define JETFP8_NOALLOC_SCRATCH_BYTES (32ll << 20)
+int gemm_fprop_splitk_noalloc(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
+                              int64_t M, int64_t N, int64_t K, uint16_t* y, void* stream);
+
+/*
  * gemm_fprop_quant -- gemm_fprop, plus the 1x128 quantisation of its output for
  * the next layer's GEMM (the fused quantisation that removes a separate pass
  * over Y: [P3-CORE] on fusing quantisation into the producing kernels, [P3-STEPS]

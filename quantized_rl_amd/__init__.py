@@ -8,11 +8,13 @@ The library is loaded on first use; nothing here falls back to another path.
 """
 
 from ._lib import (  # noqa: F401
+    NOALLOC_SCRATCH_BYTES,
     JetFP8Error,
     gemm_dgrad,
     gemm_fprop,
     gemm_fprop_quant,
     gemm_fprop_splitk,
+    gemm_fprop_splitk_noalloc,
     gemm_fprop_splitk_workspace_bytes,
     gemm_wgrad,
     gemm_wgrad_f32,

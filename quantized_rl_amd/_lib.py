@@ -25,6 +25,7 @@ SIGNATURES = {
     "swiglu_quant": [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "gemm_fprop": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
     "gemm_fprop_splitk": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p],
+    "gemm_fprop_splitk_noalloc": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
     "gemm_fprop_quant": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p],
     "gemm_dgrad": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
     "gemm_wgrad": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
@@ -259,6 +260,26 @@ def gemm_fprop_splitk(qx, sx, qw, sw, y=None, workspace=None):
     _check("gemm_fprop_splitk", lib().gemm_fprop_splitk(
         qx.data_ptr(), sx.data_ptr(), qw.data_ptr(), sw.data_ptr(), M, N, K, y.data_ptr(),
         workspace.data_ptr(), workspace.numel() * 4, _stream(qx.device)))
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def gemm_fprop_splitk_noalloc(qx, sx, qw, sw, y):
+    """gemm_fprop_splitk through the library's own static workspace (at most
+    NOALLOC_SCRATCH_BYTES): no device allocation by the library, nor here, so
+    the output y (bf16 [M, N]) is required."""
+    torch = _torch()
+    M, K = qx.shape
+    N = qw.shape[0]
+    _need(qx, torch.uint8, (M, K), "qx")
+    _need(sx, torch.float32, (K // 128, M), "sx")
+    _need(qw, torch.uint8, (N, K), "qw")
+    _need(sw, torch.float32, (N // 128, K // 128), "sw")
+    _need(y, torch.bfloat16, (M, N), "y")
+    _check("gemm_fprop_splitk_noalloc", lib().gemm_fprop_splitk_noalloc(
+        qx.data_ptr(), sx.data_ptr(), qw.data_ptr(), sw.data_ptr(), M, N, K, y.data_ptr(), _stream(qx.device)))
     return y
 
 

@@ -168,6 +168,19 @@ int gemm_fprop_splitk(const uint8_t* qx, const float* sx, const uint8_t* qw, con
   return launched(jetfp8::launch_gemm_fprop_splitk(qx, sx, qw, sw, M, N, K, y, workspace, as_stream(stream)));
 }
 
+int gemm_fprop_splitk_noalloc(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
+                              int64_t M, int64_t N, int64_t K, uint16_t* y, void* stream) {
+  static_assert(JETFP8_NOALLOC_SCRATCH_BYTES == (int64_t(32) << 20), "header and library agree on the size");
+  const int64_t ws = gemm_fprop_splitk_workspace_bytes(M, N, K);
+  if (ws < 0) return JETFP8_EINVAL;
+  if (int st = check_ptrs({{qx, M * K}, {sx, 4 * (M * K / 128)}, {qw, N * K},
+                           {sw, 4 * (N * K / (128 * 128))}},
+                          {{y, 2 * M * N}}))
+    return st;
+  if (!gemm_fits(M, N, K) || ws > jetfp8::fprop_noalloc_scratch_bytes()) return JETFP8_EUNSUPPORTED;
+  return launched(jetfp8::launch_gemm_fprop_splitk_noalloc(qx, sx, qw, sw, M, N, K, y, as_stream(stream)));
+}
+
 int gemm_fprop_quant(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
                      int64_t M, int64_t N, int64_t K, uint16_t* y, uint8_t* qy, float* sy,
                      void* stream) {

@@ -46,6 +46,7 @@
 // order with the same fp32 operations, so a row's FProp output does not depend
 // on the kernel (nor on the batch it is computed in).
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -1462,6 +1463,52 @@ hipError_t launch_gemm_fprop_splitk(const uint8_t* qx, const float* sx, const ui
   hipLaunchKernelGGL(splitk_reduce_bf16_kernel, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, stream, ws, s,
                      n, y);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned split-K workspace of gemm_fprop_splitk_noalloc, the variant of
+// gemm_fprop_splitk for callers that cannot allocate device memory (code under
+// HIP graph capture, serving loops).  Every device the library runs on holds
+// its own copy of this array until the process ends, and every call on that
+// device shares it: calls that overlap on one device race.  The K-share kernels
+// write every partial the reduction reads, so nothing needs clearing between
+// calls.  In host code `scratch` names a host-side stand-in, never the device
+// memory: kernels get the address from scratch_address() only.
+constexpr int64_t kNoAllocScratchBytes = int64_t(32) << 20;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / 4];
+
+// This device's copy of `scratch`: looked up with hipGetSymbolAddress on the
+// first call on each device (with that device current) and kept per device.
+static hipError_t scratch_address(float** out) {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    ptrs[dev] = p;
+  }
+  *out = static_cast<float*>(ptrs[dev]);
+  return hipSuccess;
+}
+
+int64_t fprop_noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+hipError_t launch_gemm_fprop_splitk_noalloc(const uint8_t* qx, const float* sx, const uint8_t* qw,
+                                            const float* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                                            hipStream_t stream) {
+  float* ws = nullptr;
+  if (fprop_splitk_workspace_bytes(M, N, K) > 0) {
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return e;
+  }
+  return launch_gemm_fprop_splitk(qx, sx, qw, sw, M, N, K, y, ws, stream);
 }
 
 }  // namespace jetfp8

@@ -32,6 +32,11 @@ int64_t fprop_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_fprop_splitk(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
                                     int64_t M, int64_t N, int64_t K, uint16_t* y, float* ws,
                                     hipStream_t stream);
+// The same with the library's own workspace (at most fprop_noalloc_scratch_bytes()).
+int64_t fprop_noalloc_scratch_bytes();
+hipError_t launch_gemm_fprop_splitk_noalloc(const uint8_t* qx, const float* sx, const uint8_t* qw,
+                                            const float* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                                            hipStream_t stream);
 hipError_t launch_gemm_dgrad(const uint8_t* qdy, const float* sdy, const uint8_t* qw,
                              const float* sw, int64_t M, int64_t N, int64_t K, uint16_t* dx,
                              hipStream_t stream);

@@ -207,3 +207,20 @@ def test_swiglu_quant_validation(jetlib):
         assert c("swiglu_quant", P[0], 4, 128, P[0] + 2048, P[2], 0) != EALIAS  # right after y
     assert c("swiglu_quant", P[0], 4, 128, P[1], P[1] + 256, 0) == EALIAS   # s inside q
     assert c("swiglu_quant", 0, 0, 128, 0, 0, 0) == OK
+
+
+def test_fprop_splitk_noalloc_validation(jetlib):
+    # (qx, sx, qw, sw, M, N, K, y)
+    n = "gemm_fprop_splitk_noalloc"
+    assert c(n, P[0], P[1], P[2], P[3], 256, 100, 4096, P[4], 0) == EINVAL      # N % 128
+    assert c(n, P[0], P[1], P[2], P[3], 256, 4096, 4000, P[4], 0) == EINVAL     # K % 128
+    assert c(n, P[0], P[1], P[2], P[3], 256, 4096, 4096, 0, 0) == ENULL          # no output
+    assert c(n, P[0], P[1], P[2], P[3] + 8, 256, 4096, 4096, P[4], 0) == EALIGN
+    assert c(n, P[0], P[1], P[2], P[3], 256, 4096, 4096, P[2] + 64, 0) == EALIAS  # y over qw
+    assert c(n, 0, 0, P[2], P[3], 0, 4096, 4096, 0, 0) == OK                     # M = 0: nothing to do
+    # the split rule never asks for more than the library's 32 MiB
+    ws = _lib.gemm_fprop_splitk_workspace_bytes
+    assert max(ws(m, nn, k) for m in (17, 33, 64, 100, 128, 200, 256) for nn in (4096, 6144, 8192, 16256)
+               for k in (4096, 12288, 16384)) <= _lib.NOALLOC_SCRATCH_BYTES
+    text = open(HEADER).read()
+    assert "#define JETFP8_NOALLOC_SCRATCH_BYTES (32ll << 20)" in text

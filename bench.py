@@ -39,8 +39,9 @@ FProp, dY quantisation, DGrad, both requants, WGrad).  They report every
 GEMM's rate; ``value`` is again all GEMM work over the step time.
 
 ``--workload llama_mlp`` times the forward of a Llama-3.1-8B MLP at M = 16384
-as one chain (RMSNorm+quant, gate+up FProp, fused SwiGLU + 1x128 quantisation,
-down FProp), and the same chain with the SwiGLU unfused for comparison.
+as one chain (RMSNorm+quant, the gate+up FProp with SwiGLU and the 1x128
+quantisation in its epilogue, down FProp), and for comparison the same chain
+with swiglu_quant as a separate kernel and with the SwiGLU unfused.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--workload linear_8b_up|decode_8b|llama_layer|qwen32b_half_mlp|llama_mlp]
@@ -357,11 +358,13 @@ def bench_decode(args):
 
 def bench_mlp(args):
     """Forward of a Llama-3.1-8B MLP at M = 16384 tokens as one chain:
-    rmsnorm_quant -> FProp gate+up (4096 -> 28672) -> swiglu_quant -> FProp down
-    (14336 -> 4096), weights quantised once outside the timed region.  The same
-    chain with the SwiGLU left unfused (torch's silu and multiply writing a bf16
-    h, then quantize_act_1x128) is timed beside it; ``value`` is the fused
-    chain's GEMM work over its step time."""
+    rmsnorm_quant -> gemm_fprop_swiglu_quant (gate+up FProp, 4096 -> 28672, whose
+    epilogue applies SwiGLU and the 1x128 quantisation) -> FProp down (14336 ->
+    4096), weights quantised once outside the timed region.  Timed beside it:
+    the same chain with the gate+up output written in bf16 and swiglu_quant as a
+    kernel of its own, and with the SwiGLU unfused (torch's silu and multiply
+    writing a bf16 h, then quantize_act_1x128).  ``value`` is the fused chain's
+    GEMM work over its step time."""
     import torch
     import quantized_rl_amd as jet
     from quantized_rl_amd import synth
@@ -390,18 +393,22 @@ def bench_mlp(args):
     def silu_mul():
         torch.mul(torch.nn.functional.silu(ygu[:, :inter]), ygu[:, inter:], out=hbuf)
 
-    head = [("rmsnorm_quant", lambda: jet.rmsnorm_quant(x, gamma, EPS, qx, sx)),
-            ("gemm_fprop_gate_up", lambda: jet.gemm_fprop(qx, sx, qwg, swg, ygu))]
+    norm = [("rmsnorm_quant", lambda: jet.rmsnorm_quant(x, gamma, EPS, qx, sx))]
+    head = norm + [("gemm_fprop_gate_up", lambda: jet.gemm_fprop(qx, sx, qwg, swg, ygu))]
     tail = [("gemm_fprop_down", lambda: jet.gemm_fprop(qh, sh, qwd, swd, ydn))]
-    fused = head + [("swiglu_quant", lambda: jet.swiglu_quant(ygu, qh, sh))] + tail
+    # the gate+up FProp's epilogue applies SwiGLU and quantises: no bf16 gate+up output
+    fused = norm + [("gemm_fprop_swiglu_quant", lambda: jet.gemm_fprop_swiglu_quant(qx, sx, qwg, swg, qh, sh))] + tail
+    two_kernel = head + [("swiglu_quant", lambda: jet.swiglu_quant(ygu, qh, sh))] + tail
     unfused = head + [("torch_silu_mul", silu_mul),
                       ("quantize_act_1x128", lambda: jet.quantize_act_1x128(hbuf, qh, sh))] + tail
     flops = 2.0 * m * n_gu * k + 2.0 * m * n_dn * inter
     per, step_ms, wall, n_settle = time_steps(torch, fused, args.steps, args.warmup, dev)
+    per_t, step_t, _, _ = time_steps(torch, two_kernel, args.steps, args.warmup, dev)
     per_u, step_u, _, _ = time_steps(torch, unfused, args.steps, args.warmup, dev)
-    ms_per_step, ms_unfused = float(np.mean(step_ms)), float(np.mean(step_u))
+    ms_per_step, ms_two, ms_unfused = float(np.mean(step_ms)), float(np.mean(step_t)), float(np.mean(step_u))
     act = lambda r, c: r * c * 3 + 4 * r * c // 128  # noqa: E731
     work = {"rmsnorm_quant": ("GB/s", act(m, k) + 2 * k), "gemm_fprop_gate_up": ("TFLOP/s", 2.0 * m * n_gu * k),
+            "gemm_fprop_swiglu_quant": ("TFLOP/s", 2.0 * m * n_gu * k),
             "swiglu_quant": ("GB/s", m * inter * 5 + 4 * m * inter // 128),
             "gemm_fprop_down": ("TFLOP/s", 2.0 * m * n_dn * inter),
             # silu reads gate and writes a bf16 temporary, mul reads it and up and writes h
@@ -419,7 +426,7 @@ def bench_mlp(args):
         return out
 
     kernels = rates(per)
-    dom = max(("gemm_fprop_gate_up", "gemm_fprop_down"), key=lambda n: kernels[n]["avg_us"])
+    dom = max(("gemm_fprop_swiglu_quant", "gemm_fprop_down"), key=lambda n: kernels[n]["avg_us"])
     out = {
         "metric": METRIC, "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -431,9 +438,12 @@ def bench_mlp(args):
                      "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(kernels[dom]["rate"] / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None},
         "kernels": kernels,
+        "gate_up_output_bytes_not_written": 2 * m * n_gu,
+        "two_kernel_swiglu": {"ms_per_step": round(ms_two, 4), "kernels": rates(per_t),
+                              "bytes_moved_between_the_gemms": 2 * m * n_gu + work["swiglu_quant"][1]},
         "unfused_swiglu": {"ms_per_step": round(ms_unfused, 4), "kernels": rates(per_u),
-                           "bytes_moved_between_the_gemms": work["torch_silu_mul"][1] + work["quantize_act_1x128"][1],
-                           "fused_bytes_moved_between_the_gemms": work["swiglu_quant"][1]},
+                           "bytes_moved_between_the_gemms": 2 * m * n_gu + work["torch_silu_mul"][1]
+                           + work["quantize_act_1x128"][1]},
         "kernels_timing": KERNELS_TIMING,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         "settle": settle_info(n_settle),

@@ -264,6 +264,26 @@ int gemm_fprop_splitk_noalloc(const uint8_t* qx, const float* sx, const uint8_t*
                               int64_t M, int64_t N, int64_t K, uint16_t* y, void* stream);
 
 /*
+ * gemm_fprop_swiglu_quant -- the gate+up projection's FProp fused with SwiGLU
+ * and the 1x128 quantisation of its result: the FP8 input of the down
+ * projection, with no bf16 gate+up output written at all ([P3-CORE] on fusing
+ * the quantisation into the producing kernels; [P3-STEPS] step 2):
+ *   (qh, sh) = swiglu_quant(gemm_fprop(qx, sx, qw, sw)), bit for bit: the GEMM
+ *   epilogue rounds each output to bf16 exactly as gemm_fprop does and then
+ *   applies swiglu_quant's arithmetic.
+ *   qx : u8 [M][K], sx : f32 [K/128][M]
+ *   qw : u8 [N][K], sw : f32 [N/128][K/128]: the gate+up weight, N = 2I rows,
+ *        gate in rows 0 .. I-1 and up in rows I .. 2I-1 (swiglu_quant's layout)
+ *   qh : u8 [M][I], sh : f32 [I/128][M] outputs.
+ * N % 256 == 0 (I % 128 == 0), K % 128 == 0, M >= 0.  K == 0 gives h = 0
+ * (codes 0, scales 1).  Runs the 256 x 256 tile kernel at every size: for
+ * rollout batches (M of a few hundred or less) gemm_fprop_splitk followed by
+ * swiglu_quant is faster.
+ */
+int gemm_fprop_swiglu_quant(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw, int64_t M,
+                            int64_t N, int64_t K, uint8_t* qh, float* sh, void* stream);
+
+/*
  * gemm_fprop_quant -- gemm_fprop, plus the 1x128 quantisation of its output for
  * the next layer's GEMM (the fused quantisation that removes a separate pass
  * over Y: [P3-CORE] on fusing quantisation into the producing kernels, [P3-STEPS]

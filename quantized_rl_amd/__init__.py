@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     gemm_fprop_quant,
     gemm_fprop_splitk,
     gemm_fprop_splitk_noalloc,
+    gemm_fprop_swiglu_quant,
     gemm_fprop_splitk_workspace_bytes,
     gemm_wgrad,
     gemm_wgrad_f32,

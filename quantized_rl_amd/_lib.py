@@ -26,6 +26,7 @@ SIGNATURES = {
     "gemm_fprop": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
     "gemm_fprop_splitk": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p],
     "gemm_fprop_splitk_noalloc": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
+    "gemm_fprop_swiglu_quant": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "gemm_fprop_quant": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p],
     "gemm_dgrad": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
     "gemm_wgrad": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
@@ -261,6 +262,27 @@ def gemm_fprop_splitk(qx, sx, qw, sw, y=None, workspace=None):
         qx.data_ptr(), sx.data_ptr(), qw.data_ptr(), sw.data_ptr(), M, N, K, y.data_ptr(),
         workspace.data_ptr(), workspace.numel() * 4, _stream(qx.device)))
     return y
+
+
+def gemm_fprop_swiglu_quant(qx, sx, qw, sw, qh=None, sh=None):
+    """FProp of a gate+up weight qw [2I, K] (gate rows, then up rows) fused with
+    SwiGLU and the 1x128 quantisation: (qh uint8 [M, I], sh float32 [I/128, M]),
+    bit for bit swiglu_quant(gemm_fprop(qx, sx, qw, sw))."""
+    torch = _torch()
+    M, K = qx.shape
+    N = qw.shape[0]
+    I = N // 2
+    _need(qx, torch.uint8, (M, K), "qx")
+    _need(sx, torch.float32, (K // 128, M), "sx")
+    _need(qw, torch.uint8, (N, K), "qw")
+    _need(sw, torch.float32, (N // 128, K // 128), "sw")
+    qh = _empty((M, I), torch.uint8, qx.device) if qh is None else _need(qh, torch.uint8, (M, I), "qh")
+    sh = _empty((I // 128, M), torch.float32, qx.device) if sh is None else \
+        _need(sh, torch.float32, (I // 128, M), "sh")
+    _check("gemm_fprop_swiglu_quant", lib().gemm_fprop_swiglu_quant(
+        qx.data_ptr(), sx.data_ptr(), qw.data_ptr(), sw.data_ptr(), M, N, K, qh.data_ptr(), sh.data_ptr(),
+        _stream(qx.device)))
+    return qh, sh
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20

@@ -181,6 +181,19 @@ int gemm_fprop_splitk_noalloc(const uint8_t* qx, const float* sx, const uint8_t*
   return launched(jetfp8::launch_gemm_fprop_splitk_noalloc(qx, sx, qw, sw, M, N, K, y, as_stream(stream)));
 }
 
+int gemm_fprop_swiglu_quant(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw, int64_t M,
+                            int64_t N, int64_t K, uint8_t* qh, float* sh, void* stream) {
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || N % 256 || K % 128) return JETFP8_EINVAL;
+  const int64_t nh = M * (N / 2);
+  if (int st = check_ptrs({{qx, M * K}, {sx, 4 * (M * K / 128)}, {qw, N * K},
+                           {sw, 4 * (N * K / (128 * 128))}},
+                          {{qh, nh}, {sh, 4 * (nh / 128)}}))
+    return st;
+  const int64_t lim = int64_t(1) << 31;
+  if ((M + 256) * K >= lim || N * K >= lim || (M + 256) * (N / 2) >= lim) return JETFP8_EUNSUPPORTED;
+  return launched(jetfp8::launch_gemm_fprop_swiglu_quant(qx, sx, qw, sw, M, N, K, qh, sh, as_stream(stream)));
+}
+
 int gemm_fprop_quant(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
                      int64_t M, int64_t N, int64_t K, uint16_t* y, uint8_t* qy, float* sy,
                      void* stream) {

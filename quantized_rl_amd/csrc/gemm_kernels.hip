@@ -177,10 +177,15 @@ struct LStage {
 // output row 16 i + (l % 16) of its A sub-tile and the four consecutive output
 // columns 16 j + 4 (l / 16) .. + 3 of its B sub-tile.  One row scale then
 // covers a whole 4-value partial, and the epilogue writes 8-byte pieces.
-template <int kMode>
+template <int kMode, bool kSwiglu = false>
 struct LargeTile {
   int t, l, w, wm, wn, lr, lk;
   uint32_t M, N, K, row0, col0, nkb, t8, arow;
+  // kSwiglu (FProp fused with SwiGLU): the tile's output columns are the
+  // h-columns col0 .. col0 + 127 (tile columns step by 128), and B row r of
+  // the stage is weight row col0 + r (gate) for r < 128, col0 + bskip + r (up,
+  // bskip = N / 2 - 128) otherwise.
+  uint32_t bskip = 0;
   bool b_half;
   rsrc_t ra, rb;
   uint32_t va[4], vb[4];
@@ -214,7 +219,7 @@ struct LargeTile {
     const uint32_t g0 = (id / per_group) * kGroupM;
     const uint32_t gm = (ntm - g0) < (uint32_t)kGroupM ? (ntm - g0) : (uint32_t)kGroupM;
     row0 = (g0 + (id % per_group) % gm) * kLBM;
-    col0 = ((id % per_group) / gm) * kLBN;
+    col0 = ((id % per_group) / gm) * (kSwiglu ? 128u : (uint32_t)kLBN);
     arow = (row0 + t8) < M ? (row0 + t8) : (M - 1);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -226,7 +231,7 @@ struct LargeTile {
         const int rr = 32 * (w & 3) + 8 * p + (l >> 3);
         vb[p] = rr * N + col0 + 128 * (w >> 2) + (((l & 7) ^ lf(rr)) << 4);
       } else {
-        vb[p] = (col0 + r) * K + (((l & 7) ^ lf(r)) << 4);
+        vb[p] = (col0 + r + (kSwiglu && r >= 128 ? bskip : 0u)) * K + (((l & 7) ^ lf(r)) << 4);
       }
     }
   }
@@ -259,7 +264,7 @@ struct LargeTile {
   // is never waited for up front.
   __device__ __forceinline__ float2 load_scale(uint32_t kb) const {
     if (kMode == kWgrad) return make_float2(b_half ? sb[kb * N + col0 + t8] : sa[kb * M + arow], 1.0f);
-    const uint32_t cb = col0 / kBN + ((uint32_t)t >> 8);
+    const uint32_t cb = kSwiglu ? (col0 + (t >= 256 ? 128u + bskip : 0u)) / kBN : col0 / kBN + ((uint32_t)t >> 8);
     const uint32_t bi = (kMode == kFprop) ? cb * nkb + kb : kb * (N / kBN) + cb;
     return make_float2(sa[kb * M + arow], sb[bi]);
   }
@@ -405,7 +410,20 @@ struct LargeTile {
 // Output element kinds of the tile kernels: bf16 (every entry point), fp32
 // written, fp32 added to what the output already holds (WGrad into an fp32
 // gradient buffer).
-enum OutKind { kOutBf16 = 0, kOutF32 = 1, kOutF32Add = 2 };
+// kOutSwiglu (FProp only): the tile's gate and up columns are combined into
+// SiLU(gate) * up and written as its 1x128 FP8 quantisation (codes + scales).
+enum OutKind { kOutBf16 = 0, kOutF32 = 1, kOutF32Add = 2, kOutSwiglu = 3 };
+
+// silu of every bf16 bit pattern (256 KB, generated at build time by the same
+// program and definition as swiglu_quant's table, and compared with the oracle
+// on every finite argument by the test-suite), read from global memory (it
+// stays in L2) by the fused epilogue, where the operand stages leave no room
+// in LDS: one gather per value, indexed by the gate's bits.
+__device__ const uint32_t kSiluBitsAll[65536] __attribute__((aligned(16))) = {
+#include "silu_table_full.inc"
+};
+
+__device__ __forceinline__ float silu_of_bits_g(uint32_t b) { return __uint_as_float(kSiluBitsAll[b]); }
 
 // fp32 output straight from the accumulators: each lane's four consecutive
 // columns of a 16 x 16 sub-tile go out as one 16-byte store (a quarter-wave
@@ -423,11 +441,14 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
                                                                     const uint8_t* __restrict__ B,
                                                                     const float* __restrict__ sb,
                                                                     uint32_t M, uint32_t N, uint32_t K,
-                                                                    void* __restrict__ Cv) {
+                                                                    void* __restrict__ Cv,
+                                                                    float* __restrict__ Sv) {
+  static_assert(kOut != kOutSwiglu || kMode == kFprop, "the SwiGLU epilogue follows FProp");
   __shared__ __attribute__((aligned(16))) LStage st0;
   __shared__ __attribute__((aligned(16))) LStage st1;
 
-  LargeTile<kMode> g;
+  LargeTile<kMode, kOut == kOutSwiglu> g;
+  if constexpr (kOut == kOutSwiglu) g.bskip = N / 2 - 128;
   g.t = threadIdx.x;
   g.l = g.t & 63;
   g.w = __builtin_amdgcn_readfirstlane(g.t >> 6);  // wave index, held in a scalar register
@@ -469,7 +490,7 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
   g.issue(0, st0);
   wait_vmem();
   __syncthreads();
-  typename LargeTile<kMode>::Head head;
+  typename LargeTile<kMode, kOut == kOutSwiglu>::Head head;
   g.read_head(st0, head);
 
   const uint32_t last = g.nkb - 1;
@@ -507,7 +528,82 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
       }
     }
 
-    if constexpr (kOut != kOutBf16) {
+    if constexpr (kOut == kOutSwiglu) {
+      // SwiGLU + 1x128 quantisation of the tile: h-columns col0 .. col0 + 127
+      // (gate in tile columns 0..127, up in 128..255), bit for bit what
+      // swiglu_quant computes from gemm_fprop's bf16 output.  The accumulators
+      // are first rounded to bf16 as gemm_fprop rounds them (packed, which frees
+      // the fp32 registers), then each 128-row half is staged in stage 1 and
+      // thread t takes row t / 4 of it, h-columns 32 (t % 4) .. + 31: silu from
+      // the table, h = fl32(silu * up), the group amax across the row's four
+      // threads, the scale and the codes (two 16-byte stores).  Rows past M
+      // fall outside the codes' buffer and are dropped; their scales are not
+      // written.
+      const uint32_t I = N / 2;
+      uint32_t pk[8][4][2];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pk[i][j][0] = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+          pk[i][j][1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+        }
+      constexpr int kPitch = kLBN * 2 + 16;
+      static_assert(128 * kPitch == sizeof(LStage), "epilogue staging must fill one stage exactly");
+      const rsrc_t rq = make_rsrc(Cv, M * I);
+      uint8_t* stage = reinterpret_cast<uint8_t*>(&st1);
+      const int er = g.t >> 2, eq = g.t & 3;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (g.wm == h) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int r = 16 * i + g.lr, c = g.wn * 64 + 16 * j + 4 * g.lk;
+              *reinterpret_cast<uint2*>(stage + r * kPitch + 2 * c) = make_uint2(pk[i][j][0], pk[i][j][1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        __syncthreads();
+        const uint8_t* rowp = stage + er * kPitch + 2 * 32 * eq;
+        uint4 gv[4], uv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          gv[c] = *reinterpret_cast<const uint4*>(rowp + 16 * c);
+          uv[c] = *reinterpret_cast<const uint4*>(rowp + 2 * 128 + 16 * c);
+        }
+        float hv[4][8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float u[8];
+          unpack_bf16x8(uv[c], u);
+          const uint32_t gw[4] = {gv[c].x, gv[c].y, gv[c].z, gv[c].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hv[c][2 * e] = silu_of_bits_g(gw[e] & 0xFFFFu) * u[2 * e];
+            hv[c][2 * e + 1] = silu_of_bits_g(gw[e] >> 16) * u[2 * e + 1];
+          }
+        }
+        uint32_t am = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) am = max(am, __float_as_uint(absmax8(hv[c])));
+        am = max(am, dpp_u32<kXor1>(am));
+        am = max(am, dpp_u32<kXor2>(am));
+        const float sc = scale_from_amax(__uint_as_float(am));
+        const double inv = inv_scale(sc);
+        const uint2 c0 = quant8(hv[0], inv), c1 = quant8(hv[1], inv);
+        const uint2 c2 = quant8(hv[2], inv), c3 = quant8(hv[3], inv);
+        const uint32_t grow = row0 + 128 * h + er;
+        const uint32_t qoff = grow * I + col0 + 32 * eq;
+        __builtin_amdgcn_raw_buffer_store_b128(v4i_t{(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y}, rq, qoff, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v4i_t{(int)c2.x, (int)c2.y, (int)c3.x, (int)c3.y}, rq, qoff + 16, 0,
+                                               0);
+        if (eq == 0 && grow < M) Sv[(col0 / kGroup) * M + grow] = sc;
+        __syncthreads();
+      }
+    } else if constexpr (kOut != kOutBf16) {
       const rsrc_t rc = make_rsrc(Cv, M * N * 4u);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
@@ -1337,7 +1433,7 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
       if (cus >= 8 && cus < grid) grid = cus;
     }
     hipLaunchKernelGGL((gemm_fp8_large_kernel<kMode, kOut>), dim3((unsigned)grid), dim3(kLThreads), 0, stream,
-                       A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, Cv);
+                       A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, Cv, (float*)nullptr);
     return hipGetLastError();
   }
   // the medium-tile kernel (the caller guarantees 32-bit byte offsets): four
@@ -1353,6 +1449,39 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
   else
     hipLaunchKernelGGL((gemm_fp8_med_kernel<kMode, kOut, 2>), dim3((unsigned)tiles), dim3(kMThreads), 0, stream,
                        A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, Cv);
+  return hipGetLastError();
+}
+
+// K == 0: the gate+up output is zero, so h = silu(0) * 0 = 0: codes 0, scales 1
+__global__ void fill_swiglu_empty(uint8_t* __restrict__ q, int64_t nq, float* __restrict__ s, int64_t ns) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nq; i += (int64_t)gridDim.x * blockDim.x)
+    q[i] = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < ns; i += (int64_t)gridDim.x * blockDim.x)
+    s[i] = 1.0f;
+}
+
+hipError_t launch_gemm_fprop_swiglu_quant(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
+                                          int64_t M, int64_t N, int64_t K, uint8_t* q, float* s,
+                                          hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (K == 0) {
+    const int64_t nq = M * (N / 2);
+    int64_t blocks = (nq + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(fill_swiglu_empty, dim3((unsigned)blocks), dim3(256), 0, stream, q, nq, s, nq / kGroup);
+    return hipGetLastError();
+  }
+  // 256 x 256 tiles of (rows, gate block + up block); one workgroup per CU
+  // looping over the tiles when the block count is even, as FProp
+  const int64_t nkb = K / kBK;
+  const int64_t tiles = ((M + kLBM - 1) / kLBM) * (N / kLBN);
+  int64_t grid = tiles;
+  if (nkb % 2 == 0) {
+    const int64_t cus = device_cu_count() & ~7;
+    if (cus >= 8 && cus < grid) grid = cus;
+  }
+  hipLaunchKernelGGL((gemm_fp8_large_kernel<kFprop, kOutSwiglu>), dim3((unsigned)grid), dim3(kLThreads), 0, stream,
+                     qx, sx, qw, sw, (uint32_t)M, (uint32_t)N, (uint32_t)K, (void*)q, s);
   return hipGetLastError();
 }
 

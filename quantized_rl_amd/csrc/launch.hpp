@@ -37,6 +37,11 @@ int64_t fprop_noalloc_scratch_bytes();
 hipError_t launch_gemm_fprop_splitk_noalloc(const uint8_t* qx, const float* sx, const uint8_t* qw,
                                             const float* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
                                             hipStream_t stream);
+// FProp of a gate+up projection (N = 2I weight rows: gate then up) fused with
+// SwiGLU and the 1x128 quantisation of its result (q [M][I], s [I/128][M]).
+hipError_t launch_gemm_fprop_swiglu_quant(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
+                                          int64_t M, int64_t N, int64_t K, uint8_t* q, float* s,
+                                          hipStream_t stream);
 hipError_t launch_gemm_dgrad(const uint8_t* qdy, const float* sdy, const uint8_t* qw,
                              const float* sw, int64_t M, int64_t N, int64_t K, uint16_t* dx,
                              hipStream_t stream);

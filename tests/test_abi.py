@@ -224,3 +224,17 @@ def test_fprop_splitk_noalloc_validation(jetlib):
                for k in (4096, 12288, 16384)) <= _lib.NOALLOC_SCRATCH_BYTES
     text = open(HEADER).read()
     assert "#define JETFP8_NOALLOC_SCRATCH_BYTES (32ll << 20)" in text
+
+
+def test_fprop_swiglu_quant_validation(jetlib):
+    # (qx, sx, qw, sw, M, N, K, qh, sh)
+    n = "gemm_fprop_swiglu_quant"
+    assert n in declared_functions()
+    assert c(n, P[0], P[1], P[2], P[3], 256, 384, 256, P[4], P[5], 0) == EINVAL   # N % 256
+    assert c(n, P[0], P[1], P[2], P[3], 256, 512, 200, P[4], P[5], 0) == EINVAL   # K % 128
+    assert c(n, P[0], P[1], P[2], P[3], 256, 512, 256, 0, P[5], 0) == ENULL
+    assert c(n, P[0], P[1], P[2], P[3], 256, 512, 256, P[4], P[5] + 4, 0) == EALIGN
+    assert c(n, P[0], P[1], P[2], P[3], 256, 512, 256, P[4], P[4] + 1024, 0) == EALIAS  # sh inside qh
+    B = [(i + 1) << 40 for i in range(6)]  # far apart: no overlap even for huge shapes
+    assert c(n, B[0], B[1], B[2], B[3], 1 << 20, 512, 4096, B[4], B[5], 0) == 5   # past 32-bit offsets
+    assert c(n, 0, 0, P[2], P[3], 0, 512, 256, 0, 0, 0) == OK

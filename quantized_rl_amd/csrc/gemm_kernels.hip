@@ -163,13 +163,21 @@ __device__ __forceinline__ void static_for(F&& f) {
 // access names its stage statically, which lets the compiler see that the
 // fragment reads of one stage do not alias the in-flight direct loads into
 // the other (otherwise it waits for those loads before every read).
+// Row factors are stored transposed, row r at [(r % 16) * kLScPitch + r / 16]:
+// lane lr then reads its eight row sub-tiles' factors as two float4s at
+// lr * kLScPitch + 8 wm, and with a pitch of 20 floats (not 16) the sixteen
+// lanes of a quarter-wave cover disjoint four-bank groups (20 lr mod 64 runs
+// over the multiples of 4), as do the 64 lanes' 4-byte stores.  With a pitch of
+// 16, lanes lr and lr + 4 shared banks: a 4-way conflict on every read, which
+// cost 9-20 % of the GEMMs' time (measured with SQ_LDS_BANK_CONFLICT: 13-17 M
+// conflict cycles per 8B-step GEMM, 0.5-1.6 M without these accesses).
+constexpr int kLScPitch = 20;
 struct LStage {
   uint8_t ab[kLStage];
   // FProp, DGrad: sc[h] holds fl32(sa(row) * sb(block h)) for the tile's two
   // 128-column halves h, so the rescale needs no multiply; WGrad: sc[0] holds
-  // the A-row scales, sc[1] the 256 B-column scales in column order.  Rows are
-  // stored transposed: row r at [(r % 16) * 16 + r / 16].
-  float sc[2][kLBM];
+  // the A-row scales, sc[1] the 256 B-column scales in column order.
+  float sc[2][16 * kLScPitch];
 };
 
 // The MFMAs take the B-tile fragment as their first operand and the A-tile
@@ -203,7 +211,7 @@ struct LargeTile {
     const uint32_t rb0 = (uint32_t)(kLBM * kBK) + (uint32_t)(wn * 64 + lr) * 128u;
     b_even = rb0 + (((uint32_t)(2 * lk) ^ f0) << 4);
     b_odd = rb0 + (((uint32_t)(2 * lk + 1) ^ f0) << 4);
-    s_row = (uint32_t)(lr * 16 + wm * 8) * 4u;
+    s_row = (uint32_t)(lr * kLScPitch + wm * 8) * 4u;
     // DGrad: transposed reads of B[n][c]; n = 32 lk + 8 q + lr / 2, chunk 4 (wn % 2) + j
     const uint32_t x = (uint32_t)(((lr >> 1) & 7) ^ (lk & 1) ^ (4 * (wn & 1)));
     const uint32_t dbase = (uint32_t)(kLBM * kBK) + (uint32_t)(wn >> 1) * (128u * 128u) +
@@ -269,7 +277,7 @@ struct LargeTile {
     return make_float2(sa[kb * M + arow], sb[bi]);
   }
   __device__ __forceinline__ void store_scale(LStage& st, float2 x) const {
-    const uint32_t tr = (t8 & 15u) * 16u + (t8 >> 4);
+    const uint32_t tr = (t8 & 15u) * (uint32_t)kLScPitch + (t8 >> 4);
     st.sc[t >> 8][(kMode == kWgrad && t >= kLBM) ? t8 : tr] = (kMode == kWgrad) ? x.x : x.x * x.y;
   }
 
@@ -549,7 +557,7 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
           pk[i][j][1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
         }
       constexpr int kPitch = kLBN * 2 + 16;
-      static_assert(128 * kPitch == sizeof(LStage), "epilogue staging must fill one stage exactly");
+      static_assert(128 * kPitch <= sizeof(LStage), "epilogue staging must fit one stage");
       const rsrc_t rq = make_rsrc(Cv, M * I);
       uint8_t* stage = reinterpret_cast<uint8_t*>(&st1);
       const int er = g.t >> 2, eq = g.t & 3;
@@ -619,7 +627,7 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
       // then written with 16-byte buffer stores, streaming in FProp and DGrad
       // (rows past M fall outside the buffer and are dropped)
       constexpr int kPitch = kLBN * 2 + 16;
-      static_assert(128 * kPitch == sizeof(LStage), "epilogue staging must fill one stage exactly");
+      static_assert(128 * kPitch <= sizeof(LStage), "epilogue staging must fit one stage");
       uint16_t* C = static_cast<uint16_t*>(Cv);
       const rsrc_t rc = make_rsrc(C, M * N * 2u);
       uint8_t* stage = reinterpret_cast<uint8_t*>(&st1);
@@ -675,12 +683,16 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
 constexpr int kMBM = 128, kMBN = 128;
 constexpr int kMThreads = 256;
 
+// Row factors transposed, r at [(r % 16) * kMScPitch + r / 16]: a pitch of 12
+// floats (not 8) puts the sixteen float4 reads of a quarter-wave (lane lr at
+// lr * kMScPitch + 4 wm) on disjoint bank groups, as in the large kernel.
+constexpr int kMScPitch = 12;
 struct MStage {
   uint8_t ab[kMBM * kBK + kMBN * kBK];  // 32 KB: A rows then B rows
   // FProp, DGrad: sc[0] holds fl32(sa(row) * sb(block)) (the tile's 128
   // columns are one weight block); WGrad: sc[0] the A-row scales, sc[1] the
-  // 128 B-column scales in column order.  Rows transposed: r at [(r % 16) * 8 + r / 16].
-  float sc[2][kMBM];
+  // 128 B-column scales in column order.
+  float sc[2][16 * kMScPitch];
 };
 
 template <int kMode>
@@ -706,7 +718,7 @@ struct MedTile {
     const uint32_t rb0 = (uint32_t)(kMBM * kBK) + (uint32_t)(wn * 64 + lr) * 128u;
     b_even = rb0 + (((uint32_t)(2 * lk) ^ f0) << 4);
     b_odd = rb0 + (((uint32_t)(2 * lk + 1) ^ f0) << 4);
-    s_row = (uint32_t)(lr * 8 + wm * 4) * 4u;
+    s_row = (uint32_t)(lr * kMScPitch + wm * 4) * 4u;
     // DGrad: transposed reads of B[n][c]; n = 32 lk + 8 q + lr / 2, chunk 4 wn + j
     const uint32_t x = (uint32_t)(((lr >> 1) & 7) ^ (lk & 1) ^ (4 * wn));
     const uint32_t dbase = (uint32_t)(kMBM * kBK) + (uint32_t)(32 * lk + (lr >> 1)) * 128u + 8u * (uint32_t)(lr & 1);
@@ -743,7 +755,7 @@ struct MedTile {
     return make_float2(sa[kb * M + arow], sb[bi]);
   }
   __device__ __forceinline__ void store_scale(MStage& st, float2 x) const {
-    if (t < kMBM) st.sc[0][(t & 15) * 8 + (t >> 4)] = (kMode == kWgrad) ? x.x : x.x * x.y;
+    if (t < kMBM) st.sc[0][(t & 15) * kMScPitch + (t >> 4)] = (kMode == kWgrad) ? x.x : x.x * x.y;
     else if (kMode == kWgrad) st.sc[1][t - kMBM] = x.x;
   }
 

@@ -22,6 +22,8 @@ page "paper.rainbus.top/paper/2601.14243", sections "FP8 量化 (E4M3 格式)",
 * ``swiglu`` -- SiLU(gate) * up of the gate+up projection's output, quantised
   1x128 for the down projection (the fused quantisation of "核心方法"; SiLU with
   a correctly rounded fp32 exponential).
+* ``layout`` -- the rollout-packed byte order of the weight codes (a
+  permutation the library defines for its rollout FProp; no arithmetic).
 * ``gemm``   -- the three block-scaled GEMMs (FProp Y = X W^T, DGrad
   dX = dY W, WGrad dW = dY^T X) as their plain definition on dequantised values
   in fp64, the bf16 rounding of the result, and the acceptance check.
@@ -55,6 +57,7 @@ from .quant import (
 )
 from .norm import check_rmsnorm_backward, rmsnorm_backward_ref
 from .swiglu import exp_rn32, silu_f32, swiglu_f32, swiglu_quant
+from .layout import pack_weight_rollout
 from .gemm import (
     dequant_groups,
     dequant_blocks,
@@ -78,4 +81,5 @@ __all__ = [
     "gemm_fprop_ref_at", "gemm_dgrad_ref_at", "gemm_wgrad_ref_at",
     "f64_to_bf16_bits", "bf16_ulp", "check_gemm", "check_gemm_f32",
     "exp_rn32", "silu_f32", "swiglu_f32", "swiglu_quant",
+    "pack_weight_rollout",
 ]

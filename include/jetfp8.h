@@ -19,7 +19,11 @@
  *              granularity, forward GEMM, FP8 activation saving, backward with
  *              BF16 dY and the 1x128 -> 128x1 requantisation, fused RMSNorm);
  *   [P3-NOVEL] same page, section "技术新颖性" (forward saves 1x128, backward
- *              needs 128x1).
+ *              needs 128x1);
+ *   [P3-RESULTS] same page, section "实验结果" (the rollout speed-up of FP8,
+ *              1.33x on the 32B model);
+ *   [P3-WEAK]  same page, section "独立分析的弱点" (8B rollout is bound by
+ *              memory traffic rather than arithmetic).
  *
  * Conventions common to every entry point
  * ---------------------------------------
@@ -262,6 +266,39 @@ int64_t gemm_fprop_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
 #define JETFP8_NOALLOC_SCRATCH_BYTES (32ll << 20)
 int gemm_fprop_splitk_noalloc(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
                               int64_t M, int64_t N, int64_t K, uint16_t* y, void* stream);
+
+/*
+ * pack_weight_rollout -- the rollout engine's copy of a quantised weight: the
+ * codes of quantize_weight_128x128 in the order gemm_fprop_packed streams them
+ * (the rollout runs the training forward's FP8 GEMM, [P3-CORE], [P3-STEPS]
+ * step 2; at rollout batch sizes that GEMM is bound by reading the weight,
+ * [P3-WEAK], and the rollout speed-up is the method's headline result,
+ * [P3-RESULTS]).  A byte permutation, no arithmetic:
+ *   qwp[((t * (K/128) + kb) * 2 + h) * 1024 + 16 l + b]
+ *     = qw[16 t + (l mod 16)][128 kb + 32 floor(l / 16) + 16 h + b]
+ *   for t < N/16, kb < K/128, h < 2, l < 64, b < 16:
+ * each 16-row strip's 128-deep K-block is one contiguous 2 KB chunk.
+ *   qw  : u8 [N][K] input;  qwp : u8, N * K bytes, output.
+ * The weight's scales sw [N/128][K/128] are used unchanged.
+ * N % 128 == 0, K % 128 == 0; N * K < 2^31 (gemm_fprop_packed's bound;
+ * JETFP8_EUNSUPPORTED otherwise).
+ */
+int pack_weight_rollout(const uint8_t* qw, int64_t N, int64_t K, uint8_t* qwp, void* stream);
+
+/*
+ * gemm_fprop_packed -- gemm_fprop for rollout batches of up to 64 rows over
+ * the packed weight ([P3-LAYOUT], [P3-CORE], [P3-STEPS] step 2):
+ *   y = gemm_fprop(qx, sx, qw, sw) bit for bit, with qwp = pack_weight_rollout(qw).
+ *   qx : u8 [M][K], sx : f32 [K/128][M]; qwp : u8, N * K bytes;
+ *   sw : f32 [N/128][K/128]; y : bf16 [M][N].
+ * 0 <= M <= 64 (JETFP8_EUNSUPPORTED above), N % 128 == 0, K % 128 == 0,
+ * N * K < 2^31 and M * K < 2^31 (JETFP8_EUNSUPPORTED otherwise).  K == 0
+ * writes zeros.  A row's output is the sequential K fold of gemm_fprop, so it
+ * is bitwise the same as in a training batch of any size above 256 rows or
+ * any rollout batch of up to 64.
+ */
+int gemm_fprop_packed(const uint8_t* qx, const float* sx, const uint8_t* qwp, const float* sw, int64_t M,
+                      int64_t N, int64_t K, uint16_t* y, void* stream);
 
 /*
  * gemm_fprop_swiglu_quant -- the gate+up projection's FProp fused with SwiGLU

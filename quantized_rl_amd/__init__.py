@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     JetFP8Error,
     gemm_dgrad,
     gemm_fprop,
+    gemm_fprop_packed,
     gemm_fprop_quant,
     gemm_fprop_splitk,
     gemm_fprop_splitk_noalloc,
@@ -19,6 +20,7 @@ from ._lib import (  # noqa: F401
     gemm_fprop_splitk_workspace_bytes,
     gemm_wgrad,
     gemm_wgrad_f32,
+    pack_weight_rollout,
     quantize_act_1x128,
     quantize_weight_128x128,
     requant_transpose_128x1,

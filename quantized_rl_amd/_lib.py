@@ -26,6 +26,8 @@ SIGNATURES = {
     "gemm_fprop": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
     "gemm_fprop_splitk": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p],
     "gemm_fprop_splitk_noalloc": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
+    "pack_weight_rollout": [_c_p, _c_i64, _c_i64, _c_p, _c_p],
+    "gemm_fprop_packed": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
     "gemm_fprop_swiglu_quant": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "gemm_fprop_quant": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p],
     "gemm_dgrad": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
@@ -261,6 +263,35 @@ def gemm_fprop_splitk(qx, sx, qw, sw, y=None, workspace=None):
     _check("gemm_fprop_splitk", lib().gemm_fprop_splitk(
         qx.data_ptr(), sx.data_ptr(), qw.data_ptr(), sw.data_ptr(), M, N, K, y.data_ptr(),
         workspace.data_ptr(), workspace.numel() * 4, _stream(qx.device)))
+    return y
+
+
+def pack_weight_rollout(qw, qwp=None):
+    """Rollout-packed copy of the weight codes qw uint8 [N, K]: a uint8 tensor of the
+    same shape whose bytes are in the order gemm_fprop_packed streams (each 16-row
+    strip's 128-deep K-block one contiguous 2 KB chunk; the scales are unchanged)."""
+    torch = _torch()
+    N, K = qw.shape
+    _need(qw, torch.uint8, (N, K), "qw")
+    qwp = _empty((N, K), torch.uint8, qw.device) if qwp is None else _need(qwp, torch.uint8, (N, K), "qwp")
+    _check("pack_weight_rollout", lib().pack_weight_rollout(qw.data_ptr(), N, K, qwp.data_ptr(), _stream(qw.device)))
+    return qwp
+
+
+def gemm_fprop_packed(qx, sx, qwp, sw, y=None):
+    """gemm_fprop for up to 64 rows over the packed weight qwp = pack_weight_rollout(qw):
+    Y bf16 [M, N], bit for bit gemm_fprop(qx, sx, qw, sw)."""
+    torch = _torch()
+    M, K = qx.shape
+    N = qwp.shape[0]
+    _need(qx, torch.uint8, (M, K), "qx")
+    _need(sx, torch.float32, (K // 128, M), "sx")
+    _need(qwp, torch.uint8, (N, K), "qwp")
+    _need(sw, torch.float32, (N // 128, K // 128), "sw")
+    y = _empty((M, N), torch.bfloat16, qx.device) if y is None else _need(y, torch.bfloat16, (M, N), "y")
+    _check("gemm_fprop_packed", lib().gemm_fprop_packed(
+        qx.data_ptr(), sx.data_ptr(), qwp.data_ptr(), sw.data_ptr(), M, N, K, y.data_ptr(),
+        _stream(qx.device)))
     return y
 
 

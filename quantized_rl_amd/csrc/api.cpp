@@ -181,6 +181,26 @@ int gemm_fprop_splitk_noalloc(const uint8_t* qx, const float* sx, const uint8_t*
   return launched(jetfp8::launch_gemm_fprop_splitk_noalloc(qx, sx, qw, sw, M, N, K, y, as_stream(stream)));
 }
 
+int pack_weight_rollout(const uint8_t* qw, int64_t N, int64_t K, uint8_t* qwp, void* stream) {
+  if (!dim_ok(N) || !dim_ok(K) || N % 128 || K % 128) return JETFP8_EINVAL;
+  const int64_t n = N * K;
+  if (int st = check_ptrs({{qw, n}}, {{qwp, n}})) return st;
+  if (n >= (int64_t(1) << 31)) return JETFP8_EUNSUPPORTED;
+  return launched(jetfp8::launch_pack_weight_rollout(qw, N, K, qwp, as_stream(stream)));
+}
+
+int gemm_fprop_packed(const uint8_t* qx, const float* sx, const uint8_t* qwp, const float* sw, int64_t M,
+                      int64_t N, int64_t K, uint16_t* y, void* stream) {
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || N % 128 || K % 128) return JETFP8_EINVAL;
+  if (int st = check_ptrs({{qx, M * K}, {sx, 4 * (M * K / 128)}, {qwp, N * K},
+                           {sw, 4 * (N * K / (128 * 128))}},
+                          {{y, 2 * M * N}}))
+    return st;
+  const int64_t lim = int64_t(1) << 31;
+  if (M > 64 || N * K >= lim || M * K >= lim) return JETFP8_EUNSUPPORTED;
+  return launched(jetfp8::launch_gemm_fprop_packed(qx, sx, qwp, sw, M, N, K, y, as_stream(stream)));
+}
+
 int gemm_fprop_swiglu_quant(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw, int64_t M,
                             int64_t N, int64_t K, uint8_t* qh, float* sh, void* stream) {
   if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || N % 256 || K % 128) return JETFP8_EINVAL;

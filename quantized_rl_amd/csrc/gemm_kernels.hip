@@ -28,7 +28,8 @@
 // cancel (the normwise bound holds).
 //
 // Kernels (chosen in launch_gemm):
-//   gemm_fp8_decode_kernel       FProp with M <= 64 (weight streaming);
+//   gemm_fp8_decode_kernel       FProp with M <= 64 (weight streaming), also
+//                                over the rollout-packed weight (gemm_fprop_packed);
 //   gemm_fp8_mid_kernel          FProp with 65 .. 256 rows, long K and few
 //                                column tiles (K split over 8 waves);
 //   gemm_fp8_large_kernel<mode>  256 x 256 tiles: problems with >= 256 of them
@@ -62,6 +63,7 @@ typedef int v4i_t __attribute__((ext_vector_type(4)));
 enum GemmMode { kFprop = 0, kDgrad = 1, kWgrad = 2 };
 
 constexpr int kBN = 128, kBK = 128;  // weight block width, K-block depth
+constexpr uint32_t kPackChunk = 2048;  // rollout-packed weight: bytes of one 16-row strip's K-block
 
 __device__ __forceinline__ v2i_t lds_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
@@ -1049,11 +1051,16 @@ __device__ __forceinline__ float ld_scale(rsrc_t r, uint32_t byte_off) {
 }
 
 
-template <int kMT, int kW, int kS>
+// kPk: W is in the rollout-packed order of pack_weight_rollout_kernel (each
+// 16-row strip's K-block a contiguous 2 KB chunk holding every lane's operand
+// bytes in lane order) instead of row-major [N][K]; the loads then cover 1 KB
+// of consecutive bytes each and a wave walks one contiguous range of memory.
+template <int kMT, int kW, int kS, bool kPk>
 __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
     const uint8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, uint32_t M, uint32_t N, uint32_t K, uint16_t* __restrict__ Y) {
   constexpr int kD = DecodeCfg<kMT, kW, kS>::kD;
+  constexpr uint32_t kWHalf = kPk ? 1024u : 16u;  // byte offset of a lane's second 16 operand bytes
   const int t = threadIdx.x, l = t & 63, lr = l & 15, lk = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const uint32_t n0 = blockIdx.x * (16u * kS);  // the workgroup's kS strips of 16 columns
@@ -1063,7 +1070,8 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
   const rsrc_t rx = make_rsrc(X, M * K);
   uint32_t w_off[kS], x_off[kMT], xm[kMT];
 #pragma unroll
-  for (int s = 0; s < kS; ++s) w_off[s] = (n0 + 16u * s + lr) * K + 32u * lk;
+  for (int s = 0; s < kS; ++s)
+    w_off[s] = kPk ? (n0 / 16u + s) * nkb * kPackChunk + 16u * l : (n0 + 16u * s + lr) * K + 32u * lk;
 #pragma unroll
   for (int i = 0; i < kMT; ++i) {
     xm[i] = (16u * i + lr) < M ? (16u * i + lr) : (M - 1);  // ragged tail: repeat the last token
@@ -1077,11 +1085,11 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
   auto load = [&](int slot, uint32_t c) {
     uint32_t kb = c * kW + (uint32_t)w;
     kb = kb < nkb ? kb : nkb - 1;  // past the end: a valid block whose product is not used
-    const uint32_t kofs = kb * kBK;
+    const uint32_t kofs = kb * kBK, wofs = kPk ? kb * kPackChunk : kofs;
 #pragma unroll
     for (int s = 0; s < kS; ++s) {
-      const v4i_t w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[s], kofs, 0);
-      const v4i_t w1 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[s] + 16u, kofs, 0);
+      const v4i_t w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[s], wofs, 0);
+      const v4i_t w1 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[s] + kWHalf, wofs, 0);
       wr[slot][s] = v8i_t{w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
     }
 #pragma unroll
@@ -1094,7 +1102,10 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
     swr[slot] = ld_scale(rsw, kb * 4u);
   };
 #pragma unroll
-  for (int j = 0; j < kD; ++j) load(j, (uint32_t)j);
+  for (int j = 0; j < kD; ++j) {
+    load(j, (uint32_t)j);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   if constexpr (kW == 1) {
     // a lone wave per strip group: fold each partial as soon as it is computed
@@ -1103,8 +1114,9 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
     for (int i = 0; i < kMT; ++i)
 #pragma unroll
       for (int s = 0; s < kS; ++s) acc1[i][s] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+    uint32_t c0 = 0;
 #pragma clang loop unroll(disable)
-    for (uint32_t c0 = 0; c0 < nch; c0 += kD) {
+    do {
 #pragma unroll
       for (int j = 0; j < kD; ++j) {
         // Branch-free: a step past the end (a clamped, valid block) gets the
@@ -1121,8 +1133,10 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
           }
         }
         load(j, kb + kD);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
+      c0 += kD;
+    } while (c0 < nch);
 #pragma unroll
     for (int i = 0; i < kMT; ++i) {
       const uint32_t m = 16u * i + lr;
@@ -1142,8 +1156,9 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
     v4f_t acc[kS];
 #pragma unroll
     for (int s = 0; s < kS; ++s) acc[s] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+    uint32_t c0 = 0;
 #pragma clang loop unroll(disable)
-    for (uint32_t c0 = 0; c0 < nch; c0 += kD) {
+    do {
 #pragma unroll
       for (int j = 0; j < kD; ++j) {
         // Branch-free partials (past the end they are parked but never folded),
@@ -1172,8 +1187,10 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
           }
         }
         load(j, c + kD);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
+      c0 += kD;
+    } while (c0 < nch);
     if (w < kMT && 16u * (uint32_t)w + lr < M) {
       const uint32_t m = 16u * (uint32_t)w + lr;
 #pragma unroll
@@ -1344,16 +1361,16 @@ static hipError_t launch_zero(uint16_t* p, int64_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int kMT, int kW, int kS>
+template <int kMT, int kW, int kS, bool kPk>
 static void launch_decode_t(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
                             uint32_t m, uint32_t n, uint32_t k, uint16_t* C, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_fp8_decode_kernel<kMT, kW, kS>), dim3(n / (16 * kS)), dim3(64 * kW), 0, stream,
+  hipLaunchKernelGGL((gemm_fp8_decode_kernel<kMT, kW, kS, kPk>), dim3(n / (16 * kS)), dim3(64 * kW), 0, stream,
                      A, sa, B, sb, m, n, k, C);
 }
 
 // kw is rounded to an instantiated value: at least kMT (one folding wave per
 // token sub-tile) and with the parked partials within LDS.
-template <int kMT, int kS>
+template <int kMT, int kS, bool kPk>
 static void launch_decode_ms(int kw, const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
                              uint32_t m, uint32_t n, uint32_t k, uint16_t* C, hipStream_t stream) {
   constexpr int kW2 = kMT > 2 ? kMT : 2;
@@ -1361,28 +1378,61 @@ static void launch_decode_ms(int kw, const uint8_t* A, const float* sa, const ui
   constexpr int kW16 = 16 * kMT * kS <= 64 ? 16 : kW8;
   constexpr int kW4 = 4 * kMT * kS <= 64 ? 4 : kW2;
   switch (kw) {
-    case 1: launch_decode_t<kMT, 1, kS>(A, sa, B, sb, m, n, k, C, stream); break;
-    case 2: launch_decode_t<kMT, kW2, kS>(A, sa, B, sb, m, n, k, C, stream); break;
-    case 4: launch_decode_t<kMT, kW4, kS>(A, sa, B, sb, m, n, k, C, stream); break;
-    case 8: launch_decode_t<kMT, kW8, kS>(A, sa, B, sb, m, n, k, C, stream); break;
-    default: launch_decode_t<kMT, kW16, kS>(A, sa, B, sb, m, n, k, C, stream); break;
+    case 1: launch_decode_t<kMT, 1, kS, kPk>(A, sa, B, sb, m, n, k, C, stream); break;
+    case 2: launch_decode_t<kMT, kW2, kS, kPk>(A, sa, B, sb, m, n, k, C, stream); break;
+    case 4: launch_decode_t<kMT, kW4, kS, kPk>(A, sa, B, sb, m, n, k, C, stream); break;
+    case 8: launch_decode_t<kMT, kW8, kS, kPk>(A, sa, B, sb, m, n, k, C, stream); break;
+    default: launch_decode_t<kMT, kW16, kS, kPk>(A, sa, B, sb, m, n, k, C, stream); break;
   }
 }
 
-template <int kMT>
+template <int kMT, bool kPk>
 static void launch_decode_m(int kw, int ks, const uint8_t* A, const float* sa, const uint8_t* B,
                             const float* sb, uint32_t m, uint32_t n, uint32_t k, uint16_t* C,
                             hipStream_t stream) {
-  if (ks == 2) launch_decode_ms<kMT, 2>(kw, A, sa, B, sb, m, n, k, C, stream);
-  else launch_decode_ms<kMT, 1>(kw, A, sa, B, sb, m, n, k, C, stream);
+  if (ks == 2) launch_decode_ms<kMT, 2, kPk>(kw, A, sa, B, sb, m, n, k, C, stream);
+  else launch_decode_ms<kMT, 1, kPk>(kw, A, sa, B, sb, m, n, k, C, stream);
 }
 
-static void launch_decode(int mt, int kw, int ks, const uint8_t* A, const float* sa, const uint8_t* B,
-                          const float* sb, uint32_t m, uint32_t n, uint32_t k, uint16_t* C,
-                          hipStream_t stream) {
-  if (mt == 1) launch_decode_m<1>(kw, ks, A, sa, B, sb, m, n, k, C, stream);
-  else if (mt == 2) launch_decode_m<2>(kw, ks, A, sa, B, sb, m, n, k, C, stream);
-  else launch_decode_m<4>(kw, ks, A, sa, B, sb, m, n, k, C, stream);
+template <bool kPk>
+static void launch_decode_p(int mt, int kw, int ks, const uint8_t* A, const float* sa, const uint8_t* B,
+                            const float* sb, uint32_t m, uint32_t n, uint32_t k, uint16_t* C,
+                            hipStream_t stream) {
+  if (mt == 1) launch_decode_m<1, kPk>(kw, ks, A, sa, B, sb, m, n, k, C, stream);
+  else if (mt == 2) launch_decode_m<2, kPk>(kw, ks, A, sa, B, sb, m, n, k, C, stream);
+  else launch_decode_m<4, kPk>(kw, ks, A, sa, B, sb, m, n, k, C, stream);
+}
+
+// Decode FProp (M <= 64) with the launch shape chosen from the problem size.
+// Strips per wave: 2 when there are at least 384 strips of 16 columns (each X
+// fragment then serves two strips), else 1.  Waves per strip group (K-phases):
+//   row-major weight: enough for about 1024 / mt streaming waves (a wave with
+//     mt token sub-tiles does mt times the MFMA and X-load work per K-block),
+//     or 2048 for long K, where a group's sequential chain is long;
+//   packed weight: one (a lone wave streaming its strips' contiguous range
+//     with no LDS fold was fastest at every 8B decode shape and M = 16 .. 64),
+//     more only while there are fewer than 192 strip groups;
+// at most 16, and at most one per two K-blocks.  Measured on the 8B decode
+// shapes (K = 4096 and 12288, N = 4096 .. 24576, M = 1 .. 64).
+static void launch_decode(bool packed, int64_t Mr, int64_t Nc, int64_t Kc, const uint8_t* A, const float* sa,
+                          const uint8_t* B, const float* sb, uint16_t* C, hipStream_t stream) {
+  const int64_t nkb = Kc / kBK;
+  const int mt = Mr <= 16 ? 1 : (Mr <= 32 ? 2 : 4);
+  const int ks = Nc / 16 >= 384 ? 2 : 1;
+  const int64_t groups = Nc / (16 * ks);
+  int kw = 16;
+  if (packed) {
+    kw = 1;
+    while (kw < 16 && groups * kw < 192 && 2 * kw <= (nkb + 1) / 2) kw *= 2;
+  } else {
+    const int64_t target = nkb >= 64 ? 2048 : 1024 / mt;
+    while (kw > 1 && (groups * kw > target || kw > (nkb + 1) / 2)) kw /= 2;
+  }
+  if (kw > 1 && kw < mt) kw = mt;  // wave i folds token sub-tile i
+  if (packed)
+    launch_decode_p<true>(mt, kw, ks, A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C, stream);
+  else
+    launch_decode_p<false>(mt, kw, ks, A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C, stream);
 }
 
 template <int kMode, int kOut = kOutBf16>
@@ -1399,22 +1449,7 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
   // rollout decode: weight-streaming kernel for up to 64 tokens (FProp)
   if (kMode == kFprop && kOut == kOutBf16 && Mr <= 64 && Nc * Kc < (int64_t(1) << 31) &&
       Mr * Kc < (int64_t(1) << 31)) {
-    // Strips per wave: 2 when there are at least 384 strips of 16 columns
-    // (each X fragment then serves two strips), else 1.  Waves per strip
-    // group: enough for about 1024 / mt streaming waves (a wave with mt token
-    // sub-tiles does mt times the MFMA and X-load work per K-block), or 2048
-    // for long K, where a group's sequential chain is long; at most 16, and
-    // at most one per two K-blocks.  Measured on the 8B decode shapes
-    // (K = 4096 and 12288, N = 4096 .. 24576, M = 1 .. 64).
-    const int64_t nkb = Kc / kBK;
-    const int mt = Mr <= 16 ? 1 : (Mr <= 32 ? 2 : 4);
-    const int ks = Nc / 16 >= 384 ? 2 : 1;
-    const int64_t groups = Nc / (16 * ks);
-    const int64_t target = nkb >= 64 ? 2048 : 1024 / mt;
-    int kw = 16;
-    while (kw > 1 && (groups * kw > target || kw > (nkb + 1) / 2)) kw /= 2;
-    if (kw > 1 && kw < mt) kw = mt;  // wave i folds token sub-tile i
-    launch_decode(mt, kw, ks, A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C, stream);
+    launch_decode(false, Mr, Nc, Kc, A, sa, B, sb, C, stream);
     return hipGetLastError();
   }
   // 65..256 rows: the K-split kernel when K is long and there are few column
@@ -1650,6 +1685,50 @@ hipError_t launch_gemm_fprop_splitk_noalloc(const uint8_t* qx, const float* sx, 
     if (e != hipSuccess) return e;
   }
   return launch_gemm_fprop_splitk(qx, sx, qw, sw, M, N, K, y, ws, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Rollout-packed weight codes.  A rollout batch re-reads the whole FP8 weight
+// at every decode step, and at that step the weight stream is the kernel's
+// whole cost.  Row-major [N][K] codes make each wave pull 128 bytes from each of
+// 16 rows 4 KB apart per K-block, which keeps HBM at about 4.3 TB/s however the
+// loads are grouped (measured: 16 to 1024 consecutive bytes per row and load,
+// 1 to 8 K-blocks per step); the same bytes stored so that each wave reads one
+// contiguous range reach about 5.5 TB/s.  The packed copy holds the same
+// codes in the order the decode kernel's lanes consume them:
+//   qwp[((t * nkb + kb) * 2 + h) * 1024 + 16 l + b] = qw[16 t + (l & 15)][128 kb + 32 (l >> 4) + 16 h + b]
+// (strip t of 16 rows, K-block kb, half h, lane l, byte b): lane l's two
+// 16-byte loads at 16 l and 1024 + 16 l of a chunk are the 32 consecutive
+// codes of row l & 15, K-slice l >> 4 that the 16x16x128 MFMA takes from it.
+// A permutation of bytes only: the packed FProp's products, scales and fold
+// are those of the row-major decode kernel, bit for bit.
+__global__ __launch_bounds__(256) void pack_weight_rollout_kernel(const uint8_t* __restrict__ qw, uint64_t N,
+                                                                  uint64_t K, uint8_t* __restrict__ qwp) {
+  const uint64_t nkb = K / kBK, units = N * K / 16;  // 16-byte units of the packed copy
+  for (uint64_t u = (uint64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += (uint64_t)gridDim.x * 256) {
+    const uint64_t l = u & 63, h = (u >> 6) & 1, c = u >> 7;
+    const uint64_t kb = c % nkb, t = c / nkb;
+    const uint64_t src = (16 * t + (l & 15)) * K + kBK * kb + 32 * (l >> 4) + 16 * h;
+    *reinterpret_cast<uint4*>(qwp + 16 * u) = *reinterpret_cast<const uint4*>(qw + src);
+  }
+}
+
+hipError_t launch_pack_weight_rollout(const uint8_t* qw, int64_t N, int64_t K, uint8_t* qwp, hipStream_t stream) {
+  const int64_t units = N * K / 16;
+  if (units == 0) return hipSuccess;
+  int64_t blocks = (units + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(pack_weight_rollout_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, qw, (uint64_t)N,
+                     (uint64_t)K, qwp);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fprop_packed(const uint8_t* qx, const float* sx, const uint8_t* qwp, const float* sw,
+                                    int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (K == 0) return launch_zero(y, M * N, stream);
+  launch_decode(true, M, N, K, qx, sx, qwp, sw, y, stream);
+  return hipGetLastError();
 }
 
 }  // namespace jetfp8

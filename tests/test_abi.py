@@ -238,3 +238,29 @@ def test_fprop_swiglu_quant_validation(jetlib):
     B = [(i + 1) << 40 for i in range(6)]  # far apart: no overlap even for huge shapes
     assert c(n, B[0], B[1], B[2], B[3], 1 << 20, 512, 4096, B[4], B[5], 0) == 5   # past 32-bit offsets
     assert c(n, 0, 0, P[2], P[3], 0, 512, 256, 0, 0, 0) == OK
+
+
+def test_pack_weight_rollout_and_fprop_packed_validation(jetlib):
+    for n in ("pack_weight_rollout", "gemm_fprop_packed"):
+        assert n in declared_functions()
+    # (qw, N, K, qwp)
+    p = "pack_weight_rollout"
+    assert c(p, P[0], 100, 128, P[1], 0) == EINVAL                  # N % 128
+    assert c(p, P[0], 128, 200, P[1], 0) == EINVAL                  # K % 128
+    assert c(p, P[0], -128, 128, P[1], 0) == EINVAL
+    assert c(p, 0, 128, 128, P[1], 0) == ENULL
+    assert c(p, P[0], 128, 128, P[1] + 8, 0) == EALIGN
+    assert c(p, P[0], 128, 128, P[0] + 8192, 0) == EALIAS            # qwp inside qw (16 KB)
+    B = [(i + 1) << 40 for i in range(6)]
+    assert c(p, B[0], 1 << 16, 1 << 15, B[1], 0) == 5               # 2^31 bytes: past 32-bit offsets
+    assert c(p, 0, 0, 128, 0, 0) == OK and c(p, 0, 128, 0, 0, 0) == OK
+    # (qx, sx, qwp, sw, M, N, K, y)
+    f = "gemm_fprop_packed"
+    assert c(f, P[0], P[1], P[2], P[3], 16, 100, 128, P[4], 0) == EINVAL       # N % 128
+    assert c(f, P[0], P[1], P[2], P[3], 16, 128, 100, P[4], 0) == EINVAL       # K % 128
+    assert c(f, P[0], P[1], P[2], P[3], 16, 128, 128, 0, 0) == ENULL
+    assert c(f, P[0], P[1], P[2] + 4, P[3], 16, 128, 128, P[4], 0) == EALIGN
+    assert c(f, P[0], P[1], P[2], P[3], 16, 128, 128, P[2] + 64, 0) == EALIAS  # y over qwp
+    assert c(f, P[0], P[1], P[2], P[3], 65, 128, 128, P[4], 0) == 5            # more than 64 rows
+    assert c(f, B[0], B[1], B[2], B[3], 16, 1 << 16, 1 << 15, B[4], 0) == 5    # weight past 2^31 bytes
+    assert c(f, 0, 0, P[2], P[3], 0, 128, 128, 0, 0) == OK                      # M = 0: nothing to do

@@ -24,11 +24,13 @@ object describes the slowest GEMM against the dense FP8 MFMA peak.  The
 (``--decode-m``, default 16): RMSNorm+quant, FProp against the FP8 QKV and
 gate+up weights, the fused SwiGLU + 1x128 quantisation of the gate+up output
 (the down projection's input) and the down FProp (weights quantised once,
-outside the timed region).  The FProps go
-through gemm_fprop_splitk, which at 65..256 tokens splits K across workgroups
-for the shapes with fewer output tiles than CUs (its workspace is allocated
-before the timed region).  Decode is bound by streaming the FP8 weights, so its
-kernels also report weight GB/s.
+outside the timed region).  Up to 64 tokens the weights are held in the
+rollout-packed order (pack_weight_rollout, outside the timed region) and the
+FProps go through gemm_fprop_packed_splitk; larger batches (or
+``--decode-rowmajor``) use the row-major codes and gemm_fprop_splitk.  Both
+split K across workgroups for the shapes too narrow to fill the chip (the
+workspace is allocated before the timed region).  Decode is bound by streaming
+the FP8 weights, so its kernels also report weight GB/s.
 
 ``--workload llama_layer`` times the forward + backward of the four linears
 of one Llama-3.1-8B layer (QKV, O, gate+up, down) at M = 16384 tokens, and
@@ -45,7 +47,7 @@ with swiglu_quant as a separate kernel and with the SwiGLU unfused.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--workload linear_8b_up|decode_8b|llama_layer|qwen32b_half_mlp|llama_mlp]
-                       [--decode-m M]
+                       [--decode-m M] [--decode-rowmajor]
 """
 
 import argparse
@@ -80,6 +82,8 @@ def parse():
     ap.add_argument("--workload", default="linear_8b_up",
                     choices=["linear_8b_up", "decode_8b", "llama_layer", "qwen32b_half_mlp", "llama_mlp"])
     ap.add_argument("--decode-m", type=int, default=16)
+    ap.add_argument("--decode-rowmajor", action="store_true",
+                    help="decode_8b: row-major weights and gemm_fprop_splitk at every batch size")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (torch copy_), whose HBM counters "
                          "calibrate FETCH_SIZE / WRITE_SIZE")
@@ -298,16 +302,24 @@ def bench_decode(args):
     # step to the next; consecutive steps therefore rotate over DECODE_WEIGHT_SETS
     # copies (704 MB), so every step streams its weights from HBM.
     sets = [wq] + [{k: (q.clone(), s.clone()) for k, (q, s) in wq.items()} for _ in range(DECODE_WEIGHT_SETS - 1)]
+    # Up to 64 tokens the rollout engine keeps its weight copy in the packed order
+    # (pack_weight_rollout, once per weight update: outside the timed region) and
+    # runs gemm_fprop_packed_splitk; larger batches use the row-major codes and
+    # gemm_fprop_splitk.  Either way, shapes with too few output tiles or strips
+    # for the chip split K through this workspace (allocated once, untimed).
+    packed = m <= 64 and not args.decode_rowmajor
+    if packed:
+        sets = [{k: (jet.pack_weight_rollout(q), s) for k, (q, s) in st.items()} for st in sets]
+        fprop, ws_bytes = jet.gemm_fprop_packed_splitk, jet.gemm_fprop_packed_splitk_workspace_bytes
+    else:
+        fprop, ws_bytes = jet.gemm_fprop_splitk, jet.gemm_fprop_splitk_workspace_bytes
     torch.cuda.synchronize()
     qx, sx = jet.rmsnorm_quant(x, gamma, d["eps"])
     y = {k: torch.empty((m, wq[k][0].shape[0]), dtype=torch.bfloat16, device=dev) for k in wq}
     inter = wq["w_down"][0].shape[1]  # 12288: the down projection's input width
     qh = torch.empty((m, inter), dtype=torch.uint8, device=dev)
     sh = torch.empty((inter // 128, m), dtype=torch.float32, device=dev)
-    # FProp through gemm_fprop_splitk: at 65..256 tokens the shapes with fewer
-    # output tiles than CUs split K across workgroups through this workspace
-    # (allocated once, outside the timed region); other shapes run gemm_fprop
-    need = max(jet.gemm_fprop_splitk_workspace_bytes(m, q.shape[0], q.shape[1]) for q, _ in wq.values())
+    need = max(ws_bytes(m, q.shape[0], q.shape[1]) for q, _ in wq.values())
     ws = torch.empty((max(need, 4) // 4,), dtype=torch.float32, device=dev)
     cur = [0]
 
@@ -317,10 +329,10 @@ def bench_decode(args):
 
     steps = [
         ("rmsnorm_quant", norm),
-        ("gemm_fprop_qkv", lambda: jet.gemm_fprop_splitk(qx, sx, *sets[cur[0]]["w_qkv"], y["w_qkv"], ws)),
-        ("gemm_fprop_gate_up", lambda: jet.gemm_fprop_splitk(qx, sx, *sets[cur[0]]["w_gu"], y["w_gu"], ws)),
+        ("gemm_fprop_qkv", lambda: fprop(qx, sx, *sets[cur[0]]["w_qkv"], y["w_qkv"], ws)),
+        ("gemm_fprop_gate_up", lambda: fprop(qx, sx, *sets[cur[0]]["w_gu"], y["w_gu"], ws)),
         ("swiglu_quant", lambda: jet.swiglu_quant(y["w_gu"], qh, sh)),
-        ("gemm_fprop_down", lambda: jet.gemm_fprop_splitk(qh, sh, *sets[cur[0]]["w_down"], y["w_down"], ws)),
+        ("gemm_fprop_down", lambda: fprop(qh, sh, *sets[cur[0]]["w_down"], y["w_down"], ws)),
     ]
     per, step_ms, wall, n_settle = time_steps(torch, steps, args.steps, args.warmup, dev)
     ms_per_step = float(np.mean(step_ms))
@@ -345,7 +357,9 @@ def bench_decode(args):
         "data": "synthetic",
         "config": {"workload": "qwen3_8b_decode", "M": m, "K": 4096,
                    "weights": "qkv 6144x4096, gate_up 24576x4096, down 4096x12288", "seed": 2,
-                   "weight_sets_rotated": DECODE_WEIGHT_SETS},
+                   "weight_sets_rotated": DECODE_WEIGHT_SETS,
+                   "weight_layout": "rollout-packed" if packed else "row-major",
+                   "fprop": "gemm_fprop_packed_splitk" if packed else "gemm_fprop_splitk"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["weight_GBps"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": kernels[dom]["frac_hbm"], "traffic": None},
         "kernels": kernels,

@@ -1204,6 +1204,193 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Decode FProp over the packed weight with the token operand shared through
+// LDS (gemm_fprop_packed).  At 17 .. 64 tokens a lone streaming wave fetches
+// kMT X fragments (2 KB each) per K-block next to its kS strips' 2 KB weight
+// chunks, so the token operand, re-read by every strip group from L2,
+// outweighs the weight.  Here a workgroup of kNW waves (each owning kS
+// strips) stages each K-block of X once, with direct-to-LDS loads that land in
+// fragment order (lane l's 16 bytes at 16 l of a 1 KB piece: token row
+// 16 i + l mod 16, K-bytes 32 (l div 16) + 16 h of the block, for sub-tile i
+// and half h), so the waves read their fragments back with conflict-free
+// 16-byte LDS reads.  Weight chunks stream into registers kD K-blocks ahead;
+// X stages are filled kD - 1 blocks ahead into kD LDS stages.  One barrier per
+// K-block publishes its X stage: every wave first waits for its own loads of
+// that block (the loads of a block are issued as one group per wave).  The
+// fold is the sequential one of the other FProp kernels, acc = fma(P_kb,
+// fl32(sx * sw), acc) in ascending K order, so the output is bitwise
+// gemm_fprop's.  With kPart, workgroup (g, s) folds only the s-th of gridDim.y
+// equal contiguous K ranges, from zero, and writes the fp32 partial to slice s
+// of a workspace (gemm_fprop_packed_splitk, which then adds the slices as
+// gemm_fprop_splitk does).
+template <int kMT, int kS, int kNW>
+struct DecodeXsCfg {
+  static constexpr int kPieces = 2 * kMT;                // 1 KB pieces of X per K-block
+  static constexpr int kPW = (kPieces + kNW - 1) / kNW;  // pieces each wave loads (a few twice when kNW > kPieces)
+  static constexpr int kGw = 2 * kS + 1;                 // weight and sw loads per K-block
+  static constexpr int kG = kGw + kPW + 1;               // all loads of one wave per K-block (X, its own sx copy)
+  static constexpr int kSlotRegs = 8 * kS + 1;
+  // registers: the slots, X fragments (8 kMT), accumulators (4 kMT kS) and
+  // addresses within the 256 a lone wave per SIMD may hold (no spills at any
+  // instantiated shape)
+  static constexpr int kFit = (150 - 8 * kMT - 4 * kMT * kS) / kSlotRegs;
+  static constexpr int kCnt = 63 / kG;                   // at most 63 loads in flight (the vmcnt field)
+  static constexpr int kD0 = kFit < kCnt ? kFit : kCnt;
+  static constexpr int kD = kD0 > 8 ? 8 : kD0;           // K-blocks in flight: weight slots = X stages
+  static constexpr int kXBytes = 2048 * kMT;             // X fragments of one stage
+  static constexpr int kStage = kXBytes + 256 * kNW;     // + each wave's copy of the block's 64 sx values
+  static_assert(kD >= 2, "at least two K-blocks in flight");
+  static_assert(kGw + (kD - 2) * kG <= 63, "wait count fits vmcnt");
+  static_assert(16 * kS * kNW <= kBN && kBN % (16 * kS * kNW) == 0, "a workgroup's strips lie in one weight block row");
+};
+
+template <int kMT, int kS, int kNW, bool kPart>
+__global__ __launch_bounds__(64 * kNW) void gemm_fp8_decode_xs_kernel(
+    const uint8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ Wp,
+    const float* __restrict__ sw, uint32_t M, uint32_t N, uint32_t K, void* __restrict__ Yv) {
+  using C = DecodeXsCfg<kMT, kS, kNW>;
+  constexpr int kD = C::kD;
+  // one array per stage, so that the compiler can tell a stage's LDS reads
+  // from the direct-to-LDS loads still in flight into the others
+  __shared__ __attribute__((aligned(1024))) uint8_t xs0[C::kStage], xs1[C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs2[kD > 2 ? C::kStage : 16], xs3[kD > 3 ? C::kStage : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs4[kD > 4 ? C::kStage : 16], xs5[kD > 5 ? C::kStage : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs6[kD > 6 ? C::kStage : 16], xs7[kD > 7 ? C::kStage : 16];
+  auto stage = [&](auto c) -> uint8_t* {
+    constexpr int i = decltype(c)::value;
+    if constexpr (i == 0) return xs0;
+    else if constexpr (i == 1) return xs1;
+    else if constexpr (i == 2) return xs2;
+    else if constexpr (i == 3) return xs3;
+    else if constexpr (i == 4) return xs4;
+    else if constexpr (i == 5) return xs5;
+    else if constexpr (i == 6) return xs6;
+    else return xs7;
+  };
+  const int t = threadIdx.x, l = t & 63, lr = l & 15, lk = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const uint32_t strip0 = (blockIdx.x * kNW + (uint32_t)w) * kS;  // this wave's first strip of 16 columns
+  const uint32_t n0 = 16u * strip0;
+  const uint32_t nkb = K / kBK;
+  const uint32_t nloc = nkb / gridDim.y, kbase = blockIdx.y * nloc;  // this workgroup's K-blocks
+  const uint32_t last = kbase + nloc - 1;
+  const rsrc_t rw = make_rsrc(Wp, N * K);
+  const rsrc_t rx = make_rsrc(X, M * K);
+  const rsrc_t rsx = make_rsrc(sx, nkb * M * 4u);
+  const rsrc_t rsw = make_rsrc(sw + (n0 / kBN) * nkb, nkb * 4u);
+  uint32_t w_off[kS], xm[kMT], xp_off[C::kPW], xp_lds[C::kPW];
+  const uint32_t sx_lane = (uint32_t)(l < (int)M ? l : (int)M - 1) * 4u;  // token l's sx (ragged: the last token's)
+  const uint32_t sx_lds = C::kXBytes + 256u * w;                         // this wave's sx copy in a stage
+#pragma unroll
+  for (int s = 0; s < kS; ++s) w_off[s] = (strip0 + s) * nkb * kPackChunk + 16u * l;
+#pragma unroll
+  for (int i = 0; i < kMT; ++i) xm[i] = (16u * i + lr) < M ? (16u * i + lr) : (M - 1);  // ragged: repeat the last token
+#pragma unroll
+  for (int q = 0; q < C::kPW; ++q) {
+    const int p = (w + kNW * q) % C::kPieces;  // piece p: sub-tile p / 2, half p % 2
+    xp_off[q] = xm[p >> 1] * K + 32u * lk + 16u * (p & 1);
+    xp_lds[q] = 1024u * p;
+  }
+  v8i_t wr[kD][kS];
+  float swr[kD];
+  auto load_w = [&](int slot, uint32_t kb) {
+    const uint32_t wofs = kb * kPackChunk;
+#pragma unroll
+    for (int s = 0; s < kS; ++s) {
+      const v4i_t w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[s], wofs, 0);
+      const v4i_t w1 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[s] + 1024u, wofs, 0);
+      wr[slot][s] = v8i_t{w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    }
+    swr[slot] = ld_scale(rsw, kb * 4u);
+  };
+  // the block's X pieces (shared) and its M sx values (this wave's own copy)
+  auto load_x = [&](uint8_t* st, uint32_t kb) {
+#pragma unroll
+    for (int q = 0; q < C::kPW; ++q) buf_to_lds16(rx, st + xp_lds[q], xp_off[q], kb * kBK);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, (__attribute__((address_space(3))) void*)(st + sx_lds), 4,
+                                             sx_lane, kb * M * 4u, 0, 0);
+  };
+  // local block index -> K-block (past the end: the last one, loaded but not folded)
+  auto clampb = [&](uint32_t kl) { return kl < nloc ? kbase + kl : last; };
+
+  // prologue: W(0), then X(j - 1), W(j) for j = 1 .. kD - 1 -- the order of the
+  // groups the loop issues, X(kb + kD - 1) then W(kb + kD)
+  load_w(0, kbase);
+  __builtin_amdgcn_sched_barrier(0);
+  static_for<kD - 1>([&](auto c) {
+    constexpr int j = decltype(c)::value + 1;
+    load_x(stage(std::integral_constant<int, j - 1>{}), clampb(j - 1));
+    load_w(j, clampb(j));
+    __builtin_amdgcn_sched_barrier(0);
+  });
+
+  v4f_t acc[kMT][kS];
+#pragma unroll
+  for (int i = 0; i < kMT; ++i)
+#pragma unroll
+    for (int s = 0; s < kS; ++s) acc[i][s] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+  uint32_t c0 = 0;
+#pragma clang loop unroll(disable)
+  do {
+    static_for<kD>([&](auto c) {
+      constexpr int j = decltype(c)::value;
+      const uint32_t kb = c0 + j;
+      // X(kb) was issued before W(kb + 1) and the kD - 2 later groups
+      wait_vmem_le<C::kGw + (kD - 2) * C::kG>();
+      lds_barrier();
+      const uint8_t* st = stage(c);
+      v8i_t xf[kMT];
+      float sxv[kMT];
+#pragma unroll
+      for (int i = 0; i < kMT; ++i) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(st + 2048 * i + 16 * l);
+        const uint4 hi = *reinterpret_cast<const uint4*>(st + 2048 * i + 1024 + 16 * l);
+        xf[i] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        sxv[i] = reinterpret_cast<const float*>(st + sx_lds)[xm[i]];
+      }
+#pragma unroll
+      for (int i = 0; i < kMT; ++i) {
+        // branch-free: a block past the end gets the factor 0 and leaves acc
+        // unchanged bit for bit (acc is never -0)
+        const float sc = kb < nloc ? sxv[i] * swr[j] : 0.0f;
+#pragma unroll
+        for (int s = 0; s < kS; ++s) {
+          const v4f_t p = mfma_fp8(wr[j][s], xf[i]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][s][e] = fmaf(p[e], sc, acc[i][s][e]);
+        }
+      }
+      // refill: X(kb + kD - 1) into the stage of block kb - 1, which every wave
+      // finished reading before this step's barrier; W(kb + kD) into slot j
+      load_x(stage(std::integral_constant<int, (j + kD - 1) % kD>{}), clampb(kb + kD - 1));
+      load_w(j, clampb(kb + kD));
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    c0 += kD;
+  } while (c0 < nloc);
+#pragma unroll
+  for (int i = 0; i < kMT; ++i) {
+    const uint32_t m = 16u * i + lr;
+    if (m < M) {
+#pragma unroll
+      for (int s = 0; s < kS; ++s) {
+        const size_t o = (size_t)m * N + n0 + 16 * s + 4 * lk;
+        if constexpr (kPart) {
+          float* P = static_cast<float*>(Yv) + (size_t)blockIdx.y * M * N;
+          *reinterpret_cast<float4*>(P + o) = make_float4(acc[i][s][0], acc[i][s][1], acc[i][s][2], acc[i][s][3]);
+        } else {
+          const uint32_t lo = f32_to_bf16_rne(acc[i][s][0]) | (f32_to_bf16_rne(acc[i][s][1]) << 16);
+          const uint32_t hi = f32_to_bf16_rne(acc[i][s][2]) | (f32_to_bf16_rne(acc[i][s][3]) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Yv) + o) = make_uint2(lo, hi);
+        }
+      }
+    }
+  }
+  // no direct-to-LDS load may still be in flight when the workgroup ends
+  wait_vmem();
+}
+
+// ---------------------------------------------------------------------------
 // Mid-size FProp (64 < M <= 256 tokens: large rollout batches).  Too few
 // output tiles to fill the chip without splitting K, so each workgroup owns a
 // 64 x 64 output tile and its 8 waves split the K-blocks: wave w takes blocks
@@ -1723,11 +1910,94 @@ hipError_t launch_pack_weight_rollout(const uint8_t* qw, int64_t N, int64_t K, u
   return hipGetLastError();
 }
 
+template <int kMT, int kS, int kNW>
+static void launch_decode_xs_t(int splits, const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
+                               uint32_t m, uint32_t n, uint32_t k, void* C, hipStream_t stream) {
+  const dim3 grid(n / (16 * kS * kNW), (unsigned)splits);
+  if (splits > 1)
+    hipLaunchKernelGGL((gemm_fp8_decode_xs_kernel<kMT, kS, kNW, true>), grid, dim3(64 * kNW), 0, stream, A, sa, B,
+                       sb, m, n, k, C);
+  else
+    hipLaunchKernelGGL((gemm_fp8_decode_xs_kernel<kMT, kS, kNW, false>), grid, dim3(64 * kNW), 0, stream, A, sa, B,
+                       sb, m, n, k, C);
+}
+
+template <int kMT>
+static void launch_decode_xs_m(int nw, int ks, int splits, const uint8_t* A, const float* sa, const uint8_t* B,
+                               const float* sb, uint32_t m, uint32_t n, uint32_t k, void* C, hipStream_t stream) {
+  if (nw == 2) {
+    if (ks == 2) launch_decode_xs_t<kMT, 2, 2>(splits, A, sa, B, sb, m, n, k, C, stream);
+    else launch_decode_xs_t<kMT, 1, 2>(splits, A, sa, B, sb, m, n, k, C, stream);
+  } else {
+    if (ks == 2) launch_decode_xs_t<kMT, 2, 4>(splits, A, sa, B, sb, m, n, k, C, stream);
+    else launch_decode_xs_t<kMT, 1, 4>(splits, A, sa, B, sb, m, n, k, C, stream);
+  }
+}
+
+// splits > 1: fp32 partials into C (splits x M x N floats); splits must divide K / 128
+static void launch_decode_xs(int nw, int ks, int splits, int64_t Mr, int64_t Nc, int64_t Kc, const uint8_t* A,
+                             const float* sa, const uint8_t* B, const float* sb, void* C, hipStream_t stream) {
+  const uint32_t m = (uint32_t)Mr, n = (uint32_t)Nc, k = (uint32_t)Kc;
+  if (Mr <= 16) launch_decode_xs_m<1>(nw, ks, splits, A, sa, B, sb, m, n, k, C, stream);
+  else if (Mr <= 32) launch_decode_xs_m<2>(nw, ks, splits, A, sa, B, sb, m, n, k, C, stream);
+  else launch_decode_xs_m<4>(nw, ks, splits, A, sa, B, sb, m, n, k, C, stream);
+}
+
+// Packed FProp, sequential fold.  Up to 32 rows the lone-wave decode kernel;
+// from 33 rows, when there are at least 384 strips of 16 columns, the
+// X-sharing kernel with 4 waves of 2 strips (from 1536 strips) or 2 waves of
+// 1 (at most 192 workgroups then hold every strip); below 384 strips the
+// decode kernel, whose K-phases keep the chip busy.  Measured at the 8B decode
+// shapes (graph replays, 4 rotated weights): M = 64: QKV 16.3 -> 12.9 us,
+// gate+up 31.7 -> 28.0 us; M = 32 and the down projection at M = 64: the
+// decode kernel was as fast or faster.
 hipError_t launch_gemm_fprop_packed(const uint8_t* qx, const float* sx, const uint8_t* qwp, const float* sw,
                                     int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   if (K == 0) return launch_zero(y, M * N, stream);
+  const int64_t strips = N / 16;
+  if (M > 32 && strips >= 384) {
+    if (strips >= 1536) launch_decode_xs(4, 2, 1, M, N, K, qx, sx, qwp, sw, y, stream);
+    else launch_decode_xs(2, 1, 1, M, N, K, qx, sx, qwp, sw, y, stream);
+    return hipGetLastError();
+  }
   launch_decode(true, M, N, K, qx, sx, qwp, sw, y, stream);
+  return hipGetLastError();
+}
+
+// K-shares of gemm_fprop_packed_splitk: none up to 16 rows or with at least
+// 384 strips (the sequential kernels fill the chip); otherwise X-sharing
+// workgroups of 2 waves (17 .. 32 rows) or 4 (33 .. 64), one strip each, and
+// the fewest power-of-two shares that give 256 workgroups, each share at
+// least four K-blocks.  Measured on the 8B down projection (N = 4096,
+// K = 12288): M = 64: 21.6 us with gemm_fprop_splitk's 16 shares of the
+// 128 x 128 kernel, 18.1 us with 4 shares here; M = 32: 19.3 -> 14.4 us.
+int fprop_packed_split_count(int64_t M, int64_t N, int64_t K) {
+  if (M <= 16 || M > 64 || N % kBN != 0 || K % kBK != 0) return 1;
+  const int64_t strips = N / 16, nkb = K / kBK;
+  if (strips >= 384) return 1;
+  const int64_t groups = strips / (M > 32 ? 4 : 2);
+  int s = 1;
+  while (groups * s < 256 && nkb % (2 * s) == 0 && nkb / (2 * s) >= 4) s *= 2;
+  return s;
+}
+
+int64_t fprop_packed_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const int s = fprop_packed_split_count(M, N, K);
+  return s > 1 ? (int64_t)s * M * N * 4 : 0;
+}
+
+hipError_t launch_gemm_fprop_packed_splitk(const uint8_t* qx, const float* sx, const uint8_t* qwp, const float* sw,
+                                           int64_t M, int64_t N, int64_t K, uint16_t* y, float* ws,
+                                           hipStream_t stream) {
+  const int s = fprop_packed_split_count(M, N, K);
+  if (s <= 1) return launch_gemm_fprop_packed(qx, sx, qwp, sw, M, N, K, y, stream);
+  launch_decode_xs(M > 32 ? 4 : 2, 1, s, M, N, K, qx, sx, qwp, sw, ws, stream);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = M * N;
+  hipLaunchKernelGGL(splitk_reduce_bf16_kernel, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, stream, ws, s,
+                     n, y);
   return hipGetLastError();
 }
 

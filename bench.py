@@ -26,10 +26,10 @@ gate+up weights, the fused SwiGLU + 1x128 quantisation of the gate+up output
 (the down projection's input) and the down FProp (weights quantised once,
 outside the timed region).  Up to 64 tokens the weights are held in the
 rollout-packed order (pack_weight_rollout, outside the timed region) and the
-FProps go through gemm_fprop_packed_splitk; larger batches (or
-``--decode-rowmajor``) use the row-major codes and gemm_fprop_splitk.  Both
-split K across workgroups for the shapes too narrow to fill the chip (the
-workspace is allocated before the timed region).  Decode is bound by streaming
+FProps go through gemm_fprop_packed; larger batches (or ``--decode-rowmajor``)
+use the row-major codes and gemm_fprop_splitk, which splits K across
+workgroups for the shapes with fewer output tiles than CUs (its workspace is
+allocated before the timed region).  Decode is bound by streaming
 the FP8 weights, so its kernels also report weight GB/s.
 
 ``--workload llama_layer`` times the forward + backward of the four linears
@@ -304,23 +304,25 @@ def bench_decode(args):
     sets = [wq] + [{k: (q.clone(), s.clone()) for k, (q, s) in wq.items()} for _ in range(DECODE_WEIGHT_SETS - 1)]
     # Up to 64 tokens the rollout engine keeps its weight copy in the packed order
     # (pack_weight_rollout, once per weight update: outside the timed region) and
-    # runs gemm_fprop_packed_splitk; larger batches use the row-major codes and
-    # gemm_fprop_splitk.  Either way, shapes with too few output tiles or strips
-    # for the chip split K through this workspace (allocated once, untimed).
+    # runs gemm_fprop_packed; larger batches use the row-major codes and
+    # gemm_fprop_splitk, which splits K for the shapes with fewer output tiles
+    # than CUs through this workspace (allocated once, untimed).
     packed = m <= 64 and not args.decode_rowmajor
     if packed:
         sets = [{k: (jet.pack_weight_rollout(q), s) for k, (q, s) in st.items()} for st in sets]
-        fprop, ws_bytes = jet.gemm_fprop_packed_splitk, jet.gemm_fprop_packed_splitk_workspace_bytes
-    else:
-        fprop, ws_bytes = jet.gemm_fprop_splitk, jet.gemm_fprop_splitk_workspace_bytes
     torch.cuda.synchronize()
     qx, sx = jet.rmsnorm_quant(x, gamma, d["eps"])
     y = {k: torch.empty((m, wq[k][0].shape[0]), dtype=torch.bfloat16, device=dev) for k in wq}
     inter = wq["w_down"][0].shape[1]  # 12288: the down projection's input width
     qh = torch.empty((m, inter), dtype=torch.uint8, device=dev)
     sh = torch.empty((inter // 128, m), dtype=torch.float32, device=dev)
-    need = max(ws_bytes(m, q.shape[0], q.shape[1]) for q, _ in wq.values())
+    need = max(jet.gemm_fprop_splitk_workspace_bytes(m, q.shape[0], q.shape[1]) for q, _ in wq.values())
     ws = torch.empty((max(need, 4) // 4,), dtype=torch.float32, device=dev)
+
+    def fprop(qa, sa, qb, sb, out, work):
+        if packed:
+            return jet.gemm_fprop_packed(qa, sa, qb, sb, out)
+        return jet.gemm_fprop_splitk(qa, sa, qb, sb, out, work)
     cur = [0]
 
     def norm():
@@ -359,7 +361,7 @@ def bench_decode(args):
                    "weights": "qkv 6144x4096, gate_up 24576x4096, down 4096x12288", "seed": 2,
                    "weight_sets_rotated": DECODE_WEIGHT_SETS,
                    "weight_layout": "rollout-packed" if packed else "row-major",
-                   "fprop": "gemm_fprop_packed_splitk" if packed else "gemm_fprop_splitk"},
+                   "fprop": "gemm_fprop_packed" if packed else "gemm_fprop_splitk"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["weight_GBps"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": kernels[dom]["frac_hbm"], "traffic": None},
         "kernels": kernels,

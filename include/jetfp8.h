@@ -301,38 +301,6 @@ int gemm_fprop_packed(const uint8_t* qx, const float* sx, const uint8_t* qwp, co
                       int64_t N, int64_t K, uint16_t* y, void* stream);
 
 /*
- * gemm_fprop_packed_splitk -- gemm_fprop_packed with the contraction split
- * across workgroups where the sequential kernels cannot fill the chip: 17 ..
- * 64 rows and fewer than 384 strips of 16 columns (N < 6144), such as the 8B
- * down projection ([P3-LAYOUT], [P3-CORE], [P3-STEPS] step 2; the rollout's
- * FProp, [P3-WEAK]).  K's 128-deep blocks are split into S equal contiguous
- * ranges (S a power of two: the fewest that give 256 workgroups of 2 waves
- * (17 .. 32 rows) or 4 (33 .. 64), one strip per wave, and at least four
- * blocks per range); range s is folded in ascending order, from zero, as in
- * gemm_fprop, into an fp32 partial P_s, and
- *   y[m][n] = bf16(((P_0 + P_1) + P_2) + ... + P_{S-1}),
- * deterministic, and the same for a row in any batch of the same S, but not
- * bitwise the sequential fold.  Shapes it does not split run gemm_fprop_packed
- * (S = 1, bitwise gemm_fprop).
- *   qx, sx, qwp, sw, y : as gemm_fprop_packed.
- *   workspace       : f32 device buffer of at least
- *                     gemm_fprop_packed_splitk_workspace_bytes(M, N, K) bytes
- *                     (S * M * N * 4; 16-byte aligned, overlapping no operand);
- *                     contents ignored on entry and unspecified on return; may
- *                     be NULL when that size is 0.
- *   workspace_bytes : its size; smaller than required -> JETFP8_EINVAL.
- * 0 <= M <= 64 (JETFP8_EUNSUPPORTED above), N % 128 == 0, K % 128 == 0,
- * N * K < 2^31, M * K < 2^31.
- */
-int gemm_fprop_packed_splitk(const uint8_t* qx, const float* sx, const uint8_t* qwp, const float* sw, int64_t M,
-                             int64_t N, int64_t K, uint16_t* y, float* workspace, int64_t workspace_bytes,
-                             void* stream);
-
-/* Workspace bytes gemm_fprop_packed_splitk needs (S * M * N * 4, or 0 when it
- * does not split); -1 for an invalid shape.  Needs no GPU. */
-int64_t gemm_fprop_packed_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
-
-/*
  * gemm_fprop_swiglu_quant -- the gate+up projection's FProp fused with SwiGLU
  * and the 1x128 quantisation of its result: the FP8 input of the down
  * projection, with no bf16 gate+up output written at all ([P3-CORE] on fusing

@@ -13,8 +13,6 @@ from ._lib import (  # noqa: F401
     gemm_dgrad,
     gemm_fprop,
     gemm_fprop_packed,
-    gemm_fprop_packed_splitk,
-    gemm_fprop_packed_splitk_workspace_bytes,
     gemm_fprop_quant,
     gemm_fprop_splitk,
     gemm_fprop_splitk_noalloc,

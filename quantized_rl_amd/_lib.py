@@ -28,7 +28,6 @@ SIGNATURES = {
     "gemm_fprop_splitk_noalloc": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
     "pack_weight_rollout": [_c_p, _c_i64, _c_i64, _c_p, _c_p],
     "gemm_fprop_packed": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
-    "gemm_fprop_packed_splitk": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p],
     "gemm_fprop_swiglu_quant": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "gemm_fprop_quant": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p],
     "gemm_dgrad": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
@@ -64,8 +63,6 @@ def lib():
         L.rmsnorm_backward_workspace_bytes.restype = _c_i64
         L.gemm_fprop_splitk_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64]
         L.gemm_fprop_splitk_workspace_bytes.restype = _c_i64
-        L.gemm_fprop_packed_splitk_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64]
-        L.gemm_fprop_packed_splitk_workspace_bytes.restype = _c_i64
         L.jetfp8_status_string.argtypes = [ctypes.c_int]
         L.jetfp8_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -295,37 +292,6 @@ def gemm_fprop_packed(qx, sx, qwp, sw, y=None):
     _check("gemm_fprop_packed", lib().gemm_fprop_packed(
         qx.data_ptr(), sx.data_ptr(), qwp.data_ptr(), sw.data_ptr(), M, N, K, y.data_ptr(),
         _stream(qx.device)))
-    return y
-
-
-def gemm_fprop_packed_splitk_workspace_bytes(M, N, K):
-    """Bytes of fp32 workspace gemm_fprop_packed_splitk needs (0: it does not split)."""
-    n = lib().gemm_fprop_packed_splitk_workspace_bytes(M, N, K)
-    if n < 0:
-        raise JetFP8Error("gemm_fprop_packed_splitk_workspace_bytes", 1, f"invalid shape {M}x{N}x{K}")
-    return n
-
-
-def gemm_fprop_packed_splitk(qx, sx, qwp, sw, y=None, workspace=None):
-    """gemm_fprop_packed with K split across workgroups for 17..64 rows and fewer
-    than 384 strips of 16 columns, through an fp32 workspace of
-    gemm_fprop_packed_splitk_workspace_bytes (allocated here when not given)."""
-    torch = _torch()
-    M, K = qx.shape
-    N = qwp.shape[0]
-    _need(qx, torch.uint8, (M, K), "qx")
-    _need(sx, torch.float32, (K // 128, M), "sx")
-    _need(qwp, torch.uint8, (N, K), "qwp")
-    _need(sw, torch.float32, (N // 128, K // 128), "sw")
-    y = _empty((M, N), torch.bfloat16, qx.device) if y is None else _need(y, torch.bfloat16, (M, N), "y")
-    need = gemm_fprop_packed_splitk_workspace_bytes(M, N, K)
-    if workspace is None:
-        workspace = _empty((max(need, 4) // 4,), torch.float32, qx.device)
-    if workspace.dtype != torch.float32 or not workspace.is_contiguous() or workspace.device != qx.device:
-        raise ValueError("workspace: a contiguous float32 tensor on the operands' device")
-    _check("gemm_fprop_packed_splitk", lib().gemm_fprop_packed_splitk(
-        qx.data_ptr(), sx.data_ptr(), qwp.data_ptr(), sw.data_ptr(), M, N, K, y.data_ptr(),
-        workspace.data_ptr(), workspace.numel() * 4, _stream(qx.device)))
     return y
 
 

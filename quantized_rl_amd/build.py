@@ -28,6 +28,10 @@ FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the decode and 128 x 128 kernels rescale
+    # every block product with VALU FMAs, which otherwise first copy it out of
+    # the accumulation registers (v_accvgpr_read, 4 per MFMA)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall",
 ]
 

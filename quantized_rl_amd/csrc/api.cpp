@@ -201,25 +201,6 @@ int gemm_fprop_packed(const uint8_t* qx, const float* sx, const uint8_t* qwp, co
   return launched(jetfp8::launch_gemm_fprop_packed(qx, sx, qwp, sw, M, N, K, y, as_stream(stream)));
 }
 
-int64_t gemm_fprop_packed_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || N % 128 || K % 128) return -1;
-  return jetfp8::fprop_packed_splitk_workspace_bytes(M, N, K);
-}
-
-int gemm_fprop_packed_splitk(const uint8_t* qx, const float* sx, const uint8_t* qwp, const float* sw, int64_t M,
-                             int64_t N, int64_t K, uint16_t* y, float* workspace, int64_t workspace_bytes,
-                             void* stream) {
-  const int64_t ws = gemm_fprop_packed_splitk_workspace_bytes(M, N, K);
-  if (ws < 0 || workspace_bytes < ws) return JETFP8_EINVAL;
-  if (int st = check_ptrs({{qx, M * K}, {sx, 4 * (M * K / 128)}, {qwp, N * K},
-                           {sw, 4 * (N * K / (128 * 128))}},
-                          {{y, 2 * M * N}, {workspace, ws}}))
-    return st;
-  const int64_t lim = int64_t(1) << 31;
-  if (M > 64 || N * K >= lim || M * K >= lim) return JETFP8_EUNSUPPORTED;
-  return launched(jetfp8::launch_gemm_fprop_packed_splitk(qx, sx, qwp, sw, M, N, K, y, workspace, as_stream(stream)));
-}
-
 int gemm_fprop_swiglu_quant(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw, int64_t M,
                             int64_t N, int64_t K, uint8_t* qh, float* sh, void* stream) {
   if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || N % 256 || K % 128) return JETFP8_EINVAL;

@@ -1064,6 +1064,7 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
   const int t = threadIdx.x, l = t & 63, lr = l & 15, lk = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const uint32_t n0 = blockIdx.x * (16u * kS);  // the workgroup's kS strips of 16 columns
+  const uint32_t mb = blockIdx.y * (16u * kMT);  // its first token (a grid row per 16 kMT tokens)
   const uint32_t nkb = K / kBK;
   const uint32_t nch = (nkb + kW - 1) / kW;
   const rsrc_t rw = make_rsrc(W, N * K);
@@ -1074,7 +1075,7 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
     w_off[s] = kPk ? (n0 / 16u + s) * nkb * kPackChunk + 16u * l : (n0 + 16u * s + lr) * K + 32u * lk;
 #pragma unroll
   for (int i = 0; i < kMT; ++i) {
-    xm[i] = (16u * i + lr) < M ? (16u * i + lr) : (M - 1);  // ragged tail: repeat the last token
+    xm[i] = (mb + 16u * i + lr) < M ? (mb + 16u * i + lr) : (M - 1);  // ragged tail: repeat the last token
     x_off[i] = xm[i] * K + 32u * lk;
   }
   const rsrc_t rsx = make_rsrc(sx, nkb * M * 4u);
@@ -1139,7 +1140,7 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
     } while (c0 < nch);
 #pragma unroll
     for (int i = 0; i < kMT; ++i) {
-      const uint32_t m = 16u * i + lr;
+      const uint32_t m = mb + 16u * i + lr;
       if (m < M) {
 #pragma unroll
         for (int s = 0; s < kS; ++s) {
@@ -1191,8 +1192,8 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
       }
       c0 += kD;
     } while (c0 < nch);
-    if (w < kMT && 16u * (uint32_t)w + lr < M) {
-      const uint32_t m = 16u * (uint32_t)w + lr;
+    if (w < kMT && mb + 16u * (uint32_t)w + lr < M) {
+      const uint32_t m = mb + 16u * (uint32_t)w + lr;
 #pragma unroll
       for (int s = 0; s < kS; ++s) {
         const uint32_t lo = f32_to_bf16_rne(acc[s][0]) | (f32_to_bf16_rne(acc[s][1]) << 16);
@@ -1219,10 +1220,7 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
 // that block (the loads of a block are issued as one group per wave).  The
 // fold is the sequential one of the other FProp kernels, acc = fma(P_kb,
 // fl32(sx * sw), acc) in ascending K order, so the output is bitwise
-// gemm_fprop's.  With kPart, workgroup (g, s) folds only the s-th of gridDim.y
-// equal contiguous K ranges, from zero, and writes the fp32 partial to slice s
-// of a workspace (gemm_fprop_packed_splitk, which then adds the slices as
-// gemm_fprop_splitk does).
+// gemm_fprop's.
 template <int kMT, int kS, int kNW>
 struct DecodeXsCfg {
   static constexpr int kPieces = 2 * kMT;                // 1 KB pieces of X per K-block
@@ -1244,10 +1242,10 @@ struct DecodeXsCfg {
   static_assert(16 * kS * kNW <= kBN && kBN % (16 * kS * kNW) == 0, "a workgroup's strips lie in one weight block row");
 };
 
-template <int kMT, int kS, int kNW, bool kPart>
+template <int kMT, int kS, int kNW>
 __global__ __launch_bounds__(64 * kNW) void gemm_fp8_decode_xs_kernel(
     const uint8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ Wp,
-    const float* __restrict__ sw, uint32_t M, uint32_t N, uint32_t K, void* __restrict__ Yv) {
+    const float* __restrict__ sw, uint32_t M, uint32_t N, uint32_t K, uint16_t* __restrict__ Y) {
   using C = DecodeXsCfg<kMT, kS, kNW>;
   constexpr int kD = C::kD;
   // one array per stage, so that the compiler can tell a stage's LDS reads
@@ -1271,9 +1269,7 @@ __global__ __launch_bounds__(64 * kNW) void gemm_fp8_decode_xs_kernel(
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const uint32_t strip0 = (blockIdx.x * kNW + (uint32_t)w) * kS;  // this wave's first strip of 16 columns
   const uint32_t n0 = 16u * strip0;
-  const uint32_t nkb = K / kBK;
-  const uint32_t nloc = nkb / gridDim.y, kbase = blockIdx.y * nloc;  // this workgroup's K-blocks
-  const uint32_t last = kbase + nloc - 1;
+  const uint32_t nkb = K / kBK, last = nkb - 1;
   const rsrc_t rw = make_rsrc(Wp, N * K);
   const rsrc_t rx = make_rsrc(X, M * K);
   const rsrc_t rsx = make_rsrc(sx, nkb * M * 4u);
@@ -1310,12 +1306,11 @@ __global__ __launch_bounds__(64 * kNW) void gemm_fp8_decode_xs_kernel(
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, (__attribute__((address_space(3))) void*)(st + sx_lds), 4,
                                              sx_lane, kb * M * 4u, 0, 0);
   };
-  // local block index -> K-block (past the end: the last one, loaded but not folded)
-  auto clampb = [&](uint32_t kl) { return kl < nloc ? kbase + kl : last; };
+  auto clampb = [&](uint32_t kb) { return kb < last ? kb : last; };  // past the end: a valid block, not folded
 
   // prologue: W(0), then X(j - 1), W(j) for j = 1 .. kD - 1 -- the order of the
   // groups the loop issues, X(kb + kD - 1) then W(kb + kD)
-  load_w(0, kbase);
+  load_w(0, 0);
   __builtin_amdgcn_sched_barrier(0);
   static_for<kD - 1>([&](auto c) {
     constexpr int j = decltype(c)::value + 1;
@@ -1352,7 +1347,7 @@ __global__ __launch_bounds__(64 * kNW) void gemm_fp8_decode_xs_kernel(
       for (int i = 0; i < kMT; ++i) {
         // branch-free: a block past the end gets the factor 0 and leaves acc
         // unchanged bit for bit (acc is never -0)
-        const float sc = kb < nloc ? sxv[i] * swr[j] : 0.0f;
+        const float sc = kb < nkb ? sxv[i] * swr[j] : 0.0f;
 #pragma unroll
         for (int s = 0; s < kS; ++s) {
           const v4f_t p = mfma_fp8(wr[j][s], xf[i]);
@@ -1367,22 +1362,16 @@ __global__ __launch_bounds__(64 * kNW) void gemm_fp8_decode_xs_kernel(
       __builtin_amdgcn_sched_barrier(0);
     });
     c0 += kD;
-  } while (c0 < nloc);
+  } while (c0 < nkb);
 #pragma unroll
   for (int i = 0; i < kMT; ++i) {
     const uint32_t m = 16u * i + lr;
     if (m < M) {
 #pragma unroll
       for (int s = 0; s < kS; ++s) {
-        const size_t o = (size_t)m * N + n0 + 16 * s + 4 * lk;
-        if constexpr (kPart) {
-          float* P = static_cast<float*>(Yv) + (size_t)blockIdx.y * M * N;
-          *reinterpret_cast<float4*>(P + o) = make_float4(acc[i][s][0], acc[i][s][1], acc[i][s][2], acc[i][s][3]);
-        } else {
-          const uint32_t lo = f32_to_bf16_rne(acc[i][s][0]) | (f32_to_bf16_rne(acc[i][s][1]) << 16);
-          const uint32_t hi = f32_to_bf16_rne(acc[i][s][2]) | (f32_to_bf16_rne(acc[i][s][3]) << 16);
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Yv) + o) = make_uint2(lo, hi);
-        }
+        const uint32_t lo = f32_to_bf16_rne(acc[i][s][0]) | (f32_to_bf16_rne(acc[i][s][1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(acc[i][s][2]) | (f32_to_bf16_rne(acc[i][s][3]) << 16);
+        *reinterpret_cast<uint2*>(Y + (size_t)m * N + n0 + 16 * s + 4 * lk) = make_uint2(lo, hi);
       }
     }
   }
@@ -1548,11 +1537,14 @@ static hipError_t launch_zero(uint16_t* p, int64_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// grid rows: one per 16 kMT tokens (kMT = 1 with several rows runs each
+// 16-token slice in waves of its own)
 template <int kMT, int kW, int kS, bool kPk>
 static void launch_decode_t(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
                             uint32_t m, uint32_t n, uint32_t k, uint16_t* C, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_fp8_decode_kernel<kMT, kW, kS, kPk>), dim3(n / (16 * kS)), dim3(64 * kW), 0, stream,
-                     A, sa, B, sb, m, n, k, C);
+  const dim3 grid(n / (16 * kS), (m + 16 * kMT - 1) / (16 * kMT));
+  hipLaunchKernelGGL((gemm_fp8_decode_kernel<kMT, kW, kS, kPk>), grid, dim3(64 * kW), 0, stream, A, sa, B, sb, m,
+                     n, k, C);
 }
 
 // kw is rounded to an instantiated value: at least kMT (one folding wave per
@@ -1598,20 +1590,29 @@ static void launch_decode_p(int mt, int kw, int ks, const uint8_t* A, const floa
 //     or 2048 for long K, where a group's sequential chain is long;
 //   packed weight: one (a lone wave streaming its strips' contiguous range
 //     with no LDS fold was fastest at every 8B decode shape and M = 16 .. 64),
-//     more only while there are fewer than 192 strip groups;
+//     more only while there are fewer than 192 waves; over 16 rows the tokens
+//     are split into grid rows of 16 or 32 (see below);
 // at most 16, and at most one per two K-blocks.  Measured on the 8B decode
 // shapes (K = 4096 and 12288, N = 4096 .. 24576, M = 1 .. 64).
 static void launch_decode(bool packed, int64_t Mr, int64_t Nc, int64_t Kc, const uint8_t* A, const float* sa,
                           const uint8_t* B, const float* sb, uint16_t* C, hipStream_t stream) {
-  const int64_t nkb = Kc / kBK;
-  const int mt = Mr <= 16 ? 1 : (Mr <= 32 ? 2 : 4);
-  const int ks = Nc / 16 >= 384 ? 2 : 1;
-  const int64_t groups = Nc / (16 * ks);
+  const int64_t nkb = Kc / kBK, strips = Nc / 16;
+  int mt = Mr <= 16 ? 1 : (Mr <= 32 ? 2 : 4);
+  int ks = strips >= 384 ? 2 : 1;
   int kw = 16;
   if (packed) {
+    // over 16 rows: two strips per wave from 256 strips, and the tokens in
+    // slices of 16 (17 .. 32 rows with long K) or 32 that run in waves of their
+    // own (grid rows), each slice's waves streaming the same weight range
+    if (Mr > 16) {
+      ks = strips >= 256 ? 2 : 1;
+      mt = (Mr > 32 || nkb < 64) ? 2 : 1;
+    }
+    const int64_t waves = (strips / ks) * ((Mr + 16 * mt - 1) / (16 * mt));
     kw = 1;
-    while (kw < 16 && groups * kw < 192 && 2 * kw <= (nkb + 1) / 2) kw *= 2;
+    while (kw < 16 && waves * kw < 192 && 2 * kw <= (nkb + 1) / 2) kw *= 2;
   } else {
+    const int64_t groups = strips / ks;
     const int64_t target = nkb >= 64 ? 2048 : 1024 / mt;
     while (kw > 1 && (groups * kw > target || kw > (nkb + 1) / 2)) kw /= 2;
   }
@@ -1911,93 +1912,27 @@ hipError_t launch_pack_weight_rollout(const uint8_t* qw, int64_t N, int64_t K, u
 }
 
 template <int kMT, int kS, int kNW>
-static void launch_decode_xs_t(int splits, const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
-                               uint32_t m, uint32_t n, uint32_t k, void* C, hipStream_t stream) {
-  const dim3 grid(n / (16 * kS * kNW), (unsigned)splits);
-  if (splits > 1)
-    hipLaunchKernelGGL((gemm_fp8_decode_xs_kernel<kMT, kS, kNW, true>), grid, dim3(64 * kNW), 0, stream, A, sa, B,
-                       sb, m, n, k, C);
-  else
-    hipLaunchKernelGGL((gemm_fp8_decode_xs_kernel<kMT, kS, kNW, false>), grid, dim3(64 * kNW), 0, stream, A, sa, B,
-                       sb, m, n, k, C);
+static void launch_decode_xs_t(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb, uint32_t m,
+                               uint32_t n, uint32_t k, uint16_t* C, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_fp8_decode_xs_kernel<kMT, kS, kNW>), dim3(n / (16 * kS * kNW)), dim3(64 * kNW), 0,
+                     stream, A, sa, B, sb, m, n, k, C);
 }
 
-template <int kMT>
-static void launch_decode_xs_m(int nw, int ks, int splits, const uint8_t* A, const float* sa, const uint8_t* B,
-                               const float* sb, uint32_t m, uint32_t n, uint32_t k, void* C, hipStream_t stream) {
-  if (nw == 2) {
-    if (ks == 2) launch_decode_xs_t<kMT, 2, 2>(splits, A, sa, B, sb, m, n, k, C, stream);
-    else launch_decode_xs_t<kMT, 1, 2>(splits, A, sa, B, sb, m, n, k, C, stream);
-  } else {
-    if (ks == 2) launch_decode_xs_t<kMT, 2, 4>(splits, A, sa, B, sb, m, n, k, C, stream);
-    else launch_decode_xs_t<kMT, 1, 4>(splits, A, sa, B, sb, m, n, k, C, stream);
-  }
-}
-
-// splits > 1: fp32 partials into C (splits x M x N floats); splits must divide K / 128
-static void launch_decode_xs(int nw, int ks, int splits, int64_t Mr, int64_t Nc, int64_t Kc, const uint8_t* A,
-                             const float* sa, const uint8_t* B, const float* sb, void* C, hipStream_t stream) {
-  const uint32_t m = (uint32_t)Mr, n = (uint32_t)Nc, k = (uint32_t)Kc;
-  if (Mr <= 16) launch_decode_xs_m<1>(nw, ks, splits, A, sa, B, sb, m, n, k, C, stream);
-  else if (Mr <= 32) launch_decode_xs_m<2>(nw, ks, splits, A, sa, B, sb, m, n, k, C, stream);
-  else launch_decode_xs_m<4>(nw, ks, splits, A, sa, B, sb, m, n, k, C, stream);
-}
-
-// Packed FProp, sequential fold.  Up to 32 rows the lone-wave decode kernel;
-// from 33 rows, when there are at least 384 strips of 16 columns, the
-// X-sharing kernel with 4 waves of 2 strips (from 1536 strips) or 2 waves of
-// 1 (at most 192 workgroups then hold every strip); below 384 strips the
-// decode kernel, whose K-phases keep the chip busy.  Measured at the 8B decode
-// shapes (graph replays, 4 rotated weights): M = 64: QKV 16.3 -> 12.9 us,
-// gate+up 31.7 -> 28.0 us; M = 32 and the down projection at M = 64: the
-// decode kernel was as fast or faster.
+// Packed FProp, sequential fold: the decode kernel (launch_decode's packed
+// rule), except from 33 rows with at least 1536 strips of 16 columns, where the
+// X-sharing kernel's workgroups of 4 waves x 2 strips stage each K-block of
+// the tokens once for 128 columns.  Measured at the 8B gate+up projection
+// (N = 24576, M = 64; graph replays, 4 rotated weights): 27.6 us against
+// 31.2 us for the best decode-kernel launch.
 hipError_t launch_gemm_fprop_packed(const uint8_t* qx, const float* sx, const uint8_t* qwp, const float* sw,
                                     int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   if (K == 0) return launch_zero(y, M * N, stream);
-  const int64_t strips = N / 16;
-  if (M > 32 && strips >= 384) {
-    if (strips >= 1536) launch_decode_xs(4, 2, 1, M, N, K, qx, sx, qwp, sw, y, stream);
-    else launch_decode_xs(2, 1, 1, M, N, K, qx, sx, qwp, sw, y, stream);
+  if (M > 32 && N / 16 >= 1536) {
+    launch_decode_xs_t<4, 2, 4>(qx, sx, qwp, sw, (uint32_t)M, (uint32_t)N, (uint32_t)K, y, stream);
     return hipGetLastError();
   }
   launch_decode(true, M, N, K, qx, sx, qwp, sw, y, stream);
-  return hipGetLastError();
-}
-
-// K-shares of gemm_fprop_packed_splitk: none up to 16 rows or with at least
-// 384 strips (the sequential kernels fill the chip); otherwise X-sharing
-// workgroups of 2 waves (17 .. 32 rows) or 4 (33 .. 64), one strip each, and
-// the fewest power-of-two shares that give 256 workgroups, each share at
-// least four K-blocks.  Measured on the 8B down projection (N = 4096,
-// K = 12288): M = 64: 21.6 us with gemm_fprop_splitk's 16 shares of the
-// 128 x 128 kernel, 18.1 us with 4 shares here; M = 32: 19.3 -> 14.4 us.
-int fprop_packed_split_count(int64_t M, int64_t N, int64_t K) {
-  if (M <= 16 || M > 64 || N % kBN != 0 || K % kBK != 0) return 1;
-  const int64_t strips = N / 16, nkb = K / kBK;
-  if (strips >= 384) return 1;
-  const int64_t groups = strips / (M > 32 ? 4 : 2);
-  int s = 1;
-  while (groups * s < 256 && nkb % (2 * s) == 0 && nkb / (2 * s) >= 4) s *= 2;
-  return s;
-}
-
-int64_t fprop_packed_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  const int s = fprop_packed_split_count(M, N, K);
-  return s > 1 ? (int64_t)s * M * N * 4 : 0;
-}
-
-hipError_t launch_gemm_fprop_packed_splitk(const uint8_t* qx, const float* sx, const uint8_t* qwp, const float* sw,
-                                           int64_t M, int64_t N, int64_t K, uint16_t* y, float* ws,
-                                           hipStream_t stream) {
-  const int s = fprop_packed_split_count(M, N, K);
-  if (s <= 1) return launch_gemm_fprop_packed(qx, sx, qwp, sw, M, N, K, y, stream);
-  launch_decode_xs(M > 32 ? 4 : 2, 1, s, M, N, K, qx, sx, qwp, sw, ws, stream);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t n = M * N;
-  hipLaunchKernelGGL(splitk_reduce_bf16_kernel, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, stream, ws, s,
-                     n, y);
   return hipGetLastError();
 }
 

@@ -47,12 +47,6 @@ hipError_t launch_gemm_fprop_swiglu_quant(const uint8_t* qx, const float* sx, co
 hipError_t launch_pack_weight_rollout(const uint8_t* qw, int64_t N, int64_t K, uint8_t* qwp, hipStream_t stream);
 hipError_t launch_gemm_fprop_packed(const uint8_t* qx, const float* sx, const uint8_t* qwp, const float* sw,
                                     int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
-// The same with K split across workgroups (fp32 partials in ws, then the
-// fixed-order reduction); fprop_packed_splitk_workspace_bytes: 0 when unsplit.
-int64_t fprop_packed_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
-hipError_t launch_gemm_fprop_packed_splitk(const uint8_t* qx, const float* sx, const uint8_t* qwp, const float* sw,
-                                           int64_t M, int64_t N, int64_t K, uint16_t* y, float* ws,
-                                           hipStream_t stream);
 hipError_t launch_gemm_dgrad(const uint8_t* qdy, const float* sdy, const uint8_t* qw,
                              const float* sw, int64_t M, int64_t N, int64_t K, uint16_t* dx,
                              hipStream_t stream);

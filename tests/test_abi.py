@@ -264,29 +264,3 @@ def test_pack_weight_rollout_and_fprop_packed_validation(jetlib):
     assert c(f, P[0], P[1], P[2], P[3], 65, 128, 128, P[4], 0) == 5            # more than 64 rows
     assert c(f, B[0], B[1], B[2], B[3], 16, 1 << 16, 1 << 15, B[4], 0) == 5    # weight past 2^31 bytes
     assert c(f, 0, 0, P[2], P[3], 0, 128, 128, 0, 0) == OK                      # M = 0: nothing to do
-
-
-def test_fprop_packed_splitk_validation(jetlib):
-    f = "gemm_fprop_packed_splitk"
-    assert f in declared_functions() and "gemm_fprop_packed_splitk_workspace_bytes" in declared_functions()
-    ws = _lib.gemm_fprop_packed_splitk_workspace_bytes
-    # S * M * N * 4: the fewest power-of-two shares giving 256 workgroups of 2 (17..32
-    # rows) or 4 (33..64) one-strip waves, >= 4 K-blocks each, below 384 strips
-    assert ws(64, 4096, 12288) == 4 * 64 * 4096 * 4      # 8B down: 256 strips, 64 groups
-    assert ws(32, 4096, 12288) == 2 * 32 * 4096 * 4      # 128 groups
-    assert ws(64, 384, 4096) == 8 * 64 * 384 * 4         # 6 groups: capped at 32 / 8 = 4 blocks per share
-    assert ws(16, 4096, 12288) == 0                       # up to 16 rows: sequential
-    assert ws(64, 6144, 4096) == ws(64, 24576, 4096) == 0  # >= 384 strips fill the chip unsplit
-    assert ws(64, 256, 384) == 0                          # 3 K-blocks: no share of four
-    raw = jetlib.gemm_fprop_packed_splitk_workspace_bytes
-    assert raw(16, 100, 128) == -1 and raw(-1, 128, 128) == -1 and raw(16, 128, 64) == -1
-    need = ws(64, 4096, 12288)
-    # (qx, sx, qwp, sw, M, N, K, y, workspace, workspace_bytes)
-    assert c(f, P[0], P[1], P[2], P[3], 64, 4096, 12288, P[4], P[5], need - 4, 0) == EINVAL  # too small
-    assert c(f, P[0], P[1], P[2], P[3], 64, 100, 12288, P[4], P[5], need, 0) == EINVAL       # N % 128
-    Q = [(i + 1) << 36 for i in range(8)]
-    assert c(f, Q[0], Q[1], Q[2], Q[3], 64, 4096, 12288, Q[4], 0, need, 0) == ENULL
-    assert c(f, Q[0], Q[1], Q[2], Q[3], 64, 4096, 12288, Q[4], Q[5] + 8, need, 0) == EALIGN
-    assert c(f, Q[0], Q[1], Q[2], Q[3], 64, 4096, 12288, Q[4], Q[4] + 1024, need, 0) == EALIAS  # over y
-    assert c(f, Q[0], Q[1], Q[2], Q[3], 65, 4096, 12288, Q[4], Q[5], need, 0) == 5           # more than 64 rows
-    assert c(f, 0, 0, P[2], P[3], 0, 128, 128, 0, 0, 0, 0) == OK                              # M = 0

@@ -66,11 +66,16 @@ def test_every_gate_value_as_a_uniform_group():
     check_bits(np.concatenate([gate, one], axis=1), "every gate, uniform groups")
 
 
-@pytest.mark.parametrize("case", golden_io.quant_cases(), ids=lambda c: c["name"])
+def _exact_over_32(case):
+    """The hand-derived group can be placed as h = silu(32) * (x / 32) only where x / 32
+    is exact in bf16 (the subnormal-scale case is not)."""
+    x = np.array(case["x"], np.float32)
+    return np.array_equal(oracle.bf16_bits_to_f32(f32_to_bf16_bits(x / np.float32(32))) * np.float32(32), x)
+
+
+@pytest.mark.parametrize("case", [c for c in golden_io.quant_cases() if _exact_over_32(c)], ids=lambda c: c["name"])
 def test_golden_group(case):
     x = np.array(case["x"], np.float32)
-    if not np.array_equal(oracle.bf16_bits_to_f32(f32_to_bf16_bits(x / np.float32(32))) * np.float32(32), x):
-        pytest.skip("x / 32 is not exact in bf16")
     m, i = 3, 512
     gate = np.full((m, i), -100.0, np.float32)
     up = np.ones((m, i), np.float32)

@@ -20,8 +20,8 @@
 // exponential runs in the kernel, which would make it ALU-bound.
 //
 // Workgroups of 256 threads, two per CU, walk tiles of 32 rows x 4 groups (512
-// outputs); a lane holds 8 consecutive outputs of a group (quarter-wave =
-// group) in 8 rows.  The loop is software-pipelined over two register buffers:
+// outputs; 4 or 8 rows for rollout batches); a lane holds 8 consecutive outputs
+// of a group (quarter-wave = group) in 8 rows (1 or 2).  The loop is software-pipelined over two register buffers:
 // the next tile's 16 loads per lane are in flight while the current tile is
 // computed and stored.
 #include "device_common.hpp"
@@ -30,8 +30,6 @@
 namespace jetfp8 {
 
 constexpr int kSwThreads = 256;
-constexpr int kSwRows = 32;
-constexpr int kSwIters = kSwRows / (kSwThreads / 64);  // rows per wave and tile: 8
 constexpr uint32_t kSiluExpLo = 102, kSiluExpHi = 134;  // biased exponents of 2^-25 and 2^7
 constexpr int kSiluBinades = (int)(kSiluExpHi - kSiluExpLo);
 constexpr int kSiluTable = 2 * kSiluBinades * 128;  // 8192 entries (32 KB)
@@ -50,11 +48,17 @@ __device__ __forceinline__ float silu_of_bits(uint32_t b, const float* tab) {
   return in ? t : outside;
 }
 
+// kRows rows per tile (32 for training batches, fewer for rollout batches, so
+// that their few rows still spread over many workgroups); kIters rows per wave
+template <int kRows>
 struct SwTile {
-  uint4 gv[kSwIters], uv[kSwIters];
+  static constexpr int kIters = kRows / (kSwThreads / 64);
+  uint4 gv[kIters], uv[kIters];
 };
 
+template <int kRows>
 struct SwGeom {
+  static constexpr int kIters = SwTile<kRows>::kIters;
   const uint16_t* y;
   int64_t M, I, ctiles;
   int l, lane16, wave;
@@ -62,27 +66,27 @@ struct SwGeom {
     g = (tile % ctiles) * 4 + (l >> 4);
     g_ok = g * kGroup < I;  // ragged last column tile (I % 512 != 0)
     col = g * kGroup + lane16 * 8;
-    row0 = (tile / ctiles) * kSwRows + wave;
+    row0 = (tile / ctiles) * kRows + wave;
   }
-  __device__ __forceinline__ void load(int64_t tile, SwTile& b) const {
+  __device__ __forceinline__ void load(int64_t tile, SwTile<kRows>& b) const {
     int64_t g, col, row0;
     bool g_ok;
     at(tile, g, g_ok, col, row0);
 #pragma unroll
-    for (int it = 0; it < kSwIters; ++it) {
+    for (int it = 0; it < kIters; ++it) {
       const int64_t r = row0 + (kSwThreads / 64) * it;
       const bool ok = r < M && g_ok;
       b.gv[it] = ok ? ld_stream16(y + r * 2 * I + col) : make_uint4(0, 0, 0, 0);
       b.uv[it] = ok ? ld_stream16(y + r * 2 * I + I + col) : make_uint4(0, 0, 0, 0);
     }
   }
-  __device__ __forceinline__ void compute(int64_t tile, const SwTile& b, const float* tab, uint8_t* q,
+  __device__ __forceinline__ void compute(int64_t tile, const SwTile<kRows>& b, const float* tab, uint8_t* q,
                                           float* s) const {
     int64_t g, col, row0;
     bool g_ok;
     at(tile, g, g_ok, col, row0);
 #pragma unroll
-    for (int it = 0; it < kSwIters; ++it) {
+    for (int it = 0; it < kIters; ++it) {
       const int64_t r = row0 + (kSwThreads / 64) * it;
       float u[8], h[8];
       unpack_bf16x8(b.uv[it], u);
@@ -104,17 +108,18 @@ struct SwGeom {
   }
 };
 
+template <int kRows>
 __global__ __launch_bounds__(kSwThreads) void swiglu_quant_kernel(const uint16_t* __restrict__ y, int64_t M,
                                                                   int64_t I, uint8_t* __restrict__ q,
                                                                   float* __restrict__ s, int64_t tiles) {
   __shared__ __attribute__((aligned(16))) float tab[kSiluTable];
-  SwGeom geo;
+  SwGeom<kRows> geo;
   geo.y = y; geo.M = M; geo.I = I;
   geo.ctiles = (I / kGroup + 3) / 4;
   geo.l = threadIdx.x & 63; geo.lane16 = geo.l & 15; geo.wave = threadIdx.x >> 6;
   const int64_t stride = gridDim.x;
   int64_t tile = blockIdx.x;
-  SwTile b0, b1;
+  SwTile<kRows> b0, b1;
   geo.load(tile, b0);  // the first tile's loads go out before the table copy
 #pragma unroll
   for (int i = 0; i < kSiluTable / (4 * kSwThreads); ++i) {
@@ -137,12 +142,24 @@ __global__ __launch_bounds__(kSwThreads) void swiglu_quant_kernel(const uint16_t
 hipError_t launch_swiglu_quant(const uint16_t* y, int64_t M, int64_t I, uint8_t* q, float* s,
                                hipStream_t stream) {
   if (M == 0 || I == 0) return hipSuccess;
-  const int64_t tiles = ((I / kGroup + 3) / 4) * ((M + kSwRows - 1) / kSwRows);
+  // rows per tile: rollout batches spread over more workgroups (each copies the
+  // 32 KB table once): measured at I = 12288, M = 16 / 64 / 128 / 256: 7.3 / 8.0
+  // / 8.2 / 9.0 us with 32-row tiles, 3.2 / 3.7 / 4.5 us with 4 rows, 6.3 us with
+  // 8 at M = 256; training batches (8192, 16384 rows) are fastest with 32
+  const int rows = M <= 128 ? 4 : (M <= 512 ? 8 : 32);
+  const int64_t tiles = ((I / kGroup + 3) / 4) * ((M + rows - 1) / rows);
   int64_t grid = 2 * (int64_t)device_cu_count();
   if (grid <= 0) grid = 512;
   if (grid > tiles) grid = tiles;
-  hipLaunchKernelGGL(swiglu_quant_kernel, dim3((unsigned)grid), dim3(kSwThreads), 0, stream, y, M, I, q, s,
-                     tiles);
+  if (rows == 4)
+    hipLaunchKernelGGL(swiglu_quant_kernel<4>, dim3((unsigned)grid), dim3(kSwThreads), 0, stream, y, M, I, q, s,
+                       tiles);
+  else if (rows == 8)
+    hipLaunchKernelGGL(swiglu_quant_kernel<8>, dim3((unsigned)grid), dim3(kSwThreads), 0, stream, y, M, I, q, s,
+                       tiles);
+  else
+    hipLaunchKernelGGL(swiglu_quant_kernel<32>, dim3((unsigned)grid), dim3(kSwThreads), 0, stream, y, M, I, q, s,
+                       tiles);
   return hipGetLastError();
 }
 

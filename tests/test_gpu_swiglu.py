@@ -88,8 +88,9 @@ def test_golden_group(case):
     check_bits(y, f"golden {case['name']}")
 
 
+# 4-row tiles up to 128 rows, 8-row tiles up to 512, 32-row tiles above (ragged in each)
 @pytest.mark.parametrize("m,i", [(1, 128), (33, 384), (64, 640), (100, 1152), (257, 512), (2, 12288),
-                                 (16, 14336), (65, 12800), (256, 12288)])
+                                 (16, 14336), (65, 12800), (256, 12288), (300, 384), (520, 640)])
 def test_shapes(m, i):
     y = synth.random_bf16((m, 2 * i), seed=m + i, std=3.0)
     check_bits(y, f"{m}x{i}")

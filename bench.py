@@ -562,8 +562,9 @@ def bench_layers(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (this path is the one-GPU share; see DESIGN.md); "
-              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU: it times one GPU's share of the data-parallel layer, "
+              f"whose only collective would be the weight-gradient all-reduce; --gpus {args.gpus} is not "
+              f"supported", file=sys.stderr)
         sys.exit(2)
     if args.workload == "decode_8b":
         sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))

@@ -29,7 +29,10 @@
 //
 // Kernels (chosen in launch_gemm):
 //   gemm_fp8_decode_kernel       FProp with M <= 64 (weight streaming), also
-//                                over the rollout-packed weight (gemm_fprop_packed);
+//                                over the rollout-packed weight (gemm_fprop_packed,
+//                                which runs gemm_fp8_decode_xs_kernel for 33 .. 64
+//                                rows and many strips; pack_weight_rollout_kernel
+//                                writes that weight);
 //   gemm_fp8_mid_kernel          FProp with 65 .. 256 rows, long K and few
 //                                column tiles (K split over 8 waves);
 //   gemm_fp8_large_kernel<mode>  256 x 256 tiles: problems with >= 256 of them

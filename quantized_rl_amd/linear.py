@@ -22,6 +22,12 @@ the pages' "核心方法" section: one FP8 weight per update, shared by every
 forward, rollout or training, and by the backward's DGrad): ``WeightCache``
 keeps the 128x128 FP8 form and re-quantises only when the parameter's storage
 or its in-place version counter changes.
+
+Rollout: a forward that builds no autograd graph (``torch.no_grad()``, or
+neither input nor weight requiring grad) over at most 64 rows runs
+``gemm_fprop_packed`` on the cached weight's rollout-packed copy
+(``pack_weight_rollout``, made once per weight version).  Its output is bitwise
+the training forward's: same codes, scales and fold.
 """
 
 import torch
@@ -30,6 +36,18 @@ from . import _lib
 
 # widest row the RMSNorm backward kernel takes (rmsnorm_backward_workspace_bytes)
 RMSNORM_BACKWARD_MAX_K = 24576
+# most rows gemm_fprop_packed takes
+ROLLOUT_MAX_ROWS = 64
+
+
+def rollout_path(x2, w):
+    """True when a forward of x2 [M, K] against w [N, K] needs no autograd graph and
+    fits gemm_fprop_packed (M <= 64, 32-bit byte offsets): the rollout path."""
+    if torch.is_grad_enabled() and (x2.requires_grad or w.requires_grad):
+        return False
+    M, K = x2.shape
+    N = w.shape[0]
+    return M <= ROLLOUT_MAX_ROWS and N * K < 2 ** 31 and M * K < 2 ** 31
 
 
 class WeightCache:
@@ -42,6 +60,9 @@ class WeightCache:
         self.key = None
         self.q = self.s = None
         self.quantizations = 0
+        self.packed_key = None
+        self.packed = None
+        self.packs = 0
 
     def get(self, w):
         key = (w.data_ptr(), tuple(w.shape), w.device, w._version)
@@ -50,6 +71,16 @@ class WeightCache:
             self.quantizations += 1
             self.key = key
         return self.q, self.s
+
+    def get_packed(self, w):
+        """(rollout-packed codes, scales) of the current FP8 weight: pack_weight_rollout
+        of ``get(w)``'s codes, made once per weight version (``packs`` counts them)."""
+        q, s = self.get(w)
+        if self.packed_key != self.key:
+            self.packed = _lib.pack_weight_rollout(q)
+            self.packs += 1
+            self.packed_key = self.key
+        return self.packed, s
 
 
 class FP8LinearFunction(torch.autograd.Function):
@@ -129,7 +160,12 @@ class FP8Linear(torch.nn.Module):
 
     def forward(self, x):
         shape = x.shape
-        y = fp8_linear(x.reshape(-1, shape[-1]), self.weight, self.main_grad, self.wcache)
+        x2 = x.reshape(-1, shape[-1])
+        if rollout_path(x2, self.weight):
+            qx, sx = _lib.quantize_act_1x128(x2.contiguous())
+            y = _lib.gemm_fprop_packed(qx, sx, *self.wcache.get_packed(self.weight))
+        else:
+            y = fp8_linear(x2, self.weight, self.main_grad, self.wcache)
         return y.reshape(*shape[:-1], self.weight.shape[0])
 
 
@@ -177,8 +213,12 @@ class RMSNormFP8Linear(torch.nn.Module):
 
     def forward(self, x):
         shape = x.shape
-        y = RMSNormFP8LinearFunction.apply(x.reshape(-1, shape[-1]), self.gamma, self.weight, self.eps,
-                                           self.wcache)
+        x2 = x.reshape(-1, shape[-1])
+        if rollout_path(x2, self.weight) and not (torch.is_grad_enabled() and self.gamma.requires_grad):
+            qx, sx = _lib.rmsnorm_quant(x2.contiguous(), self.gamma.contiguous(), self.eps)
+            y = _lib.gemm_fprop_packed(qx, sx, *self.wcache.get_packed(self.weight))
+        else:
+            y = RMSNormFP8LinearFunction.apply(x2, self.gamma, self.weight, self.eps, self.wcache)
         return y.reshape(*shape[:-1], self.weight.shape[0])
 
 

@@ -68,3 +68,34 @@ def test_weight_cache_requantises_only_on_change(monkeypatch):
     w2 = w.clone()                                                             # another tensor
     c.get(w2)
     assert c.quantizations == 3 and calls[-1] == w2.data_ptr()
+
+
+def test_rollout_path_rule():
+    """The rollout path is taken only when no autograd graph is needed and the batch
+    fits gemm_fprop_packed (at most 64 rows)."""
+    w = torch.zeros(256, 512, dtype=torch.bfloat16, requires_grad=True)
+    x = torch.zeros(16, 512, dtype=torch.bfloat16)
+    assert not linear.rollout_path(x, w)                   # the weight needs a gradient
+    with torch.no_grad():
+        assert linear.rollout_path(x, w)
+        assert linear.rollout_path(torch.zeros(64, 512, dtype=torch.bfloat16), w)
+        assert not linear.rollout_path(torch.zeros(65, 512, dtype=torch.bfloat16), w)
+    w_frozen = w.detach()
+    assert linear.rollout_path(x, w_frozen)                # frozen weight, plain input
+    assert not linear.rollout_path(x.clone().requires_grad_(), w_frozen)
+
+
+def test_weight_cache_packs_once_per_version(monkeypatch):
+    packs = []
+    monkeypatch.setattr(linear._lib, "quantize_weight_128x128", lambda w: (("q", w._version), "s"))
+    monkeypatch.setattr(linear._lib, "pack_weight_rollout", lambda q: packs.append(q) or ("p", q))
+    w = torch.zeros(128, 256, dtype=torch.bfloat16)
+    c = linear.WeightCache()
+    a = c.get_packed(w)
+    assert c.get_packed(w) == a and c.packs == 1 and c.quantizations == 1
+    with torch.no_grad():
+        w.add_(1)
+    b = c.get_packed(w)
+    assert b != a and c.packs == 2 and c.quantizations == 2
+    c.get(w)                                               # the FP8 form alone: no new pack
+    assert c.packs == 2

@@ -24,7 +24,7 @@ object describes the slowest GEMM against the dense FP8 MFMA peak.  The
 (``--decode-m``, default 16): RMSNorm+quant, FProp against the FP8 QKV and
 gate+up weights, the fused SwiGLU + 1x128 quantisation of the gate+up output
 (the down projection's input) and the down FProp (weights quantised once,
-outside the timed region).  Up to 64 tokens the weights are held in the
+outside the timed region).  Up to 256 tokens the weights are held in the
 rollout-packed order (pack_weight_rollout, outside the timed region) and the
 FProps go through gemm_fprop_packed; larger batches (or ``--decode-rowmajor``)
 use the row-major codes and gemm_fprop_splitk, which splits K across
@@ -302,12 +302,12 @@ def bench_decode(args):
     # step to the next; consecutive steps therefore rotate over DECODE_WEIGHT_SETS
     # copies (704 MB), so every step streams its weights from HBM.
     sets = [wq] + [{k: (q.clone(), s.clone()) for k, (q, s) in wq.items()} for _ in range(DECODE_WEIGHT_SETS - 1)]
-    # Up to 64 tokens the rollout engine keeps its weight copy in the packed order
+    # Up to 256 tokens the rollout engine keeps its weight copy in the packed order
     # (pack_weight_rollout, once per weight update: outside the timed region) and
     # runs gemm_fprop_packed; larger batches use the row-major codes and
     # gemm_fprop_splitk, which splits K for the shapes with fewer output tiles
     # than CUs through this workspace (allocated once, untimed).
-    packed = m <= 64 and not args.decode_rowmajor
+    packed = m <= 256 and not args.decode_rowmajor
     if packed:
         sets = [{k: (jet.pack_weight_rollout(q), s) for k, (q, s) in st.items()} for st in sets]
     torch.cuda.synchronize()

@@ -209,12 +209,9 @@ int requant_transpose_128x1(const uint8_t* q, const float* s, int64_t M, int64_t
  *   y  : bf16 [M][N].
  * K % 128 == 0, N % 128 == 0, M >= 0 (any M).  K == 0 writes zeros.
  * Batch invariance: a row's output depends only on that row of (qx, sx) and on
- * the weight.  For M <= 64 and M > 256 every kernel folds the K-blocks in
- * ascending order with acc = fma(P_kb, fl32(sx * sw), acc), so the row is
- * bitwise the same whatever M is.  Batches of 65..256 rows may run a kernel
- * that folds 8 interleaved K-block subsets and sums them in a fixed order:
- * deterministic and bitwise the same across such batches, but it may differ
- * from the sequential fold in the last bits.
+ * the weight.  Every kernel folds the K-blocks in ascending order with
+ * acc = fma(P_kb, fl32(sx * sw), acc), so the row is bitwise the same whatever
+ * M is (a rollout batch or a training batch).
  */
 int gemm_fprop(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw, int64_t M,
                int64_t N, int64_t K, uint16_t* y, void* stream);
@@ -286,16 +283,15 @@ int gemm_fprop_splitk_noalloc(const uint8_t* qx, const float* sx, const uint8_t*
 int pack_weight_rollout(const uint8_t* qw, int64_t N, int64_t K, uint8_t* qwp, void* stream);
 
 /*
- * gemm_fprop_packed -- gemm_fprop for rollout batches of up to 64 rows over
+ * gemm_fprop_packed -- gemm_fprop for rollout batches of up to 256 rows over
  * the packed weight ([P3-LAYOUT], [P3-CORE], [P3-STEPS] step 2):
  *   y = gemm_fprop(qx, sx, qw, sw) bit for bit, with qwp = pack_weight_rollout(qw).
  *   qx : u8 [M][K], sx : f32 [K/128][M]; qwp : u8, N * K bytes;
  *   sw : f32 [N/128][K/128]; y : bf16 [M][N].
- * 0 <= M <= 64 (JETFP8_EUNSUPPORTED above), N % 128 == 0, K % 128 == 0,
+ * 0 <= M <= 256 (JETFP8_EUNSUPPORTED above), N % 128 == 0, K % 128 == 0,
  * N * K < 2^31 and M * K < 2^31 (JETFP8_EUNSUPPORTED otherwise).  K == 0
  * writes zeros.  A row's output is the sequential K fold of gemm_fprop, so it
- * is bitwise the same as in a training batch of any size above 256 rows or
- * any rollout batch of up to 64.
+ * is bitwise the same as in a training batch or a rollout batch of any size.
  */
 int gemm_fprop_packed(const uint8_t* qx, const float* sx, const uint8_t* qwp, const float* sw, int64_t M,
                       int64_t N, int64_t K, uint16_t* y, void* stream);

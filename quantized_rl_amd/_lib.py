@@ -279,7 +279,7 @@ def pack_weight_rollout(qw, qwp=None):
 
 
 def gemm_fprop_packed(qx, sx, qwp, sw, y=None):
-    """gemm_fprop for up to 64 rows over the packed weight qwp = pack_weight_rollout(qw):
+    """gemm_fprop for up to 256 rows over the packed weight qwp = pack_weight_rollout(qw):
     Y bf16 [M, N], bit for bit gemm_fprop(qx, sx, qw, sw)."""
     torch = _torch()
     M, K = qx.shape

@@ -197,7 +197,7 @@ int gemm_fprop_packed(const uint8_t* qx, const float* sx, const uint8_t* qwp, co
                           {{y, 2 * M * N}}))
     return st;
   const int64_t lim = int64_t(1) << 31;
-  if (M > 64 || N * K >= lim || M * K >= lim) return JETFP8_EUNSUPPORTED;
+  if (M > 256 || N * K >= lim || M * K >= lim) return JETFP8_EUNSUPPORTED;
   return launched(jetfp8::launch_gemm_fprop_packed(qx, sx, qwp, sw, M, N, K, y, as_stream(stream)));
 }
 

@@ -28,13 +28,15 @@
 // cancel (the normwise bound holds).
 //
 // Kernels (chosen in launch_gemm):
-//   gemm_fp8_decode_kernel       FProp with M <= 64 (weight streaming), also
-//                                over the rollout-packed weight (gemm_fprop_packed,
-//                                which runs gemm_fp8_decode_xs_kernel for 33 .. 64
-//                                rows and many strips; pack_weight_rollout_kernel
+//   gemm_fp8_decode_kernel       FProp with M <= 32 (weight streaming; up to 64
+//                                rows where the weight-sharing kernel is not
+//                                chosen);
+//   gemm_fp8_decode_ws_kernel    FProp with 33 .. 256 rows (weight chunks staged
+//                                in LDS once per workgroup for several waves of
+//                                tokens);
+//                                both also over the rollout-packed weight
+//                                (gemm_fprop_packed; pack_weight_rollout_kernel
 //                                writes that weight);
-//   gemm_fp8_mid_kernel          FProp with 65 .. 256 rows, long K and few
-//                                column tiles (K split over 8 waves);
 //   gemm_fp8_large_kernel<mode>  256 x 256 tiles: problems with >= 256 of them
 //                                (FProp and DGrad: one workgroup per CU looping
 //                                over the tiles);
@@ -46,9 +48,9 @@
 // splitk_reduce_bf16_kernel.
 // Byte offsets are 32-bit (buffer resources): the API rejects GEMMs whose
 // operands or output, with one tile of ragged rows, reach 2^31 bytes.
-// All but the K-split kernels fold the K-blocks of an output in ascending
-// order with the same fp32 operations, so a row's FProp output does not depend
-// on the kernel (nor on the batch it is computed in).
+// Every kernel but the split-K FProp's folds the K-blocks of an output in
+// ascending order with the same fp32 operations, so a row's FProp output does
+// not depend on the kernel (nor on the batch it is computed in).
 #include <atomic>
 #include <mutex>
 #include <type_traits>
@@ -1208,167 +1210,238 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Decode FProp over the packed weight with the token operand shared through
-// LDS (gemm_fprop_packed).  At 17 .. 64 tokens a lone streaming wave fetches
-// kMT X fragments (2 KB each) per K-block next to its kS strips' 2 KB weight
-// chunks, so the token operand, re-read by every strip group from L2,
-// outweighs the weight.  Here a workgroup of kNW waves (each owning kS
-// strips) stages each K-block of X once, with direct-to-LDS loads that land in
-// fragment order (lane l's 16 bytes at 16 l of a 1 KB piece: token row
-// 16 i + l mod 16, K-bytes 32 (l div 16) + 16 h of the block, for sub-tile i
-// and half h), so the waves read their fragments back with conflict-free
-// 16-byte LDS reads.  Weight chunks stream into registers kD K-blocks ahead;
-// X stages are filled kD - 1 blocks ahead into kD LDS stages.  One barrier per
-// K-block publishes its X stage: every wave first waits for its own loads of
-// that block (the loads of a block are issued as one group per wave).  The
+// FProp for rollout batches of 33 .. 256 tokens, weight shared through LDS.
+// Once each weight byte feeds more than a few dozen tokens, a wave can no
+// longer stream its own strips: the MFMA work per weight byte grows with the
+// batch while one wave per SIMD keeps few bytes in flight.  Here a workgroup
+// of kNW waves owns kS strips of 16 columns and 16 kR kNW tokens; every
+// K-block it stages the kS weight chunks once with direct-to-LDS loads, and all
+// its waves read them, each for its own kR sub-tiles of 16 tokens, whose X
+// fragments (and the block's sx values) the wave stages into its own part of
+// the same LDS stage.  Packed weight (kPk): a strip's K-block is one 2 KB
+// chunk in fragment order (lane l's 16 bytes at 16 l of each 1 KB piece).
+// Row-major weight, and always X: each 1 KB piece is 8 whole 128-byte rows
+// whose 16-byte chunks land at the large kernel's swizzled positions (chunk c
+// of row r at c ^ f(r)), so that whole cache lines are fetched and the
+// fragment reads are conflict-free 16-byte LDS reads.  kD stages hold the
+// next kD K-blocks; the K-block steps are software-pipelined (see below).  The
+// weight-block scales of the workgroup's (at most two) 128-column blocks are
+// copied to LDS once.  The grid walks (strip group, token group) pairs with
+// the token groups of a strip group adjacent on one XCD, so a weight chunk
+// read from HBM by one of them is found in that XCD's L2 by the others.  The
 // fold is the sequential one of the other FProp kernels, acc = fma(P_kb,
-// fl32(sx * sw), acc) in ascending K order, so the output is bitwise
-// gemm_fprop's.
-template <int kMT, int kS, int kNW>
-struct DecodeXsCfg {
-  static constexpr int kPieces = 2 * kMT;                // 1 KB pieces of X per K-block
-  static constexpr int kPW = (kPieces + kNW - 1) / kNW;  // pieces each wave loads (a few twice when kNW > kPieces)
-  static constexpr int kGw = 2 * kS + 1;                 // weight and sw loads per K-block
-  static constexpr int kG = kGw + kPW + 1;               // all loads of one wave per K-block (X, its own sx copy)
-  static constexpr int kSlotRegs = 8 * kS + 1;
-  // registers: the slots, X fragments (8 kMT), accumulators (4 kMT kS) and
-  // addresses within the 256 a lone wave per SIMD may hold (no spills at any
-  // instantiated shape)
-  static constexpr int kFit = (150 - 8 * kMT - 4 * kMT * kS) / kSlotRegs;
-  static constexpr int kCnt = 63 / kG;                   // at most 63 loads in flight (the vmcnt field)
+// fl32(sx * sw), acc) in ascending K order: the output is bitwise gemm_fprop's
+// on the same rows in any batch.
+constexpr int kWsMaxKb = 512;  // K <= 65536: the copied weight-block scales fit 4 KB
+template <int kR, int kS, int kNW>
+struct DecodeWsCfg {
+  static constexpr int kTM = 16 * kR * kNW;               // tokens of a workgroup
+  static constexpr int kWPieces = 2 * kS;                 // 1 KB weight pieces per K-block
+  static constexpr int kPW = (kWPieces + kNW - 1) / kNW;  // weight pieces each wave loads (a few twice)
+  static constexpr int kG = kPW + 2 * kR + 1;             // loads of one wave per K-block (+ its sx)
+  static constexpr int kWBytes = 2048 * kS;
+  static constexpr int kXBytes = 2048 * kR;               // one wave's X fragments
+  static constexpr int kStage = kWBytes + kNW * kXBytes + 256 * kNW;
+  static constexpr int kFit = (155 * 1024) / kStage;    // with the scale copy, within 160 KB of LDS
+  static constexpr int kCnt = 63 / kG + 1;                // (kD - 1) kG loads may stay in flight
   static constexpr int kD0 = kFit < kCnt ? kFit : kCnt;
-  static constexpr int kD = kD0 > 8 ? 8 : kD0;           // K-blocks in flight: weight slots = X stages
-  static constexpr int kXBytes = 2048 * kMT;             // X fragments of one stage
-  static constexpr int kStage = kXBytes + 256 * kNW;     // + each wave's copy of the block's 64 sx values
+  static constexpr int kD = kD0 > 8 ? 8 : kD0;
   static_assert(kD >= 2, "at least two K-blocks in flight");
-  static_assert(kGw + (kD - 2) * kG <= 63, "wait count fits vmcnt");
-  static_assert(16 * kS * kNW <= kBN && kBN % (16 * kS * kNW) == 0, "a workgroup's strips lie in one weight block row");
+  static_assert((kD - 1) * kG <= 63, "wait count fits vmcnt");
+  static_assert(kS <= 8, "a workgroup's strips span at most two weight blocks");
 };
 
-template <int kMT, int kS, int kNW>
-__global__ __launch_bounds__(64 * kNW) void gemm_fp8_decode_xs_kernel(
+template <int kR, int kS, int kNW, bool kPk>
+__global__ __launch_bounds__(64 * kNW) void gemm_fp8_decode_ws_kernel(
     const uint8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ Wp,
     const float* __restrict__ sw, uint32_t M, uint32_t N, uint32_t K, uint16_t* __restrict__ Y) {
-  using C = DecodeXsCfg<kMT, kS, kNW>;
+  using C = DecodeWsCfg<kR, kS, kNW>;
   constexpr int kD = C::kD;
-  // one array per stage, so that the compiler can tell a stage's LDS reads
-  // from the direct-to-LDS loads still in flight into the others
-  __shared__ __attribute__((aligned(1024))) uint8_t xs0[C::kStage], xs1[C::kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t xs2[kD > 2 ? C::kStage : 16], xs3[kD > 3 ? C::kStage : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t xs4[kD > 4 ? C::kStage : 16], xs5[kD > 5 ? C::kStage : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t xs6[kD > 6 ? C::kStage : 16], xs7[kD > 7 ? C::kStage : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ws0[C::kStage], ws1[C::kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t ws2[kD > 2 ? C::kStage : 16], ws3[kD > 3 ? C::kStage : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ws4[kD > 4 ? C::kStage : 16], ws5[kD > 5 ? C::kStage : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ws6[kD > 6 ? C::kStage : 16], ws7[kD > 7 ? C::kStage : 16];
+  __shared__ float swl[2 * kWsMaxKb];
   auto stage = [&](auto c) -> uint8_t* {
     constexpr int i = decltype(c)::value;
-    if constexpr (i == 0) return xs0;
-    else if constexpr (i == 1) return xs1;
-    else if constexpr (i == 2) return xs2;
-    else if constexpr (i == 3) return xs3;
-    else if constexpr (i == 4) return xs4;
-    else if constexpr (i == 5) return xs5;
-    else if constexpr (i == 6) return xs6;
-    else return xs7;
+    if constexpr (i == 0) return ws0;
+    else if constexpr (i == 1) return ws1;
+    else if constexpr (i == 2) return ws2;
+    else if constexpr (i == 3) return ws3;
+    else if constexpr (i == 4) return ws4;
+    else if constexpr (i == 5) return ws5;
+    else if constexpr (i == 6) return ws6;
+    else return ws7;
   };
   const int t = threadIdx.x, l = t & 63, lr = l & 15, lk = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const uint32_t strip0 = (blockIdx.x * kNW + (uint32_t)w) * kS;  // this wave's first strip of 16 columns
-  const uint32_t n0 = 16u * strip0;
   const uint32_t nkb = K / kBK, last = nkb - 1;
+  // (strip group, token group) of this workgroup: with a grid of 8 n
+  // workgroups, XCD x (blockIdx mod 8) takes pairs x n .. x n + n - 1, token
+  // group fastest
+  const uint32_t ntg = (M + C::kTM - 1) / C::kTM, total = (N / (16u * kS)) * ntg;
+  uint32_t pair = blockIdx.x;
+  if ((total & 7) == 0) pair = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const uint32_t sg = pair / ntg, tg = pair - sg * ntg;
+  const uint32_t strip0 = sg * kS, n0 = 16u * strip0;
+  const uint32_t mw = tg * C::kTM + (uint32_t)w * (16u * kR);  // this wave's first token
+
+  // the weight-block scales sw[b0 + h][kb] of the (one or two) 128-column
+  // blocks holding the strips, h = 0, 1
+  const uint32_t b0 = n0 / kBN, nb = (n0 + 16u * kS - 1u) / kBN - b0 + 1u;
+  for (uint32_t i = (uint32_t)t; i < nb * nkb; i += 64u * kNW) swl[i] = sw[b0 * nkb + i];
+  __syncthreads();
+
   const rsrc_t rw = make_rsrc(Wp, N * K);
   const rsrc_t rx = make_rsrc(X, M * K);
   const rsrc_t rsx = make_rsrc(sx, nkb * M * 4u);
-  const rsrc_t rsw = make_rsrc(sw + (n0 / kBN) * nkb, nkb * 4u);
-  uint32_t w_off[kS], xm[kMT], xp_off[C::kPW], xp_lds[C::kPW];
-  const uint32_t sx_lane = (uint32_t)(l < (int)M ? l : (int)M - 1) * 4u;  // token l's sx (ragged: the last token's)
-  const uint32_t sx_lds = C::kXBytes + 256u * w;                         // this wave's sx copy in a stage
-#pragma unroll
-  for (int s = 0; s < kS; ++s) w_off[s] = (strip0 + s) * nkb * kPackChunk + 16u * l;
-#pragma unroll
-  for (int i = 0; i < kMT; ++i) xm[i] = (16u * i + lr) < M ? (16u * i + lr) : (M - 1);  // ragged: repeat the last token
+  uint32_t w_off[C::kPW], w_lds[C::kPW], x_off[kR][2];
 #pragma unroll
   for (int q = 0; q < C::kPW; ++q) {
-    const int p = (w + kNW * q) % C::kPieces;  // piece p: sub-tile p / 2, half p % 2
-    xp_off[q] = xm[p >> 1] * K + 32u * lk + 16u * (p & 1);
-    xp_lds[q] = 1024u * p;
-  }
-  v8i_t wr[kD][kS];
-  float swr[kD];
-  auto load_w = [&](int slot, uint32_t kb) {
-    const uint32_t wofs = kb * kPackChunk;
-#pragma unroll
-    for (int s = 0; s < kS; ++s) {
-      const v4i_t w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[s], wofs, 0);
-      const v4i_t w1 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[s] + 1024u, wofs, 0);
-      wr[slot][s] = v8i_t{w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    const int pc = ((int)w + kNW * q) % C::kWPieces;  // piece pc: strip pc / 2, half pc % 2
+    const uint32_t strip = strip0 + (uint32_t)(pc >> 1);
+    if constexpr (kPk) {
+      w_off[q] = strip * nkb * kPackChunk + 1024u * (pc & 1) + 16u * l;
+    } else {
+      // row-major weight: as the X pieces below, 8 whole rows with swizzled chunks
+      const int r = 8 * (pc & 1) + (l >> 3);
+      w_off[q] = (16u * strip + (uint32_t)r) * K + 16u * (uint32_t)((l & 7) ^ lf(r));
     }
-    swr[slot] = ld_scale(rsw, kb * 4u);
-  };
-  // the block's X pieces (shared) and its M sx values (this wave's own copy)
-  auto load_x = [&](uint8_t* st, uint32_t kb) {
+    w_lds[q] = 2048u * (pc >> 1) + 1024u * (pc & 1);
+  }
+  // X piece h of sub-tile i: 8 whole 128-byte token rows 8 h .. 8 h + 7 (lane l:
+  // row 8 h + l / 8), each row's 16-byte chunks stored at the swizzled
+  // positions of the large kernel (chunk c of row r at c ^ f(r)), so that the
+  // fragment reads below are conflict-free
 #pragma unroll
-    for (int q = 0; q < C::kPW; ++q) buf_to_lds16(rx, st + xp_lds[q], xp_off[q], kb * kBK);
+  for (int i = 0; i < kR; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * h + (l >> 3);
+      const uint32_t m = mw + 16u * i + (uint32_t)r;
+      x_off[i][h] = (m < M ? m : M - 1) * K + 16u * (uint32_t)((l & 7) ^ lf(r));  // ragged tail: the last token
+    }
+  const uint32_t xr0 = 128u * lr + 16u * (uint32_t)((2 * lk) ^ lf(lr));
+  const uint32_t xr1 = 128u * lr + 16u * (uint32_t)((2 * lk + 1) ^ lf(lr));
+  const uint32_t x_lds = C::kWBytes + C::kXBytes * (uint32_t)w;
+  const uint32_t sx_lds = C::kWBytes + C::kXBytes * kNW + 256u * (uint32_t)w;
+  const uint32_t sx_tok = mw + (uint32_t)(l < 16 * kR ? l : 16 * kR - 1);
+  const uint32_t sx_lane = (sx_tok < M ? sx_tok : M - 1) * 4u;
+  // strip s lies in weight block b0 + sel(s)
+  const uint32_t sub = strip0 & 7u;
+
+  auto issue = [&](uint8_t* st, uint32_t kb) {
+#pragma unroll
+    for (int q = 0; q < C::kPW; ++q) buf_to_lds16(rw, st + w_lds[q], w_off[q], kb * (kPk ? kPackChunk : kBK));
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      buf_to_lds16(rx, st + x_lds + 2048 * i, x_off[i][0], kb * kBK);
+      buf_to_lds16(rx, st + x_lds + 2048 * i + 1024, x_off[i][1], kb * kBK);
+    }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, (__attribute__((address_space(3))) void*)(st + sx_lds), 4,
                                              sx_lane, kb * M * 4u, 0, 0);
   };
   auto clampb = [&](uint32_t kb) { return kb < last ? kb : last; };  // past the end: a valid block, not folded
 
-  // prologue: W(0), then X(j - 1), W(j) for j = 1 .. kD - 1 -- the order of the
-  // groups the loop issues, X(kb + kD - 1) then W(kb + kD)
-  load_w(0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  static_for<kD - 1>([&](auto c) {
-    constexpr int j = decltype(c)::value + 1;
-    load_x(stage(std::integral_constant<int, j - 1>{}), clampb(j - 1));
-    load_w(j, clampb(j));
+  // What a block's steps need first, read from its stage right after the
+  // barrier that publishes it: the wave's X fragments, their sx factors (0 for a
+  // block past the end: it then leaves acc unchanged bit for bit, as acc is
+  // never -0; multiplying by 1 changes no scale), the block's weight-block
+  // scales and the first strip's weight fragment.
+  struct Head {
+    v8i_t xf[kR];
+    float sxv[kR];
+    float sw0, sw1;
+    v8i_t wf;
+  };
+  auto frag = [&](const uint8_t* p0, const uint8_t* p1) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(p0);
+    const uint4 hi = *reinterpret_cast<const uint4*>(p1);
+    return v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  auto read_head = [&](const uint8_t* st, uint32_t kb, Head& h) {
+    const float live = kb < nkb ? 1.0f : 0.0f;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      h.xf[i] = frag(st + x_lds + 2048 * i + xr0, st + x_lds + 2048 * i + xr1);
+      h.sxv[i] = reinterpret_cast<const float*>(st + sx_lds)[16 * i + lr] * live;
+    }
+    const uint32_t kc = clampb(kb);
+    h.sw0 = swl[kc];
+    h.sw1 = swl[(nb - 1u) * nkb + kc];
+    h.wf = kPk ? frag(st + 16 * l, st + 1024 + 16 * l) : frag(st + xr0, st + xr1);
+  };
+
+  // prologue: every stage filled (block j into stage j), block 0 published
+  static_for<kD>([&](auto c) {
+    issue(stage(c), clampb(decltype(c)::value));
     __builtin_amdgcn_sched_barrier(0);
   });
+  wait_vmem_le<(kD - 1) * C::kG>();
+  lds_barrier();
+  Head head;
+  read_head(ws0, 0, head);
 
-  v4f_t acc[kMT][kS];
+  v4f_t acc[kR][kS];
 #pragma unroll
-  for (int i = 0; i < kMT; ++i)
+  for (int i = 0; i < kR; ++i)
 #pragma unroll
     for (int s = 0; s < kS; ++s) acc[i][s] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // Steps q = kR s + i of a block (strip s, token sub-tile i): step q issues
+  // the MFMA of q and rescales the partial of q - 2 into acc, so two MFMAs
+  // separate every partial from its use; strip s + 1's weight fragment is read
+  // at the first step of strip s.  After the block's last MFMA (its last LDS
+  // read is done by then) the wave waits for its loads of the next block, the
+  // barrier publishes that block and frees this stage, which is refilled at
+  // once with block kb + kD, and the next block's head is read while the last
+  // two partials are rescaled.  Scheduling barriers pin the order.
+  constexpr int kQ = kR * kS;
   uint32_t c0 = 0;
 #pragma clang loop unroll(disable)
   do {
     static_for<kD>([&](auto c) {
       constexpr int j = decltype(c)::value;
       const uint32_t kb = c0 + j;
-      // X(kb) was issued before W(kb + 1) and the kD - 2 later groups
-      wait_vmem_le<C::kGw + (kD - 2) * C::kG>();
-      lds_barrier();
-      const uint8_t* st = stage(c);
-      v8i_t xf[kMT];
-      float sxv[kMT];
+      uint8_t* st = stage(c);
+      const Head cur = head;
+      float swv[kS];
 #pragma unroll
-      for (int i = 0; i < kMT; ++i) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(st + 2048 * i + 16 * l);
-        const uint4 hi = *reinterpret_cast<const uint4*>(st + 2048 * i + 1024 + 16 * l);
-        xf[i] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        sxv[i] = reinterpret_cast<const float*>(st + sx_lds)[xm[i]];
-      }
-#pragma unroll
-      for (int i = 0; i < kMT; ++i) {
-        // branch-free: a block past the end gets the factor 0 and leaves acc
-        // unchanged bit for bit (acc is never -0)
-        const float sc = kb < nkb ? sxv[i] * swr[j] : 0.0f;
-#pragma unroll
-        for (int s = 0; s < kS; ++s) {
-          const v4f_t p = mfma_fp8(wr[j][s], xf[i]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][s][e] = fmaf(p[e], sc, acc[i][s][e]);
+      for (int s = 0; s < kS; ++s) swv[s] = sub + (uint32_t)s >= 8u ? cur.sw1 : cur.sw0;
+      v8i_t wfr[2];
+      wfr[0] = cur.wf;
+      v4f_t part[3];
+      static_for<kQ + 2>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        constexpr int s = q / kR, i = q % kR;
+        if constexpr (q < kQ) {
+          if constexpr (i == 0 && s + 1 < kS) {
+            const uint8_t* sp = st + 2048 * (s + 1);
+            wfr[(s + 1) & 1] = kPk ? frag(sp + 16 * l, sp + 1024 + 16 * l) : frag(sp + xr0, sp + xr1);
+          }
+          part[q % 3] = mfma_fp8(wfr[s & 1], cur.xf[i]);
         }
-      }
-      // refill: X(kb + kD - 1) into the stage of block kb - 1, which every wave
-      // finished reading before this step's barrier; W(kb + kD) into slot j
-      load_x(stage(std::integral_constant<int, (j + kD - 1) % kD>{}), clampb(kb + kD - 1));
-      load_w(j, clampb(kb + kD));
-      __builtin_amdgcn_sched_barrier(0);
+        if constexpr (q == kQ) {
+          // this wave's loads of block kb + 1 were issued before the kD - 2 later groups
+          wait_vmem_le<(kD - 2) * C::kG>();
+          lds_barrier();
+          issue(st, clampb(kb + kD));
+          read_head(stage(std::integral_constant<int, (j + 1) % kD>{}), kb + 1, head);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (q >= 2) {
+          constexpr int qp = q - 2, ps = qp / kR, pi = qp % kR;
+          const float sc = cur.sxv[pi] * swv[ps];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[pi][ps][e] = fmaf(part[qp % 3][e], sc, acc[pi][ps][e]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
     });
     c0 += kD;
   } while (c0 < nkb);
 #pragma unroll
-  for (int i = 0; i < kMT; ++i) {
-    const uint32_t m = 16u * i + lr;
+  for (int i = 0; i < kR; ++i) {
+    const uint32_t m = mw + 16u * i + lr;
     if (m < M) {
 #pragma unroll
       for (int s = 0; s < kS; ++s) {
@@ -1380,138 +1453,6 @@ __global__ __launch_bounds__(64 * kNW) void gemm_fp8_decode_xs_kernel(
   }
   // no direct-to-LDS load may still be in flight when the workgroup ends
   wait_vmem();
-}
-
-// ---------------------------------------------------------------------------
-// Mid-size FProp (64 < M <= 256 tokens: large rollout batches).  Too few
-// output tiles to fill the chip without splitting K, so each workgroup owns a
-// 64 x 64 output tile and its 8 waves split the K-blocks: wave w takes blocks
-// w, w + 8, w + 16, .. and folds them in that order into its own fp32 tile,
-// acc = fma(P_kb, fl32(sx * sw), acc), with both operands streamed from
-// global memory straight into registers kMidD K-blocks ahead.  The eight wave
-// tiles are then summed in the fixed tree order
-// ((a0 + a4) + (a2 + a6)) + ((a1 + a5) + (a3 + a7)) through LDS.  The result is
-// deterministic and the same for a row whatever mid-size batch holds it, but
-// it is not the single sequential K fold of the other FProp kernels.
-constexpr int kMidD = 2;  // K-blocks of loads in flight per wave
-
-__global__ __launch_bounds__(512) void gemm_fp8_mid_kernel(const uint8_t* __restrict__ X,
-                                                           const float* __restrict__ sx,
-                                                           const uint8_t* __restrict__ W,
-                                                           const float* __restrict__ sw, uint32_t M,
-                                                           uint32_t N, uint32_t K,
-                                                           uint16_t* __restrict__ Y) {
-  __shared__ v4f_t red[4][16][64];  // 64 KB: one 64 x 64 fp32 tile per partner wave
-  const int t = threadIdx.x, l = t & 63, lr = l & 15, lk = l >> 4;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  // launch order: the row tiles of one 64-column weight slice are adjacent and
-  // on one XCD (blocks are dealt to the 8 XCDs round-robin), so the slice
-  // streams from HBM once and is re-read from that XCD's L2
-  const uint32_t ntm = (M + 63) / 64, total = ntm * (N / 64);
-  uint32_t id = blockIdx.x;
-  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
-  const uint32_t m0 = (id % ntm) * 64u, n0 = (id / ntm) * 64u;
-  const uint32_t nkb = K / kBK;
-  const rsrc_t rw = make_rsrc(W, N * K);
-  const rsrc_t rx = make_rsrc(X, M * K);
-  uint32_t x_off[4], w_off[4], xm[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t m = m0 + 16u * i + lr;
-    xm[i] = m < M ? m : M - 1;  // ragged rows: repeat the last token, results not stored
-    x_off[i] = xm[i] * K + 32u * lk;
-    w_off[i] = (n0 + 16u * i + lr) * K + 32u * lk;
-  }
-  const rsrc_t rsx = make_rsrc(sx, nkb * M * 4u);
-  const rsrc_t rsw = make_rsrc(sw + (n0 / kBN) * nkb, nkb * 4u);
-  const uint32_t my_n = (uint32_t)w < nkb ? (nkb - (uint32_t)w + 7u) / 8u : 0u;  // this wave's K-blocks
-
-  v8i_t xr[kMidD][4], wr[kMidD][4];
-  float sxr[kMidD][4], swr[kMidD];
-  auto load = [&](int slot, uint32_t j) {
-    uint32_t kb = (uint32_t)w + 8u * j;
-    kb = kb < nkb ? kb : nkb - 1;  // past the end: a valid block whose product is not used
-    const uint32_t kofs = kb * kBK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const v4i_t a0 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_off[i], kofs, 0);
-      const v4i_t a1 = __builtin_amdgcn_raw_buffer_load_b128(rx, x_off[i] + 16u, kofs, 0);
-      xr[slot][i] = v8i_t{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      const v4i_t b0 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[i], kofs, 0);
-      const v4i_t b1 = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[i] + 16u, kofs, 0);
-      wr[slot][i] = v8i_t{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-      sxr[slot][i] = ld_scale(rsx, (kb * M + xm[i]) * 4u);
-    }
-    swr[slot] = ld_scale(rsw, kb * 4u);
-  };
-  v4f_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int d = 0; d < kMidD; ++d) load(d, (uint32_t)d);
-
-#pragma clang loop unroll(disable)
-  for (uint32_t c = 0; c < my_n; c += kMidD) {
-#pragma unroll
-    for (int d = 0; d < kMidD; ++d) {
-      {
-        // lane: token m0 + 16 i + lr, columns n0 + 16 j + 4 lk .. + 3.  Branch-
-        // free: a step past this wave's blocks gets the factor 0.
-        const bool valid = c + d < my_n;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float sc = valid ? sxr[d][i] * swr[d] : 0.0f;
-          v4f_t p[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) p[j] = mfma_fp8(wr[d][j], xr[d][i]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(p[j][e], sc, acc[i][j][e]);
-        }
-      }
-      load(d, c + d + kMidD);  // on every path (clamped past the end): exact per-slot waits
-    }
-  }
-
-  // fixed-order combine of the eight wave tiles
-#pragma unroll
-  for (int half = 4; half >= 1; half >>= 1) {
-    if (w >= half && w < 2 * half) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) red[w - half][4 * i + j][l] = acc[i][j];
-    }
-    __syncthreads();
-    if (w < half) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v4f_t o = red[w][4 * i + j][l];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][e] = acc[i][j][e] + o[e];
-        }
-    }
-    __syncthreads();
-  }
-  if (w == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t m = m0 + 16u * i + lr;
-      if (m < M) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t lo = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
-          const uint32_t hi = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
-          *reinterpret_cast<uint2*>(Y + (size_t)m * N + n0 + 16 * j + 4 * lk) = make_uint2(lo, hi);
-        }
-      }
-    }
-  }
 }
 
 __global__ void fill_zero_u16(uint16_t* __restrict__ p, int64_t n) {
@@ -1626,6 +1567,13 @@ static void launch_decode(bool packed, int64_t Mr, int64_t Nc, int64_t Kc, const
     launch_decode_p<false>(mt, kw, ks, A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C, stream);
 }
 
+template <bool kPk>
+static bool launch_decode_ws(int r, int s, int nw, const uint8_t* A, const float* sa, const uint8_t* B,
+                             const float* sb, uint32_t m, uint32_t n, uint32_t k, uint16_t* C, hipStream_t stream);
+template <bool kPk>
+static bool launch_fprop_ws(int64_t M, int64_t N, int64_t K, const uint8_t* A, const float* sa, const uint8_t* B,
+                            const float* sb, uint16_t* C, hipStream_t stream);
+
 template <int kMode, int kOut = kOutBf16>
 static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
                               int64_t Mr, int64_t Nc, int64_t Kc, void* Cv,
@@ -1637,25 +1585,18 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
     return launch_zero(static_cast<uint16_t*>(Cv), Mr * Nc * (kOut == kOutF32 ? 2 : 1), stream);
   }
   uint16_t* C = static_cast<uint16_t*>(Cv);
-  // rollout decode: weight-streaming kernel for up to 64 tokens (FProp)
-  if (kMode == kFprop && kOut == kOutBf16 && Mr <= 64 && Nc * Kc < (int64_t(1) << 31) &&
+  // rollout batches (FProp, up to 256 tokens): the weight-sharing kernel where
+  // launch_fprop_ws chooses it, else the weight-streaming decode kernel (up to
+  // 64 tokens)
+  if (kMode == kFprop && kOut == kOutBf16 && Mr <= 256 && Nc * Kc < (int64_t(1) << 31) &&
       Mr * Kc < (int64_t(1) << 31)) {
-    launch_decode(false, Mr, Nc, Kc, A, sa, B, sb, C, stream);
-    return hipGetLastError();
+    if (launch_fprop_ws<false>(Mr, Nc, Kc, A, sa, B, sb, C, stream)) return hipGetLastError();
+    if (Mr <= 64) {
+      launch_decode(false, Mr, Nc, Kc, A, sa, B, sb, C, stream);
+      return hipGetLastError();
+    }
   }
-  // 65..256 rows: the K-split kernel when K is long and there are few column
-  // tiles (so few 128 x 128 tiles, each with a long sequential K chain), the
-  // medium-tile kernel otherwise.  Measured on the 8B and 32B rollout shapes:
-  // the K-split kernel wins only for the 8B down projection (N = 4096,
-  // K = 12288), the medium kernel for QKV, gate+up and the 32B down.
   const int64_t nkb = Kc / kBK;
-  if (kMode == kFprop && kOut == kOutBf16 && Mr <= 256 && nkb >= 64 && Nc / kBN <= 32 &&
-      Nc * Kc < (int64_t(1) << 31) && Mr * Kc < (int64_t(1) << 31)) {
-    const int64_t tiles = (Nc / 64) * ((Mr + 63) / 64);
-    hipLaunchKernelGGL(gemm_fp8_mid_kernel, dim3((unsigned)tiles), dim3(512), 0, stream, A, sa, B, sb,
-                       (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, C);
-    return hipGetLastError();
-  }
   // the large-tile kernel works with 32-bit byte offsets; it needs >= 256
   // tiles to fill the chip
   const bool fits32 = (Mr + kLBM) * Kc < (int64_t(1) << 31) && Nc * Kc < (int64_t(1) << 31) &&
@@ -1914,27 +1855,87 @@ hipError_t launch_pack_weight_rollout(const uint8_t* qw, int64_t N, int64_t K, u
   return hipGetLastError();
 }
 
-template <int kMT, int kS, int kNW>
-static void launch_decode_xs_t(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb, uint32_t m,
+template <int kR, int kS, int kNW, bool kPk>
+static void launch_decode_ws_t(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb, uint32_t m,
                                uint32_t n, uint32_t k, uint16_t* C, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_fp8_decode_xs_kernel<kMT, kS, kNW>), dim3(n / (16 * kS * kNW)), dim3(64 * kNW), 0,
-                     stream, A, sa, B, sb, m, n, k, C);
+  constexpr uint32_t tm = DecodeWsCfg<kR, kS, kNW>::kTM;
+  const uint32_t grid = (n / (16u * kS)) * ((m + tm - 1) / tm);
+  hipLaunchKernelGGL((gemm_fp8_decode_ws_kernel<kR, kS, kNW, kPk>), dim3(grid), dim3(64 * kNW), 0, stream, A, sa, B,
+                     sb, m, n, k, C);
 }
 
-// Packed FProp, sequential fold: the decode kernel (launch_decode's packed
-// rule), except from 33 rows with at least 1536 strips of 16 columns, where the
-// X-sharing kernel's workgroups of 4 waves x 2 strips stage each K-block of
-// the tokens once for 128 columns.  Measured at the 8B gate+up projection
-// (N = 24576, M = 64; graph replays, 4 rotated weights): 27.6 us against
-// 31.2 us for the best decode-kernel launch.
+// The weight-sharing kernel's instantiated shapes (tokens per wave / 16,
+// strips, waves); false for any other.
+template <bool kPk>
+static bool launch_decode_ws(int r, int s, int nw, const uint8_t* A, const float* sa, const uint8_t* B,
+                             const float* sb, uint32_t m, uint32_t n, uint32_t k, uint16_t* C, hipStream_t stream) {
+#define JETFP8_WS(R, S, NW)                                              \
+  if (r == R && s == S && nw == NW) {                                    \
+    launch_decode_ws_t<R, S, NW, kPk>(A, sa, B, sb, m, n, k, C, stream); \
+    return true;                                                         \
+  }
+  JETFP8_WS(1, 6, 4) JETFP8_WS(1, 4, 4) JETFP8_WS(1, 3, 4) JETFP8_WS(1, 2, 4) JETFP8_WS(1, 1, 4)
+  JETFP8_WS(2, 6, 4) JETFP8_WS(2, 4, 4) JETFP8_WS(2, 3, 4) JETFP8_WS(2, 2, 4) JETFP8_WS(2, 1, 4)
+  JETFP8_WS(2, 6, 8)
+#undef JETFP8_WS
+  return false;
+}
+
+// The weight-sharing kernel's launch shape for 33 .. 256 rows, or false where
+// it is not the choice (up to 32 rows, and for the packed weight 33 .. 64 rows
+// with more than 64 K-blocks: the streaming decode kernel).  The shape:
+//   at least 1536 strips of 16 columns, a multiple of 6: 6 strips per
+//     workgroup and all rows in one token group (up to 64 rows: 4 waves of 16
+//     tokens; 128: 4 of 32; 256: 8 of 32), 256 workgroups for the 8B gate+up
+//     projection;
+//   otherwise, 33 .. 64 rows: 4 waves of 16 tokens on 2 strips (1 for long
+//     contractions); over 64 rows: token groups of 64 rows (128 over 128 rows
+//     when K is at most 64 K-blocks) with the most strips per workgroup
+//     (6, 4, 3, 2, 1) that still give 256 workgroups.
+// Measured on the 8B rollout shapes (QKV, gate+up, down at 32 .. 256 rows,
+// HIP-graph replays over 4 rotated weights): from 65 rows, 1.0-1.8x faster than
+// the 128 x 128 kernel and the split-K FProp at every shape but the down
+// projection at 200 and 256 rows (13 % slower than split-K there).
+template <bool kPk>
+static bool launch_fprop_ws(int64_t M, int64_t N, int64_t K, const uint8_t* A, const float* sa, const uint8_t* B,
+                            const float* sb, uint16_t* C, hipStream_t stream) {
+  const int64_t strips = N / 16, nkb = K / kBK;
+  if (M <= 32 || M > 256 || nkb > kWsMaxKb) return false;
+  int r = 1, s = 1, nw = 4;
+  if (strips % 6 == 0 && strips / 6 >= 256) {
+    s = 6;
+    r = M <= 64 ? 1 : 2;
+    if (M > 128) nw = 8;
+  } else if (M <= 64) {
+    // long contractions: the packed weight streams fastest through the decode
+    // kernel, the row-major one through this kernel with one strip per workgroup
+    if (nkb > 64) {
+      if (kPk) return false;
+    } else {
+      s = 2;
+    }
+  } else {
+    r = (M > 128 && nkb <= 64) ? 2 : 1;
+    const int64_t tg = (M + 64 * r - 1) / (64 * r);
+    for (int c : {6, 4, 3, 2}) {
+      if (strips % c == 0 && (strips / c) * tg >= 256) {
+        s = c;
+        break;
+      }
+    }
+  }
+  return launch_decode_ws<kPk>(r, s, nw, A, sa, B, sb, (uint32_t)M, (uint32_t)N, (uint32_t)K, C, stream);
+}
+
+// Packed FProp (up to 256 rows), sequential fold: the weight-sharing kernel
+// where launch_fprop_ws chooses it, else the decode kernel (launch_decode's
+// packed rule; it also takes contractions of more than 512 K-blocks, whose
+// weight-block scales would not fit the weight-sharing kernel's LDS copy).
 hipError_t launch_gemm_fprop_packed(const uint8_t* qx, const float* sx, const uint8_t* qwp, const float* sw,
                                     int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   if (K == 0) return launch_zero(y, M * N, stream);
-  if (M > 32 && N / 16 >= 1536) {
-    launch_decode_xs_t<4, 2, 4>(qx, sx, qwp, sw, (uint32_t)M, (uint32_t)N, (uint32_t)K, y, stream);
-    return hipGetLastError();
-  }
+  if (launch_fprop_ws<true>(M, N, K, qx, sx, qwp, sw, y, stream)) return hipGetLastError();
   launch_decode(true, M, N, K, qx, sx, qwp, sw, y, stream);
   return hipGetLastError();
 }

@@ -43,7 +43,7 @@ hipError_t launch_gemm_fprop_swiglu_quant(const uint8_t* qx, const float* sx, co
                                           int64_t M, int64_t N, int64_t K, uint8_t* q, float* s,
                                           hipStream_t stream);
 // Rollout-packed copy of quantised weight codes (a byte permutation) and the
-// FProp of up to 64 rows that streams it.
+// FProp of up to 256 rows that streams it.
 hipError_t launch_pack_weight_rollout(const uint8_t* qw, int64_t N, int64_t K, uint8_t* qwp, hipStream_t stream);
 hipError_t launch_gemm_fprop_packed(const uint8_t* qx, const float* sx, const uint8_t* qwp, const float* sw,
                                     int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);

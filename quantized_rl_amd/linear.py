@@ -24,7 +24,7 @@ keeps the 128x128 FP8 form and re-quantises only when the parameter's storage
 or its in-place version counter changes.
 
 Rollout: a forward that builds no autograd graph (``torch.no_grad()``, or
-neither input nor weight requiring grad) over at most 64 rows runs
+neither input nor weight requiring grad) over at most 256 rows runs
 ``gemm_fprop_packed`` on the cached weight's rollout-packed copy
 (``pack_weight_rollout``, made once per weight version).  Its output is bitwise
 the training forward's: same codes, scales and fold.
@@ -37,12 +37,12 @@ from . import _lib
 # widest row the RMSNorm backward kernel takes (rmsnorm_backward_workspace_bytes)
 RMSNORM_BACKWARD_MAX_K = 24576
 # most rows gemm_fprop_packed takes
-ROLLOUT_MAX_ROWS = 64
+ROLLOUT_MAX_ROWS = 256
 
 
 def rollout_path(x2, w):
     """True when a forward of x2 [M, K] against w [N, K] needs no autograd graph and
-    fits gemm_fprop_packed (M <= 64, 32-bit byte offsets): the rollout path."""
+    fits gemm_fprop_packed (M <= 256, 32-bit byte offsets): the rollout path."""
     if torch.is_grad_enabled() and (x2.requires_grad or w.requires_grad):
         return False
     M, K = x2.shape

@@ -261,6 +261,6 @@ def test_pack_weight_rollout_and_fprop_packed_validation(jetlib):
     assert c(f, P[0], P[1], P[2], P[3], 16, 128, 128, 0, 0) == ENULL
     assert c(f, P[0], P[1], P[2] + 4, P[3], 16, 128, 128, P[4], 0) == EALIGN
     assert c(f, P[0], P[1], P[2], P[3], 16, 128, 128, P[2] + 64, 0) == EALIAS  # y over qwp
-    assert c(f, P[0], P[1], P[2], P[3], 65, 128, 128, P[4], 0) == 5            # more than 64 rows
+    assert c(f, P[0], P[1], P[2], P[3], 257, 128, 128, P[4], 0) == 5           # more than 256 rows
     assert c(f, B[0], B[1], B[2], B[3], 16, 1 << 16, 1 << 15, B[4], 0) == 5    # weight past 2^31 bytes
     assert c(f, 0, 0, P[2], P[3], 0, 128, 128, 0, 0) == OK                      # M = 0: nothing to do

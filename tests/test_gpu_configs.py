@@ -50,14 +50,15 @@ def test_decode_8b(m):
                   f"decode down M={m}")
 
 
-@pytest.mark.parametrize("m", [16, 64])
+@pytest.mark.parametrize("m", [16, 64, 256])
 def test_unified_flow_rollout_rows_inside_training_batch(m):
     """The unified precision flow at kernel level: the rollout graph is a
     subgraph of the training forward.  The decode tokens of the 8B workload,
     normalised+quantised and multiplied by the FP8 QKV weight at rollout shape
-    (M = 16 / 64: decode kernel) and inside an 8192-token training batch
-    (256 x 256 kernel), give identical FP8 codes, scales and FProp outputs, bit
-    for bit; the rollout side also matches the oracle."""
+    (M = 16: decode kernel; 64 and 256: weight-sharing kernel; over the
+    row-major weight and over its rollout-packed copy) and inside an 8192-token
+    training batch (256 x 256 kernel), give identical FP8 codes, scales and
+    FProp outputs, bit for bit; the rollout side also matches the oracle."""
     d = synth.decode_8b(m)
     eps, r0 = d["eps"], 1000
     big = synth.random_bf16((8192, 4096), seed=77 + m, std=1.0)
@@ -67,11 +68,13 @@ def test_unified_flow_rollout_rows_inside_training_batch(m):
     qb, sb = jet.rmsnorm_quant(bf16_dev(big), g_d, eps)
     qw, sw = jet.quantize_weight_128x128(bf16_dev(d["w_qkv"]))
     yd = host(jet.gemm_fprop(qd, sd, qw, sw))
+    yp = host(jet.gemm_fprop_packed(qd, sd, jet.pack_weight_rollout(qw), sw))
     yb = host(jet.gemm_fprop(qb, sb, qw, sw))[r0:r0 + m]
     qdh, sdh = host(qd), host(sd)
     assert np.array_equal(qdh, host(qb)[r0:r0 + m]), "FP8 codes differ between rollout and training batch"
     assert np.array_equal(sdh.view(np.uint32), host(sb)[:, r0:r0 + m].view(np.uint32)), "scales differ"
     assert np.array_equal(yd, yb), "FProp output differs between rollout and training batch"
+    assert np.array_equal(yp, yb), "packed FProp output differs from the training batch"
     qo, so = oracle.rmsnorm_quant(d["x"], d["gamma"], eps)
     assert np.array_equal(qdh, qo) and np.array_equal(sdh.view(np.uint32), so.view(np.uint32))
     cols = np.sort(np.random.default_rng(m).choice(6144, 96, replace=False))

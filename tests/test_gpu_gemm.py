@@ -73,11 +73,11 @@ def check_full_range(y, ref, absref, what):
 
 # ---------------------------------------------------------------- FProp
 
-# shapes with at least 256 tiles of 256 x 256 run the large-tile kernel, M <= 64
-# the decode kernel, the others the 128 x 128 medium-tile kernel (four operand
-# stages with at most one tile per CU, as for all but the marked shapes here,
-# two stages otherwise); K-block counts 1 .. 5, 8 and 16 cover the ends of the
-# four-stage loop
+# shapes with at least 256 tiles of 256 x 256 run the large-tile kernel, M <= 32
+# the decode kernel, 33 .. 256 rows the weight-sharing kernel, the others the
+# 128 x 128 medium-tile kernel (four operand stages with at most one tile per
+# CU, two otherwise); K-block counts 1 .. 5, 8 and 16 cover the ends of the
+# pipelined loops
 FPROP_SHAPES = [(256, 384, 512), (1, 128, 128), (16, 384, 256), (64, 256, 128), (200, 384, 512),
                 (130, 128, 1024), (257, 640, 384),
                 (256, 256, 256), (300, 512, 384), (513, 768, 640), (1024, 1280, 2048)]
@@ -318,10 +318,10 @@ def test_linear_8b_up_forward_backward_sampled():
 def test_fprop_batch_invariant_across_kernels():
     """The pages' unified flow makes the rollout graph a subgraph of the training
     forward; at kernel level a token's FProp output must not depend on the batch
-    it is computed in.  Rows computed alone or in decode batches (M <= 64,
-    weight-streaming kernel), in a batch of a few hundred (128 x 128 kernel) and
-    inside a large training batch (256 x 256 kernel) must be bitwise identical.
-    (Batches of 65..256 rows use the K-split kernel: see test_fprop_mid_*.)"""
+    it is computed in.  Rows computed alone or in decode batches (weight-streaming
+    kernel up to 32 rows, weight-sharing kernel from 33 to 256), in a batch of a
+    few hundred (128 x 128 kernel) and inside a large training batch (256 x 256
+    kernel) must be bitwise identical."""
     rng = np.random.default_rng(21)
     M, N, K = 2048, 1024, 1024  # 8 x 4 = 32 large tiles: below the large-kernel threshold
     qx_all, qw = codes(rng, (M, K)), codes(rng, (N, K))
@@ -333,7 +333,7 @@ def test_fprop_batch_invariant_across_kernels():
     y_big = host(jet.gemm_fprop(u8_dev(qx_big), f32_dev(sx_big), qw_d, sw_d))[:M]
     y_mid = host(jet.gemm_fprop(u8_dev(qx_all), f32_dev(sx_all), qw_d, sw_d))
     assert np.array_equal(y_mid, y_big), "128x128 vs 256x256 kernel"
-    for m0, m in [(0, 1), (5, 16), (100, 33), (640, 64), (1000, 300)]:
+    for m0, m in [(0, 1), (5, 16), (100, 33), (640, 64), (700, 100), (1200, 256), (1000, 300)]:
         y = host(jet.gemm_fprop(u8_dev(qx_all[m0:m0 + m]), f32_dev(np.ascontiguousarray(sx_all[:, m0:m0 + m])),
                                 qw_d, sw_d))
         assert np.array_equal(y, y_big[m0:m0 + m]), f"rows {m0}..{m0 + m}"
@@ -343,10 +343,11 @@ def test_fprop_batch_invariant_across_kernels():
 @pytest.mark.parametrize("m", [1, 16, 17, 32, 50, 64])
 def test_fprop_decode_wave_splits(m, k):
     """Decode FProp (M <= 64) at N = 384 (24 strips of 16 columns): K from one
-    K-block to 64 K-blocks walks the waves-per-strip choice through 1, 2, 4, 8
-    and 16, and M through 1, 2 and 4 token sub-tiles (17 and 50 are ragged).
-    Each result matches the oracle and equals, bit for bit, the same rows
-    computed inside a 257-token batch by the 128 x 128 kernel."""
+    K-block to 64 K-blocks walks the decode kernel's waves-per-strip choice
+    through 1, 2, 4, 8 and 16, and M through 1, 2 and 4 token sub-tiles (17 and
+    50 are ragged; from 33 rows the weight-sharing kernel with 2 strips per
+    workgroup).  Each result matches the oracle and equals, bit for bit, the same
+    rows computed inside a 257-token batch by the 128 x 128 kernel."""
     n, mb = 384, 257
     rng = np.random.default_rng(1000 + 13 * m + k)
     qx, qw = codes(rng, (mb, k)), codes(rng, (n, k))
@@ -365,33 +366,36 @@ def test_fprop_decode_wave_splits(m, k):
 @pytest.mark.parametrize("n,k", [(128, 128), (384, 1152), (640, 4096), (256, 12288)])
 @pytest.mark.parametrize("m", [65, 100, 128, 200, 256])
 def test_fprop_mid_batches(m, n, k):
-    """FProp at 65..256 rows: the K-split kernel for K = 96 blocks with few column
-    tiles (waves with several blocks), the medium-tile kernel otherwise.  Parity
-    with the oracle, guards intact, and every row bitwise equal to the same row
-    computed in another batch of this size range (rows are independent and
-    neither kernel's order depends on M)."""
+    """FProp at 65..256 rows: the weight-sharing kernel (token groups of 64 or 128
+    rows, ragged at 100 and 200; 1 .. 6 strips per workgroup; K from 1 to 96
+    blocks).  Parity with the oracle, guards intact, and every row bitwise equal to
+    the same row computed in another batch of this size range and inside a
+    300-row batch (128 x 128 kernel): every kernel folds K in order."""
     rng = np.random.default_rng(2000 + m + n + k)
-    qx, qw = codes(rng, (256, k)), codes(rng, (n, k))
-    sx, sw = scales(rng, (k // 128, 256)), scales(rng, (n // 128, k // 128))
+    qx, qw = codes(rng, (300, k)), codes(rng, (n, k))
+    sx, sw = scales(rng, (k // 128, 300)), scales(rng, (n // 128, k // 128))
     qw_d, sw_d = u8_dev(qw), f32_dev(sw)
     sxm = np.ascontiguousarray(sx[:, :m])
     yg = Guarded((m, n), torch.bfloat16)
     jet.gemm_fprop(u8_dev(qx[:m]), f32_dev(sxm), qw_d, sw_d, yg.t)
     other = 97 if m != 97 else 256
     y_o = host(jet.gemm_fprop(u8_dev(qx[:other]), f32_dev(np.ascontiguousarray(sx[:, :other])), qw_d, sw_d))
+    y_big = host(jet.gemm_fprop(u8_dev(qx), f32_dev(sx), qw_d, sw_d))
     torch.cuda.synchronize()
     assert yg.intact()
     y = host(yg.t)
     check(y, oracle.gemm_fprop_ref(qx[:m], sxm, qw, sw), f"mid fprop {m}x{n}x{k}")
     r = min(m, other)
     assert np.array_equal(y[:r], y_o[:r]), "rows differ between mid-size batches"
+    assert np.array_equal(y, y_big[:m]), "rows differ from the training-size batch"
 
 
 @pytest.mark.parametrize("m,n,k", [(130, 16384, 256), (256, 24576, 128), (97, 24576, 384)])
 def test_fprop_medium_kernel_below_256_rows(m, n, k):
-    """65..256 rows with many output columns: the 128 x 128 medium-tile kernel (a
-    ragged last row tile).  Parity with the oracle, and every row bitwise equal to
-    the same row inside a 257-row batch: both fold K sequentially."""
+    """65..256 rows with many output columns (1024 or 1536 strips of 16 columns:
+    the weight-sharing kernel with 6 strips per workgroup where they divide,
+    else 4).  Parity with the oracle, and every row bitwise equal to the same row
+    inside a 257-row batch: both fold K sequentially."""
     rng = np.random.default_rng(3000 + m + k)
     qx, qw = codes(rng, (257, k)), codes(rng, (n, k))
     sx, sw = scales(rng, (k // 128, 257)), scales(rng, (n // 128, k // 128))
@@ -411,10 +415,11 @@ def test_fprop_medium_kernel_below_256_rows(m, n, k):
 @pytest.mark.parametrize("m", [1, 17, 33, 64])
 def test_fprop_decode_two_strips_per_wave(m, k):
     """Decode FProp with 384 strips of 16 columns (N = 6144, the 8B QKV width):
-    each wave serves two strips with one set of X fragments.  M = 1 .. 64 and
-    K = 2 .. 32 blocks walk one, two and four token sub-tiles with 1, 2 and 4
-    waves per strip pair.  Parity with the oracle, and every row bitwise equal
-    to the same row in a 257-row batch (128 x 128 kernel)."""
+    each wave serves two strips with one set of X fragments.  M = 1 .. 32 and
+    K = 2 .. 32 blocks walk one and two token sub-tiles with 1, 2 and 4 waves
+    per strip pair (33 and 64 rows: the weight-sharing kernel).  Parity with the
+    oracle, and every row bitwise equal to the same row in a 257-row batch
+    (128 x 128 kernel)."""
     n, mb = 6144, 257
     rng = np.random.default_rng(4000 + 7 * m + k)
     qx, qw = codes(rng, (mb, k)), codes(rng, (n, k))

@@ -72,14 +72,14 @@ def test_weight_cache_requantises_only_on_change(monkeypatch):
 
 def test_rollout_path_rule():
     """The rollout path is taken only when no autograd graph is needed and the batch
-    fits gemm_fprop_packed (at most 64 rows)."""
+    fits gemm_fprop_packed (at most 256 rows)."""
     w = torch.zeros(256, 512, dtype=torch.bfloat16, requires_grad=True)
     x = torch.zeros(16, 512, dtype=torch.bfloat16)
     assert not linear.rollout_path(x, w)                   # the weight needs a gradient
     with torch.no_grad():
         assert linear.rollout_path(x, w)
-        assert linear.rollout_path(torch.zeros(64, 512, dtype=torch.bfloat16), w)
-        assert not linear.rollout_path(torch.zeros(65, 512, dtype=torch.bfloat16), w)
+        assert linear.rollout_path(torch.zeros(256, 512, dtype=torch.bfloat16), w)
+        assert not linear.rollout_path(torch.zeros(257, 512, dtype=torch.bfloat16), w)
     w_frozen = w.detach()
     assert linear.rollout_path(x, w_frozen)                # frozen weight, plain input
     assert not linear.rollout_path(x.clone().requires_grad_(), w_frozen)

@@ -1233,7 +1233,7 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
 // fl32(sx * sw), acc) in ascending K order: the output is bitwise gemm_fprop's
 // on the same rows in any batch.
 constexpr int kWsMaxKb = 512;  // K <= 65536: the copied weight-block scales fit 4 KB
-template <int kR, int kS, int kNW>
+template <int kR, int kS, int kNW, int kOcc = 1>  // kOcc: workgroups per CU (LDS split between them)
 struct DecodeWsCfg {
   static constexpr int kTM = 16 * kR * kNW;               // tokens of a workgroup
   static constexpr int kWPieces = 2 * kS;                 // 1 KB weight pieces per K-block
@@ -1242,7 +1242,7 @@ struct DecodeWsCfg {
   static constexpr int kWBytes = 2048 * kS;
   static constexpr int kXBytes = 2048 * kR;               // one wave's X fragments
   static constexpr int kStage = kWBytes + kNW * kXBytes + 256 * kNW;
-  static constexpr int kFit = (155 * 1024) / kStage;    // with the scale copy, within 160 KB of LDS
+  static constexpr int kFit = (kOcc == 1 ? 155 * 1024 : 75 * 1024) / kStage;  // with the scale copy, within the LDS share
   static constexpr int kCnt = 63 / kG + 1;                // (kD - 1) kG loads may stay in flight
   static constexpr int kD0 = kFit < kCnt ? kFit : kCnt;
   static constexpr int kD = kD0 > 8 ? 8 : kD0;
@@ -1251,11 +1251,11 @@ struct DecodeWsCfg {
   static_assert(kS <= 8, "a workgroup's strips span at most two weight blocks");
 };
 
-template <int kR, int kS, int kNW, bool kPk>
-__global__ __launch_bounds__(64 * kNW) void gemm_fp8_decode_ws_kernel(
+template <int kR, int kS, int kNW, bool kPk, int kOcc>
+__global__ __launch_bounds__(64 * kNW, kOcc) void gemm_fp8_decode_ws_kernel(
     const uint8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ Wp,
     const float* __restrict__ sw, uint32_t M, uint32_t N, uint32_t K, uint16_t* __restrict__ Y) {
-  using C = DecodeWsCfg<kR, kS, kNW>;
+  using C = DecodeWsCfg<kR, kS, kNW, kOcc>;
   constexpr int kD = C::kD;
   __shared__ __attribute__((aligned(16))) uint8_t ws0[C::kStage], ws1[C::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t ws2[kD > 2 ? C::kStage : 16], ws3[kD > 3 ? C::kStage : 16];
@@ -1568,7 +1568,7 @@ static void launch_decode(bool packed, int64_t Mr, int64_t Nc, int64_t Kc, const
 }
 
 template <bool kPk>
-static bool launch_decode_ws(int r, int s, int nw, const uint8_t* A, const float* sa, const uint8_t* B,
+static bool launch_decode_ws(int r, int s, int nw, int occ, const uint8_t* A, const float* sa, const uint8_t* B,
                              const float* sb, uint32_t m, uint32_t n, uint32_t k, uint16_t* C, hipStream_t stream);
 template <bool kPk>
 static bool launch_fprop_ws(int64_t M, int64_t N, int64_t K, const uint8_t* A, const float* sa, const uint8_t* B,
@@ -1855,28 +1855,28 @@ hipError_t launch_pack_weight_rollout(const uint8_t* qw, int64_t N, int64_t K, u
   return hipGetLastError();
 }
 
-template <int kR, int kS, int kNW, bool kPk>
+template <int kR, int kS, int kNW, bool kPk, int kOcc = 1>
 static void launch_decode_ws_t(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb, uint32_t m,
                                uint32_t n, uint32_t k, uint16_t* C, hipStream_t stream) {
-  constexpr uint32_t tm = DecodeWsCfg<kR, kS, kNW>::kTM;
+  constexpr uint32_t tm = DecodeWsCfg<kR, kS, kNW, kOcc>::kTM;
   const uint32_t grid = (n / (16u * kS)) * ((m + tm - 1) / tm);
-  hipLaunchKernelGGL((gemm_fp8_decode_ws_kernel<kR, kS, kNW, kPk>), dim3(grid), dim3(64 * kNW), 0, stream, A, sa, B,
-                     sb, m, n, k, C);
+  hipLaunchKernelGGL((gemm_fp8_decode_ws_kernel<kR, kS, kNW, kPk, kOcc>), dim3(grid), dim3(64 * kNW), 0, stream, A,
+                     sa, B, sb, m, n, k, C);
 }
 
 // The weight-sharing kernel's instantiated shapes (tokens per wave / 16,
-// strips, waves); false for any other.
+// strips, waves, workgroups per CU); false for any other.
 template <bool kPk>
-static bool launch_decode_ws(int r, int s, int nw, const uint8_t* A, const float* sa, const uint8_t* B,
+static bool launch_decode_ws(int r, int s, int nw, int occ, const uint8_t* A, const float* sa, const uint8_t* B,
                              const float* sb, uint32_t m, uint32_t n, uint32_t k, uint16_t* C, hipStream_t stream) {
-#define JETFP8_WS(R, S, NW)                                              \
-  if (r == R && s == S && nw == NW) {                                    \
-    launch_decode_ws_t<R, S, NW, kPk>(A, sa, B, sb, m, n, k, C, stream); \
-    return true;                                                         \
+#define JETFP8_WS(R, S, NW, OCC)                                              \
+  if (r == R && s == S && nw == NW && occ == OCC) {                           \
+    launch_decode_ws_t<R, S, NW, kPk, OCC>(A, sa, B, sb, m, n, k, C, stream); \
+    return true;                                                              \
   }
-  JETFP8_WS(1, 6, 4) JETFP8_WS(1, 4, 4) JETFP8_WS(1, 3, 4) JETFP8_WS(1, 2, 4) JETFP8_WS(1, 1, 4)
-  JETFP8_WS(2, 6, 4) JETFP8_WS(2, 4, 4) JETFP8_WS(2, 3, 4) JETFP8_WS(2, 2, 4) JETFP8_WS(2, 1, 4)
-  JETFP8_WS(2, 6, 8)
+  JETFP8_WS(1, 6, 4, 2) JETFP8_WS(2, 6, 4, 1) JETFP8_WS(2, 6, 4, 2) JETFP8_WS(1, 2, 4, 1) JETFP8_WS(1, 1, 4, 1)
+  JETFP8_WS(1, 4, 4, 2) JETFP8_WS(1, 3, 4, 2) JETFP8_WS(1, 2, 4, 2) JETFP8_WS(1, 1, 4, 2)
+  JETFP8_WS(2, 4, 4, 2) JETFP8_WS(2, 3, 4, 2) JETFP8_WS(2, 2, 4, 2) JETFP8_WS(2, 1, 4, 2)
 #undef JETFP8_WS
   return false;
 }
@@ -1885,27 +1885,31 @@ static bool launch_decode_ws(int r, int s, int nw, const uint8_t* A, const float
 // it is not the choice (up to 32 rows, and for the packed weight 33 .. 64 rows
 // with more than 64 K-blocks: the streaming decode kernel).  The shape:
 //   at least 1536 strips of 16 columns, a multiple of 6: 6 strips per
-//     workgroup and all rows in one token group (up to 64 rows: 4 waves of 16
-//     tokens; 128: 4 of 32; 256: 8 of 32), 256 workgroups for the 8B gate+up
-//     projection;
+//     workgroup of 4 waves; up to 64 rows one token group of 16 tokens per
+//     wave, two workgroups per CU; 65 .. 128 rows one group of 32 per wave,
+//     one workgroup per CU; over 128 rows groups of 128 rows, two per CU
+//     (512 workgroups for the 8B gate+up projection at 256 tokens);
 //   otherwise, 33 .. 64 rows: 4 waves of 16 tokens on 2 strips (1 for long
 //     contractions); over 64 rows: token groups of 64 rows (128 over 128 rows
 //     when K is at most 64 K-blocks) with the most strips per workgroup
-//     (6, 4, 3, 2, 1) that still give 256 workgroups.
-// Measured on the 8B rollout shapes (QKV, gate+up, down at 32 .. 256 rows,
-// HIP-graph replays over 4 rotated weights): from 65 rows, 1.0-1.8x faster than
-// the 128 x 128 kernel and the split-K FProp at every shape but the down
-// projection at 200 and 256 rows (13 % slower than split-K there).
+//     (6, 4, 3, 2, 1) that still give 256 workgroups, two workgroups per CU.
+// Two workgroups per CU split the LDS, so each holds fewer K-blocks in flight
+// (2 - 4 instead of 3 - 8), and one computes while the other waits at its
+// block barrier.  Measured on the 8B rollout shapes (QKV, gate+up, down at
+// 32 .. 256 rows, HIP-graph replays over 4 rotated weights): from 65 rows
+// 1.0-2.0x faster than the 128 x 128 kernel and the split-K FProp at every
+// shape; two workgroups per CU gained 4-12 % at 256 tokens and 10 % for
+// gate+up at 64, and lost 9 % for gate+up at 128.
 template <bool kPk>
 static bool launch_fprop_ws(int64_t M, int64_t N, int64_t K, const uint8_t* A, const float* sa, const uint8_t* B,
                             const float* sb, uint16_t* C, hipStream_t stream) {
   const int64_t strips = N / 16, nkb = K / kBK;
   if (M <= 32 || M > 256 || nkb > kWsMaxKb) return false;
-  int r = 1, s = 1, nw = 4;
+  int r = 1, s = 1, occ = 1;
   if (strips % 6 == 0 && strips / 6 >= 256) {
     s = 6;
     r = M <= 64 ? 1 : 2;
-    if (M > 128) nw = 8;
+    occ = (M <= 64 || M > 128) ? 2 : 1;
   } else if (M <= 64) {
     // long contractions: the packed weight streams fastest through the decode
     // kernel, the row-major one through this kernel with one strip per workgroup
@@ -1915,6 +1919,7 @@ static bool launch_fprop_ws(int64_t M, int64_t N, int64_t K, const uint8_t* A, c
       s = 2;
     }
   } else {
+    occ = 2;
     r = (M > 128 && nkb <= 64) ? 2 : 1;
     const int64_t tg = (M + 64 * r - 1) / (64 * r);
     for (int c : {6, 4, 3, 2}) {
@@ -1924,7 +1929,7 @@ static bool launch_fprop_ws(int64_t M, int64_t N, int64_t K, const uint8_t* A, c
       }
     }
   }
-  return launch_decode_ws<kPk>(r, s, nw, A, sa, B, sb, (uint32_t)M, (uint32_t)N, (uint32_t)K, C, stream);
+  return launch_decode_ws<kPk>(r, s, 4, occ, A, sa, B, sb, (uint32_t)M, (uint32_t)N, (uint32_t)K, C, stream);
 }
 
 // Packed FProp (up to 256 rows), sequential fold: the weight-sharing kernel

@@ -68,9 +68,15 @@
  *   empty); outputs must not overlap inputs or each other; sizes >= 0 and at
  *   most 2^31 - 1 per dimension; the divisibility rules stated per function.
  *   A status of JETFP8_ELAUNCH reports a HIP error from the enqueue itself.
- * - GEMMs address operands with 32-bit byte offsets: a call whose operands or
- *   output would reach 2^31 bytes (counting one 256-row tile of padding on
- *   the row dimension) returns JETFP8_EUNSUPPORTED and writes nothing.
+ * - GEMMs address operands with 32-bit byte offsets per launch.  A GEMM whose
+ *   row operand or output does not fit runs as several launches over row
+ *   ranges (the rows of X, dY and the output for FProp and DGrad, the output
+ *   features of dY^T and dW for WGrad), with the same result as one launch:
+ *   the rows are independent and each range folds K in the same order.  What
+ *   must fit is the column operand (the weight [N][K] for FProp and DGrad, the
+ *   128x1-requantised X^T [K][M] for WGrad: below 2^31 bytes) and 512 rows of
+ *   the row operand and of the output; a call beyond that returns
+ *   JETFP8_EUNSUPPORTED and writes nothing.
  * - Inputs must be finite (NaN/Inf are outside the contract; the kernels do
  *   not hang on them, but the result is unspecified).
  * - Identical inputs give bitwise identical outputs (no atomics, no split-K
@@ -371,8 +377,9 @@ int gemm_wgrad(const uint8_t* qdyt, const float* sdyt, const uint8_t* qxt, const
  * G is the fp32 accumulator that gemm_wgrad rounds: gemm_wgrad's output is
  * exactly the bf16 (nearest-even) rounding of G.
  *   dw : f32 [N][K], read as well as written when accumulate == 1.
- * Shape rules as gemm_wgrad, with 4-byte output elements in the 2^31-byte
- * limit; accumulate must be 0 or 1 (else JETFP8_EINVAL).  M == 0 writes zeros
+ * Shape rules as gemm_wgrad, with 4-byte output elements in the size limit
+ * (512 rows of dw below 2^31 bytes); accumulate must be 0 or 1 (else
+ * JETFP8_EINVAL).  M == 0 writes zeros
  * (accumulate == 0) or leaves dw unchanged (accumulate == 1).
  */
 int gemm_wgrad_f32(const uint8_t* qdyt, const float* sdyt, const uint8_t* qxt, const float* sxt,

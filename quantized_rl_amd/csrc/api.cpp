@@ -48,11 +48,13 @@ int check_ptrs(std::initializer_list<Buf> ins, std::initializer_list<Buf> outs) 
 int launched(hipError_t e) { return e == hipSuccess ? JETFP8_OK : JETFP8_ELAUNCH; }
 
 // The GEMM kernels address their operands with 32-bit byte offsets (buffer
-// resources).  With one 256-row tile of ragged-row padding, both operands and
-// the output (rows x cols elements of out_bytes each) must stay below 2^31 bytes.
-bool gemm_fits(int64_t rows, int64_t cols, int64_t kc, int64_t out_bytes = 2) {
+// resources).  The library launches a problem whose rows do not fit as
+// several row ranges, so what must fit is the B operand (cols x kc bytes) and
+// a range of 512 rows of A (kc bytes each) and of the output (cols elements of
+// out_bytes each).
+bool gemm_fits(int64_t cols, int64_t kc, int64_t out_bytes = 2) {
   const int64_t lim = int64_t(1) << 31;
-  return (rows + 256) * kc < lim && cols * kc < lim && (rows + 256) * cols * out_bytes < lim;
+  return cols * kc < lim && 512 * kc < lim && 512 * cols * out_bytes < lim;
 }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -146,7 +148,7 @@ int gemm_fprop(const uint8_t* qx, const float* sx, const uint8_t* qw, const floa
                            {sw, 4 * (N * K / (128 * 128))}},
                           {{y, 2 * M * N}}))
     return st;
-  if (!gemm_fits(M, N, K)) return JETFP8_EUNSUPPORTED;
+  if (!gemm_fits(N, K)) return JETFP8_EUNSUPPORTED;
   return launched(jetfp8::launch_gemm_fprop(qx, sx, qw, sw, M, N, K, y, as_stream(stream)));
 }
 
@@ -164,7 +166,7 @@ int gemm_fprop_splitk(const uint8_t* qx, const float* sx, const uint8_t* qw, con
                            {sw, 4 * (N * K / (128 * 128))}},
                           {{y, 2 * M * N}, {workspace, ws}}))
     return st;
-  if (!gemm_fits(M, N, K)) return JETFP8_EUNSUPPORTED;
+  if (!gemm_fits(N, K)) return JETFP8_EUNSUPPORTED;
   return launched(jetfp8::launch_gemm_fprop_splitk(qx, sx, qw, sw, M, N, K, y, workspace, as_stream(stream)));
 }
 
@@ -177,7 +179,7 @@ int gemm_fprop_splitk_noalloc(const uint8_t* qx, const float* sx, const uint8_t*
                            {sw, 4 * (N * K / (128 * 128))}},
                           {{y, 2 * M * N}}))
     return st;
-  if (!gemm_fits(M, N, K) || ws > jetfp8::fprop_noalloc_scratch_bytes()) return JETFP8_EUNSUPPORTED;
+  if (!gemm_fits(N, K) || ws > jetfp8::fprop_noalloc_scratch_bytes()) return JETFP8_EUNSUPPORTED;
   return launched(jetfp8::launch_gemm_fprop_splitk_noalloc(qx, sx, qw, sw, M, N, K, y, as_stream(stream)));
 }
 
@@ -210,7 +212,7 @@ int gemm_fprop_swiglu_quant(const uint8_t* qx, const float* sx, const uint8_t* q
                           {{qh, nh}, {sh, 4 * (nh / 128)}}))
     return st;
   const int64_t lim = int64_t(1) << 31;
-  if ((M + 256) * K >= lim || N * K >= lim || (M + 256) * (N / 2) >= lim) return JETFP8_EUNSUPPORTED;
+  if (N * K >= lim || 512 * K >= lim || 512 * (N / 2) >= lim) return JETFP8_EUNSUPPORTED;
   return launched(jetfp8::launch_gemm_fprop_swiglu_quant(qx, sx, qw, sw, M, N, K, qh, sh, as_stream(stream)));
 }
 
@@ -222,7 +224,7 @@ int gemm_fprop_quant(const uint8_t* qx, const float* sx, const uint8_t* qw, cons
                            {sw, 4 * (N * K / (128 * 128))}},
                           {{y, 2 * M * N}, {qy, M * N}, {sy, 4 * (M * N / 128)}}))
     return st;
-  if (!gemm_fits(M, N, K)) return JETFP8_EUNSUPPORTED;
+  if (!gemm_fits(N, K)) return JETFP8_EUNSUPPORTED;
   // FProp, then the 1x128 quantiser on y, back to back on the stream.  (Doing the
   // quantisation in the 256 x 256 kernel's epilogue was measured slower: there it
   // runs after the main loop at two waves per SIMD with nothing to overlap, while
@@ -239,7 +241,7 @@ int gemm_dgrad(const uint8_t* qdy, const float* sdy, const uint8_t* qw, const fl
                            {sw, 4 * (N * K / (128 * 128))}},
                           {{dx, 2 * M * K}}))
     return st;
-  if (!gemm_fits(M, K, N)) return JETFP8_EUNSUPPORTED;
+  if (!gemm_fits(K, N)) return JETFP8_EUNSUPPORTED;
   return launched(jetfp8::launch_gemm_dgrad(qdy, sdy, qw, sw, M, N, K, dx, as_stream(stream)));
 }
 
@@ -251,7 +253,7 @@ int gemm_wgrad(const uint8_t* qdyt, const float* sdyt, const uint8_t* qxt, const
                            {sxt, 4 * (K * M / 128)}},
                           {{dw, 2 * N * K}}))
     return st;
-  if (!gemm_fits(N, K, M)) return JETFP8_EUNSUPPORTED;
+  if (!gemm_fits(K, M)) return JETFP8_EUNSUPPORTED;
   return launched(jetfp8::launch_gemm_wgrad(qdyt, sdyt, qxt, sxt, M, N, K, dw, as_stream(stream)));
 }
 
@@ -263,7 +265,7 @@ int gemm_wgrad_f32(const uint8_t* qdyt, const float* sdyt, const uint8_t* qxt, c
                            {sxt, 4 * (K * M / 128)}},
                           {{dw, 4 * N * K}}))
     return st;
-  if (!gemm_fits(N, K, M, 4)) return JETFP8_EUNSUPPORTED;
+  if (!gemm_fits(K, M, 4)) return JETFP8_EUNSUPPORTED;
   return launched(jetfp8::launch_gemm_wgrad_f32(qdyt, sdyt, qxt, sxt, M, N, K, dw, accumulate != 0,
                                                 as_stream(stream)));
 }

@@ -195,7 +195,7 @@ struct LStage {
 template <int kMode, bool kSwiglu = false>
 struct LargeTile {
   int t, l, w, wm, wn, lr, lk;
-  uint32_t M, N, K, row0, col0, nkb, t8, arow;
+  uint32_t M, N, K, lds, row0, col0, nkb, t8, arow;  // lds: row stride of the A scales
   // kSwiglu (FProp fused with SwiGLU): the tile's output columns are the
   // h-columns col0 .. col0 + 127 (tile columns step by 128), and B row r of
   // the stage is weight row col0 + r (gate) for r < 128, col0 + bskip + r (up,
@@ -278,10 +278,10 @@ struct LargeTile {
   // formed in store_scale, after the block's MFMAs, so that the loads' latency
   // is never waited for up front.
   __device__ __forceinline__ float2 load_scale(uint32_t kb) const {
-    if (kMode == kWgrad) return make_float2(b_half ? sb[kb * N + col0 + t8] : sa[kb * M + arow], 1.0f);
+    if (kMode == kWgrad) return make_float2(b_half ? sb[kb * N + col0 + t8] : sa[kb * lds + arow], 1.0f);
     const uint32_t cb = kSwiglu ? (col0 + (t >= 256 ? 128u + bskip : 0u)) / kBN : col0 / kBN + ((uint32_t)t >> 8);
     const uint32_t bi = (kMode == kFprop) ? cb * nkb + kb : kb * (N / kBN) + cb;
-    return make_float2(sa[kb * M + arow], sb[bi]);
+    return make_float2(sa[kb * lds + arow], sb[bi]);
   }
   __device__ __forceinline__ void store_scale(LStage& st, float2 x) const {
     const uint32_t tr = (t8 & 15u) * (uint32_t)kLScPitch + (t8 >> 4);
@@ -456,7 +456,7 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
                                                                     const uint8_t* __restrict__ B,
                                                                     const float* __restrict__ sb,
                                                                     uint32_t M, uint32_t N, uint32_t K,
-                                                                    void* __restrict__ Cv,
+                                                                    uint32_t lds, void* __restrict__ Cv,
                                                                     float* __restrict__ Sv) {
   static_assert(kOut != kOutSwiglu || kMode == kFprop, "the SwiGLU epilogue follows FProp");
   __shared__ __attribute__((aligned(16))) LStage st0;
@@ -471,7 +471,7 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
   g.wn = g.w & 3;                                   //            cols wn*64 .. +64
   g.lr = g.l & 15;
   g.lk = g.l >> 4;
-  g.M = M; g.N = N; g.K = K;
+  g.M = M; g.N = N; g.K = K; g.lds = lds;
   g.sa = sa; g.sb = sb;
   g.setup_offsets();
   g.nkb = K / kBK;
@@ -615,7 +615,7 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
         __builtin_amdgcn_raw_buffer_store_b128(v4i_t{(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y}, rq, qoff, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(v4i_t{(int)c2.x, (int)c2.y, (int)c3.x, (int)c3.y}, rq, qoff + 16, 0,
                                                0);
-        if (eq == 0 && grow < M) Sv[(col0 / kGroup) * M + grow] = sc;
+        if (eq == 0 && grow < M) Sv[(col0 / kGroup) * lds + grow] = sc;
         __syncthreads();
       }
     } else if constexpr (kOut != kOutBf16) {
@@ -708,7 +708,7 @@ struct MedTile {
   // nkb K-blocks starting at block kb0 (a K-split share; kb0 = 0 and
   // nkb = nkbt, all K / 128 blocks, otherwise); the block arguments below are
   // relative to kb0
-  uint32_t M, N, K, row0, col0, nkb, nkbt, kb0, arow;
+  uint32_t M, N, K, lds, row0, col0, nkb, nkbt, kb0, arow;  // lds: row stride of the A scales
   rsrc_t ra, rb;
   uint32_t va[4], vb[4];
   const float* sa;
@@ -756,10 +756,10 @@ struct MedTile {
   // formed in store_scale, after the block's MFMAs.
   __device__ __forceinline__ float2 load_scale(uint32_t kb) const {
     kb += kb0;
-    if (kMode == kWgrad) return make_float2(t >= kMBM ? sb[kb * N + col0 + (t - kMBM)] : sa[kb * M + arow], 1.0f);
+    if (kMode == kWgrad) return make_float2(t >= kMBM ? sb[kb * N + col0 + (t - kMBM)] : sa[kb * lds + arow], 1.0f);
     const uint32_t cb = col0 / kBN;
     const uint32_t bi = (kMode == kFprop) ? cb * nkbt + kb : kb * (N / kBN) + cb;
-    return make_float2(sa[kb * M + arow], sb[bi]);
+    return make_float2(sa[kb * lds + arow], sb[bi]);
   }
   __device__ __forceinline__ void store_scale(MStage& st, float2 x) const {
     if (t < kMBM) st.sc[0][(t & 15) * kMScPitch + (t >> 4)] = (kMode == kWgrad) ? x.x : x.x * x.y;
@@ -849,7 +849,7 @@ struct MedStages {
 template <int kMode, int kOut = kOutBf16, int kSt = 2>
 __global__ __launch_bounds__(kMThreads, MedStages<kSt>::kMinBlocks) void gemm_fp8_med_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ B,
-    const float* __restrict__ sb, uint32_t M, uint32_t N, uint32_t K, void* __restrict__ Cv) {
+    const float* __restrict__ sb, uint32_t M, uint32_t N, uint32_t K, uint32_t lds, void* __restrict__ Cv) {
   static_assert(kSt == 2 || kSt == 4, "two or four operand stages");
   // separate LDS objects, named statically below (see LStage); st2 and st3
   // exist only with four stages
@@ -867,7 +867,7 @@ __global__ __launch_bounds__(kMThreads, MedStages<kSt>::kMinBlocks) void gemm_fp
   g.wn = g.w & 1;
   g.lr = g.l & 15;
   g.lk = g.l >> 4;
-  g.M = M; g.N = N; g.K = K;
+  g.M = M; g.N = N; g.K = K; g.lds = lds;
   g.sa = sa; g.sb = sb;
   g.setup_offsets();
 
@@ -1574,21 +1574,18 @@ template <bool kPk>
 static bool launch_fprop_ws(int64_t M, int64_t N, int64_t K, const uint8_t* A, const float* sa, const uint8_t* B,
                             const float* sb, uint16_t* C, hipStream_t stream);
 
-template <int kMode, int kOut = kOutBf16>
-static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
-                              int64_t Mr, int64_t Nc, int64_t Kc, void* Cv,
-                              hipStream_t stream) {
-  if (Mr == 0 || Nc == 0) return hipSuccess;
-  // an empty contraction: the product is zero (nothing to add for kOutF32Add)
-  if (Kc == 0) {
-    if (kOut == kOutF32Add) return hipSuccess;
-    return launch_zero(static_cast<uint16_t*>(Cv), Mr * Nc * (kOut == kOutF32 ? 2 : 1), stream);
-  }
+// Rows Mr of A (rows of Kc bytes), their scales sa[kb * lds + row] (lds: the
+// row count of the whole scale tensor, of which this launch may cover a row
+// range), B and the output C [Mr][Nc]; every operand and the output within
+// 32-bit byte offsets (launch_gemm splits larger problems into such ranges).
+template <int kMode, int kOut>
+static hipError_t launch_gemm_rows(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
+                                   int64_t Mr, int64_t Nc, int64_t Kc, int64_t lds, void* Cv, hipStream_t stream) {
   uint16_t* C = static_cast<uint16_t*>(Cv);
   // rollout batches (FProp, up to 256 tokens): the weight-sharing kernel where
   // launch_fprop_ws chooses it, else the weight-streaming decode kernel (up to
   // 64 tokens)
-  if (kMode == kFprop && kOut == kOutBf16 && Mr <= 256 && Nc * Kc < (int64_t(1) << 31) &&
+  if (kMode == kFprop && kOut == kOutBf16 && Mr <= 256 && lds == Mr && Nc * Kc < (int64_t(1) << 31) &&
       Mr * Kc < (int64_t(1) << 31)) {
     if (launch_fprop_ws<false>(Mr, Nc, Kc, A, sa, B, sb, C, stream)) return hipGetLastError();
     if (Mr <= 64) {
@@ -1612,7 +1609,7 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
       if (cus >= 8 && cus < grid) grid = cus;
     }
     hipLaunchKernelGGL((gemm_fp8_large_kernel<kMode, kOut>), dim3((unsigned)grid), dim3(kLThreads), 0, stream,
-                       A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, Cv, (float*)nullptr);
+                       A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, (uint32_t)lds, Cv, (float*)nullptr);
     return hipGetLastError();
   }
   // the medium-tile kernel (the caller guarantees 32-bit byte offsets): four
@@ -1624,11 +1621,56 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
   const int64_t tiles = ((Mr + kMBM - 1) / kMBM) * (Nc / kMBN);
   if (tiles <= (int64_t)device_cu_count())
     hipLaunchKernelGGL((gemm_fp8_med_kernel<kMode, kOut, 4>), dim3((unsigned)tiles), dim3(kMThreads), 0, stream,
-                       A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, Cv);
+                       A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, (uint32_t)lds, Cv);
   else
     hipLaunchKernelGGL((gemm_fp8_med_kernel<kMode, kOut, 2>), dim3((unsigned)tiles), dim3(kMThreads), 0, stream,
-                       A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, Cv);
+                       A, sa, B, sb, (uint32_t)Mr, (uint32_t)Nc, (uint32_t)Kc, (uint32_t)lds, Cv);
   return hipGetLastError();
+}
+
+// Row ranges of an Mr-row problem whose A rows (rb bytes each) and output rows
+// (ob bytes each) must stay below 2^31 bytes per launch, with one 256-row tile
+// of ragged rows: nearly equal ranges of a multiple of 256 rows (each above
+// 256 rows whenever the problem is split, so all take the tile kernels).
+struct RowChunks {
+  int64_t chunk, count;
+};
+static RowChunks row_chunks(int64_t Mr, int64_t rb, int64_t ob) {
+  const int64_t lim = int64_t(1) << 31;
+  int64_t cap = (lim - 1) / (rb > ob ? rb : ob) - kLBM;
+  cap -= cap % kLBM;
+  if (Mr <= cap) return {Mr, 1};
+  const int64_t n = (Mr + cap - 1) / cap;
+  int64_t chunk = (Mr + n - 1) / n;
+  chunk = (chunk + kLBM - 1) / kLBM * kLBM;
+  if (chunk > cap) chunk = cap;
+  return {chunk, (Mr + chunk - 1) / chunk};
+}
+
+// C [Mr][Nc] = the block-scaled product of A [Mr][Kc] and B: beyond 32-bit
+// byte offsets, one launch per row range (rows are independent, and every
+// range runs a kernel with the sequential K fold, so the result is the one a
+// single launch would give).  The caller guarantees that B, and a range of
+// 512 rows of A and of C, fit 32-bit offsets.
+template <int kMode, int kOut = kOutBf16>
+static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
+                              int64_t Mr, int64_t Nc, int64_t Kc, void* Cv,
+                              hipStream_t stream) {
+  if (Mr == 0 || Nc == 0) return hipSuccess;
+  // an empty contraction: the product is zero (nothing to add for kOutF32Add)
+  if (Kc == 0) {
+    if (kOut == kOutF32Add) return hipSuccess;
+    return launch_zero(static_cast<uint16_t*>(Cv), Mr * Nc * (kOut == kOutF32 ? 2 : 1), stream);
+  }
+  const int64_t ob = kOut == kOutBf16 ? 2 : 4;
+  const RowChunks rc = row_chunks(Mr, Kc, Nc * ob);
+  for (int64_t i = 0; i < rc.count; ++i) {
+    const int64_t m0 = i * rc.chunk, mc = (Mr - m0 < rc.chunk) ? Mr - m0 : rc.chunk;
+    const hipError_t e = launch_gemm_rows<kMode, kOut>(A + m0 * Kc, sa + m0, B, sb, mc, Nc, Kc, Mr,
+                                                       static_cast<char*>(Cv) + m0 * Nc * ob, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // K == 0: the gate+up output is zero, so h = silu(0) * 0 = 0: codes 0, scales 1
@@ -1651,17 +1693,25 @@ hipError_t launch_gemm_fprop_swiglu_quant(const uint8_t* qx, const float* sx, co
     return hipGetLastError();
   }
   // 256 x 256 tiles of (rows, gate block + up block); one workgroup per CU
-  // looping over the tiles when the block count is even, as FProp
-  const int64_t nkb = K / kBK;
-  const int64_t tiles = ((M + kLBM - 1) / kLBM) * (N / kLBN);
-  int64_t grid = tiles;
-  if (nkb % 2 == 0) {
-    const int64_t cus = device_cu_count() & ~7;
-    if (cus >= 8 && cus < grid) grid = cus;
+  // looping over the tiles when the block count is even, as FProp; one launch
+  // per row range beyond 32-bit offsets (as launch_gemm)
+  const int64_t nkb = K / kBK, I = N / 2;
+  const RowChunks rc = row_chunks(M, K, I);
+  for (int64_t i = 0; i < rc.count; ++i) {
+    const int64_t m0 = i * rc.chunk, mc = (M - m0 < rc.chunk) ? M - m0 : rc.chunk;
+    const int64_t tiles = ((mc + kLBM - 1) / kLBM) * (N / kLBN);
+    int64_t grid = tiles;
+    if (nkb % 2 == 0) {
+      const int64_t cus = device_cu_count() & ~7;
+      if (cus >= 8 && cus < grid) grid = cus;
+    }
+    hipLaunchKernelGGL((gemm_fp8_large_kernel<kFprop, kOutSwiglu>), dim3((unsigned)grid), dim3(kLThreads), 0,
+                       stream, qx + m0 * K, sx + m0, qw, sw, (uint32_t)mc, (uint32_t)N, (uint32_t)K, (uint32_t)M,
+                       (void*)(q + m0 * I), s + m0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((gemm_fp8_large_kernel<kFprop, kOutSwiglu>), dim3((unsigned)grid), dim3(kLThreads), 0, stream,
-                     qx, sx, qw, sw, (uint32_t)M, (uint32_t)N, (uint32_t)K, (void*)q, s);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t launch_gemm_fprop(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw,
@@ -1761,10 +1811,10 @@ hipError_t launch_gemm_fprop_splitk(const uint8_t* qx, const float* sx, const ui
   const dim3 grid((unsigned)tiles, (unsigned)s);
   if (tiles * s <= kSplitTargetCUs)
     hipLaunchKernelGGL((gemm_fp8_med_kernel<kFprop, kOutF32, 4>), grid, dim3(kMThreads), 0, stream, qx, sx, qw,
-                       sw, (uint32_t)M, (uint32_t)N, (uint32_t)K, (void*)ws);
+                       sw, (uint32_t)M, (uint32_t)N, (uint32_t)K, (uint32_t)M, (void*)ws);
   else
     hipLaunchKernelGGL((gemm_fp8_med_kernel<kFprop, kOutF32, 2>), grid, dim3(kMThreads), 0, stream, qx, sx, qw,
-                       sw, (uint32_t)M, (uint32_t)N, (uint32_t)K, (void*)ws);
+                       sw, (uint32_t)M, (uint32_t)N, (uint32_t)K, (uint32_t)M, (void*)ws);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = M * N;  // a multiple of 128

@@ -92,13 +92,23 @@ def test_requant_validation(jetlib):
 
 
 def test_gemm_size_limit(jetlib):
+    """Row operands and outputs of any size run as row ranges (tested on the GPU);
+    what stays unsupported is a column operand of 2^31 bytes or more, or 512 rows
+    of the row operand or of the output reaching 2^31 bytes."""
     EUNSUP = 5
     Q = [(i + 1) << 40 for i in range(8)]  # fake addresses far enough apart for 4 GiB tensors
-    # 2^20 tokens x 4096: a 4 GiB operand, beyond the kernels' 32-bit offsets
-    assert c("gemm_fprop", Q[0], Q[1], Q[2], Q[3], 1 << 20, 128, 4096, Q[4], 0) == EUNSUP
-    assert c("gemm_dgrad", Q[0], Q[1], Q[2], Q[3], 1 << 20, 4096, 128, Q[4], 0) == EUNSUP
+    # the weight [N][K] at 2^31 bytes
+    assert c("gemm_fprop", Q[0], Q[1], Q[2], Q[3], 16, 1 << 16, 1 << 15, Q[4], 0) == EUNSUP
+    assert c("gemm_dgrad", Q[0], Q[1], Q[2], Q[3], 16, 1 << 16, 1 << 15, Q[4], 0) == EUNSUP
+    assert c("gemm_fprop_quant", Q[0], Q[1], Q[2], Q[3], 16, 1 << 16, 1 << 15, Q[4], Q[5], Q[6], 0) == EUNSUP
+    assert c("gemm_fprop_swiglu_quant", Q[0], Q[1], Q[2], Q[3], 16, 1 << 16, 1 << 15, Q[4], Q[5], 0) == EUNSUP
+    # WGrad's column operand X^T [K][M]: 2^20 tokens x 4096 features = 4 GiB
     assert c("gemm_wgrad", Q[0], Q[1], Q[2], Q[3], 1 << 20, 128, 4096, Q[4], 0) == EUNSUP
-    assert c("gemm_fprop_quant", Q[0], Q[1], Q[2], Q[3], 1 << 20, 128, 4096, Q[4], Q[5], Q[6], 0) == EUNSUP
+    assert c("gemm_wgrad_f32", Q[0], Q[1], Q[2], Q[3], 1 << 20, 128, 4096, Q[4], 0, 0) == EUNSUP
+    # 512 output rows of 2^21 bf16 columns reach 2^31 bytes (the weight itself fits)
+    assert c("gemm_fprop", Q[0], Q[1], Q[2], Q[3], 16, 1 << 21, 128, Q[4], 0) == EUNSUP
+    # a 2^22-byte contraction: 512 rows of the row operand reach 2^31 bytes
+    assert c("gemm_dgrad", Q[0], Q[1], Q[2], Q[3], 16, 1 << 22, 128, Q[4], 0) == EUNSUP
 
 
 def test_gemm_fprop_quant_validation(jetlib):
@@ -138,9 +148,9 @@ def test_gemm_wgrad_f32_validation(jetlib):
     assert c(f, P[0], P[1], P[2], P[3], 128, 128, 128, P[4] + 8, 1, 0) == EALIGN
     assert c(f, P[0], P[1], P[2], P[3], 128, 128, 128, P[3] - 16, 0, 0) == EALIAS  # dw runs into sxt
     assert c(f, P[0], P[1], P[2], P[3], 128, 0, 128, 0, 1, 0) == OK  # N = 0: empty output
-    # 4-byte output elements: dW [2^17, 4096] fp32 is 2 GiB (its bf16 form would fit)
+    # 4-byte output elements: 512 rows of dW [128, 2^20] fp32 reach 2^31 bytes (in bf16 they would not)
     Q = [(i + 1) << 40 for i in range(8)]
-    assert c(f, Q[0], Q[1], Q[2], Q[3], 128, 1 << 17, 4096, Q[4], 0, 0) == 5
+    assert c(f, Q[0], Q[1], Q[2], Q[3], 128, 128, 1 << 20, Q[4], 0, 0) == 5
 
 
 def test_rmsnorm_rstd_and_backward_validation(jetlib):
@@ -236,7 +246,7 @@ def test_fprop_swiglu_quant_validation(jetlib):
     assert c(n, P[0], P[1], P[2], P[3], 256, 512, 256, P[4], P[5] + 4, 0) == EALIGN
     assert c(n, P[0], P[1], P[2], P[3], 256, 512, 256, P[4], P[4] + 1024, 0) == EALIAS  # sh inside qh
     B = [(i + 1) << 40 for i in range(6)]  # far apart: no overlap even for huge shapes
-    assert c(n, B[0], B[1], B[2], B[3], 1 << 20, 512, 4096, B[4], B[5], 0) == 5   # past 32-bit offsets
+    assert c(n, B[0], B[1], B[2], B[3], 16, 1 << 16, 1 << 15, B[4], B[5], 0) == 5  # the weight at 2^31 bytes
     assert c(n, 0, 0, P[2], P[3], 0, 512, 256, 0, 0, 0) == OK
 
 

@@ -316,8 +316,8 @@ int gemm_fprop_packed(const uint8_t* qx, const float* sx, const uint8_t* qwp, co
  *   qh : u8 [M][I], sh : f32 [I/128][M] outputs.
  * N % 256 == 0 (I % 128 == 0), K % 128 == 0, M >= 0.  K == 0 gives h = 0
  * (codes 0, scales 1).  Runs the 256 x 256 tile kernel at every size: for
- * rollout batches (M of a few hundred or less) gemm_fprop_splitk followed by
- * swiglu_quant is faster.
+ * rollout batches (M of a few hundred or less) gemm_fprop or gemm_fprop_packed
+ * followed by swiglu_quant is faster (same bits).
  */
 int gemm_fprop_swiglu_quant(const uint8_t* qx, const float* sx, const uint8_t* qw, const float* sw, int64_t M,
                             int64_t N, int64_t K, uint8_t* qh, float* sh, void* stream);

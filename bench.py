@@ -30,7 +30,10 @@ FProps go through gemm_fprop_packed; larger batches (or ``--decode-rowmajor``)
 use the row-major codes and gemm_fprop_splitk, which splits K across
 workgroups for the shapes with fewer output tiles than CUs (its workspace is
 allocated before the timed region).  Decode is bound by streaming
-the FP8 weights, so its kernels also report weight GB/s.
+the FP8 weights, so its kernels also report weight GB/s.  Beside it the bench
+times the same step in BF16 through torch (``bf16_reference``: hipBLASLt GEMMs
+over bf16 weights rotated the same way), the FP8-against-BF16 rollout
+comparison of the pages, unless ``--no-bf16-reference``.
 
 ``--workload llama_layer`` times the forward + backward of the four linears
 of one Llama-3.1-8B layer (QKV, O, gate+up, down) at M = 16384 tokens, and
@@ -47,7 +50,7 @@ with swiglu_quant as a separate kernel and with the SwiGLU unfused.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--workload linear_8b_up|decode_8b|llama_layer|qwen32b_half_mlp|llama_mlp]
-                       [--decode-m M] [--decode-rowmajor]
+                       [--decode-m M] [--decode-rowmajor] [--no-bf16-reference]
 """
 
 import argparse
@@ -84,6 +87,8 @@ def parse():
     ap.add_argument("--decode-m", type=int, default=16)
     ap.add_argument("--decode-rowmajor", action="store_true",
                     help="decode_8b: row-major weights and gemm_fprop_splitk at every batch size")
+    ap.add_argument("--no-bf16-reference", action="store_true",
+                    help="decode_8b: skip timing the same step in BF16 through torch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (torch copy_), whose HBM counters "
                          "calibrate FETCH_SIZE / WRITE_SIZE")
@@ -338,6 +343,9 @@ def bench_decode(args):
     ]
     per, step_ms, wall, n_settle = time_steps(torch, steps, args.steps, args.warmup, dev)
     ms_per_step = float(np.mean(step_ms))
+    ref = None if args.no_bf16_reference else decode_bf16_reference(torch, d, bf16, args)
+    if ref is not None:
+        ref["speedup_fp8_over_bf16"] = round(ref["ms_per_step"] / ms_per_step, 3)
     shapes = {"gemm_fprop_qkv": (6144, 4096), "gemm_fprop_gate_up": (24576, 4096), "gemm_fprop_down": (4096, 12288)}
     flops = sum(2.0 * m * n * k for n, k in shapes.values())
     kernels = {}
@@ -369,7 +377,52 @@ def bench_decode(args):
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         "settle": settle_info(n_settle),
     }
+    if ref is not None:
+        out["bf16_reference"] = ref
     print(json.dumps(out), flush=True)
+
+
+def decode_bf16_reference(torch, d, bf16, args):
+    """The decode step in BF16 through torch, timed like the FP8 step: RMSNorm in fp32
+    arithmetic rounded to bf16, the three projections as bf16 GEMMs (torch.matmul:
+    hipBLASLt) against weights stored transposed and contiguous, SwiGLU in fp32
+    rounded to bf16; the weights rotate over the same number of copies, so each
+    step streams them from HBM.  The rollout comparison the pages report (FP8
+    against BF16 rollout) on this GPU; a reference only, none of it is the FP8 path."""
+    m = args.decode_m
+    x, gamma = bf16(d["x"]), bf16(d["gamma"]).float()
+    eps = d["eps"]
+    w0 = {k: bf16(d[k]).t().contiguous() for k in ("w_qkv", "w_gu", "w_down")}  # [K, N]
+    sets = [w0] + [{k: v.clone() for k, v in w0.items()} for _ in range(DECODE_WEIGHT_SETS - 1)]
+    inter = w0["w_down"].shape[0]
+    h = torch.empty_like(x)
+    cur = [0]
+    out = {}
+
+    def norm():
+        cur[0] = (cur[0] + 1) % len(sets)
+        xf = x.float()
+        h.copy_(xf * torch.rsqrt(xf.pow(2).mean(-1, keepdim=True) + eps) * gamma)
+
+    def qkv():
+        out["qkv"] = torch.matmul(h, sets[cur[0]]["w_qkv"])
+
+    def gate_up():
+        out["gu"] = torch.matmul(h, sets[cur[0]]["w_gu"])
+
+    def swiglu():
+        gu = out["gu"].float()
+        out["a"] = (torch.nn.functional.silu(gu[:, :inter]) * gu[:, inter:]).to(torch.bfloat16)
+
+    def down():
+        out["y"] = torch.matmul(out["a"], sets[cur[0]]["w_down"])
+
+    steps = [("rmsnorm", norm), ("matmul_qkv", qkv), ("matmul_gate_up", gate_up), ("swiglu", swiglu),
+             ("matmul_down", down)]
+    per, step_ms, _, _ = time_steps(torch, steps, args.steps, args.warmup, torch.device("cuda:0"))
+    return {"what": "the same decode step in BF16 through torch (hipBLASLt GEMMs, fp32 RMSNorm and SwiGLU)",
+            "ms_per_step": round(float(np.mean(step_ms)), 4),
+            "kernels_us": {k: round(float(np.mean(v)) * 1e3, 2) for k, v in per.items()}}
 
 
 def bench_mlp(args):

@@ -1224,8 +1224,9 @@ __global__ __launch_bounds__(64 * kW) void gemm_fp8_decode_kernel(
 // whose 16-byte chunks land at the large kernel's swizzled positions (chunk c
 // of row r at c ^ f(r)), so that whole cache lines are fetched and the
 // fragment reads are conflict-free 16-byte LDS reads.  kD stages hold the
-// next kD K-blocks; the K-block steps are software-pipelined (see below).  The
-// weight-block scales of the workgroup's (at most two) 128-column blocks are
+// next kD K-blocks; a block's fragments are read into registers while the
+// block before it computes, and its steps are software-pipelined (see below).
+// The weight-block scales of the workgroup's (at most two) 128-column blocks are
 // copied to LDS once.  The grid walks (strip group, token group) pairs with
 // the token groups of a strip group adjacent on one XCD, so a weight chunk
 // read from HBM by one of them is found in that XCD's L2 by the others.  The
@@ -1343,33 +1344,37 @@ __global__ __launch_bounds__(64 * kNW, kOcc) void gemm_fp8_decode_ws_kernel(
   };
   auto clampb = [&](uint32_t kb) { return kb < last ? kb : last; };  // past the end: a valid block, not folded
 
-  // What a block's steps need first, read from its stage right after the
-  // barrier that publishes it: the wave's X fragments, their sx factors (0 for a
-  // block past the end: it then leaves acc unchanged bit for bit, as acc is
-  // never -0; multiplying by 1 changes no scale), the block's weight-block
-  // scales and the first strip's weight fragment.
-  struct Head {
+  // Every fragment a block's steps use, read from its stage into registers
+  // one block ahead: the wave's X fragments, their sx factors (0 for a block
+  // past the end: it then leaves acc unchanged bit for bit, as acc is never
+  // -0; multiplying by 1 changes no scale), the block's weight-block scales and
+  // the weight fragments of all kS strips.
+  struct Frags {
     v8i_t xf[kR];
     float sxv[kR];
     float sw0, sw1;
-    v8i_t wf;
+    v8i_t wf[kS];
   };
   auto frag = [&](const uint8_t* p0, const uint8_t* p1) {
     const uint4 lo = *reinterpret_cast<const uint4*>(p0);
     const uint4 hi = *reinterpret_cast<const uint4*>(p1);
     return v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
-  auto read_head = [&](const uint8_t* st, uint32_t kb, Head& h) {
+  auto read_frags = [&](const uint8_t* st, uint32_t kb, Frags& f) {
     const float live = kb < nkb ? 1.0f : 0.0f;
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
-      h.xf[i] = frag(st + x_lds + 2048 * i + xr0, st + x_lds + 2048 * i + xr1);
-      h.sxv[i] = reinterpret_cast<const float*>(st + sx_lds)[16 * i + lr] * live;
+      f.xf[i] = frag(st + x_lds + 2048 * i + xr0, st + x_lds + 2048 * i + xr1);
+      f.sxv[i] = reinterpret_cast<const float*>(st + sx_lds)[16 * i + lr] * live;
     }
     const uint32_t kc = clampb(kb);
-    h.sw0 = swl[kc];
-    h.sw1 = swl[(nb - 1u) * nkb + kc];
-    h.wf = kPk ? frag(st + 16 * l, st + 1024 + 16 * l) : frag(st + xr0, st + xr1);
+    f.sw0 = swl[kc];
+    f.sw1 = swl[(nb - 1u) * nkb + kc];
+#pragma unroll
+    for (int s = 0; s < kS; ++s) {
+      const uint8_t* sp = st + 2048 * s;
+      f.wf[s] = kPk ? frag(sp + 16 * l, sp + 1024 + 16 * l) : frag(sp + xr0, sp + xr1);
+    }
   };
 
   // prologue: every stage filled (block j into stage j), block 0 published
@@ -1379,23 +1384,25 @@ __global__ __launch_bounds__(64 * kNW, kOcc) void gemm_fp8_decode_ws_kernel(
   });
   wait_vmem_le<(kD - 1) * C::kG>();
   lds_barrier();
-  Head head;
-  read_head(ws0, 0, head);
+  Frags nxt;
+  read_frags(ws0, 0, nxt);
 
   v4f_t acc[kR][kS];
 #pragma unroll
   for (int i = 0; i < kR; ++i)
 #pragma unroll
     for (int s = 0; s < kS; ++s) acc[i][s] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
-  // Steps q = kR s + i of a block (strip s, token sub-tile i): step q issues
-  // the MFMA of q and rescales the partial of q - 2 into acc, so two MFMAs
-  // separate every partial from its use; strip s + 1's weight fragment is read
-  // at the first step of strip s.  After the block's last MFMA (its last LDS
-  // read is done by then) the wave waits for its loads of the next block, the
-  // barrier publishes that block and frees this stage, which is refilled at
-  // once with block kb + kD, and the next block's head is read while the last
-  // two partials are rescaled.  Scheduling barriers pin the order.
+  // Steps q = kR s + i of a block (strip s, token sub-tile i) run from
+  // registers: step q issues the MFMA of q and rescales the partial of q - 2
+  // into acc, so two MFMAs separate every partial from its use.  At the block's
+  // second step (at its only one when it has one MFMA) the wave waits for its
+  // loads of the next block; the barrier publishes that block and, since every
+  // wave's reads of this block's stage completed before it (the barrier waits
+  // for the wave's LDS reads), frees this stage, which is refilled at once with
+  // block kb + kD; then the next block's fragments are read into registers
+  // while this block's remaining MFMAs run.  Scheduling barriers pin the order.
   constexpr int kQ = kR * kS;
+  constexpr int kB = kQ >= 2 ? 1 : 0;  // the step that holds the barrier
   uint32_t c0 = 0;
 #pragma clang loop unroll(disable)
   do {
@@ -1403,29 +1410,21 @@ __global__ __launch_bounds__(64 * kNW, kOcc) void gemm_fp8_decode_ws_kernel(
       constexpr int j = decltype(c)::value;
       const uint32_t kb = c0 + j;
       uint8_t* st = stage(c);
-      const Head cur = head;
+      const Frags cur = nxt;
       float swv[kS];
 #pragma unroll
       for (int s = 0; s < kS; ++s) swv[s] = sub + (uint32_t)s >= 8u ? cur.sw1 : cur.sw0;
-      v8i_t wfr[2];
-      wfr[0] = cur.wf;
       v4f_t part[3];
       static_for<kQ + 2>([&](auto qc) {
         constexpr int q = decltype(qc)::value;
         constexpr int s = q / kR, i = q % kR;
-        if constexpr (q < kQ) {
-          if constexpr (i == 0 && s + 1 < kS) {
-            const uint8_t* sp = st + 2048 * (s + 1);
-            wfr[(s + 1) & 1] = kPk ? frag(sp + 16 * l, sp + 1024 + 16 * l) : frag(sp + xr0, sp + xr1);
-          }
-          part[q % 3] = mfma_fp8(wfr[s & 1], cur.xf[i]);
-        }
-        if constexpr (q == kQ) {
+        if constexpr (q < kQ) part[q % 3] = mfma_fp8(cur.wf[s], cur.xf[i]);
+        if constexpr (q == kB) {
           // this wave's loads of block kb + 1 were issued before the kD - 2 later groups
           wait_vmem_le<(kD - 2) * C::kG>();
           lds_barrier();
           issue(st, clampb(kb + kD));
-          read_head(stage(std::integral_constant<int, (j + 1) % kD>{}), kb + 1, head);
+          read_frags(stage(std::integral_constant<int, (j + 1) % kD>{}), kb + 1, nxt);
         }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (q >= 2) {

@@ -436,12 +436,13 @@ def test_fprop_decode_two_strips_per_wave(m, k):
     assert np.array_equal(y, yb[:m]), "decode kernel vs 128 x 128 kernel"
 
 
-@pytest.mark.parametrize("m,n,k", [(2048, 8192, 256), (2125, 8192, 128), (64, 384, 512), (200, 384, 512),
+@pytest.mark.parametrize("m,n,k", [(2048, 8192, 256), (2125, 9216, 128), (64, 384, 512), (200, 384, 512),
                                    (300, 512, 256)])
 def test_fprop_quant_fused(m, n, k):
     """gemm_fprop_quant: y equals gemm_fprop's and (qy, sy) equal quantize_act_1x128(y),
     bit for bit, across the kernels FProp dispatches to (256 x 256 for the first two
-    shapes, the second with a ragged last row tile; decode, K-split, 128 x 128).  Against
+    shapes, the second with a ragged last row tile; the rollout kernels and 128 x 128
+    for the others).  Against
     the oracle: y within the GEMM tolerance, and the dequantised (qy, sy) within 1e-3
     normwise of the oracle's 1x128 quantisation of bf16(Yref)."""
     rng = np.random.default_rng(5000 + m + n + k)
@@ -466,11 +467,12 @@ def test_fprop_quant_fused(m, n, k):
 
 
 def test_dgrad_wgrad_large_kernel_ragged_rows():
-    """DGrad and WGrad on the 256 x 256 kernel (>= 256 tiles) with a ragged last row
-    tile: DGrad with M = 4100 tokens, WGrad with N = 4224 output rows (33 x 128).
-    Full outputs against the oracle, guard zones intact."""
+    """DGrad and WGrad on the 256 x 256 kernel (>= 256 tiles, a last round of more
+    than half the CUs, so it stays on that kernel) with a ragged last row tile:
+    DGrad with M = 6148 tokens, WGrad with N = 6528 output rows (51 x 128).  Full
+    outputs against the oracle, guard zones intact."""
     rng = np.random.default_rng(6000)
-    m, n, k = 4100, 256, 4096
+    m, n, k = 6148, 256, 4096
     qdy, qw = codes(rng, (m, n)), codes(rng, (n, k))
     sdy, sw = scales(rng, (n // 128, m)), scales(rng, (n // 128, k // 128))
     dxg = Guarded((m, k), torch.bfloat16)
@@ -479,7 +481,7 @@ def test_dgrad_wgrad_large_kernel_ragged_rows():
     assert dxg.intact()
     check(host(dxg.t), oracle.gemm_dgrad_ref(qdy, sdy, qw, sw), f"dgrad {m}x{n}x{k}")
 
-    m, n, k = 256, 4224, 4096
+    m, n, k = 256, 6528, 4096
     qdyt, qxt = codes(rng, (n, m)), codes(rng, (k, m))
     sdyt, sxt = scales(rng, (m // 128, n)), scales(rng, (m // 128, k))
     dwg = Guarded((n, k), torch.bfloat16)
@@ -487,6 +489,32 @@ def test_dgrad_wgrad_large_kernel_ragged_rows():
     torch.cuda.synchronize()
     assert dwg.intact()
     check(host(dwg.t), oracle.gemm_wgrad_ref(qdyt, sdyt, qxt, sxt), f"wgrad {m}x{n}x{k}")
+
+
+def test_partial_last_round_of_tiles_bitwise():
+    """384 tiles of 256 x 256 (a second round of half the CUs' tiles): the rows past
+    the first round run as a launch of their own on the 128 x 128 kernel.  They equal,
+    bit for bit, the same rows inside a launch of exactly one round (all on the
+    256 x 256 kernel), and the whole output meets the oracle's acceptance.  WGrad
+    with 6144 output rows over 256 tokens, FProp with 6144 rows, N = 4096, K = 256."""
+    rng = np.random.default_rng(6100)
+    m, n, k = 256, 6144, 4096  # WGrad: tokens, output rows, output columns
+    qdyt, qxt = codes(rng, (n, m)), codes(rng, (k, m))
+    sdyt, sxt = scales(rng, (m // 128, n)), scales(rng, (m // 128, k))
+    d_qdyt, d_sdyt, d_qxt, d_sxt = u8_dev(qdyt), f32_dev(sdyt), u8_dev(qxt), f32_dev(sxt)
+    dw = host(jet.gemm_wgrad(d_qdyt, d_sdyt, d_qxt, d_sxt))
+    dw_one_round = host(jet.gemm_wgrad(d_qdyt[2048:].contiguous(), d_sdyt[:, 2048:].contiguous(), d_qxt, d_sxt))
+    assert np.array_equal(dw[4096:], dw_one_round[2048:])
+    check(dw, oracle.gemm_wgrad_ref(qdyt, sdyt, qxt, sxt), f"wgrad {m}x{n}x{k}")
+
+    m, n, k = 6144, 4096, 256
+    qx, qw = codes(rng, (m, k)), codes(rng, (n, k))
+    sx, sw = scales(rng, (k // 128, m)), scales(rng, (n // 128, k // 128))
+    d_qx, d_sx, d_qw, d_sw = u8_dev(qx), f32_dev(sx), u8_dev(qw), f32_dev(sw)
+    y = host(jet.gemm_fprop(d_qx, d_sx, d_qw, d_sw))
+    y_one_round = host(jet.gemm_fprop(d_qx[2048:].contiguous(), d_sx[:, 2048:].contiguous(), d_qw, d_sw))
+    assert np.array_equal(y[4096:], y_one_round[2048:])
+    check(y, oracle.gemm_fprop_ref(qx, sx, qw, sw), f"fprop {m}x{n}x{k}")
 
 
 @pytest.mark.parametrize("m,n,k", [(8348, 2304, 512), (8192, 2304, 768)])

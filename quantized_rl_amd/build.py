@@ -52,10 +52,8 @@ def gen_silu_table():
     subprocess.run([cxx, "-O2", "-std=c++17", "-ffp-contract=off", "-o", exe,
                     os.path.join(CSRC, "silu_table_gen.cpp")], check=True)
     out = os.path.join(CSRC, "silu_table.inc")
-    full = os.path.join(CSRC, "silu_table_full.inc")
-    subprocess.run([exe, out + ".tmp", full + ".tmp"], check=True)
+    subprocess.run([exe, out + ".tmp"], check=True)
     os.replace(out + ".tmp", out)
-    os.replace(full + ".tmp", full)
     os.remove(exe)
     return out
 

@@ -57,6 +57,7 @@
 
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "silu_lookup.hpp"
 
 namespace jetfp8 {
 
@@ -429,16 +430,11 @@ struct LargeTile {
 // SiLU(gate) * up and written as its 1x128 FP8 quantisation (codes + scales).
 enum OutKind { kOutBf16 = 0, kOutF32 = 1, kOutF32Add = 2, kOutSwiglu = 3 };
 
-// silu of every bf16 bit pattern (256 KB, generated at build time by the same
-// program and definition as swiglu_quant's table, and compared with the oracle
-// on every finite argument by the test-suite), read from global memory (it
-// stays in L2) by the fused epilogue, where the operand stages leave no room
-// in LDS: one gather per value, indexed by the gate's bits.
-__device__ const uint32_t kSiluBitsAll[65536] __attribute__((aligned(16))) = {
-#include "silu_table_full.inc"
+// swiglu_quant's SiLU table (silu_lookup.hpp; the same generated entries),
+// which the fused epilogue copies into its staging stage once per tile.
+__device__ const uint32_t kSiluBitsEp[kSiluTable] __attribute__((aligned(16))) = {
+#include "silu_table.inc"
 };
-
-__device__ __forceinline__ float silu_of_bits_g(uint32_t b) { return __uint_as_float(kSiluBitsAll[b]); }
 
 // fp32 output straight from the accumulators: each lane's four consecutive
 // columns of a 16 x 16 sub-tile go out as one 16-byte store (a quarter-wave
@@ -548,12 +544,13 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
       // (gate in tile columns 0..127, up in 128..255), bit for bit what
       // swiglu_quant computes from gemm_fprop's bf16 output.  The accumulators
       // are first rounded to bf16 as gemm_fprop rounds them (packed, which frees
-      // the fp32 registers), then each 128-row half is staged in stage 1 and
-      // thread t takes row t / 4 of it, h-columns 32 (t % 4) .. + 31: silu from
-      // the table, h = fl32(silu * up), the group amax across the row's four
-      // threads, the scale and the codes (two 16-byte stores).  Rows past M
-      // fall outside the codes' buffer and are dropped; their scales are not
-      // written.
+      // the fp32 registers).  Stage 1 holds the SiLU table (32 KB, copied in
+      // with direct loads as the epilogue starts) and a 64-row slice of the
+      // tile at a time: thread t takes row t / 8 of it, h-columns
+      // 16 (t % 8) .. + 15: silu from the table, h = fl32(silu * up), the group
+      // amax across the row's eight threads, the scale and the codes (one
+      // 16-byte store).  Rows past M fall outside the codes' buffer and are
+      // dropped; their scales are not written.
       const uint32_t I = N / 2;
       uint32_t pk[8][4][2];
 #pragma unroll
@@ -564,59 +561,68 @@ __global__ __launch_bounds__(kLThreads) void gemm_fp8_large_kernel(const uint8_t
           pk[i][j][1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
         }
       constexpr int kPitch = kLBN * 2 + 16;
-      static_assert(128 * kPitch <= sizeof(LStage), "epilogue staging must fit one stage");
+      constexpr int kTab = 64 * kPitch;  // byte offset of the table in the stage
+      static_assert(kTab + 4 * kSiluTable <= (int)sizeof(LStage), "epilogue staging and table must fit one stage");
       const rsrc_t rq = make_rsrc(Cv, M * I);
       uint8_t* stage = reinterpret_cast<uint8_t*>(&st1);
-      const int er = g.t >> 2, eq = g.t & 3;
+      {
+        // every wave copies 4 KB of the table (four 1 KB direct loads)
+        const rsrc_t rt = make_rsrc(kSiluBitsEp, 4u * kSiluTable);
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          buf_to_lds16(rt, stage + kTab + 1024 * (4 * g.w + p), 16u * (uint32_t)g.l, 1024u * (uint32_t)(4 * g.w + p));
+      }
+      const float* tab = reinterpret_cast<const float*>(stage + kTab);
+      const int er = g.t >> 3, eo = g.t & 7;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        if (g.wm == h) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
+        for (int q = 0; q < 2; ++q) {
+          if (g.wm == h) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int r = 16 * i + g.lr, c = g.wn * 64 + 16 * j + 4 * g.lk;
-              *reinterpret_cast<uint2*>(stage + r * kPitch + 2 * c) = make_uint2(pk[i][j][0], pk[i][j][1]);
+            for (int i = 4 * q; i < 4 * q + 4; ++i) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int r = 16 * (i - 4 * q) + g.lr, c = g.wn * 64 + 16 * j + 4 * g.lk;
+                *reinterpret_cast<uint2*>(stage + r * kPitch + 2 * c) = make_uint2(pk[i][j][0], pk[i][j][1]);
+              }
+              __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
           }
-        }
-        __syncthreads();
-        const uint8_t* rowp = stage + er * kPitch + 2 * 32 * eq;
-        uint4 gv[4], uv[4];
+          if (h == 0 && q == 0) wait_vmem();  // this wave's part of the table has landed
+          __syncthreads();
+          const uint8_t* rowp = stage + er * kPitch + 2 * 16 * eo;
+          uint4 gv[2], uv[2];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          gv[c] = *reinterpret_cast<const uint4*>(rowp + 16 * c);
-          uv[c] = *reinterpret_cast<const uint4*>(rowp + 2 * 128 + 16 * c);
-        }
-        float hv[4][8];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          float u[8];
-          unpack_bf16x8(uv[c], u);
-          const uint32_t gw[4] = {gv[c].x, gv[c].y, gv[c].z, gv[c].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            hv[c][2 * e] = silu_of_bits_g(gw[e] & 0xFFFFu) * u[2 * e];
-            hv[c][2 * e + 1] = silu_of_bits_g(gw[e] >> 16) * u[2 * e + 1];
+          for (int c = 0; c < 2; ++c) {
+            gv[c] = *reinterpret_cast<const uint4*>(rowp + 16 * c);
+            uv[c] = *reinterpret_cast<const uint4*>(rowp + 2 * 128 + 16 * c);
           }
-        }
-        uint32_t am = 0;
+          float hv[2][8];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) am = max(am, __float_as_uint(absmax8(hv[c])));
-        am = max(am, dpp_u32<kXor1>(am));
-        am = max(am, dpp_u32<kXor2>(am));
-        const float sc = scale_from_amax(__uint_as_float(am));
-        const double inv = inv_scale(sc);
-        const uint2 c0 = quant8(hv[0], inv), c1 = quant8(hv[1], inv);
-        const uint2 c2 = quant8(hv[2], inv), c3 = quant8(hv[3], inv);
-        const uint32_t grow = row0 + 128 * h + er;
-        const uint32_t qoff = grow * I + col0 + 32 * eq;
-        __builtin_amdgcn_raw_buffer_store_b128(v4i_t{(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y}, rq, qoff, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(v4i_t{(int)c2.x, (int)c2.y, (int)c3.x, (int)c3.y}, rq, qoff + 16, 0,
-                                               0);
-        if (eq == 0 && grow < M) Sv[(col0 / kGroup) * lds + grow] = sc;
-        __syncthreads();
+          for (int c = 0; c < 2; ++c) {
+            float u[8];
+            unpack_bf16x8(uv[c], u);
+            const uint32_t gw[4] = {gv[c].x, gv[c].y, gv[c].z, gv[c].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              hv[c][2 * e] = silu_of_bits(gw[e] & 0xFFFFu, tab) * u[2 * e];
+              hv[c][2 * e + 1] = silu_of_bits(gw[e] >> 16, tab) * u[2 * e + 1];
+            }
+          }
+          uint32_t am = max(__float_as_uint(absmax8(hv[0])), __float_as_uint(absmax8(hv[1])));
+          am = max(am, dpp_u32<kXor1>(am));
+          am = max(am, dpp_u32<kXor2>(am));
+          am = max(am, dpp_u32<kHalfMirror>(am));
+          const float sc = scale_from_amax(__uint_as_float(am));
+          const double inv = inv_scale(sc);
+          const uint2 c0 = quant8(hv[0], inv), c1 = quant8(hv[1], inv);
+          const uint32_t grow = row0 + 128 * h + 64 * q + er;
+          const uint32_t qoff = grow * I + col0 + 16 * eo;
+          __builtin_amdgcn_raw_buffer_store_b128(v4i_t{(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y}, rq, qoff, 0, 0);
+          if (eo == 0 && grow < M) Sv[(col0 / kGroup) * lds + grow] = sc;
+          __syncthreads();
+        }
       }
     } else if constexpr (kOut != kOutBf16) {
       const rsrc_t rc = make_rsrc(Cv, M * N * 4u);

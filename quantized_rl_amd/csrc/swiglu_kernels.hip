@@ -11,13 +11,10 @@
 // gate/up layout are readings (the pages print no formula for them).
 //
 // HBM-bound: 4 bytes in, 1 + 4/128 out per output element.  silu depends only
-// on the 16 bits of the bf16 gate.  For the 8192 bf16 values with
-// 2^-25 <= |g| < 2^7 it comes from a table generated at build time by the
-// definition (silu_table_gen.cpp; the test-suite compares every entry with the
-// oracle), copied into LDS by each workgroup; outside that range silu has a
-// closed form: |g| < 2^-25 gives E = 1 and silu = g / 2 (exact), g >= 2^7 gives
-// E = 0 and silu = g, g <= -2^7 gives E = +inf and silu = -0.  No fp64
-// exponential runs in the kernel, which would make it ALU-bound.
+// on the 16 bits of the bf16 gate: it is looked up (silu_lookup.hpp) in a
+// 32 KB table that each workgroup copies into LDS, with closed forms outside
+// the table's range.  No fp64 exponential runs in the kernel, which would make
+// it ALU-bound.
 //
 // Workgroups of 256 threads, two per CU, walk tiles of 32 rows x 4 groups (512
 // outputs; 4 or 8 rows for rollout batches); a lane holds 8 consecutive outputs
@@ -26,27 +23,15 @@
 // computed and stored.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "silu_lookup.hpp"
 
 namespace jetfp8 {
 
 constexpr int kSwThreads = 256;
-constexpr uint32_t kSiluExpLo = 102, kSiluExpHi = 134;  // biased exponents of 2^-25 and 2^7
-constexpr int kSiluBinades = (int)(kSiluExpHi - kSiluExpLo);
-constexpr int kSiluTable = 2 * kSiluBinades * 128;  // 8192 entries (32 KB)
 
 __device__ const uint32_t kSiluBits[kSiluTable] __attribute__((aligned(16))) = {
 #include "silu_table.inc"
 };
-
-__device__ __forceinline__ float silu_of_bits(uint32_t b, const float* tab) {
-  const float g = __uint_as_float(b << 16);
-  const uint32_t e = (b >> 7) & 0xFFu;
-  const bool in = e - kSiluExpLo < (uint32_t)kSiluBinades;
-  const uint32_t idx = in ? (((b >> 15) & 1u) << 12) + ((e - kSiluExpLo) << 7) + (b & 0x7Fu) : 0u;
-  const float t = tab[idx];
-  const float outside = e < kSiluExpLo ? g * 0.5f : ((b & 0x8000u) ? -0.0f : g);
-  return in ? t : outside;
-}
 
 // kRows rows per tile (32 for training batches, fewer for rollout batches, so
 // that their few rows still spread over many workgroups); kIters rows per wave

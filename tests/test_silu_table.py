@@ -1,7 +1,8 @@
-"""The SiLU tables that the kernels compile in (generated at build time by
-quantized_rl_amd/csrc/silu_table_gen.cpp with the C library's exp) equal the
-oracle's silu, bit for bit: swiglu_quant's 8192-entry table on every one of its
-arguments, and the fused GEMM epilogue's full table on every finite bf16 value."""
+"""The SiLU table that the kernels compile in (generated at build time by
+quantized_rl_amd/csrc/silu_table_gen.cpp with the C library's exp; used by
+swiglu_quant and the fused gate+up FProp epilogue) equals the oracle's silu, bit
+for bit, on every one of its 8192 arguments; the closed forms outside its range
+are checked on the GPU against the oracle on every finite bf16 value."""
 
 import os
 import subprocess
@@ -17,14 +18,7 @@ GEN = os.path.join(ROOT, "quantized_rl_amd", "csrc", "silu_table_gen.cpp")
 def test_generated_silu_table_matches_the_oracle(tmp_path):
     exe, out = tmp_path / "gen", tmp_path / "silu_table.inc"
     subprocess.run(["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-o", str(exe), GEN], check=True)
-    full = tmp_path / "silu_table_full.inc"
-    subprocess.run([str(exe), str(out), str(full)], check=True)
-    tab_full = np.array([int(ln.strip().rstrip(",").rstrip("u"), 16) for ln in open(full) if ln.startswith("0x")],
-                        np.uint32)
-    assert tab_full.size == 65536
-    allg = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
-    fin = np.isfinite(allg)
-    assert np.array_equal(tab_full[fin], oracle.silu_f32(allg[fin]).view(np.uint32))
+    subprocess.run([str(exe), str(out)], check=True)
     tab = np.array([int(ln.strip().rstrip(",").rstrip("u"), 16) for ln in open(out) if ln.startswith("0x")],
                    np.uint32)
     assert tab.size == 8192

@@ -39,15 +39,19 @@
 //                                writes that weight);
 //   gemm_fp8_large_kernel<mode>  256 x 256 tiles: problems with >= 256 of them
 //                                (FProp and DGrad: one workgroup per CU looping
-//                                over the tiles);
+//                                over the tiles; a last round of at most half
+//                                the CUs' tiles goes to the 128 x 128 kernel);
+//                                FProp also with the SwiGLU + 1x128
+//                                quantisation epilogue (gemm_fprop_swiglu_quant);
 //   gemm_fp8_med_kernel<mode>    128 x 128 tiles, same machinery: everything else
 //                                (four operand stages when the tiles do not
 //                                fill the CUs, two otherwise).
 // gemm_fprop_splitk (launch_gemm_fprop_splitk) runs the 128 x 128 kernel on K
 // shares with fp32 partials in a caller workspace, then
 // splitk_reduce_bf16_kernel.
-// Byte offsets are 32-bit (buffer resources): the API rejects GEMMs whose
-// operands or output, with one tile of ragged rows, reach 2^31 bytes.
+// Byte offsets are 32-bit (buffer resources): launch_gemm runs a problem whose
+// row operand or output reaches 2^31 bytes as launches over row ranges that
+// stay below it.
 // Every kernel but the split-K FProp's folds the K-blocks of an output in
 // ascending order with the same fp32 operations, so a row's FProp output does
 // not depend on the kernel (nor on the batch it is computed in).

@@ -127,3 +127,60 @@ def test_rollout_step_with_split_k_replays_equal_eager():
         assert torch.equal(y, ref[0]) and torch.equal(yd, ref[1]), f"replay {rep}"
         step()  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_packed_rollout_fused_swiglu_and_split_round_replay_equal_eager():
+    """More launch sequences under capture: pack_weight_rollout and the packed FProp at
+    16 and 100 tokens (the decode and weight-sharing kernels), the gate+up FProp whose
+    epilogue applies SwiGLU and the quantisation (its SiLU table copied into LDS with
+    direct loads), and a WGrad with 384 tiles of 256 x 256, whose last half-round runs as
+    a second launch on the 128 x 128 kernel.  Every replay, with eager work between,
+    equals the eager results bit for bit."""
+    dev = torch.device("cuda:0")
+    k, n = 512, 768
+    x16 = jet.quantize_act_1x128(bf16_dev(synth.random_bf16((16, k), seed=51)))
+    x100 = jet.quantize_act_1x128(bf16_dev(synth.random_bf16((100, k), seed=52)))
+    qw, sw = jet.quantize_weight_128x128(bf16_dev(synth.random_bf16((n, k), seed=53, std=0.02)))
+    mg, ng, kg = 512, 2048, 256  # gate+up: I = 1024
+    xg = jet.quantize_act_1x128(bf16_dev(synth.random_bf16((mg, kg), seed=54)))
+    wg = jet.quantize_weight_128x128(bf16_dev(synth.random_bf16((ng, kg), seed=55, std=0.02)))
+    tok, rows, cols = 256, 6144, 4096  # WGrad: dW [6144][4096] over 256 tokens
+    dyt = jet.quantize_act_1x128(bf16_dev(synth.random_bf16((rows, tok), seed=56, std=1e-3)))
+    xt = jet.quantize_act_1x128(bf16_dev(synth.random_bf16((cols, tok), seed=57)))
+    u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+    qwp = torch.empty(n, k, dtype=u8, device=dev)
+    y16, y100 = torch.empty(16, n, dtype=bf, device=dev), torch.empty(100, n, dtype=bf, device=dev)
+    qh, sh = torch.empty(mg, ng // 2, dtype=u8, device=dev), torch.empty(ng // 256, mg, dtype=f32, device=dev)
+    dw = torch.empty(rows, cols, dtype=bf, device=dev)
+
+    def step():
+        jet.pack_weight_rollout(qw, qwp)
+        jet.gemm_fprop_packed(*x16, qwp, sw, y16)
+        jet.gemm_fprop_packed(*x100, qwp, sw, y100)
+        jet.gemm_fprop_swiglu_quant(*xg, *wg, qh, sh)
+        jet.gemm_wgrad(*dyt, *xt, dw)
+
+    outs = (qwp, y16, y100, qh, sh, dw)
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, ref)):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}, output {i}"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
